@@ -1,0 +1,202 @@
+/*
+ * pagedkv.h -- C ABI of libpagedkv: paged KV cache and single-query decode
+ * attention for AMD Instinct MI355X (gfx950).
+ *
+ * What the library does (sources are web pages on vLLM / PagedAttention):
+ *   - The KV cache is split into fixed 16-token blocks that need not be
+ *     contiguous; each sequence owns a block table from logical to physical
+ *     block (explore.n1n.ai, "vLLM 深度解析：PagedAttention 如何让大模型推理更快、
+ *     更省钱", 映射机制详解; ybb.press, "vLLM PagedAttention 大模型推理架构深度
+ *     实战", §2.2).
+ *   - The attention kernel walks ceil(len / 16) table entries of a sequence
+ *     and reads the blocks they name (unionyoga.cn, "vLLM：重塑大模型推理性能的
+ *     关键引擎", PagedAttention section, kernel sketch).
+ *   - Each decode iteration writes the new token's K/V into its block and
+ *     then checks whether the sequence needs a new block (ybb.press, §6).
+ *   - Shared blocks carry reference counts; a sequence about to modify a
+ *     block shared with others copies it first (ybb.press, §2.3).
+ *
+ * Conventions for every call:
+ *   - Return value: PA_OK (0) or a negative pa_status.  On error nothing was
+ *     launched and no state changed; pa_last_error() returns a message
+ *     (thread-local, valid until the next failing call on that thread).
+ *   - Device pointers are caller-owned device memory (for example torch
+ *     tensors); the library never allocates, frees or synchronises device
+ *     memory.  Device calls are asynchronous on `stream` (a hipStream_t passed
+ *     as void*; NULL = the null stream).
+ *   - Arguments are validated on the host before any launch.  Values inside
+ *     device arrays (block ids, slots, context lengths) cannot be checked on
+ *     the host; out-of-range values there are undefined behaviour.
+ *
+ * Cache layout (one K and one V tensor, same shape and dtype):
+ *   cache[num_blocks][num_kv_heads][16][head_dim], row-major, so element
+ *   (block b, kv head g, slot t, dim d) is at ((b*Hkv + g)*16 + t)*D + d and
+ *   one (block, head) tile is 16*D contiguous elements.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1,        /* null pointer, bad size, bad enum value */
+  PA_ERR_UNSUPPORTED = -2,        /* valid but not implemented combination */
+  PA_ERR_NO_BLOCKS = -3,          /* block manager: free pool too small */
+  PA_ERR_UNKNOWN_SEQ = -4,        /* block manager: no such sequence id */
+  PA_ERR_SEQ_EXISTS = -5,         /* block manager: id already in use */
+  PA_ERR_WORKSPACE_TOO_SMALL = -6,
+  PA_ERR_HIP = -7                 /* a HIP runtime call or launch failed */
+} pa_status;
+
+typedef enum {
+  PA_F32 = 0,       /* IEEE binary32 */
+  PA_BF16 = 1,      /* bfloat16 */
+  PA_FP8_E4M3 = 2   /* OCP E4M3 ("e4m3fn"): bias 7, max 448, no inf, NaN 0x7F/0xFF */
+} pa_dtype;
+
+#define PA_BLOCK_SIZE 16
+/* Context positions handled by one work-group of the decode pass. */
+#define PA_PARTITION_TOKENS 512
+
+typedef struct {
+  int32_t num_blocks;    /* physical blocks in each of the K and V caches */
+  int32_t block_size;    /* tokens per block; must be PA_BLOCK_SIZE */
+  int32_t num_kv_heads;  /* Hkv >= 1 */
+  int32_t head_dim;      /* D: 64 or 128 */
+  int32_t cache_dtype;   /* pa_dtype of both caches */
+  float k_scale;         /* PA_FP8_E4M3 only: stored K value = code value * k_scale */
+  float v_scale;         /* PA_FP8_E4M3 only: same for V; both finite and > 0 */
+} pa_cache_desc;
+
+/* Version string of the library build. */
+const char* pa_version(void);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* pa_last_error(void);
+
+/* Bytes of one (K or V) cache tensor described by `c`; 0 if `c` is invalid. */
+size_t pa_cache_bytes(const pa_cache_desc* c);
+
+/*
+ * pa_write_kv -- store new K/V rows into their cache slots (the "write KV
+ * into its block" step of each decode iteration, ybb.press §6).
+ *   k, v          : [num_tokens][num_kv_heads][head_dim] contiguous, dtype
+ *                   src_dtype (device).
+ *   slot_mapping  : int64 [num_tokens] (device); slot = block * 16 + offset;
+ *                   a negative slot skips that row.  Non-negative slots must
+ *                   be distinct and < num_blocks * 16.
+ *   Supported (src_dtype -> cache_dtype): F32 -> F32, BF16 -> BF16 (bit
+ *   copies) and BF16 -> FP8_E4M3 (code = round-to-nearest-even of
+ *   min(|x * fp32(1/scale)|, 448) with x's sign; NaN -> 0x7F).
+ *   Bytes of slots that are not written are left untouched.
+ */
+pa_status pa_write_kv(const pa_cache_desc* c, void* k_cache, void* v_cache,
+                      const void* k, const void* v, int32_t src_dtype,
+                      const int64_t* slot_mapping, int32_t num_tokens,
+                      void* stream);
+
+/*
+ * pa_copy_blocks -- copy-on-write block duplication (ybb.press §2.3).
+ *   pairs : int32 [num_pairs][2] (device), each (src, dst): the whole block
+ *           -- every KV head, all 16 slots -- of both caches is copied byte
+ *           for byte from src to dst.  Destinations must be distinct and none
+ *           may also be a source (the block manager never emits otherwise).
+ */
+pa_status pa_copy_blocks(const pa_cache_desc* c, void* k_cache, void* v_cache,
+                         const int32_t* pairs, int32_t num_pairs, void* stream);
+
+/* Workspace bytes pa_decode needs for this shape (0 when no sequence can
+ * span more than one partition). */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t head_dim, int32_t max_context_len);
+
+/*
+ * pa_decode -- single-query decode attention through block tables.
+ *   For every sequence s < num_seqs and query head h < num_q_heads:
+ *     g = h / (num_q_heads / num_kv_heads)         (contiguous head groups)
+ *     L = context_lens[s]; token t < L lives in block block_tables[s][t/16],
+ *     slot t % 16;
+ *     out[s][h] = sum_t softmax_t(scale * q[s][h] . K[t]) * V[t]
+ *   which is exact attention, computed blockwise with online-softmax
+ *   renormalisation (ybb.press §5.1).  L == 0 gives a zero row.  Only the first
+ *   ceil(L/16) table entries and the first L slots are read.
+ *   q, out       : [num_seqs][num_q_heads][head_dim] contiguous (device).
+ *                  q dtype: F32 with an F32 cache, BF16 with a BF16 or FP8
+ *                  cache; out has q's dtype.  Accumulation is fp32.
+ *   block_tables : int32 [num_seqs][max_blocks_per_seq] (device).
+ *   context_lens : int32 [num_seqs] (device), each in [0, max_context_len].
+ *   max_context_len: host-side upper bound on context_lens, sizes the grid.
+ *   workspace    : device scratch of at least
+ *                  pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
+ *                  max_context_len) bytes (may be NULL when that is 0); it
+ *                  holds per-partition partial results of this call only.
+ *   Contexts longer than PA_PARTITION_TOKENS are split into partitions whose
+ *   partial (max, sum, output) are merged by a log-sum-exp reduction.
+ */
+pa_status pa_decode(const pa_cache_desc* c, const void* k_cache,
+                    const void* v_cache, const void* q, int32_t q_dtype,
+                    void* out, const int32_t* block_tables,
+                    int32_t max_blocks_per_seq, const int32_t* context_lens,
+                    int32_t max_context_len, int32_t num_seqs,
+                    int32_t num_q_heads, float scale, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Host block manager (plain host memory, no GPU calls).  One owner; not
+ * thread-safe.  Policy: the free pool is a FIFO queue initialised from
+ * `free_order` (a permutation of 0..num_blocks-1; NULL = 0,1,2,...);
+ * allocation pops the front and a block whose reference count drops to zero
+ * is pushed to the back, a freed sequence releasing its blocks in logical
+ * order.  Appending token p to a sequence: if p % 16 == 0 a fresh block is
+ * appended to its table; otherwise, if its last block is shared (count > 1),
+ * that block is replaced by a fresh one and the pair (old, new) is reported
+ * for pa_copy_blocks.  Every mutating call is all-or-nothing.
+ * ------------------------------------------------------------------------- */
+typedef struct pa_bm pa_bm;
+
+/* NULL on invalid arguments (see pa_last_error). */
+pa_bm* pa_bm_create(int32_t num_blocks, int32_t block_size,
+                    const int32_t* free_order);
+void pa_bm_destroy(pa_bm* bm);
+
+pa_status pa_bm_add_seq(pa_bm* bm, int64_t seq_id);
+/* child shares all of parent's blocks (each gains one reference). */
+pa_status pa_bm_fork(pa_bm* bm, int64_t parent_id, int64_t child_id);
+/* Append one token: *slot receives its cache slot; *cow_src / *cow_dst
+ * receive the copy pair, or -1 / -1 when no copy is needed. */
+pa_status pa_bm_append_slot(pa_bm* bm, int64_t seq_id, int64_t* slot,
+                            int32_t* cow_src, int32_t* cow_dst);
+/* Append n >= 0 tokens: slots[n]; at most one copy pair (the first token). */
+pa_status pa_bm_append_tokens(pa_bm* bm, int64_t seq_id, int32_t n,
+                              int64_t* slots, int32_t* cow_src,
+                              int32_t* cow_dst);
+/* One decode step for a batch: append one token to each of seq_ids[0..n-1],
+ * in order.  slots[n] receive the slots; cow_pairs[2*k], cow_pairs[2*k+1]
+ * the k-th copy pair (room for n pairs); *num_pairs their count.  All or
+ * nothing across the whole batch. */
+pa_status pa_bm_append_batch(pa_bm* bm, const int64_t* seq_ids, int32_t n,
+                             int64_t* slots, int32_t* cow_pairs,
+                             int32_t* num_pairs);
+pa_status pa_bm_free_seq(pa_bm* bm, int64_t seq_id);
+
+int32_t pa_bm_num_free(const pa_bm* bm);
+/* Reference count of `block`, or -1 if out of range. */
+int32_t pa_bm_refcount(const pa_bm* bm, int32_t block);
+/* Context length of a sequence in *len. */
+pa_status pa_bm_length(const pa_bm* bm, int64_t seq_id, int32_t* len);
+/* Pack tables of seq_ids[0..n-1]: block_tables[n][cap] padded with -1,
+ * context_lens[n].  Host memory. */
+pa_status pa_bm_pack(const pa_bm* bm, const int64_t* seq_ids, int32_t n,
+                     int32_t* block_tables, int32_t cap, int32_t* context_lens);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

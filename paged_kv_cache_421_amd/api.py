@@ -1,0 +1,211 @@
+"""Torch-facing wrappers of the C ABI: argument marshalling only.
+
+Device tensors must be contiguous and on the current HIP device; calls are
+asynchronous on the current torch stream unless ``stream`` is given.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+from ._lib import CacheDescC, PagedKVError, check, lib
+
+BLOCK_SIZE = 16
+PARTITION_TOKENS = 512
+
+PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
+_DTYPES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.uint8: PA_FP8_E4M3,
+           torch.float8_e4m3fn: PA_FP8_E4M3}
+_NAMES = {"f32": PA_F32, "bf16": PA_BF16, "fp8": PA_FP8_E4M3}
+
+
+def dtype_code(x) -> int:
+    """pa_dtype of a torch dtype or of "f32" / "bf16" / "fp8"."""
+    if isinstance(x, str):
+        return _NAMES[x]
+    return _DTYPES[x]
+
+
+class CacheDesc:
+    """pa_cache_desc: shape and format of a pair of K/V caches, each
+    ``[num_blocks, num_kv_heads, 16, head_dim]``."""
+
+    def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, dtype,
+                 k_scale: float = 1.0, v_scale: float = 1.0):
+        self.c = CacheDescC(int(num_blocks), BLOCK_SIZE, int(num_kv_heads), int(head_dim),
+                            dtype_code(dtype), float(k_scale), float(v_scale))
+
+    @property
+    def shape(self) -> Tuple[int, int, int, int]:
+        return (self.c.num_blocks, self.c.num_kv_heads, BLOCK_SIZE, self.c.head_dim)
+
+    @property
+    def torch_dtype(self):
+        return {PA_F32: torch.float32, PA_BF16: torch.bfloat16,
+                PA_FP8_E4M3: torch.uint8}[self.c.cache_dtype]
+
+    def cache_bytes(self) -> int:
+        return int(lib.pa_cache_bytes(ctypes.byref(self.c)))
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str) -> ctypes.c_void_p:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def write_kv(desc: CacheDesc, k_cache: torch.Tensor, v_cache: torch.Tensor,
+             k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+             stream=None) -> None:
+    """pa_write_kv: rows k[i], v[i] ([Hkv, D]) into slot slot_mapping[i]."""
+    if slot_mapping.dtype != torch.int64:
+        raise ValueError("slot_mapping must be int64")
+    if k.shape != v.shape or k.dtype != v.dtype:
+        raise ValueError("k and v must match")
+    T = k.shape[0]
+    if tuple(k.shape[1:]) != (desc.c.num_kv_heads, desc.c.head_dim) or slot_mapping.numel() != T:
+        raise ValueError("k/v must be [T, Hkv, D] and slot_mapping [T]")
+    check(lib.pa_write_kv(ctypes.byref(desc.c), _dev(k_cache, "k_cache"),
+                          _dev(v_cache, "v_cache"), _dev(k, "k"), _dev(v, "v"),
+                          dtype_code(k.dtype), _dev(slot_mapping, "slot_mapping"), T,
+                          _stream(stream)))
+
+
+def copy_blocks(desc: CacheDesc, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                pairs: torch.Tensor, stream=None) -> None:
+    """pa_copy_blocks: pairs int32 [n, 2] of (src, dst) blocks."""
+    if pairs.dtype != torch.int32:
+        raise ValueError("pairs must be int32")
+    n = pairs.numel() // 2
+    if n == 0:
+        return
+    check(lib.pa_copy_blocks(ctypes.byref(desc.c), _dev(k_cache, "k_cache"),
+                             _dev(v_cache, "v_cache"), _dev(pairs, "pairs"), n,
+                             _stream(stream)))
+
+
+def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
+                           max_context_len: int) -> int:
+    return int(lib.pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len))
+
+
+def decode(desc: CacheDesc, k_cache: torch.Tensor, v_cache: torch.Tensor, q: torch.Tensor,
+           out: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+           max_context_len: int, scale: float, workspace: Optional[torch.Tensor] = None,
+           stream=None) -> torch.Tensor:
+    """pa_decode: out[s, h] = softmax(scale q[s,h] K_s^T) V_s through block tables."""
+    B, Hq, D = q.shape
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must have q's shape and dtype")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
+        raise ValueError("block_tables must be [B, max_blocks] and context_lens [B]")
+    ws_ptr, ws_bytes = ctypes.c_void_p(0), 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    check(lib.pa_decode(ctypes.byref(desc.c), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                        _dev(q, "q"), dtype_code(q.dtype), _dev(out, "out"),
+                        _dev(block_tables, "block_tables"), block_tables.shape[1],
+                        _dev(context_lens, "context_lens"), int(max_context_len), B, Hq,
+                        float(scale), ws_ptr, ws_bytes, _stream(stream)))
+    return out
+
+
+def _ptr(a: np.ndarray) -> ctypes.c_void_p:
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+class BlockManager:
+    """Host block manager (pa_bm_*): FIFO free pool, refcounts, copy-on-write."""
+
+    def __init__(self, num_blocks: int, free_order: Optional[Sequence[int]] = None):
+        self._order = None
+        ptr = ctypes.c_void_p(0)
+        if free_order is not None:
+            self._order = np.ascontiguousarray(free_order, dtype=np.int32)
+            ptr = _ptr(self._order)
+        h = lib.pa_bm_create(int(num_blocks), BLOCK_SIZE, ptr)
+        if not h:
+            raise PagedKVError(-1, lib.pa_last_error().decode())
+        self._h = ctypes.c_void_p(h)
+        self.num_blocks = int(num_blocks)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            lib.pa_bm_destroy(h)
+            self._h = None
+
+    def add_seq(self, seq: int) -> None:
+        check(lib.pa_bm_add_seq(self._h, int(seq)))
+
+    def fork(self, parent: int, child: int) -> None:
+        check(lib.pa_bm_fork(self._h, int(parent), int(child)))
+
+    def append_slot(self, seq: int):
+        slot = ctypes.c_int64()
+        src, dst = ctypes.c_int32(), ctypes.c_int32()
+        check(lib.pa_bm_append_slot(self._h, int(seq), ctypes.byref(slot), ctypes.byref(src),
+                                    ctypes.byref(dst)))
+        return slot.value, (None if src.value < 0 else (src.value, dst.value))
+
+    def append_tokens(self, seq: int, n: int):
+        slots = np.empty(max(int(n), 1), dtype=np.int64)
+        src, dst = ctypes.c_int32(), ctypes.c_int32()
+        check(lib.pa_bm_append_tokens(self._h, int(seq), int(n), _ptr(slots), ctypes.byref(src),
+                                      ctypes.byref(dst)))
+        return slots[:int(n)], (None if src.value < 0 else (src.value, dst.value))
+
+    def append_batch(self, seq_ids: np.ndarray, slots: Optional[np.ndarray] = None,
+                     pairs: Optional[np.ndarray] = None):
+        """One token for each sequence; returns (slots int64 [n], pairs int32 [k, 2]).
+        ``slots``/``pairs`` may be preallocated (e.g. pinned) host arrays."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        n = len(ids)
+        if slots is None:
+            slots = np.empty(n, dtype=np.int64)
+        if pairs is None:
+            pairs = np.empty((max(n, 1), 2), dtype=np.int32)
+        npairs = ctypes.c_int32()
+        check(lib.pa_bm_append_batch(self._h, _ptr(ids), n, _ptr(slots), _ptr(pairs),
+                                     ctypes.byref(npairs)))
+        return slots[:n], pairs[:npairs.value]
+
+    def free_seq(self, seq: int) -> None:
+        check(lib.pa_bm_free_seq(self._h, int(seq)))
+
+    def num_free(self) -> int:
+        return int(lib.pa_bm_num_free(self._h))
+
+    def refcount(self, block: int) -> int:
+        return int(lib.pa_bm_refcount(self._h, int(block)))
+
+    def length(self, seq: int) -> int:
+        n = ctypes.c_int32()
+        check(lib.pa_bm_length(self._h, int(seq), ctypes.byref(n)))
+        return n.value
+
+    def pack(self, seq_ids, cap: int, block_tables: Optional[np.ndarray] = None,
+             context_lens: Optional[np.ndarray] = None):
+        """block_tables int32 [n, cap] (pad -1), context_lens int32 [n]."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        n = len(ids)
+        if block_tables is None:
+            block_tables = np.empty((n, cap), dtype=np.int32)
+        if context_lens is None:
+            context_lens = np.empty(n, dtype=np.int32)
+        check(lib.pa_bm_pack(self._h, _ptr(ids), n, _ptr(block_tables), int(cap),
+                             _ptr(context_lens)))
+        return block_tables, context_lens

@@ -1,0 +1,286 @@
+// Host block manager: FIFO free pool, per-block reference counts,
+// append-slot allocation with copy-on-write of a shared partial last block.
+//
+// Blocks are allocated only when a sequence needs one and are returned as
+// soon as their last user goes away (ybb.press, "vLLM PagedAttention
+// 大模型推理架构深度实战", §2.2); every decode iteration checks whether the
+// sequence needs a new block (§6); shared blocks are reference counted and
+// a sequence about to modify a shared block copies it first (§2.3).
+//
+// The queue discipline, the choice of which sharer copies (the one that
+// appends, while the block is still shared) and the all-or-nothing rule make
+// the tables reproducible; they are readings, the pages fix none of them.
+#include <cstdint>
+#include <deque>
+#include <new>
+#include <unordered_map>
+#include <unordered_set>
+#include <vector>
+
+#include "pagedkv.h"
+#include "status.h"
+
+using pagedkv::fail;
+
+namespace {
+
+constexpr int32_t kBlock = PA_BLOCK_SIZE;
+
+struct Seq {
+  std::vector<int32_t> table;  // logical -> physical block
+  int32_t len = 0;             // tokens appended so far
+};
+
+}  // namespace
+
+struct pa_bm {
+  int32_t num_blocks = 0;
+  std::deque<int32_t> free_q;
+  std::vector<int32_t> ref;
+  std::unordered_map<int64_t, Seq> seqs;
+
+  // Blocks an append of n tokens to `s` takes from the pool.
+  int64_t blocks_needed(const Seq& s, int64_t n) const {
+    if (n <= 0) return 0;
+    const int64_t p = s.len;
+    int64_t fresh = (p + n + kBlock - 1) / kBlock - (p + kBlock - 1) / kBlock;
+    int64_t cow = (p % kBlock != 0 && ref[s.table.back()] > 1) ? 1 : 0;
+    return fresh + cow;
+  }
+
+  int32_t pop() {
+    int32_t b = free_q.front();
+    free_q.pop_front();
+    ref[b] = 1;
+    return b;
+  }
+
+  // Appends one token; the caller has checked that blocks are available.
+  int64_t append_one(Seq& s, int32_t* cow_src, int32_t* cow_dst) {
+    const int32_t p = s.len;
+    if (p % kBlock == 0) {
+      s.table.push_back(pop());
+    } else if (ref[s.table.back()] > 1) {
+      const int32_t old = s.table.back();
+      const int32_t b = pop();
+      ref[old] -= 1;
+      s.table.back() = b;
+      *cow_src = old;
+      *cow_dst = b;
+    }
+    s.len = p + 1;
+    return static_cast<int64_t>(s.table[p / kBlock]) * kBlock + p % kBlock;
+  }
+};
+
+extern "C" {
+
+pa_bm* pa_bm_create(int32_t num_blocks, int32_t block_size,
+                    const int32_t* free_order) {
+  if (num_blocks < 0) {
+    fail(PA_ERR_INVALID_ARG, "pa_bm_create: num_blocks %d < 0", num_blocks);
+    return nullptr;
+  }
+  if (block_size != kBlock) {
+    fail(PA_ERR_UNSUPPORTED, "pa_bm_create: block_size %d (only %d)",
+         block_size, kBlock);
+    return nullptr;
+  }
+  pa_bm* bm = new (std::nothrow) pa_bm;
+  if (!bm) {
+    fail(PA_ERR_INVALID_ARG, "pa_bm_create: out of host memory");
+    return nullptr;
+  }
+  bm->num_blocks = num_blocks;
+  bm->ref.assign(num_blocks, 0);
+  if (free_order) {
+    std::vector<char> seen(num_blocks, 0);
+    for (int32_t i = 0; i < num_blocks; ++i) {
+      const int32_t b = free_order[i];
+      if (b < 0 || b >= num_blocks || seen[b]) {
+        delete bm;
+        fail(PA_ERR_INVALID_ARG,
+             "pa_bm_create: free_order is not a permutation (entry %d = %d)",
+             i, b);
+        return nullptr;
+      }
+      seen[b] = 1;
+      bm->free_q.push_back(b);
+    }
+  } else {
+    for (int32_t i = 0; i < num_blocks; ++i) bm->free_q.push_back(i);
+  }
+  return bm;
+}
+
+void pa_bm_destroy(pa_bm* bm) { delete bm; }
+
+pa_status pa_bm_add_seq(pa_bm* bm, int64_t seq_id) {
+  if (!bm) return fail(PA_ERR_INVALID_ARG, "pa_bm_add_seq: null manager");
+  if (bm->seqs.count(seq_id))
+    return fail(PA_ERR_SEQ_EXISTS, "pa_bm_add_seq: sequence %lld exists",
+                (long long)seq_id);
+  bm->seqs.emplace(seq_id, Seq{});
+  return PA_OK;
+}
+
+pa_status pa_bm_fork(pa_bm* bm, int64_t parent_id, int64_t child_id) {
+  if (!bm) return fail(PA_ERR_INVALID_ARG, "pa_bm_fork: null manager");
+  auto it = bm->seqs.find(parent_id);
+  if (it == bm->seqs.end())
+    return fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_fork: unknown parent %lld",
+                (long long)parent_id);
+  if (bm->seqs.count(child_id))
+    return fail(PA_ERR_SEQ_EXISTS, "pa_bm_fork: child %lld exists",
+                (long long)child_id);
+  Seq child = it->second;  // copy before emplace may rehash
+  for (int32_t b : child.table) bm->ref[b] += 1;
+  bm->seqs.emplace(child_id, std::move(child));
+  return PA_OK;
+}
+
+pa_status pa_bm_append_tokens(pa_bm* bm, int64_t seq_id, int32_t n,
+                              int64_t* slots, int32_t* cow_src,
+                              int32_t* cow_dst) {
+  if (!bm || !cow_src || !cow_dst || (n > 0 && !slots))
+    return fail(PA_ERR_INVALID_ARG, "pa_bm_append_tokens: null argument");
+  if (n < 0)
+    return fail(PA_ERR_INVALID_ARG, "pa_bm_append_tokens: n = %d < 0", n);
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end())
+    return fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_append_tokens: unknown sequence %lld",
+                (long long)seq_id);
+  Seq& s = it->second;
+  if (static_cast<int64_t>(s.len) + n > INT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "pa_bm_append_tokens: length overflow");
+  const int64_t need = bm->blocks_needed(s, n);
+  if (need > static_cast<int64_t>(bm->free_q.size()))
+    return fail(PA_ERR_NO_BLOCKS,
+                "pa_bm_append_tokens: sequence %lld needs %lld blocks, %zu free",
+                (long long)seq_id, (long long)need, bm->free_q.size());
+  *cow_src = -1;
+  *cow_dst = -1;
+  for (int32_t i = 0; i < n; ++i) slots[i] = bm->append_one(s, cow_src, cow_dst);
+  return PA_OK;
+}
+
+pa_status pa_bm_append_slot(pa_bm* bm, int64_t seq_id, int64_t* slot,
+                            int32_t* cow_src, int32_t* cow_dst) {
+  if (!slot) return fail(PA_ERR_INVALID_ARG, "pa_bm_append_slot: null slot");
+  return pa_bm_append_tokens(bm, seq_id, 1, slot, cow_src, cow_dst);
+}
+
+pa_status pa_bm_append_batch(pa_bm* bm, const int64_t* seq_ids, int32_t n,
+                             int64_t* slots, int32_t* cow_pairs,
+                             int32_t* num_pairs) {
+  if (!bm || !num_pairs || (n > 0 && (!seq_ids || !slots || !cow_pairs)))
+    return fail(PA_ERR_INVALID_ARG, "pa_bm_append_batch: null argument");
+  if (n < 0) return fail(PA_ERR_INVALID_ARG, "pa_bm_append_batch: n < 0");
+  // Validate everything and count blocks first: all or nothing.
+  std::vector<Seq*> ss(n);
+  std::unordered_set<int64_t> seen;
+  seen.reserve(static_cast<size_t>(n) * 2);
+  int64_t need = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = bm->seqs.find(seq_ids[i]);
+    if (it == bm->seqs.end())
+      return fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_append_batch: unknown sequence %lld",
+                  (long long)seq_ids[i]);
+    if (!seen.insert(seq_ids[i]).second)
+      return fail(PA_ERR_INVALID_ARG, "pa_bm_append_batch: sequence %lld listed twice",
+                  (long long)seq_ids[i]);
+    ss[i] = &it->second;
+    if (ss[i]->len == INT32_MAX)
+      return fail(PA_ERR_INVALID_ARG, "pa_bm_append_batch: length overflow");
+  }
+  // Copies caused by earlier members of the batch lower the counts later
+  // members see, so count in order on a scratch copy of the touched counts.
+  std::unordered_map<int32_t, int32_t> ref_delta;
+  for (int32_t i = 0; i < n; ++i) {
+    const Seq& s = *ss[i];
+    if (s.len % kBlock == 0) {
+      need += 1;
+    } else {
+      const int32_t last = s.table.back();
+      const int32_t r = bm->ref[last] + ref_delta[last];
+      if (r > 1) {
+        need += 1;
+        ref_delta[last] -= 1;
+      }
+    }
+  }
+  if (need > static_cast<int64_t>(bm->free_q.size()))
+    return fail(PA_ERR_NO_BLOCKS, "pa_bm_append_batch: batch needs %lld blocks, %zu free",
+                (long long)need, bm->free_q.size());
+  int32_t np = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t src = -1, dst = -1;
+    slots[i] = bm->append_one(*ss[i], &src, &dst);
+    if (src >= 0) {
+      cow_pairs[2 * np] = src;
+      cow_pairs[2 * np + 1] = dst;
+      ++np;
+    }
+  }
+  *num_pairs = np;
+  return PA_OK;
+}
+
+pa_status pa_bm_free_seq(pa_bm* bm, int64_t seq_id) {
+  if (!bm) return fail(PA_ERR_INVALID_ARG, "pa_bm_free_seq: null manager");
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end())
+    return fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_free_seq: unknown sequence %lld",
+                (long long)seq_id);
+  for (int32_t b : it->second.table) {
+    if (--bm->ref[b] == 0) bm->free_q.push_back(b);
+  }
+  bm->seqs.erase(it);
+  return PA_OK;
+}
+
+int32_t pa_bm_num_free(const pa_bm* bm) {
+  return bm ? static_cast<int32_t>(bm->free_q.size()) : -1;
+}
+
+int32_t pa_bm_refcount(const pa_bm* bm, int32_t block) {
+  if (!bm || block < 0 || block >= bm->num_blocks) return -1;
+  return bm->ref[block];
+}
+
+pa_status pa_bm_length(const pa_bm* bm, int64_t seq_id, int32_t* len) {
+  if (!bm || !len) return fail(PA_ERR_INVALID_ARG, "pa_bm_length: null argument");
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end())
+    return fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_length: unknown sequence %lld",
+                (long long)seq_id);
+  *len = it->second.len;
+  return PA_OK;
+}
+
+pa_status pa_bm_pack(const pa_bm* bm, const int64_t* seq_ids, int32_t n,
+                     int32_t* block_tables, int32_t cap, int32_t* context_lens) {
+  if (!bm || (n > 0 && (!seq_ids || !block_tables || !context_lens)))
+    return fail(PA_ERR_INVALID_ARG, "pa_bm_pack: null argument");
+  if (n < 0 || cap < 0) return fail(PA_ERR_INVALID_ARG, "pa_bm_pack: negative size");
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = bm->seqs.find(seq_ids[i]);
+    if (it == bm->seqs.end())
+      return fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_pack: unknown sequence %lld",
+                  (long long)seq_ids[i]);
+    if (static_cast<int64_t>(it->second.table.size()) > cap)
+      return fail(PA_ERR_INVALID_ARG, "pa_bm_pack: sequence %lld has %zu blocks > cap %d",
+                  (long long)seq_ids[i], it->second.table.size(), cap);
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const Seq& s = bm->seqs.find(seq_ids[i])->second;
+    int32_t* row = block_tables + static_cast<int64_t>(i) * cap;
+    const int32_t m = static_cast<int32_t>(s.table.size());
+    for (int32_t j = 0; j < m; ++j) row[j] = s.table[j];
+    for (int32_t j = m; j < cap; ++j) row[j] = -1;
+    context_lens[i] = s.len;
+  }
+  return PA_OK;
+}
+
+}  // extern "C"
