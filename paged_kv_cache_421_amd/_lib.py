@@ -63,7 +63,7 @@ class PagedKVError(RuntimeError):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} not found: build it with `python -m paged_kv_cache_421_amd.build`")
+            f"{LIB_PATH} not found: build it with `python paged_kv_cache_421_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)

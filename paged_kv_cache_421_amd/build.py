@@ -3,7 +3,7 @@
 Host-only C++ (the block manager, error plumbing) is compiled with g++;
 the HIP sources with hipcc for gfx950; hipcc links the shared library.
 
-    python -m paged_kv_cache_421_amd.build [--verbose]
+    python paged_kv_cache_421_amd/build.py [--verbose]
 """
 from __future__ import annotations
 
