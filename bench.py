@@ -95,8 +95,8 @@ def cpu_baseline(w, budget_s=10.0):
     slots = np.concatenate([per[s] for s in range(w.B)])
     assert len(slots) == len(w.row_seq) and np.all(w.row_pos == np.arange(len(slots)) -
                                                   np.repeat(starts, w.lens))
-    shape = (w.num_blocks, w.Hkv, 16, w.D)
-    kc, vc = oracle.write_kv(np.zeros(shape, np.uint16), np.zeros(shape, np.uint16),
+    kc, vc = oracle.write_kv(np.zeros((w.num_blocks, w.Hkv, 16, w.D), np.uint16),
+                             np.zeros((w.num_blocks, w.Hkv, w.D, 16), np.uint16),
                              w.k_rows, w.v_rows, slots, "bf16", "bf16")
     cap = max(-(-int(L) // 16) for L in w.lens)
     bt, cl = bm.pack(list(range(w.B)), cap)
@@ -145,7 +145,6 @@ def main():
     w = workloads.config3()
     B, Hq, Hkv, D = w.B, w.Hq, w.Hkv, w.D
     desc = pk.CacheDesc(w.num_blocks, Hkv, D, "bf16")
-    shape = desc.shape
 
     # ---- caches of layer 0 through the library's own write path; the other
     # layers get copies (distinct HBM, same contents)
@@ -157,8 +156,8 @@ def main():
         assert pair is None
         per.append(sl)
     slots = torch.from_numpy(np.concatenate(per)).to(dev)
-    kc = [torch.zeros(shape, dtype=torch.bfloat16, device=dev) for _ in range(NL)]
-    vc = [torch.zeros(shape, dtype=torch.bfloat16, device=dev) for _ in range(NL)]
+    kc = [torch.zeros(desc.shape, dtype=torch.bfloat16, device=dev) for _ in range(NL)]
+    vc = [torch.zeros(desc.v_shape, dtype=torch.bfloat16, device=dev) for _ in range(NL)]
     k_rows = torch.from_numpy(w.k_rows.view(np.int16)).to(dev).view(torch.bfloat16)
     v_rows = torch.from_numpy(w.v_rows.view(np.int16)).to(dev).view(torch.bfloat16)
     pk.write_kv(desc, kc[0], vc[0], k_rows, v_rows, slots)
@@ -180,8 +179,7 @@ def main():
     total = args.steps + args.warmup
     max_len_final = int(w.lens.max()) + total
     cap = -(-max_len_final // 16)
-    ws_bytes = pk.decode_workspace_bytes(B, Hq, D, max_len_final)
-    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    workspace = pk.new_decode_workspace(desc, B, Hq, max_len_final, dev)
 
     # ---- pinned host staging, triple-buffered against the running GPU
     NBUF = 3

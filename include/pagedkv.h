@@ -28,10 +28,14 @@
  *     device arrays (block ids, slots, context lengths) cannot be checked on
  *     the host; out-of-range values there are undefined behaviour.
  *
- * Cache layout (one K and one V tensor, same shape and dtype):
- *   cache[num_blocks][num_kv_heads][16][head_dim], row-major, so element
- *   (block b, kv head g, slot t, dim d) is at ((b*Hkv + g)*16 + t)*D + d and
- *   one (block, head) tile is 16*D contiguous elements.
+ * Cache layout (one K and one V tensor, same dtype and size):
+ *   K: k_cache[num_blocks][num_kv_heads][16][head_dim] -- element (block b,
+ *      kv head g, slot t, dim d) at ((b*Hkv + g)*16 + t)*D + d;
+ *   V: v_cache[num_blocks][num_kv_heads][head_dim][16] -- element (b, g, t, d)
+ *      at ((b*Hkv + g)*D + d)*16 + t.
+ *   Either way one (block, head) tile is 16*D contiguous elements.  The V
+ *   tile is stored dims-major so that it is directly the operand of the
+ *   matrix instruction that forms P.V on gfx950.
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H
@@ -61,7 +65,7 @@ typedef enum {
 } pa_dtype;
 
 #define PA_BLOCK_SIZE 16
-/* Context positions handled by one work-group of the decode pass. */
+/* Context positions per partition of the general (fp32) decode path. */
 #define PA_PARTITION_TOKENS 512
 
 typedef struct {
@@ -111,10 +115,25 @@ pa_status pa_write_kv(const pa_cache_desc* c, void* k_cache, void* v_cache,
 pa_status pa_copy_blocks(const pa_cache_desc* c, void* k_cache, void* v_cache,
                          const int32_t* pairs, int32_t num_pairs, void* stream);
 
-/* Workspace bytes pa_decode needs for this shape (0 when no sequence can
- * span more than one partition). */
-size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
-                                 int32_t head_dim, int32_t max_context_len);
+/*
+ * Workspace bytes pa_decode needs for this cache and batch shape; 0 if the
+ * arguments are invalid or no workspace is needed.  The size depends on the
+ * decode path the shape takes (and, for the bf16 / fp8 path, on the number
+ * of compute units of the current device), not on the context lengths.
+ */
+size_t pa_decode_workspace_bytes(const pa_cache_desc* c, int32_t num_seqs,
+                                 int32_t num_q_heads, int32_t max_context_len);
+
+/*
+ * pa_decode_workspace_init -- zero-fill `workspace_bytes` bytes of a decode
+ * workspace on `stream` (a plain fill kernel, so it may be captured in a
+ * graph).  A workspace must be zero-filled once before its first pa_decode
+ * (this call, or any other zero fill such as torch.zeros); every pa_decode
+ * that completes leaves it zero-filled again.  workspace must be 4-byte
+ * aligned.
+ */
+pa_status pa_decode_workspace_init(void* workspace, size_t workspace_bytes,
+                                   void* stream);
 
 /*
  * pa_decode -- single-query decode attention through block tables.
@@ -133,11 +152,16 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  *   context_lens : int32 [num_seqs] (device), each in [0, max_context_len].
  *   max_context_len: host-side upper bound on context_lens, sizes the grid.
  *   workspace    : device scratch of at least
- *                  pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
- *                  max_context_len) bytes (may be NULL when that is 0); it
- *                  holds per-partition partial results of this call only.
- *   Contexts longer than PA_PARTITION_TOKENS are split into partitions whose
- *   partial (max, sum, output) are merged by a log-sum-exp reduction.
+ *                  pa_decode_workspace_bytes(c, num_seqs, num_q_heads,
+ *                  max_context_len) bytes, 16-byte aligned, zero-filled
+ *                  before its first use (pa_decode_workspace_init); may be
+ *                  NULL when that size is 0.  It holds partial results and
+ *                  arrival counters of one call at a time: calls that may
+ *                  overlap (different streams) need separate workspaces.
+ *   A context is processed in pieces whose partial (max, sum, output) are
+ *   merged by the log-sum-exp rule: with a bf16 or fp8 cache, head_dim 64
+ *   or 128 and G <= 8, pieces are equal shares of the whole batch's KV
+ *   tiles; otherwise pieces are PA_PARTITION_TOKENS-token partitions.
  */
 pa_status pa_decode(const pa_cache_desc* c, const void* k_cache,
                     const void* v_cache, const void* q, int32_t q_dtype,

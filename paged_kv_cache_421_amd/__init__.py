@@ -8,8 +8,10 @@ from __future__ import annotations
 
 from ._lib import LIB_PATH, PagedKVError, lib
 from .api import (BLOCK_SIZE, PARTITION_TOKENS, BlockManager, CacheDesc, copy_blocks,
-                  decode, decode_workspace_bytes, dtype_code, write_kv)
+                  decode, decode_workspace_bytes, decode_workspace_init, dtype_code,
+                  new_decode_workspace, write_kv)
 
 __all__ = ["LIB_PATH", "PagedKVError", "lib", "BLOCK_SIZE", "PARTITION_TOKENS",
            "BlockManager", "CacheDesc", "copy_blocks", "decode",
-           "decode_workspace_bytes", "dtype_code", "write_kv"]
+           "decode_workspace_bytes", "decode_workspace_init", "dtype_code",
+           "new_decode_workspace", "write_kv"]

@@ -30,7 +30,8 @@ SIGNATURES = {
     "pa_cache_bytes": (c_sz, [P_desc]),
     "pa_write_kv": (c_i32, [P_desc, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_vp]),
     "pa_copy_blocks": (c_i32, [P_desc, c_vp, c_vp, c_vp, c_i32, c_vp]),
-    "pa_decode_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32]),
+    "pa_decode_workspace_bytes": (c_sz, [P_desc, c_i32, c_i32, c_i32]),
+    "pa_decode_workspace_init": (c_i32, [c_vp, c_sz, c_vp]),
     "pa_decode": (c_i32, [P_desc, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_vp, c_i32,
                           c_i32, c_i32, c_f32, c_vp, c_sz, c_vp]),
     "pa_bm_create": (c_vp, [c_i32, c_i32, c_vp]),

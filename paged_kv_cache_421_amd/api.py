@@ -30,8 +30,9 @@ def dtype_code(x) -> int:
 
 
 class CacheDesc:
-    """pa_cache_desc: shape and format of a pair of K/V caches, each
-    ``[num_blocks, num_kv_heads, 16, head_dim]``."""
+    """pa_cache_desc: shape and format of a pair of K/V caches: K is
+    ``[num_blocks, num_kv_heads, 16, head_dim]`` (token-major tiles), V is
+    ``[num_blocks, num_kv_heads, head_dim, 16]`` (dims-major tiles)."""
 
     def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, dtype,
                  k_scale: float = 1.0, v_scale: float = 1.0):
@@ -40,7 +41,13 @@ class CacheDesc:
 
     @property
     def shape(self) -> Tuple[int, int, int, int]:
+        """Shape of the K cache."""
         return (self.c.num_blocks, self.c.num_kv_heads, BLOCK_SIZE, self.c.head_dim)
+
+    @property
+    def v_shape(self) -> Tuple[int, int, int, int]:
+        """Shape of the V cache."""
+        return (self.c.num_blocks, self.c.num_kv_heads, self.c.head_dim, BLOCK_SIZE)
 
     @property
     def torch_dtype(self):
@@ -95,16 +102,40 @@ def copy_blocks(desc: CacheDesc, k_cache: torch.Tensor, v_cache: torch.Tensor,
                              _stream(stream)))
 
 
-def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
+def decode_workspace_bytes(desc: CacheDesc, num_seqs: int, num_q_heads: int,
                            max_context_len: int) -> int:
-    return int(lib.pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len))
+    """pa_decode_workspace_bytes: scratch bytes pa_decode needs for this shape."""
+    return int(lib.pa_decode_workspace_bytes(ctypes.byref(desc.c), int(num_seqs),
+                                             int(num_q_heads), int(max_context_len)))
+
+
+def decode_workspace_init(workspace: torch.Tensor, stream=None) -> None:
+    """pa_decode_workspace_init: zero-fill a workspace before its first use."""
+    check(lib.pa_decode_workspace_init(_dev(workspace, "workspace"),
+                                       workspace.numel() * workspace.element_size(),
+                                       _stream(stream)))
+
+
+def new_decode_workspace(desc: CacheDesc, num_seqs: int, num_q_heads: int,
+                         max_context_len: int, device=None) -> torch.Tensor:
+    """A zero-filled uint8 device tensor of pa_decode_workspace_bytes bytes
+    (at least one byte), ready for pa_decode."""
+    n = decode_workspace_bytes(desc, num_seqs, num_q_heads, max_context_len)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=device or "cuda")
+    decode_workspace_init(ws)
+    return ws
 
 
 def decode(desc: CacheDesc, k_cache: torch.Tensor, v_cache: torch.Tensor, q: torch.Tensor,
            out: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
            max_context_len: int, scale: float, workspace: Optional[torch.Tensor] = None,
            stream=None) -> torch.Tensor:
-    """pa_decode: out[s, h] = softmax(scale q[s,h] K_s^T) V_s through block tables."""
+    """pa_decode: out[s, h] = softmax(scale q[s,h] K_s^T) V_s through block tables.
+
+    ``workspace`` is a zero-filled device buffer of at least
+    ``decode_workspace_bytes`` bytes (``new_decode_workspace``), reusable by
+    later calls on the same stream; if None, a fresh one is allocated for
+    this call."""
     B, Hq, D = q.shape
     if out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("out must have q's shape and dtype")
@@ -112,9 +143,10 @@ def decode(desc: CacheDesc, k_cache: torch.Tensor, v_cache: torch.Tensor, q: tor
         raise ValueError("block_tables and context_lens must be int32")
     if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
         raise ValueError("block_tables must be [B, max_blocks] and context_lens [B]")
-    ws_ptr, ws_bytes = ctypes.c_void_p(0), 0
-    if workspace is not None:
-        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    if workspace is None:
+        workspace = new_decode_workspace(desc, B, Hq, max_context_len, q.device)
+    ws_ptr = _dev(workspace, "workspace")
+    ws_bytes = workspace.numel() * workspace.element_size()
     check(lib.pa_decode(ctypes.byref(desc.c), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
                         _dev(q, "q"), dtype_code(q.dtype), _dev(out, "out"),
                         _dev(block_tables, "block_tables"), block_tables.shape[1],

@@ -6,37 +6,51 @@
 // entries (unionyoga.cn, "vLLM：重塑大模型推理性能的关键引擎", PagedAttention
 // section; ybb.press, "vLLM PagedAttention 大模型推理架构深度实战", §2.2).
 // Partial softmax results of separate pieces of the context are combined
-// with online-softmax renormalisation (ybb.press §5.1), here both inside a
-// work-group and across partitions.  Query heads that share a KV head (GQA,
-// ybb.press §9 item 3) are processed together so each KV tile is read once.
+// with online-softmax renormalisation (ybb.press §5.1).  Query heads that
+// share a KV head (GQA, ybb.press §9 item 3) are processed together so each
+// KV tile is read once.
 //
-// Work decomposition: one work-group per (partition of 512 tokens, KV head,
-// sequence).  Decode reads every KV byte once and does 2*G flops per KV
-// element, so it is HBM-bound: the design goal is to keep HBM streaming.
+// Decode reads every KV byte once and does 2*G flops per KV element, so it
+// is bound by HBM bandwidth (ybb.press §7: decode is memory-bound).
 //
-// Fast path (bf16 or fp8 cache, bf16 q, head_dim 64/128, G <= 8), 4 waves:
-//  * wave w takes the partition's blocks w, w+4, w+8, ... and keeps its own
-//    online-softmax state; the next block's K and V are loaded before the
-//    current one is used (two tiles in flight per wave);
-//  * logits S[h][t] = q[h] . K[t] for the G heads and 16 tokens of a block
-//    come from one 16x16x32 bf16 MFMA per 32 dims: q (heads, zero-padded to
-//    16 rows) is the A operand, the K tile straight from HBM is the B
-//    operand -- each lane loads 16 contiguous bytes of one token row, which
-//    is exactly the operand layout, so K never passes through LDS;
-//  * the row max over 16 tokens is four DPP steps inside a 16-lane row;
-//    the running max is only moved when a block's max exceeds it by more
-//    than 2^8 (exact: any reference max gives the same softmax, and the
-//    exponentials stay <= 256), so the accumulator rescale is rare;
-//  * P moves to the V layout through 512 bytes of LDS per wave; V is
-//    accumulated with fp32 VALU FMAs (reduction over tokens would need a
-//    transposed V for MFMA), each lane owning 8 dims of a quarter of the
-//    tokens;
-//  * waves merge (m, l, o) through LDS at the end; a single-partition
-//    sequence writes its output row, otherwise the partition's normalised
-//    output and (max, sum) go to the workspace for the reduce kernel.
+// Fast path (bf16 or fp8 cache, bf16 q, head_dim 64/128, G <= 8):
+//  * Work unit: a tile = one 16-token block of one KV head (16 x D elements
+//    of K and of V, contiguous in the cache).  The tiles of all sequences
+//    form one ordered list, (sequence, KV head, block) with the block index
+//    fastest; a "segment" is the run of tiles of one (sequence, KV head).
+//  * Persistent waves, one per work-group: the list is cut into equal
+//    contiguous ranges, one per wave, so every wave streams the same number
+//    of bytes whatever the length mix.  A wave keeps kNT tiles in flight
+//    across segment boundaries; the next block ids, the next sequence's
+//    length and the next segment's q are fetched while earlier tiles are
+//    being used, so the load pipeline never drains inside a range.
+//  * Tiles are read with buffer loads whose range is the tile's valid rows:
+//    slots past the context length read as zero and move no data, and a
+//    slot of the ring with nothing to load has range 0.
+//  * Both products of a tile are MFMAs with the cache tile as the A operand,
+//    read straight from HBM in operand layout.  Logits are formed
+//    transposed, S^T = K q^T (16x16x32 bf16, one per 32 dims, q zero-padded
+//    to 16 heads), which leaves lane (head h, quad) holding S[h][4*quad..+3]
+//    -- exactly the B operand layout of the 16x16x16 bf16 MFMA that forms
+//    O^T = V^T P^T from the dims-major V tile, so P never moves between
+//    lanes.  The running max is moved only when a logit exceeds it by more
+//    than 2^8 (any reference max gives the same softmax): the common path
+//    has no cross-lane step at all.  P is rounded to bf16 once and the sum
+//    takes the rounded values, so the weights applied are exactly
+//    normalised.
+//  * A segment that lies inside one wave's range writes its output row
+//    directly.  A segment cut between waves leaves each piece's (max, sum,
+//    unnormalised output) in the workspace; an arrival counter per segment
+//    tells the last piece to finish, which merges all pieces by the
+//    log-sum-exp rule and resets the counter to zero.
+//
+// General path (fp32 cache, or shapes the fast path does not cover): one
+// wave per (512-token partition, query head, sequence), one token at a time,
+// plus a separate log-sum-exp reduce kernel.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <mutex>
 #include <type_traits>
 
 #include "device_common.h"
@@ -50,9 +64,15 @@ pa_status launch_status(const char* fn);
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr float kRescaleSlack = 8.0f;   // log2 units: exponentials stay <= 2^8
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+constexpr int kAuxNonTemporal = 2;      // buffer load cache policy: nt
+constexpr int kWavesPerCU = 8;          // fast path: persistent waves per CU
+constexpr int kMinTilesPerWave = 8;     // fast path: at least this many tiles per wave
+constexpr int kNT = 3;                  // fast path: tiles in flight per wave
+constexpr int kCap = 512;               // fast path: tile descriptors per round (LDS)
+constexpr int kGather = 4;              // fast path: block-id loads in flight per lane
+constexpr int kAuxCoherent = 16;        // buffer cache policy sc1: device-coherent access
 
 // DPP controls (GFX9 encoding).
 constexpr int kDppQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]
@@ -84,9 +104,32 @@ __device__ __forceinline__ float row16_sum(float x) {
 __device__ __forceinline__ float readlane_f(float x, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
+__device__ __forceinline__ int readlane_i(int x, int lane) {
+  return __builtin_amdgcn_readlane(x, lane);
+}
 
-// Result of one (partition, KV head, sequence) work-group: either the final
-// output rows, or partial results for the reduce kernel.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, kRsrcWord3);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+// Sum over the 64 lanes of a wave, as a wave-uniform value.
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d);
+  return __builtin_amdgcn_readfirstlane(x);
+}
+
+// Result of one (partition, query head or KV head, sequence) of the general
+// path: either the final output rows, or partial results for the reduce.
 struct PartOut {
   void* out;            // [B][Hq][D], q dtype
   float* ws_o;          // [B][Hq][P][D]
@@ -104,295 +147,508 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
 }
 
 // ---------------------------------------------------------------------------
-// Fast path.  kFp8: cache holds E4M3 codes (else bf16).  kD: head_dim.
-// kG: query heads per KV head (1..8).
-template <int kD, int kG, bool kFp8>
-__global__ void __launch_bounds__(kThreads)
-decode_mfma_kernel(const char* __restrict__ k_cache, const char* __restrict__ v_cache,
-                   const uint16_t* __restrict__ q, const int32_t* __restrict__ block_tables,
-                   const int32_t* __restrict__ context_lens, int max_blocks, int hkv,
-                   float logit_scale /* scale*k_scale*log2(e) */, float v_scale,
-                   PartOut po) {
+// Fast path.
+struct StreamArgs {
+  const char* k_cache;
+  const char* v_cache;
+  const uint16_t* q;          // [B][Hq][D] bf16
+  uint16_t* out;              // [B][Hq][D] bf16
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  uint32_t* counters;         // [B * Hkv], zero between calls
+  float* partials;            // [num_waves][2][kG][kD + 2]
+  int num_seqs;
+  int hkv;
+  int max_blocks;
+  int num_waves;
+  float logit_scale;          // scale * k_scale * log2(e)
+  float v_scale;
+};
+
+// kD: head_dim; kG: query heads per KV head (1..8); kFp8: E4M3 cache (else
+// bf16); kAux: cache policy bits of the KV loads.
+template <int kD, int kG, bool kFp8, int kAux>
+__global__ void __launch_bounds__(64)
+decode_stream_kernel(StreamArgs a) {
   constexpr int kE = kFp8 ? 1 : 2;                 // bytes per cache element
-  constexpr int kKK = kD / 32;                     // MFMA steps over head_dim
-  constexpr int kLanesPerRow = kD / 8;             // V: lanes covering one token row
-  constexpr int kRowsPerLoad = 64 / kLanesPerRow;  // V: token rows per load
-  constexpr int kVLoads = kBlock / kRowsPerLoad;   // V: loads (tokens) per lane
-  constexpr int kGP = (kG + 3) / 4 * 4;            // heads padded to 4
-  constexpr int kHG = kGP / 4;                     // 16-lane row groups with heads
-  constexpr int64_t kTileBytes = kBlock * kD * kE;
-
-  const int part = blockIdx.x;
-  const int g = blockIdx.y;
-  const int s = blockIdx.z;
-  const int L = context_lens[s];
-  const int nparts = (L + kPartTokens - 1) / kPartTokens;
-  const int hq = hkv * kG;
-  if (part >= (nparts > 0 ? nparts : 1)) return;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-
-  __shared__ __align__(16) float s_p[kWaves][kBlock][kGP];
-  __shared__ __align__(16) float s_o[kWaves][kG][kD];
-  __shared__ float s_m[kWaves][kG];
-  __shared__ float s_l[kWaves][kG];
-
-  if (L == 0) {   // empty context: zero output rows
-    for (int i = threadIdx.x; i < kG * kD; i += kThreads) {
-      const int h = g * kG + i / kD;
-      store_out<false>(po.out, (static_cast<int64_t>(s) * hq + h) * kD + i % kD, 0.f);
-    }
-    return;
-  }
-
-  const int blk0 = part * kPartBlocks;
-  const int nblk = min(kPartBlocks, (L + kBlock - 1) / kBlock - blk0);
-
-  // Physical block ids of this partition, one per lane (lanes < nblk).
-  int my_id = 0;
-  if (lane < nblk) my_id = block_tables[static_cast<int64_t>(s) * max_blocks + blk0 + lane];
-
-  // q as the MFMA A operand: row i = head (zero rows past kG), lane l holds
-  // dims 32*kk + 8*(l/16) .. +7 of head l%16.
-  const int row = lane & 15;
-  const int quad = lane >> 4;
-  bf16x8_t qa[kKK];
-  {
-    const int h = g * kG + row;
-#pragma unroll
-    for (int kk = 0; kk < kKK; ++kk) {
-      u32x4_t w = {0u, 0u, 0u, 0u};
-      if (row < kG)
-        w = *reinterpret_cast<const u32x4_t*>(q + (static_cast<int64_t>(s) * hq + h) * kD +
-                                              32 * kk + 8 * quad);
-      qa[kk] = __builtin_bit_cast(bf16x8_t, w);
-    }
-  }
-
-  // Lane offsets inside a (block, head) tile, in bytes.
-  const int k_off = (row * kD + 8 * quad) * kE;               // + 32*kk*kE
-  const int v_c = lane % kLanesPerRow;                        // 8-dim chunk
-  const int v_r = lane / kLanesPerRow;                        // first token row
-  const int v_off = (v_r * kD + 8 * v_c) * kE;                // + i*kRowsPerLoad*kD*kE
-
-  // Online-softmax state.  Logit rows of head group `quad` (heads 4*quad+r)
-  // live in lanes of row group `quad`; m_ref is uniform within the row,
-  // l_part is per lane (token l%16) and summed at the end.
-  float m_ref[4], l_part[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    m_ref[r] = -INFINITY;
-    l_part[r] = 0.f;
-  }
-  float o[kG][8];
-#pragma unroll
-  for (int h = 0; h < kG; ++h)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) o[h][j] = 0.f;
-
+  constexpr int kRowBytes = kD * kE;
+  constexpr int kTileBytes = kBlock * kRowBytes;
+  constexpr int kKK = kD / 32;                     // QK MFMA steps over head_dim
+  constexpr int kVC = kD / 16;                     // P.V MFMAs (16 dims each)
+  constexpr int kSlot = kG * (kD + 2);             // floats per partial slot
   using KChunk = typename std::conditional<kFp8, u32x2_t, u32x4_t>::type;
-  using VChunk = KChunk;
-  const int64_t head_off = static_cast<int64_t>(g) * kTileBytes;
-  const int64_t blk_stride = static_cast<int64_t>(hkv) * kTileBytes;
+  using VChunk = typename std::conditional<kFp8, uint32_t, u32x2_t>::type;
 
-  auto load_tile = [&](int k, KChunk (&kt)[kKK], VChunk (&vt)[kVLoads]) {
-    const int id = __builtin_amdgcn_readlane(my_id, wave + kWaves * k);
-    const int64_t base = static_cast<int64_t>(id) * blk_stride + head_off;
-    const char* kb = k_cache + base + k_off;
-    const char* vb = v_cache + base + v_off;
-#pragma unroll
-    for (int kk = 0; kk < kKK; ++kk)
-      kt[kk] = *reinterpret_cast<const KChunk*>(kb + 32 * kk * kE);
-#pragma unroll
-    for (int i = 0; i < kVLoads; ++i)
-      vt[i] = *reinterpret_cast<const VChunk*>(vb + i * kRowsPerLoad * kD * kE);
-  };
+  const int w = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int B = a.num_seqs;
+  const int hkv = a.hkv;
+  const int hq = hkv * kG;
+  const __amdgpu_buffer_rsrc_t lens_rsrc = make_rsrc(a.context_lens, B * 4);
 
-  const int nk = (nblk - wave + kWaves - 1) / kWaves;   // blocks of this wave
-
-  auto process = [&](int k, const KChunk (&kt)[kKK], const VChunk (&vt)[kVLoads]) {
-    const int valid = L - (blk0 + wave + kWaves * k) * kBlock;   // >= 1
-
-    // ---- logits: S[4*quad + r][row] in acc[r]
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < kKK; ++kk) {
-      bf16x8_t kb;
-      if constexpr (kFp8) {
-        const u32x2_t w = kt[kk];
-        const int w0 = static_cast<int>(w[0]), w1 = static_cast<int>(w[1]);
-        const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
-        const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
-        const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
-        const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
-        kb = bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-      } else {
-        kb = __builtin_bit_cast(bf16x8_t, kt[kk]);
-      }
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], kb, acc, 0, 0, 0);
-    }
-
-    float x[4], rmax[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      x[r] = acc[r] * logit_scale;
-      if (valid < kBlock && row >= valid) x[r] = -INFINITY;
-      rmax[r] = row16_max(x[r]);
-    }
-
-    // ---- lazy running-max update (wave-uniform branch)
-    bool need = false;
+  // ---- 1. total tile count; zero rows of empty sequences s = w (mod waves)
+  int T = 0;
+  for (int s0 = 0; s0 < B; s0 += 256) {
+    int c = 0;
+    int L[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      need |= (quad * 4 + r < kG) && (rmax[r] > m_ref[r] + kRescaleSlack);
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-      float alpha[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float mn = (rmax[r] > m_ref[r] + kRescaleSlack) ? rmax[r] : m_ref[r];
-        alpha[r] = __builtin_amdgcn_exp2f(m_ref[r] - mn);
-        l_part[r] *= alpha[r];
-        m_ref[r] = mn;
-      }
-#pragma unroll
-      for (int h = 0; h < kG; ++h) {
-        const float a = readlane_f(alpha[h & 3], 16 * (h >> 2));
-#pragma unroll
-        for (int j = 0; j < 8; ++j) o[h][j] *= a;
-      }
-    }
-
-    float p[4];
+      L[r] = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(lens_rsrc, (s0 + 64 * r + lane) * 4, 0, 0));
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      p[r] = __builtin_amdgcn_exp2f(x[r] - m_ref[r]);
-      l_part[r] += p[r];
+      const int s = s0 + 64 * r + lane;
+      c += (L[r] + kBlock - 1) / kBlock;
+      const uint64_t empty = __builtin_amdgcn_ballot_w64(s < B && L[r] == 0 && s % a.num_waves == w);
+      for (uint64_t m = empty; m != 0; m &= m - 1) {
+        const int se = s0 + 64 * r + __builtin_ctzll(m);
+        uint16_t* row = a.out + static_cast<int64_t>(se) * hq * kD;
+        for (int i = lane; i < hq * kD / 8; i += 64)
+          reinterpret_cast<u32x4_t*>(row)[i] = u32x4_t{0u, 0u, 0u, 0u};
+      }
     }
-    // P to LDS: s_p[wave][token][head]
-    if (quad < kHG)
-      *reinterpret_cast<f32x4_t*>(&s_p[wave][row][4 * quad]) = f32x4_t{p[0], p[1], p[2], p[3]};
+    T += wave_sum(c);
+  }
+  T *= hkv;
+  const int per = (T + a.num_waves - 1) / a.num_waves;
+  const int t_begin = w * per;
+  if (per == 0 || t_begin >= T) return;
 
-    // ---- o += P V over this lane's tokens v_r + i*kRowsPerLoad, dims 8*v_c..+7
-#pragma unroll
-    for (int i = 0; i < kVLoads; ++i) {
-      const int t = v_r + i * kRowsPerLoad;
-      float vf[8];
-      if constexpr (kFp8) {
-        const u32x2_t w = vt[i];
-        const int w0 = static_cast<int>(w[0]), w1 = static_cast<int>(w[1]);
-        const f32x2_t a0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w0, 1.0f, false);
-        const f32x2_t a1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w0, 1.0f, true);
-        const f32x2_t a2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w1, 1.0f, false);
-        const f32x2_t a3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w1, 1.0f, true);
-        vf[0] = a0[0]; vf[1] = a0[1]; vf[2] = a1[0]; vf[3] = a1[1];
-        vf[4] = a2[0]; vf[5] = a2[1]; vf[6] = a3[0]; vf[7] = a3[1];
-      } else {
-        const u32x4_t w = vt[i];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          vf[2 * j] = bf16_lo(w[j]);
-          vf[2 * j + 1] = bf16_hi(w[j]);
-        }
+  // ---- 2. the segment and block of tile t_begin
+  int s_cur = -1, off = 0, L_cur = 0, seg0 = 0;
+  {
+    int base = 0;
+    for (int s0 = 0; s0 < B && s_cur < 0; s0 += 64) {
+      const int L = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(lens_rsrc, (s0 + lane) * 4, 0, 0));
+      const int c = hkv * ((L + kBlock - 1) / kBlock);
+      const int incl = wave_incl_scan(c, lane);
+      const uint64_t m = __builtin_amdgcn_ballot_w64(base + incl > t_begin);
+      if (m != 0) {
+        const int l0 = __builtin_ctzll(m);
+        s_cur = s0 + l0;
+        const int excl = base + readlane_i(incl, l0) - readlane_i(c, l0);
+        off = t_begin - excl;
+        L_cur = readlane_i(L, l0);
+        seg0 = excl;
       }
-      if (valid < kBlock && t >= valid) {   // unused slots may hold NaN
+      base += readlane_i(incl, 63);
+    }
+  }
+  if (s_cur < 0 || L_cur <= 0) return;   // lengths changed under us: nothing safe to do
+  // tile t_begin is block j0 of KV head g0 of sequence s_cur
+  const int nb0 = (L_cur + kBlock - 1) / kBlock;
+  const int g0 = off / nb0;
+  const int j0 = off - g0 * nb0;
+  const int n_total = min(per, T - t_begin);
+
+  // q of a segment travels with each ring slot in compact form: lane c of
+  // register u holds the 16 bytes at (64*u + c)*16 of the segment's [kG][kD]
+  // bf16 rows.  The consumer rearranges it into the MFMA A operand: row i =
+  // head (zero rows past kG), lane l holds dims 32*kk + 8*(l/16) .. +7 of
+  // head l%16.
+  constexpr int kQBytes = kG * kD * 2;
+  constexpr int kQC = (kQBytes + 1023) / 1024;              // 16-byte loads per lane
+  const int row = lane & 15;
+  const int quad = lane >> 4;
+  auto build_qa = [&](const u32x4_t (&qc)[kQC], bf16x8_t (&qa)[kKK]) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) vf[j] = 0.f;
+    for (int kk = 0; kk < kKK; ++kk) {
+      const int c = row * (kD / 8) + 4 * kk + quad;        // 16-byte chunk wanted
+      const int src = (c & 63) * 4;                         // ds_bpermute byte address
+      u32x4_t v = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int u = 0; u < kQC; ++u) {
+        u32x4_t t;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          t[e] = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src, static_cast<int>(qc[u][e])));
+        if ((c >> 6) == u) v = t;
       }
-      float pt[kGP];
-#pragma unroll
-      for (int h4 = 0; h4 < kHG; ++h4) {
-        const f32x4_t pv = *reinterpret_cast<const f32x4_t*>(&s_p[wave][t][4 * h4]);
-        pt[4 * h4 + 0] = pv[0];
-        pt[4 * h4 + 1] = pv[1];
-        pt[4 * h4 + 2] = pv[2];
-        pt[4 * h4 + 3] = pv[3];
-      }
-#pragma unroll
-      for (int h = 0; h < kG; ++h)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) o[h][j] = fmaf(pt[h], vf[j], o[h][j]);
+      if (row >= kG) v = u32x4_t{0u, 0u, 0u, 0u};
+      qa[kk] = __builtin_bit_cast(bf16x8_t, v);
     }
   };
 
-  // Two tiles in flight: while block k is used, block k+1 is loading.
-  KChunk kt0[kKK], kt1[kKK];
-  VChunk vt0[kVLoads], vt1[kVLoads];
-  if (nk > 0) load_tile(0, kt0, vt0);
-  for (int k = 0; k < nk; k += 2) {
-    if (k + 1 < nk) load_tile(k + 1, kt1, vt1);
-    process(k, kt0, vt0);
-    if (k + 1 < nk) {
-      if (k + 2 < nk) load_tile(k + 2, kt0, vt0);
-      process(k + 1, kt1, vt1);
+  // ---- 3. tile descriptors, built in LDS in rounds of up to kCap tiles
+  // word 0: tile index block * Hkv + g (the block's position in the table
+  //         while building); word 1: valid rows | first << 5 | last << 6 |
+  //         g << 7 | blocks of the sequence << 16; word 2: sequence;
+  // word 3: list index of the segment's first tile.  "first"/"last" mark
+  // the ends of a piece: a segment's ends or the ends of this wave's range.
+  __shared__ u32x4_t s_desc[kCap];
+  int w_s = s_cur, w_g = g0, w_j = j0, w_L = L_cur, w_nb = nb0, w_seg = seg0 + g0 * nb0;
+  int lwin_base = s_cur + 1;           // lengths of the next 64 sequences, one per lane
+  int lwin = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(lens_rsrc, (lwin_base + lane) * 4, 0, 0));
+  const int tbl_bytes = B * a.max_blocks * 4;
+  const __amdgpu_buffer_rsrc_t tbl_rsrc = make_rsrc(a.block_tables, tbl_bytes);
+
+  // Lane offsets inside a (block, KV head) tile, in bytes.
+  //  K tile [16][D]: MFMA A operand, lane (row, quad) holds token `row`,
+  //    dims 32*kk + 8*quad .. +7.
+  //  V tile [D][16]: MFMA A operand of P.V, lane (row, quad) holds dim
+  //    16*c + row, tokens 4*quad .. +3.
+  const int k_off = (row * kD + 8 * quad) * kE;               // + 32*kk*kE
+  const int v_off = (row * kBlock + 4 * quad) * kE;           // + 16*c*kBlock*kE
+
+  // ---- 4. consumer state: online softmax of the current segment piece.
+  // Logits are computed transposed (S^T = K q^T), so lane (row, quad) holds
+  // S[head row][tokens 4*quad + r], r = 0..3 -- which is exactly the layout
+  // of the B operand of the 16x16x16 MFMA that forms P.V.  m_ref is the
+  // reference max of head `row`, the same in its four lanes; l_part is this
+  // lane's share of the exponent sum; oacc[c][r] = O[head row][16*c + 4*quad + r].
+  bf16x8_t qa[kKK];
+  float m_ref = -INFINITY, l_part = 0.f;
+  f32x4_t oacc[kVC];
+  int pend_s[2] = {-1, -1}, pend_g[2] = {0, 0}, pend_seg[2] = {0, 0}, pend_nb[2] = {0, 0};
+
+  auto slot_ptr = [&](int wave, int seg) -> int64_t {       // byte offset of a partial slot
+    const int which = (seg <= wave * per) ? 0 : 1;
+    return static_cast<int64_t>(wave * 2 + which) * kSlot * 4;
+  };
+  const __amdgpu_buffer_rsrc_t part_rsrc = make_rsrc(a.partials, 0x7FFFFFFF);
+
+  auto finalize = [&](int s, int g, int seg, int nb) {
+    float l_tot = l_part;
+    l_tot += __shfl_xor(l_tot, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    const int wf = seg / per;
+    const int wl = (seg + nb - 1) / per;
+    if (wf == wl) {   // the whole segment was in this wave: write the output
+      if (row < kG) {
+        const float inv = a.v_scale / l_tot;
+        uint16_t* orow = a.out + (static_cast<int64_t>(s) * hq + g * kG + row) * kD + 4 * quad;
+#pragma unroll
+        for (int c = 0; c < kVC; ++c) {
+          u32x2_t pk;
+          pk[0] = f32_to_bf16_bits(oacc[c][0] * inv) | (f32_to_bf16_bits(oacc[c][1] * inv) << 16);
+          pk[1] = f32_to_bf16_bits(oacc[c][2] * inv) | (f32_to_bf16_bits(oacc[c][3] * inv) << 16);
+          *reinterpret_cast<u32x2_t*>(orow + 16 * c) = pk;
+        }
+      }
+      return;
     }
+    // A piece of a segment shared with other waves: only the first and the
+    // last segment of a range can be shared, so a wave has at most two
+    // pieces, in slots 0 and 1.  Slot layout: o[kG][kD], m[kG], l[kG]
+    // (floats).  Pieces are published with device-coherent stores (sc1:
+    // written through to the point of coherence of all XCDs); the arrival
+    // count follows once they have completed, after the ring has drained.
+    // No L2 write-back or invalidation is needed: nothing else is shared.
+    const int64_t mine = slot_ptr(w, seg);
+    const int which = (seg <= w * per) ? 0 : 1;
+    if (row < kG) {
+#pragma unroll
+      for (int c = 0; c < kVC; ++c)
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(u32x4_t, oacc[c]), part_rsrc,
+            static_cast<int>(mine + (row * kD + 16 * c + 4 * quad) * 4), 0, kAuxCoherent);
+      if (quad == 0) {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_ref), part_rsrc,
+                                              static_cast<int>(mine + (kG * kD + row) * 4), 0, kAuxCoherent);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l_tot), part_rsrc,
+                                              static_cast<int>(mine + (kG * kD + kG + row) * 4), 0, kAuxCoherent);
+      }
+    }
+    pend_s[which] = s;
+    pend_g[which] = g;
+    pend_seg[which] = seg;
+    pend_nb[which] = nb;
+  };
+
+  // Arrival of a stored piece; the last piece of a segment merges them all:
+  // out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p, computed online.
+  // Lane l handles elements 4*(l + 64*i) .. +3 of the [kG][kD] output.
+  auto arrive = [&](int s, int g, int seg, int nb) {
+    const int wf = seg / per;
+    const int wl = (seg + nb - 1) / per;
+    uint32_t* ctr = a.counters + static_cast<int64_t>(s) * hkv + g;
+    uint32_t prev = 0;
+    if (lane == 0) prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    prev = static_cast<uint32_t>(readlane_i(static_cast<int>(prev), 0));
+    if (prev != static_cast<uint32_t>(wl - wf)) return;   // not the last piece
+    constexpr int kE4 = (kG * kD / 4 + 63) / 64;          // 4-float groups per lane
+    float M[kE4], den[kE4];
+    f32x4_t num[kE4];
+#pragma unroll
+    for (int i = 0; i < kE4; ++i) {
+      M[i] = -INFINITY;
+      den[i] = 0.f;
+      num[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    auto merge_one = [&](int p) {
+      const int64_t sp = slot_ptr(p, seg);
+      f32x4_t op[kE4];
+      float mp[kE4], lp[kE4];
+#pragma unroll
+      for (int i = 0; i < kE4; ++i) {
+        const int e = 4 * (lane + 64 * i);
+        const int h = min(e / kD, kG - 1);
+        const int ee = min(e, kG * kD - 4);
+        op[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                part_rsrc, static_cast<int>(sp + ee * 4), 0, kAuxCoherent));
+        mp[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            part_rsrc, static_cast<int>(sp + (kG * kD + h) * 4), 0, kAuxCoherent));
+        lp[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            part_rsrc, static_cast<int>(sp + (kG * kD + kG + h) * 4), 0, kAuxCoherent));
+      }
+#pragma unroll
+      for (int i = 0; i < kE4; ++i) {
+        const float mn = fmaxf(M[i], mp[i]);
+        const float f_old = __builtin_amdgcn_exp2f(M[i] - mn);
+        const float f_new = __builtin_amdgcn_exp2f(mp[i] - mn);
+        den[i] = den[i] * f_old + lp[i] * f_new;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) num[i][e] = num[i][e] * f_old + op[i][e] * f_new;
+        M[i] = mn;
+      }
+    };
+    for (int p = wf; p <= wl; ++p) merge_one(p);
+    uint16_t* orow = a.out + (static_cast<int64_t>(s) * hq + g * kG) * kD;
+#pragma unroll
+    for (int i = 0; i < kE4; ++i) {
+      const int e = 4 * (lane + 64 * i);
+      if (e < kG * kD) {
+        const float inv = a.v_scale / den[i];
+        u32x2_t pk;
+        pk[0] = f32_to_bf16_bits(num[i][0] * inv) | (f32_to_bf16_bits(num[i][1] * inv) << 16);
+        pk[1] = f32_to_bf16_bits(num[i][2] * inv) | (f32_to_bf16_bits(num[i][3] * inv) << 16);
+        *reinterpret_cast<u32x2_t*>(orow + e) = pk;
+      }
+    }
+    if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+
+  // ring slots: tile data and the segment's compact q
+  KChunk kt[kNT][kKK];
+  VChunk vt[kNT][kVC];
+  u32x4_t qc[kNT][kQC];
+
+  for (int done = 0; done < n_total;) {
+    const int n = min(kCap, n_total - done);
+    // pass 1: walk the pieces of this round, one lane per tile
+    for (int pos = 0; pos < n;) {
+      const int span = min(w_nb - w_j, n - pos);
+      for (int c = lane; c < span; c += 64) {
+        const int j = w_j + c;
+        const int gpos = done + pos + c;                     // position in the range
+        const uint32_t valid = static_cast<uint32_t>(min(kBlock, w_L - kBlock * j));
+        const uint32_t first = (j == 0 || gpos == 0) ? 1u : 0u;
+        const uint32_t last = (j == w_nb - 1 || gpos == n_total - 1) ? 1u : 0u;
+        s_desc[pos + c] = u32x4_t{static_cast<uint32_t>(j),
+                                  valid | (first << 5) | (last << 6) |
+                                      (static_cast<uint32_t>(w_g) << 7) |
+                                      (static_cast<uint32_t>(w_nb) << 16),
+                                  static_cast<uint32_t>(w_s), static_cast<uint32_t>(w_seg)};
+      }
+      pos += span;
+      w_j += span;
+      if (w_j == w_nb) {                                     // next segment
+        w_seg += w_nb;
+        w_j = 0;
+        if (++w_g == hkv) {                                  // next non-empty sequence
+          w_g = 0;
+          do {
+            ++w_s;
+            if (w_s - lwin_base >= 64) {
+              lwin_base = w_s;
+              lwin = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(lens_rsrc, (lwin_base + lane) * 4, 0, 0));
+            }
+            w_L = readlane_i(lwin, w_s - lwin_base);
+          } while (w_L == 0 && w_s + 1 < B);
+          w_nb = (w_L + kBlock - 1) / kBlock;
+        }
+      }
+    }
+    // pass 2: block ids from the tables, independent loads per lane
+    for (int e0 = 0; e0 < n; e0 += 64 * kGather) {
+      int ids[kGather];
+#pragma unroll
+      for (int r = 0; r < kGather; ++r) {
+        const int e = e0 + 64 * r + lane;
+        ids[r] = 0;
+        if (e < n) {
+          const u32x4_t d = s_desc[e];
+          ids[r] = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(
+              tbl_rsrc, (static_cast<int>(d[2]) * a.max_blocks + static_cast<int>(d[0])) * 4, 0, 0));
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < kGather; ++r) {
+        const int e = e0 + 64 * r + lane;
+        if (e < n) {
+          const uint32_t g = (s_desc[e][1] >> 7) & 511u;
+          s_desc[e][0] = static_cast<uint32_t>(ids[r]) * static_cast<uint32_t>(hkv) + g;
+        }
+      }
+    }
+
+    // ---- 5. the ring: kNT tiles in flight.  Every step issues the same
+    // loads (empty ranges move nothing), so the wait counts the consumer
+    // needs never depend on the path taken.
+    auto issue = [&](int slot, int t) {
+      int k_nrec = 0, v_nrec = 0, q_nrec = 0;
+      int64_t tile_off = 0, q_off = 0;
+      if (t < n) {
+        const u32x4_t d = s_desc[t];
+        const uint32_t tile = __builtin_amdgcn_readfirstlane(d[0]);
+        const uint32_t info = __builtin_amdgcn_readfirstlane(d[1]);
+        const int s = __builtin_amdgcn_readfirstlane(static_cast<int>(d[2]));
+        k_nrec = static_cast<int>(info & 31u) * kRowBytes;   // rows past the context read 0
+        v_nrec = kTileBytes;                                  // (V columns are masked below)
+        tile_off = static_cast<int64_t>(tile) * kTileBytes;
+        if (info & 32u) {
+          q_off = (static_cast<int64_t>(s) * hq + static_cast<int>((info >> 7) & 511u) * kG) * kD * 2;
+          q_nrec = kQBytes;
+        }
+      }
+      const __amdgpu_buffer_rsrc_t rq = make_rsrc(reinterpret_cast<const char*>(a.q) + q_off, q_nrec);
+#pragma unroll
+      for (int u = 0; u < kQC; ++u) qc[slot][u] = __builtin_amdgcn_raw_buffer_load_b128(rq, (64 * u + lane) * 16, 0, 0);
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k_cache + tile_off, k_nrec);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v_cache + tile_off, v_nrec);
+#pragma unroll
+      for (int kk = 0; kk < kKK; ++kk) {
+        if constexpr (kFp8)
+          kt[slot][kk] = __builtin_bit_cast(KChunk, __builtin_amdgcn_raw_buffer_load_b64(rk, k_off + 32 * kk * kE, 0, kAux));
+        else
+          kt[slot][kk] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_off + 32 * kk * kE, 0, kAux);
+      }
+#pragma unroll
+      for (int c = 0; c < kVC; ++c) {
+        if constexpr (kFp8)
+          vt[slot][c] = __builtin_amdgcn_raw_buffer_load_b32(rv, v_off + 16 * c * kBlock * kE, 0, kAux);
+        else
+          vt[slot][c] = __builtin_bit_cast(VChunk, __builtin_amdgcn_raw_buffer_load_b64(rv, v_off + 16 * c * kBlock * kE, 0, kAux));
+      }
+    };
+
+    auto consume = [&](int slot, int t) {
+      if (t >= n) return;
+      const u32x4_t d = s_desc[t];
+      const uint32_t info = __builtin_amdgcn_readfirstlane(d[1]);
+      const int valid = static_cast<int>(info & 31u);
+      if (info & 32u) {                                      // a piece starts here
+        m_ref = -INFINITY;
+        l_part = 0.f;
+#pragma unroll
+        for (int c = 0; c < kVC; ++c) oacc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        build_qa(qc[slot], qa);
+      }
+
+      // ---- logits, transposed: acc[r] = S[head row][token 4*quad + r]
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < kKK; ++kk) {
+        bf16x8_t kb;
+        if constexpr (kFp8) {
+          const u32x2_t wv = kt[slot][kk];
+          const int w0 = static_cast<int>(wv[0]), w1 = static_cast<int>(wv[1]);
+          const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+          const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+          const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+          const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+          kb = bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        } else {
+          kb = __builtin_bit_cast(bf16x8_t, kt[slot][kk]);
+        }
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qa[kk], acc, 0, 0, 0);
+      }
+      float x[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        x[r] = acc[r] * a.logit_scale;
+        if (4 * quad + r >= valid) x[r] = -INFINITY;
+      }
+
+      // ---- lazy running max: moved only when a logit exceeds it by more
+      // than 2^kRescaleSlack (rare; a wave-uniform branch)
+      const float xm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      if (__builtin_amdgcn_ballot_w64(xm > m_ref + kRescaleSlack) != 0) {
+        float mt = xm;
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));                   // max over the head's 16 tokens
+        const float mn = (mt > m_ref + kRescaleSlack) ? mt : m_ref;
+        const float alpha = __builtin_amdgcn_exp2f(m_ref - mn);
+        l_part *= alpha;
+#pragma unroll
+        for (int c = 0; c < kVC; ++c)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) oacc[c][r] *= alpha;
+        m_ref = mn;
+      }
+
+      // ---- P in bf16 (the sum takes the rounded values, so the weights the
+      // MFMA applies are exactly normalised), then O^T += V^T P^T
+      bf16x4_t pb;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float pr = __builtin_amdgcn_exp2f(x[r] - m_ref);
+        const uint32_t bits = f32_to_bf16_bits(pr);
+        pb[r] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(bits));
+        l_part += __uint_as_float(bits << 16);
+      }
+      // V columns past the context: zero them (0 * garbage could be NaN)
+      uint32_t vmask_lo = 0xFFFFFFFFu, vmask_hi = 0xFFFFFFFFu;
+      if (valid < kBlock) {
+        const int t0 = 4 * quad;
+        vmask_lo = (t0 + 0 < valid ? 0x0000FFFFu : 0u) | (t0 + 1 < valid ? 0xFFFF0000u : 0u);
+        vmask_hi = (t0 + 2 < valid ? 0x0000FFFFu : 0u) | (t0 + 3 < valid ? 0xFFFF0000u : 0u);
+      }
+#pragma unroll
+      for (int c = 0; c < kVC; ++c) {
+        u32x2_t vw;
+        if constexpr (kFp8) {
+          const int w0 = static_cast<int>(vt[slot][c]);
+          const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+          const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+          vw[0] = __builtin_bit_cast(uint32_t, p0);
+          vw[1] = __builtin_bit_cast(uint32_t, p1);
+        } else {
+          vw = vt[slot][c];
+        }
+        vw[0] &= vmask_lo;
+        vw[1] &= vmask_hi;
+        oacc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, vw),
+                                                           __builtin_bit_cast(s16x4_t, pb),
+                                                           oacc[c], 0, 0, 0);
+      }
+
+      if (info & 64u)                                        // a piece ends here
+        finalize(__builtin_amdgcn_readfirstlane(static_cast<int>(d[2])),
+                 static_cast<int>((info >> 7) & 511u),
+                 __builtin_amdgcn_readfirstlane(static_cast<int>(d[3])),
+                 static_cast<int>(info >> 16));
+    };
+
+#pragma unroll
+    for (int k = 0; k < kNT; ++k) issue(k, k);
+    for (int t0 = 0; t0 < n; t0 += kNT) {
+#pragma unroll
+      for (int k = 0; k < kNT; ++k) {
+        consume(k, t0 + k);
+        issue(k, t0 + k + kNT);
+      }
+    }
+    done += n;
   }
 
-  // ---- wave totals: l over the 16 token lanes, o over the lanes sharing v_c
-  float l_sum[4];
+  // ---- 6. count the arrivals of the stored pieces (once every store of
+  // this wave has completed), merge where this wave is the last piece
+  if (pend_s[0] >= 0 || pend_s[1] >= 0) {
+    __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) l_sum[r] = row16_sum(l_part[r]);
-#pragma unroll
-  for (int h = 0; h < kG; ++h)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float v = o[h][j];
-#pragma unroll
-      for (int sh = kLanesPerRow; sh < 64; sh <<= 1) v += __shfl_xor(v, sh);
-      o[h][j] = v;
-    }
-  if (lane < kLanesPerRow) {
-#pragma unroll
-    for (int h = 0; h < kG; ++h) {
-      *reinterpret_cast<f32x4_t*>(&s_o[wave][h][8 * v_c]) =
-          f32x4_t{o[h][0], o[h][1], o[h][2], o[h][3]};
-      *reinterpret_cast<f32x4_t*>(&s_o[wave][h][8 * v_c + 4]) =
-          f32x4_t{o[h][4], o[h][5], o[h][6], o[h][7]};
-    }
-  }
-  if (row == 0) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int h = 4 * quad + r;
-      if (h < kG) {
-        s_m[wave][h] = m_ref[r];
-        s_l[wave][h] = (nk > 0) ? l_sum[r] : 0.f;
-      }
-    }
-  }
-  __syncthreads();
-
-  // ---- merge the waves: thread -> (head, dim)
-  for (int i = threadIdx.x; i < kG * kD; i += kThreads) {
-    const int hh = i / kD;
-    const int d = i % kD;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-      if (s_l[w][hh] > 0.f) M = fmaxf(M, s_m[w][hh]);
-    float lsum = 0.f, osum = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      if (s_l[w][hh] > 0.f) {
-        const float a = __builtin_amdgcn_exp2f(s_m[w][hh] - M);
-        lsum = fmaf(a, s_l[w][hh], lsum);
-        osum = fmaf(a, s_o[w][hh][d], osum);
-      }
-    }
-    const int h = g * kG + hh;
-    const float ohat = osum / lsum;
-    if (nparts == 1) {
-      store_out<false>(po.out, (static_cast<int64_t>(s) * hq + h) * kD + d, ohat * v_scale);
-    } else {
-      const int64_t r = (static_cast<int64_t>(s) * hq + h) * po.num_parts + part;
-      po.ws_o[r * kD + d] = ohat * v_scale;
-      if (d == 0) {
-        po.ws_ml[2 * r] = M;
-        po.ws_ml[2 * r + 1] = lsum;
-      }
-    }
+    for (int i = 0; i < 2; ++i)
+      if (pend_s[i] >= 0) arrive(pend_s[i], pend_g[i], pend_seg[i], pend_nb[i]);
   }
 }
+
+// Zero-fill of a decode workspace.
+__global__ void __launch_bounds__(256)
+zero_fill_kernel(uint32_t* p, int64_t n_words) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n_words; i += stride)
+    p[i] = 0u;
+}
+
 
 // ---------------------------------------------------------------------------
 // General path: any G, fp32 / bf16 / fp8 cache.  One wave per (partition,
@@ -447,7 +703,8 @@ decode_simple_kernel(const char* __restrict__ k_cache, const char* __restrict__ 
   for (int i = 0; i < kPer; ++i) o[i] = 0.f;
   for (int t = t0; t < t1; ++t) {
     const int64_t id = block_tables[static_cast<int64_t>(s) * max_blocks + t / kBlock];
-    const int64_t base = ((id * hkv + g) * kBlock + t % kBlock) * kD;
+    const int64_t tile = (id * hkv + g) * kBlock * kD;       // K [16][D], V [D][16]
+    const int64_t base = tile + (t % kBlock) * kD;
     float dot = 0.f;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) dot = fmaf(qv[i], elem(k_cache, base + lane + 64 * i), dot);
@@ -459,7 +716,9 @@ decode_simple_kernel(const char* __restrict__ k_cache, const char* __restrict__ 
     const float p = __builtin_amdgcn_exp2f(x - mn);
     l = l * a + p;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) o[i] = fmaf(p, elem(v_cache, base + lane + 64 * i), o[i] * a);
+    for (int i = 0; i < kPer; ++i)
+      o[i] = fmaf(p, elem(v_cache, tile + static_cast<int64_t>(lane + 64 * i) * kBlock + t % kBlock),
+                  o[i] * a);
     m = mn;
   }
   if (nparts == 1) {
@@ -502,26 +761,6 @@ reduce_kernel(const int32_t* __restrict__ context_lens, PartOut po) {
 }
 
 template <int kD>
-void launch_fast(int G, bool fp8, dim3 grid, hipStream_t st, const char* kc, const char* vc,
-                 const uint16_t* q, const int32_t* bt, const int32_t* cl, int maxb, int hkv,
-                 float ls, float vs, PartOut po) {
-#define PA_FAST(GG)                                                                     \
-  case GG:                                                                              \
-    if (fp8)                                                                            \
-      decode_mfma_kernel<kD, GG, true><<<grid, kThreads, 0, st>>>(kc, vc, q, bt, cl,    \
-                                                                  maxb, hkv, ls, vs, po); \
-    else                                                                                \
-      decode_mfma_kernel<kD, GG, false><<<grid, kThreads, 0, st>>>(kc, vc, q, bt, cl,   \
-                                                                   maxb, hkv, ls, vs, po); \
-    break;
-  switch (G) {
-    PA_FAST(1) PA_FAST(2) PA_FAST(3) PA_FAST(4) PA_FAST(5) PA_FAST(6) PA_FAST(7) PA_FAST(8)
-    default: break;
-  }
-#undef PA_FAST
-}
-
-template <int kD>
 void launch_simple(int fmt, bool out_f32, dim3 grid, hipStream_t st, const char* kc,
                    const char* vc, const void* q, const int32_t* bt, const int32_t* cl,
                    int maxb, int hkv, int G, float ls, float vs, PartOut po) {
@@ -534,22 +773,107 @@ void launch_simple(int fmt, bool out_f32, dim3 grid, hipStream_t st, const char*
   (void)out_f32;
 }
 
+
+template <int kD, int kG>
+void launch_stream_g(bool fp8, int nw, hipStream_t st, const StreamArgs& a) {
+  if (fp8)
+    decode_stream_kernel<kD, kG, true, 0><<<nw, 64, 0, st>>>(a);
+  else
+    decode_stream_kernel<kD, kG, false, 0><<<nw, 64, 0, st>>>(a);
+}
+
+template <int kD>
+void launch_stream(int G, bool fp8, int nw, hipStream_t st, const StreamArgs& a) {
+  switch (G) {
+    case 1: launch_stream_g<kD, 1>(fp8, nw, st, a); break;
+    case 2: launch_stream_g<kD, 2>(fp8, nw, st, a); break;
+    case 3: launch_stream_g<kD, 3>(fp8, nw, st, a); break;
+    case 4: launch_stream_g<kD, 4>(fp8, nw, st, a); break;
+    case 5: launch_stream_g<kD, 5>(fp8, nw, st, a); break;
+    case 6: launch_stream_g<kD, 6>(fp8, nw, st, a); break;
+    case 7: launch_stream_g<kD, 7>(fp8, nw, st, a); break;
+    case 8: launch_stream_g<kD, 8>(fp8, nw, st, a); break;
+    default: break;
+  }
+}
+
 }  // namespace
 
 }  // namespace pagedkv
 
 using namespace pagedkv;
 
-static int num_partitions(int32_t max_context_len) {
+namespace {
+
+int num_partitions(int32_t max_context_len) {
   return (max_context_len + kPartTokens - 1) / kPartTokens;
 }
 
-extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
-                                            int32_t head_dim, int32_t max_context_len) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
+bool fast_path(int fmt, int q_dtype, int G, int D) {
+  return (fmt == PA_BF16 || fmt == PA_FP8_E4M3) && q_dtype == PA_BF16 && G >= 1 && G <= 8 &&
+         (D == 64 || D == 128);
+}
+
+// Compute units of the current device (256 on MI355X when it cannot be read).
+int device_cus() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    cache[dev] = cus;
+  }
+  return cache[dev];
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// Fast path workspace: arrival counters, then two partial slots per wave.
+size_t stream_workspace_bytes(int num_seqs, int hkv, int G, int D) {
+  const size_t waves = static_cast<size_t>(device_cus()) * kWavesPerCU;
+  return align256(static_cast<size_t>(num_seqs) * hkv * sizeof(uint32_t)) +
+         waves * 2 * G * (D + 2) * sizeof(float);
+}
+
+size_t general_workspace_bytes(int num_seqs, int num_q_heads, int D, int max_context_len) {
   const int P = num_partitions(max_context_len);
   if (P <= 1) return 0;
-  return static_cast<size_t>(num_seqs) * num_q_heads * P * (head_dim + 2) * sizeof(float);
+  return static_cast<size_t>(num_seqs) * num_q_heads * P * (D + 2) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" size_t pa_decode_workspace_bytes(const pa_cache_desc* c, int32_t num_seqs,
+                                            int32_t num_q_heads, int32_t max_context_len) {
+  if (check_desc(c, "pa_decode_workspace_bytes") != PA_OK) return 0;
+  if (num_seqs <= 0 || num_q_heads <= 0 || max_context_len <= 0 ||
+      num_q_heads % c->num_kv_heads != 0)
+    return 0;
+  const int G = num_q_heads / c->num_kv_heads;
+  const int q_dtype = (c->cache_dtype == PA_F32) ? PA_F32 : PA_BF16;
+  if (fast_path(c->cache_dtype, q_dtype, G, c->head_dim))
+    return stream_workspace_bytes(num_seqs, c->num_kv_heads, G, c->head_dim);
+  return general_workspace_bytes(num_seqs, num_q_heads, c->head_dim, max_context_len);
+}
+
+extern "C" pa_status pa_decode_workspace_init(void* workspace, size_t workspace_bytes,
+                                              void* stream) {
+  if (workspace_bytes == 0) return PA_OK;
+  if (!workspace) return fail(PA_ERR_INVALID_ARG, "pa_decode_workspace_init: null workspace");
+  if (reinterpret_cast<uintptr_t>(workspace) % 4 != 0)
+    return fail(PA_ERR_INVALID_ARG, "pa_decode_workspace_init: workspace not 4-byte aligned");
+  const int64_t words = static_cast<int64_t>(workspace_bytes / 4);
+  if (words > 0) {
+    const int64_t grid = std::min<int64_t>((words + 255) / 256, 4096);
+    zero_fill_kernel<<<static_cast<unsigned>(grid), 256, 0, static_cast<hipStream_t>(stream)>>>(
+        static_cast<uint32_t*>(workspace), words);
+  }
+  return launch_status("pa_decode_workspace_init");
 }
 
 extern "C" pa_status pa_decode(const pa_cache_desc* c, const void* k_cache, const void* v_cache,
@@ -579,20 +903,24 @@ extern "C" pa_status pa_decode(const pa_cache_desc* c, const void* k_cache, cons
   if (num_seqs == 0) return PA_OK;
   if (!k_cache || !v_cache || !q || !out || !block_tables || !context_lens)
     return fail(PA_ERR_INVALID_ARG, "pa_decode: null pointer");
-  if (num_seqs > 65535 || num_q_heads > 65535)
+  const int G = num_q_heads / hkv;
+  const bool fast = fast_path(fmt, q_dtype, G, D);
+  const int64_t max_tiles = static_cast<int64_t>(hkv) * num_seqs *
+                            ((static_cast<int64_t>(max_context_len) + kBlock - 1) / kBlock);
+  if (fast && (max_tiles >= (int64_t{1} << 30) ||
+               static_cast<int64_t>(max_blocks_per_seq) * 4 >= (int64_t{1} << 31)))
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: %lld tiles in one call (limit 2^30)",
+                static_cast<long long>(max_tiles));
+  if (!fast && (num_seqs > 65535 || num_q_heads > 65535))
     return fail(PA_ERR_UNSUPPORTED, "pa_decode: num_seqs / num_q_heads above 65535");
-  const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, D, max_context_len);
+  const size_t need = fast ? stream_workspace_bytes(num_seqs, hkv, G, D)
+                           : general_workspace_bytes(num_seqs, num_q_heads, D, max_context_len);
   if (workspace_bytes < need || (need > 0 && !workspace))
     return fail(PA_ERR_WORKSPACE_TOO_SMALL, "pa_decode: workspace %zu bytes, need %zu",
                 workspace_bytes, need);
+  if (need > 0 && reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+    return fail(PA_ERR_INVALID_ARG, "pa_decode: workspace not 16-byte aligned");
 
-  const int G = num_q_heads / hkv;
-  const int P = max_context_len > 0 ? num_partitions(max_context_len) : 1;
-  PartOut po;
-  po.out = out;
-  po.num_parts = P;
-  po.ws_o = static_cast<float*>(workspace);
-  po.ws_ml = need ? po.ws_o + static_cast<size_t>(num_seqs) * num_q_heads * P * D : nullptr;
   const float kscale = (fmt == PA_FP8_E4M3) ? c->k_scale : 1.f;
   const float vscale = (fmt == PA_FP8_E4M3) ? c->v_scale : 1.f;
   const float logit_scale =
@@ -601,17 +929,40 @@ extern "C" pa_status pa_decode(const pa_cache_desc* c, const void* k_cache, cons
   const char* kc = static_cast<const char*>(k_cache);
   const char* vc = static_cast<const char*>(v_cache);
 
-  const bool fast = (fmt == PA_BF16 || fmt == PA_FP8_E4M3) && G <= 8;
   if (fast) {
-    dim3 grid(P, hkv, num_seqs);
-    const auto* qb = static_cast<const uint16_t*>(q);
-    if (D == 128)
-      launch_fast<128>(G, fmt == PA_FP8_E4M3, grid, s, kc, vc, qb, block_tables, context_lens,
-                       max_blocks_per_seq, hkv, logit_scale, vscale, po);
-    else
-      launch_fast<64>(G, fmt == PA_FP8_E4M3, grid, s, kc, vc, qb, block_tables, context_lens,
-                      max_blocks_per_seq, hkv, logit_scale, vscale, po);
-  } else {
+    if (max_context_len == 0) max_context_len = 1;
+    const int64_t waves_max = static_cast<int64_t>(device_cus()) * kWavesPerCU;
+    const int64_t by_size = (max_tiles + kMinTilesPerWave - 1) / kMinTilesPerWave;
+    // enough waves to cover the empty-sequence duty (one per 64 sequences)
+    const int64_t nw = std::max<int64_t>(std::min(waves_max, by_size), 1);
+    StreamArgs a;
+    a.k_cache = kc;
+    a.v_cache = vc;
+    a.q = static_cast<const uint16_t*>(q);
+    a.out = static_cast<uint16_t*>(out);
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.counters = static_cast<uint32_t*>(workspace);
+    a.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                          align256(static_cast<size_t>(num_seqs) * hkv * 4));
+    a.num_seqs = num_seqs;
+    a.hkv = hkv;
+    a.max_blocks = max_blocks_per_seq;
+    a.num_waves = static_cast<int>(nw);
+    a.logit_scale = logit_scale;
+    a.v_scale = vscale;
+    if (D == 128) launch_stream<128>(G, fmt == PA_FP8_E4M3, a.num_waves, s, a);
+    else launch_stream<64>(G, fmt == PA_FP8_E4M3, a.num_waves, s, a);
+    return launch_status("pa_decode");
+  }
+
+  const int P = max_context_len > 0 ? num_partitions(max_context_len) : 1;
+  PartOut po;
+  po.out = out;
+  po.num_parts = P;
+  po.ws_o = static_cast<float*>(workspace);
+  po.ws_ml = need ? po.ws_o + static_cast<size_t>(num_seqs) * num_q_heads * P * D : nullptr;
+  {
     dim3 grid(P, num_q_heads, num_seqs);
     if (D == 128)
       launch_simple<128>(fmt, fmt == PA_F32, grid, s, kc, vc, q, block_tables, context_lens,

@@ -16,12 +16,14 @@ TORCH_STORE = {"f32": torch.int32, "bf16": torch.int16, "fp8": torch.uint8}
 TORCH_VIEW = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
 
 
-def device_cache(num_blocks, Hkv, D, fmt, dev="cuda"):
-    """[num_blocks, Hkv, 16, D] filled with the NaN sentinel of the format."""
+def device_cache(num_blocks, Hkv, D, fmt, dev="cuda", v=False):
+    """A K cache [num_blocks, Hkv, 16, D] (V cache [num_blocks, Hkv, D, 16]
+    with v=True) filled with the NaN sentinel of the format."""
     val = int(SENTINEL[fmt])
     if fmt == "f32":
         val = val - (1 << 32) if val >= (1 << 31) else val
-    t = torch.full((num_blocks, Hkv, 16, D), val, dtype=TORCH_STORE[fmt], device=dev)
+    shape = (num_blocks, Hkv, D, 16) if v else (num_blocks, Hkv, 16, D)
+    t = torch.full(shape, val, dtype=TORCH_STORE[fmt], device=dev)
     return t.view(TORCH_VIEW[fmt])
 
 
@@ -57,7 +59,7 @@ class GpuView:
         self.poison = w.num_blocks
         self.desc = pk.CacheDesc(w.num_blocks + 1, w.Hkv, w.D, w.fmt, w.k_scale, w.v_scale)
         self.kc = device_cache(w.num_blocks + 1, w.Hkv, w.D, w.fmt, dev)
-        self.vc = device_cache(w.num_blocks + 1, w.Hkv, w.D, w.fmt, dev)
+        self.vc = device_cache(w.num_blocks + 1, w.Hkv, w.D, w.fmt, dev, v=True)
         self.bm = pk.BlockManager(w.num_blocks, free_order=w.free_order)
         self.dev = dev
 
@@ -95,8 +97,7 @@ class GpuView:
         if max_len is None:
             max_len = int(max(1, int(np.max(self.cl_host)) if len(self.cl_host) else 1))
         if workspace is None:
-            nb = pk.decode_workspace_bytes(w.B, w.Hq, w.D, max_len)
-            workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=self.dev)
+            workspace = pk.new_decode_workspace(self.desc, w.B, w.Hq, max_len, self.dev)
         pk.decode(self.desc, self.kc, self.vc, qd, out, self.bt, self.cl, max_len,
                   float(w.scale), workspace)
         return out

@@ -130,6 +130,49 @@ def test_decode_is_deterministic():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+def test_decode_long_contexts_split_across_many_waves():
+    """Two long GQA contexts: each (sequence, KV head) run of tiles is cut
+    between well over a hundred waves, whose pieces the last one merges."""
+    lens = np.array([20000, 9000], dtype=np.int32)
+    _small_case(310, "bf16", 2, 16, 2, 128, 0, lens=lens)
+
+
+def test_decode_empty_sequences_between_others():
+    lens = np.array([0, 37, 0, 0, 600, 0, 1, 0, 2049, 0], dtype=np.int32)
+    _small_case(311, "bf16", len(lens), 8, 2, 128, 0, lens=lens)
+
+
+@pytest.mark.parametrize("L", [1, 16, 17, 130])
+def test_decode_one_sequence(L):
+    """Fewer tiles than a wave's minimum share: most waves get nothing."""
+    _small_case(312 + L, "bf16", 1, 4, 1, 128, 0, lens=np.array([L], dtype=np.int32))
+
+
+def test_decode_workspace_is_left_zeroed_and_reusable():
+    """Arrival counters return to zero after every call, so one workspace
+    serves calls of different shapes; results are reproducible bit for bit."""
+    wa = workloads.small_random(313, 6, 16, 4, 128, "bf16", 5000, 1)
+    wb = workloads.small_random(314, 3, 32, 4, 128, "bf16", 9000, 3000)
+    va, vb = GpuView(wa), GpuView(wb)
+    fill_sequential(va)
+    fill_sequential(vb)
+    va.tables(cap=9000 // 16 + 1)
+    vb.tables(cap=9000 // 16 + 1)
+    ws = pk.new_decode_workspace(va.desc, 6, 32, 9000)
+    n_ctr = 6 * 4 * 4
+    outs = []
+    for view in (va, vb, va):
+        w = view.w
+        out = view.decode(max_len=9000, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws[:n_ctr].count_nonzero()) == 0, "arrival counters not reset"
+        outs.append(out.clone())
+        bm, kc_ref, vc_ref, bt_ref, cl_ref, _ = osu.fill_sequential(w)
+        ref = oracle.decode(w.q, w.q_fmt, kc_ref, vc_ref, w.fmt, bt_ref, cl_ref, w.scale)
+        _check_out(out, ref, w.fmt)
+    assert torch.equal(outs[0].view(torch.int16), outs[2].view(torch.int16))
+
+
 # ------------------------------------------------------------------ write / copy
 @pytest.mark.parametrize("scale", [1.0, 0.0123, 7.5e-3, 3.3e4, 1.0 / 448])
 def test_fp8_quantiser_exhaustive_over_bf16(scale):
@@ -140,7 +183,7 @@ def test_fp8_quantiser_exhaustive_over_bf16(scale):
     T = bits.shape[0]
     desc = pk.CacheDesc(T // 16, Hkv, D, "fp8", scale, scale)
     kc = torch.zeros(desc.shape, dtype=torch.uint8, device="cuda")
-    vc = torch.zeros_like(kc)
+    vc = torch.zeros(desc.v_shape, dtype=torch.uint8, device="cuda")
     rows = torch.from_numpy(bits.view(np.int16)).to("cuda").view(torch.bfloat16)
     slots = torch.arange(T, dtype=torch.int64, device="cuda")
     pk.write_kv(desc, kc, vc, rows, rows, slots)
@@ -150,7 +193,8 @@ def test_fp8_quantiser_exhaustive_over_bf16(scale):
     inv = np.float32(1.0 / np.float64(np.float32(scale)))
     ref = oracle.e4m3_encode(x, inv)
     assert np.array_equal(got, ref)
-    assert np.array_equal(vc.cpu().numpy(), kc.cpu().numpy())
+    # the V cache holds the same codes in its dims-major tiles
+    assert np.array_equal(vc.cpu().numpy().transpose(0, 1, 3, 2), kc.cpu().numpy())
 
 
 def test_fp8_dequant_of_every_code_through_decode():
@@ -161,7 +205,7 @@ def test_fp8_dequant_of_every_code_through_decode():
     vs = 0.5
     desc = pk.CacheDesc(B, Hkv, D, "fp8", 1.0, vs)
     kc = torch.zeros(desc.shape, dtype=torch.uint8, device="cuda")
-    vc = torch.from_numpy(np.repeat(codes, 16 * D).reshape(B, 1, 16, D)).to("cuda")
+    vc = torch.from_numpy(np.repeat(codes, 16 * D).reshape(B, 1, D, 16)).to("cuda")
     q = torch.zeros((B, 1, D), dtype=torch.bfloat16, device="cuda")
     out = torch.empty_like(q)
     bt = torch.arange(B, dtype=torch.int32, device="cuda").reshape(B, 1)

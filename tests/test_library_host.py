@@ -62,9 +62,24 @@ def test_status_codes_and_messages_on_bad_arguments():
 
 
 def test_workspace_size_formula():
-    assert pk.decode_workspace_bytes(256, 32, 128, 512) == 0
-    assert pk.decode_workspace_bytes(256, 32, 128, 513) == 256 * 32 * 2 * 130 * 4
-    assert pk.decode_workspace_bytes(8, 64, 128, 32768) == 8 * 64 * 64 * 130 * 4
+    # general (fp32) path: one (max, sum, output) record per 512-token partition
+    f32 = pk.CacheDesc(64, 32, 128, "f32")
+    assert pk.decode_workspace_bytes(f32, 256, 32, 512) == 0
+    assert pk.decode_workspace_bytes(f32, 256, 32, 513) == 256 * 32 * 2 * 130 * 4
+    f32 = pk.CacheDesc(64, 8, 128, "f32")
+    assert pk.decode_workspace_bytes(f32, 8, 64, 32768) == 8 * 64 * 64 * 130 * 4
+    # bf16 / fp8 path: arrival counters (256-byte aligned), then two partial
+    # slots of G * (D + 2) floats for each of the 8 waves per compute unit;
+    # without a visible GPU the library assumes MI355X's 256 compute units
+    waves = 256 * 8
+    bf = pk.CacheDesc(64, 8, 128, "bf16")
+    assert pk.decode_workspace_bytes(bf, 256, 32, 4096) == 256 * 8 * 4 + waves * 2 * 4 * 130 * 4
+    assert pk.decode_workspace_bytes(bf, 3, 64, 10) == 256 + waves * 2 * 8 * 130 * 4
+    fp8 = pk.CacheDesc(64, 2, 64, "fp8", 0.5, 0.5)
+    assert pk.decode_workspace_bytes(fp8, 5, 2, 100) == 256 + waves * 2 * 1 * 66 * 4
+    # invalid shapes report 0
+    assert pk.decode_workspace_bytes(bf, 4, 12, 100) == 0
+    assert pk.decode_workspace_bytes(bf, 0, 8, 100) == 0
 
 
 def test_cache_bytes():
