@@ -67,7 +67,7 @@ namespace {
 constexpr float kRescaleSlack = 8.0f;   // log2 units: exponentials stay <= 2^8
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 constexpr int kAuxNonTemporal = 2;      // buffer load cache policy: nt
-constexpr int kWavesPerCU = 8;          // fast path: persistent waves per CU
+constexpr int kWavesPerCU = 4;          // fast path: persistent waves per CU (one per SIMD)
 constexpr int kMinTilesPerWave = 8;     // fast path: at least this many tiles per wave
 constexpr int kNT = 3;                  // fast path: tiles in flight per wave
 constexpr int kCap = 512;               // fast path: tile descriptors per round (LDS)
@@ -186,14 +186,15 @@ decode_stream_kernel(StreamArgs a) {
   const int hq = hkv * kG;
   const __amdgpu_buffer_rsrc_t lens_rsrc = make_rsrc(a.context_lens, B * 4);
 
-  // ---- 1. total tile count; zero rows of empty sequences s = w (mod waves)
-  int T = 0;
-  for (int s0 = 0; s0 < B; s0 += 256) {
-    int c = 0;
-    int L[4];
+  // ---- 1. total tile count; zero rows of empty sequences s = w (mod waves).
+  // The lengths of the first 256 sequences stay in registers (Lr[r] holds
+  // sequence 64*r + lane): batches up to 256 need a single length load.
+  int Lr[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      L[r] = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(lens_rsrc, (s0 + 64 * r + lane) * 4, 0, 0));
+  for (int r = 0; r < 4; ++r)
+    Lr[r] = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(lens_rsrc, (64 * r + lane) * 4, 0, 0));
+  auto round_blocks = [&](int s0, const int (&L)[4]) -> int {   // blocks of s0..s0+255
+    int c = 0;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int s = s0 + 64 * r + lane;
@@ -201,24 +202,32 @@ decode_stream_kernel(StreamArgs a) {
       const uint64_t empty = __builtin_amdgcn_ballot_w64(s < B && L[r] == 0 && s % a.num_waves == w);
       for (uint64_t m = empty; m != 0; m &= m - 1) {
         const int se = s0 + 64 * r + __builtin_ctzll(m);
-        uint16_t* row = a.out + static_cast<int64_t>(se) * hq * kD;
+        uint16_t* orow = a.out + static_cast<int64_t>(se) * hq * kD;
         for (int i = lane; i < hq * kD / 8; i += 64)
-          reinterpret_cast<u32x4_t*>(row)[i] = u32x4_t{0u, 0u, 0u, 0u};
+          reinterpret_cast<u32x4_t*>(orow)[i] = u32x4_t{0u, 0u, 0u, 0u};
       }
     }
-    T += wave_sum(c);
+    return wave_sum(c);
+  };
+  int T = round_blocks(0, Lr);
+  for (int s0 = 256; s0 < B; s0 += 256) {
+    int L[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      L[r] = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(lens_rsrc, (s0 + 64 * r + lane) * 4, 0, 0));
+    T += round_blocks(s0, L);
   }
   T *= hkv;
   const int per = (T + a.num_waves - 1) / a.num_waves;
   const int t_begin = w * per;
   if (per == 0 || t_begin >= T) return;
 
-  // ---- 2. the segment and block of tile t_begin
+  // ---- 2. the segment and block of tile t_begin: the first sequence whose
+  // inclusive tile prefix passes t_begin
   int s_cur = -1, off = 0, L_cur = 0, seg0 = 0;
   {
     int base = 0;
-    for (int s0 = 0; s0 < B && s_cur < 0; s0 += 64) {
-      const int L = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(lens_rsrc, (s0 + lane) * 4, 0, 0));
+    auto scan64 = [&](int s0, int L) {
       const int c = hkv * ((L + kBlock - 1) / kBlock);
       const int incl = wave_incl_scan(c, lane);
       const uint64_t m = __builtin_amdgcn_ballot_w64(base + incl > t_begin);
@@ -231,7 +240,12 @@ decode_stream_kernel(StreamArgs a) {
         seg0 = excl;
       }
       base += readlane_i(incl, 63);
-    }
+    };
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (s_cur < 0) scan64(64 * r, Lr[r]);
+    for (int s0 = 256; s0 < B && s_cur < 0; s0 += 64)
+      scan64(s0, static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(lens_rsrc, (s0 + lane) * 4, 0, 0)));
   }
   if (s_cur < 0 || L_cur <= 0) return;   // lengths changed under us: nothing safe to do
   // tile t_begin is block j0 of KV head g0 of sequence s_cur
@@ -276,8 +290,21 @@ decode_stream_kernel(StreamArgs a) {
   // the ends of a piece: a segment's ends or the ends of this wave's range.
   __shared__ u32x4_t s_desc[kCap];
   int w_s = s_cur, w_g = g0, w_j = j0, w_L = L_cur, w_nb = nb0, w_seg = seg0 + g0 * nb0;
-  int lwin_base = s_cur + 1;           // lengths of the next 64 sequences, one per lane
-  int lwin = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(lens_rsrc, (lwin_base + lane) * 4, 0, 0));
+  // lengths for the walk: from Lr for the first 256 sequences, past them
+  // from a window of 64 (lane i -> sequence lwin_base + i) loaded on demand
+  int lwin_base = -1, lwin = 0;
+  auto len_of = [&](int sq) -> int {
+    if (sq < 256) {
+      const int r = sq >> 6;
+      const int v = (r == 0) ? Lr[0] : (r == 1) ? Lr[1] : (r == 2) ? Lr[2] : Lr[3];
+      return readlane_i(v, sq & 63);
+    }
+    if (lwin_base < 0 || sq - lwin_base >= 64) {
+      lwin_base = sq;
+      lwin = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(lens_rsrc, (lwin_base + lane) * 4, 0, 0));
+    }
+    return readlane_i(lwin, sq - lwin_base);
+  };
   const int tbl_bytes = B * a.max_blocks * 4;
   const __amdgpu_buffer_rsrc_t tbl_rsrc = make_rsrc(a.block_tables, tbl_bytes);
 
@@ -448,11 +475,7 @@ decode_stream_kernel(StreamArgs a) {
           w_g = 0;
           do {
             ++w_s;
-            if (w_s - lwin_base >= 64) {
-              lwin_base = w_s;
-              lwin = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(lens_rsrc, (lwin_base + lane) * 4, 0, 0));
-            }
-            w_L = readlane_i(lwin, w_s - lwin_base);
+            w_L = (w_s < B) ? len_of(w_s) : 0;
           } while (w_L == 0 && w_s + 1 < B);
           w_nb = (w_L + kBlock - 1) / kBlock;
         }
@@ -777,9 +800,9 @@ void launch_simple(int fmt, bool out_f32, dim3 grid, hipStream_t st, const char*
 template <int kD, int kG>
 void launch_stream_g(bool fp8, int nw, hipStream_t st, const StreamArgs& a) {
   if (fp8)
-    decode_stream_kernel<kD, kG, true, 0><<<nw, 64, 0, st>>>(a);
+    decode_stream_kernel<kD, kG, true, kAuxNonTemporal><<<nw, 64, 0, st>>>(a);
   else
-    decode_stream_kernel<kD, kG, false, 0><<<nw, 64, 0, st>>>(a);
+    decode_stream_kernel<kD, kG, false, kAuxNonTemporal><<<nw, 64, 0, st>>>(a);
 }
 
 template <int kD>

@@ -69,9 +69,9 @@ def test_workspace_size_formula():
     f32 = pk.CacheDesc(64, 8, 128, "f32")
     assert pk.decode_workspace_bytes(f32, 8, 64, 32768) == 8 * 64 * 64 * 130 * 4
     # bf16 / fp8 path: arrival counters (256-byte aligned), then two partial
-    # slots of G * (D + 2) floats for each of the 8 waves per compute unit;
+    # slots of G * (D + 2) floats for each of the 4 waves per compute unit;
     # without a visible GPU the library assumes MI355X's 256 compute units
-    waves = 256 * 8
+    waves = 256 * 4
     bf = pk.CacheDesc(64, 8, 128, "bf16")
     assert pk.decode_workspace_bytes(bf, 256, 32, 4096) == 256 * 8 * 4 + waves * 2 * 4 * 130 * 4
     assert pk.decode_workspace_bytes(bf, 3, 64, 10) == 256 + waves * 2 * 8 * 130 * 4
