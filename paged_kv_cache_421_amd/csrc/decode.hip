@@ -68,6 +68,8 @@ constexpr float kRescaleSlack = 8.0f;   // log2 units: exponentials stay <= 2^8
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 constexpr int kAuxNonTemporal = 2;      // buffer load cache policy: nt
 constexpr int kWavesPerCU = 4;          // fast path: persistent waves per CU (one per SIMD)
+constexpr int kWavesPerGroup = 1;       // fast path: waves per work-group
+constexpr int kPadLds = 0;              // fast path: extra LDS per work-group (occupancy cap)
 constexpr int kMinTilesPerWave = 8;     // fast path: at least this many tiles per wave
 constexpr int kNT = 3;                  // fast path: tiles in flight per wave
 constexpr int kCap = 512;               // fast path: tile descriptors per round (LDS)
@@ -168,7 +170,7 @@ struct StreamArgs {
 // kD: head_dim; kG: query heads per KV head (1..8); kFp8: E4M3 cache (else
 // bf16); kAux: cache policy bits of the KV loads.
 template <int kD, int kG, bool kFp8, int kAux>
-__global__ void __launch_bounds__(64)
+__global__ void __launch_bounds__(64 * kWavesPerGroup)
 decode_stream_kernel(StreamArgs a) {
   constexpr int kE = kFp8 ? 1 : 2;                 // bytes per cache element
   constexpr int kRowBytes = kD * kE;
@@ -179,8 +181,11 @@ decode_stream_kernel(StreamArgs a) {
   using KChunk = typename std::conditional<kFp8, u32x2_t, u32x4_t>::type;
   using VChunk = typename std::conditional<kFp8, uint32_t, u32x2_t>::type;
 
-  const int w = blockIdx.x;
-  const int lane = threadIdx.x;
+  // waves of a work-group are independent (no barriers): a work-group only
+  // places kWavesPerGroup waves on one CU together
+  const int wig = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int w = blockIdx.x * kWavesPerGroup + wig;
+  const int lane = threadIdx.x & 63;
   const int B = a.num_seqs;
   const int hkv = a.hkv;
   const int hq = hkv * kG;
@@ -254,33 +259,14 @@ decode_stream_kernel(StreamArgs a) {
   const int j0 = off - g0 * nb0;
   const int n_total = min(per, T - t_begin);
 
-  // q of a segment travels with each ring slot in compact form: lane c of
-  // register u holds the 16 bytes at (64*u + c)*16 of the segment's [kG][kD]
-  // bf16 rows.  The consumer rearranges it into the MFMA A operand: row i =
-  // head (zero rows past kG), lane l holds dims 32*kk + 8*(l/16) .. +7 of
-  // head l%16.
+  // q of a segment travels with each ring slot, loaded straight into the
+  // MFMA B-operand layout of S^T = K q^T: lane (row, quad) holds dims
+  // 32*kk + 8*quad .. +7 of head `row`; rows past kG fall outside the
+  // load's range and read as zero.
   constexpr int kQBytes = kG * kD * 2;
-  constexpr int kQC = (kQBytes + 1023) / 1024;              // 16-byte loads per lane
   const int row = lane & 15;
   const int quad = lane >> 4;
-  auto build_qa = [&](const u32x4_t (&qc)[kQC], bf16x8_t (&qa)[kKK]) {
-#pragma unroll
-    for (int kk = 0; kk < kKK; ++kk) {
-      const int c = row * (kD / 8) + 4 * kk + quad;        // 16-byte chunk wanted
-      const int src = (c & 63) * 4;                         // ds_bpermute byte address
-      u32x4_t v = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int u = 0; u < kQC; ++u) {
-        u32x4_t t;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          t[e] = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src, static_cast<int>(qc[u][e])));
-        if ((c >> 6) == u) v = t;
-      }
-      if (row >= kG) v = u32x4_t{0u, 0u, 0u, 0u};
-      qa[kk] = __builtin_bit_cast(bf16x8_t, v);
-    }
-  };
+  const int q_lane_off = (row * kD + 8 * quad) * 2;            // + 64*kk
 
   // ---- 3. tile descriptors, built in LDS in rounds of up to kCap tiles
   // word 0: tile index block * Hkv + g (the block's position in the table
@@ -288,7 +274,8 @@ decode_stream_kernel(StreamArgs a) {
   //         g << 7 | blocks of the sequence << 16; word 2: sequence;
   // word 3: list index of the segment's first tile.  "first"/"last" mark
   // the ends of a piece: a segment's ends or the ends of this wave's range.
-  __shared__ u32x4_t s_desc[kCap];
+  __shared__ u32x4_t s_desc_all[kWavesPerGroup][kCap];
+  u32x4_t* s_desc = s_desc_all[wig];
   int w_s = s_cur, w_g = g0, w_j = j0, w_L = L_cur, w_nb = nb0, w_seg = seg0 + g0 * nb0;
   // lengths for the walk: from Lr for the first 256 sequences, past them
   // from a window of 64 (lane i -> sequence lwin_base + i) loaded on demand
@@ -341,14 +328,13 @@ decode_stream_kernel(StreamArgs a) {
     const int wl = (seg + nb - 1) / per;
     if (wf == wl) {   // the whole segment was in this wave: write the output
       if (row < kG) {
-        const float inv = a.v_scale / l_tot;
+        const float inv = a.v_scale * __builtin_amdgcn_rcpf(l_tot);
         uint16_t* orow = a.out + (static_cast<int64_t>(s) * hq + g * kG + row) * kD + 4 * quad;
 #pragma unroll
         for (int c = 0; c < kVC; ++c) {
-          u32x2_t pk;
-          pk[0] = f32_to_bf16_bits(oacc[c][0] * inv) | (f32_to_bf16_bits(oacc[c][1] * inv) << 16);
-          pk[1] = f32_to_bf16_bits(oacc[c][2] * inv) | (f32_to_bf16_bits(oacc[c][3] * inv) << 16);
-          *reinterpret_cast<u32x2_t*>(orow + 16 * c) = pk;
+          const bf16x4_t pk = {static_cast<__bf16>(oacc[c][0] * inv), static_cast<__bf16>(oacc[c][1] * inv),
+                               static_cast<__bf16>(oacc[c][2] * inv), static_cast<__bf16>(oacc[c][3] * inv)};
+          *reinterpret_cast<bf16x4_t*>(orow + 16 * c) = pk;
         }
       }
       return;
@@ -381,17 +367,13 @@ decode_stream_kernel(StreamArgs a) {
     pend_nb[which] = nb;
   };
 
-  // Arrival of a stored piece; the last piece of a segment merges them all:
+  // The last piece of a segment merges all of them:
   // out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p, computed online.
   // Lane l handles elements 4*(l + 64*i) .. +3 of the [kG][kD] output.
-  auto arrive = [&](int s, int g, int seg, int nb) {
+  auto merge = [&](int s, int g, int seg, int nb) {
     const int wf = seg / per;
     const int wl = (seg + nb - 1) / per;
     uint32_t* ctr = a.counters + static_cast<int64_t>(s) * hkv + g;
-    uint32_t prev = 0;
-    if (lane == 0) prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    prev = static_cast<uint32_t>(readlane_i(static_cast<int>(prev), 0));
-    if (prev != static_cast<uint32_t>(wl - wf)) return;   // not the last piece
     constexpr int kE4 = (kG * kD / 4 + 63) / 64;          // 4-float groups per lane
     float M[kE4], den[kE4];
     f32x4_t num[kE4];
@@ -434,20 +416,19 @@ decode_stream_kernel(StreamArgs a) {
     for (int i = 0; i < kE4; ++i) {
       const int e = 4 * (lane + 64 * i);
       if (e < kG * kD) {
-        const float inv = a.v_scale / den[i];
-        u32x2_t pk;
-        pk[0] = f32_to_bf16_bits(num[i][0] * inv) | (f32_to_bf16_bits(num[i][1] * inv) << 16);
-        pk[1] = f32_to_bf16_bits(num[i][2] * inv) | (f32_to_bf16_bits(num[i][3] * inv) << 16);
-        *reinterpret_cast<u32x2_t*>(orow + e) = pk;
+        const float inv = a.v_scale * __builtin_amdgcn_rcpf(den[i]);
+        const bf16x4_t pk = {static_cast<__bf16>(num[i][0] * inv), static_cast<__bf16>(num[i][1] * inv),
+                             static_cast<__bf16>(num[i][2] * inv), static_cast<__bf16>(num[i][3] * inv)};
+        *reinterpret_cast<bf16x4_t*>(orow + e) = pk;
       }
     }
     if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
 
-  // ring slots: tile data and the segment's compact q
+  // ring slots: tile data and the segment's q
   KChunk kt[kNT][kKK];
   VChunk vt[kNT][kVC];
-  u32x4_t qc[kNT][kQC];
+  u32x4_t qs[kNT][kKK];
 
   for (int done = 0; done < n_total;) {
     const int n = min(kCap, n_total - done);
@@ -525,7 +506,7 @@ decode_stream_kernel(StreamArgs a) {
       }
       const __amdgpu_buffer_rsrc_t rq = make_rsrc(reinterpret_cast<const char*>(a.q) + q_off, q_nrec);
 #pragma unroll
-      for (int u = 0; u < kQC; ++u) qc[slot][u] = __builtin_amdgcn_raw_buffer_load_b128(rq, (64 * u + lane) * 16, 0, 0);
+      for (int kk = 0; kk < kKK; ++kk) qs[slot][kk] = __builtin_amdgcn_raw_buffer_load_b128(rq, q_lane_off + 64 * kk, 0, 0);
       const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k_cache + tile_off, k_nrec);
       const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v_cache + tile_off, v_nrec);
 #pragma unroll
@@ -554,7 +535,8 @@ decode_stream_kernel(StreamArgs a) {
         l_part = 0.f;
 #pragma unroll
         for (int c = 0; c < kVC; ++c) oacc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        build_qa(qc[slot], qa);
+#pragma unroll
+        for (int kk = 0; kk < kKK; ++kk) qa[kk] = __builtin_bit_cast(bf16x8_t, qs[slot][kk]);
       }
 
       // ---- logits, transposed: acc[r] = S[head row][token 4*quad + r]
@@ -604,10 +586,8 @@ decode_stream_kernel(StreamArgs a) {
       bf16x4_t pb;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float pr = __builtin_amdgcn_exp2f(x[r] - m_ref);
-        const uint32_t bits = f32_to_bf16_bits(pr);
-        pb[r] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(bits));
-        l_part += __uint_as_float(bits << 16);
+        pb[r] = static_cast<__bf16>(__builtin_amdgcn_exp2f(x[r] - m_ref));
+        l_part += static_cast<float>(pb[r]);
       }
       // V columns past the context: zero them (0 * garbage could be NaN)
       uint32_t vmask_lo = 0xFFFFFFFFu, vmask_hi = 0xFFFFFFFFu;
@@ -655,12 +635,27 @@ decode_stream_kernel(StreamArgs a) {
   }
 
   // ---- 6. count the arrivals of the stored pieces (once every store of
-  // this wave has completed), merge where this wave is the last piece
+  // this wave has completed; both counters at once), then merge the
+  // segments of which this wave holds the last piece
   if (pend_s[0] >= 0 || pend_s[1] >= 0) {
     __builtin_amdgcn_s_waitcnt(0);
+    uint32_t prev[2] = {0u, 0u};
+    if (lane == 0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      if (pend_s[i] >= 0) arrive(pend_s[i], pend_g[i], pend_seg[i], pend_nb[i]);
+      for (int i = 0; i < 2; ++i)
+        if (pend_s[i] >= 0)
+          prev[i] = __hip_atomic_fetch_add(a.counters + static_cast<int64_t>(pend_s[i]) * hkv + pend_g[i],
+                                           1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if (pend_s[i] < 0) continue;
+      const int wf = pend_seg[i] / per;
+      const int wl = (pend_seg[i] + pend_nb[i] - 1) / per;
+      if (static_cast<uint32_t>(readlane_i(static_cast<int>(prev[i]), 0)) ==
+          static_cast<uint32_t>(wl - wf))                      // the last piece
+        merge(pend_s[i], pend_g[i], pend_seg[i], pend_nb[i]);
+    }
   }
 }
 
@@ -800,9 +795,11 @@ void launch_simple(int fmt, bool out_f32, dim3 grid, hipStream_t st, const char*
 template <int kD, int kG>
 void launch_stream_g(bool fp8, int nw, hipStream_t st, const StreamArgs& a) {
   if (fp8)
-    decode_stream_kernel<kD, kG, true, kAuxNonTemporal><<<nw, 64, 0, st>>>(a);
+    decode_stream_kernel<kD, kG, true, kAuxNonTemporal>
+        <<<nw / kWavesPerGroup, 64 * kWavesPerGroup, kPadLds, st>>>(a);
   else
-    decode_stream_kernel<kD, kG, false, kAuxNonTemporal><<<nw, 64, 0, st>>>(a);
+    decode_stream_kernel<kD, kG, false, kAuxNonTemporal>
+        <<<nw / kWavesPerGroup, 64 * kWavesPerGroup, kPadLds, st>>>(a);
 }
 
 template <int kD>
@@ -957,7 +954,8 @@ extern "C" pa_status pa_decode(const pa_cache_desc* c, const void* k_cache, cons
     const int64_t waves_max = static_cast<int64_t>(device_cus()) * kWavesPerCU;
     const int64_t by_size = (max_tiles + kMinTilesPerWave - 1) / kMinTilesPerWave;
     // enough waves to cover the empty-sequence duty (one per 64 sequences)
-    const int64_t nw = std::max<int64_t>(std::min(waves_max, by_size), 1);
+    const int64_t nw = (std::max<int64_t>(std::min(waves_max, by_size), 1) + kWavesPerGroup - 1) /
+                       kWavesPerGroup * kWavesPerGroup;
     StreamArgs a;
     a.k_cache = kc;
     a.v_cache = vc;
