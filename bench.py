@@ -26,12 +26,18 @@ timed region starts.
 The JSON line also carries
   * ``roofline``: pa_decode's algorithmic KV bytes per call (sum over
     sequences of L * Hkv * D * 2 bytes * 2 for K and V) over its mean
-    duration, taken with HIP events around every pa_decode call of the timed
-    steps on the stream it runs on, against the 8 TB/s HBM peak;
+    duration, taken with HIP events recorded around every pa_decode of the
+    timed steps on the stream it runs on, against the 8 TB/s HBM peak;
+    ``traffic`` is the HBM bytes per call from the committed rocprofv3
+    counter summary, when that was taken on the current kernel source;
   * ``cpu_baseline``: the CPU float64 oracle's decode of the same batch on the
     host, single-threaded.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers N]
+                      [--no-cpu-baseline] [--copy-calibration MIB]
+
+--copy-calibration MIB ends the run with plain device copies of MIB MiB, the
+reference a hardware-counter run scales FETCH_SIZE / WRITE_SIZE by.
 """
 from __future__ import annotations
 
@@ -65,18 +71,29 @@ def _kv_bytes(lens, hkv, d, elem):
     return int(np.asarray(lens, dtype=np.int64).sum()) * hkv * d * elem * 2
 
 
-def _traffic_per_call():
-    """HBM bytes per pa_decode call from the committed rocprofv3 counter
-    summary, if it was taken on the current decode source; else None."""
+def kernel_source_sha256():
+    """Hash of the decode kernel's device code: the text from the kernel's
+    signature line to the end of its body in decode.hip."""
+    text = open(DECODE_SRC).read()
+    a = text.index("decode_stream_kernel(StreamArgs a) {")
+    b = text.index("// Zero-fill of a decode workspace.")
+    return hashlib.sha256(text[a:b].encode()).hexdigest()
+
+
+def _traffic_per_call(kv_bytes):
+    """HBM bytes of one pa_decode call reading ``kv_bytes`` algorithmic KV
+    bytes, from the committed rocprofv3 counter summary (bytes read per
+    algorithmic byte, bytes written per call), if that summary was taken on
+    the current kernel source; else None."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     text = open(TRAFFIC_FILE).read()
-    src = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
-    m_src = re.search(r"decode_source_sha256:\s*([0-9a-f]{64})", text)
-    m_b = re.search(r"hbm_bytes_per_call:\s*([0-9.eE+]+)", text)
-    if not m_src or not m_b or m_src.group(1) != src:
+    m_src = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_r = re.search(r"fetch_bytes_per_algorithmic_byte:\s*([0-9.eE+]+)", text)
+    m_w = re.search(r"write_bytes_per_call:\s*([0-9.eE+]+)", text)
+    if not (m_src and m_r and m_w) or m_src.group(1) != kernel_source_sha256():
         return None
-    return float(m_b.group(1))
+    return float(m_r.group(1)) * kv_bytes + float(m_w.group(1))
 
 
 def cpu_baseline(w, budget_s=10.0):
@@ -123,6 +140,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); the decode path "
@@ -240,7 +258,7 @@ def main():
     mean_kv = statistics.mean(kv_per_call)
     achieved = mean_kv / mean_dec_s / 1e9
     steps_s = wall / args.steps
-    traffic = _traffic_per_call()
+    traffic = _traffic_per_call(mean_kv)
     _log(f"bench: pa_decode mean {mean_dec_s * 1e6:.1f} us (p10 "
          f"{np.percentile(dec_ms, 10) * 1e3:.1f}, p90 {np.percentile(dec_ms, 90) * 1e3:.1f}), "
          f"{achieved:.0f} GB/s; step {steps_s * 1e3:.3f} ms")
@@ -274,7 +292,7 @@ def main():
         "decode_us_p10": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
         "decode_us_p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),
         "roofline": {
-            "kernel": "pa_decode (partition pass + log-sum-exp reduce)",
+            "kernel": "decode_stream_kernel (pa_decode: one persistent kernel)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
@@ -283,6 +301,14 @@ def main():
             "traffic": None if traffic is None else round(traffic / mean_dec_s / 1e9, 1),
         },
     }
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        _log(f"bench: copy calibration {n} bytes x 3")
     if not args.no_cpu_baseline:
         _log("bench: timing the CPU oracle")
         res["cpu_baseline"] = cpu_baseline(w)

@@ -794,12 +794,11 @@ void launch_simple(int fmt, bool out_f32, dim3 grid, hipStream_t st, const char*
 
 template <int kD, int kG>
 void launch_stream_g(bool fp8, int nw, hipStream_t st, const StreamArgs& a) {
+  const dim3 grid(nw / kWavesPerGroup), block(64 * kWavesPerGroup);
   if (fp8)
-    decode_stream_kernel<kD, kG, true, kAuxNonTemporal>
-        <<<nw / kWavesPerGroup, 64 * kWavesPerGroup, kPadLds, st>>>(a);
+    decode_stream_kernel<kD, kG, true, kAuxNonTemporal><<<grid, block, kPadLds, st>>>(a);
   else
-    decode_stream_kernel<kD, kG, false, kAuxNonTemporal>
-        <<<nw / kWavesPerGroup, 64 * kWavesPerGroup, kPadLds, st>>>(a);
+    decode_stream_kernel<kD, kG, false, kAuxNonTemporal><<<grid, block, kPadLds, st>>>(a);
 }
 
 template <int kD>
