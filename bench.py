@@ -27,7 +27,11 @@ The JSON line also carries
   * ``roofline``: pa_decode's algorithmic KV bytes per call (sum over
     sequences of L * Hkv * D * 2 bytes * 2 for K and V) over its mean
     duration, taken with HIP events recorded around every pa_decode of the
-    timed steps on the stream it runs on, against the 8 TB/s HBM peak;
+    timed steps on the stream it runs on, against the 8 TB/s HBM peak.  The
+    events are created without the system-scope fence (the path exchanges
+    nothing with the host); each one still delays the next dispatch by a few
+    microseconds, which the event interval includes, so the figure is a
+    slight underestimate of the kernel's own rate;
     ``traffic`` is the HBM bytes per call from the committed rocprofv3
     counter summary, when that was taken on the current kernel source;
   * ``cpu_baseline``: the CPU float64 oracle's decode of the same batch on the
@@ -71,6 +75,43 @@ def _kv_bytes(lens, hkv, d, elem):
     return int(np.asarray(lens, dtype=np.int64).sum()) * hkv * d * elem * 2
 
 
+class HipEvent:
+    """A HIP timing event recorded on an explicit stream (ctypes on the HIP
+    runtime that torch has loaded).  hipEventDisableSystemFence: recording it
+    does not flush caches to system scope."""
+    _hip = None
+    FLAGS = 0x20000000          # hipEventDisableSystemFence
+
+    def __init__(self):
+        import ctypes
+        if HipEvent._hip is None:
+            HipEvent._hip = ctypes.CDLL("libamdhip64.so.7")
+        self._c = ctypes
+        self.h = ctypes.c_void_p()
+        self._check(HipEvent._hip.hipEventCreateWithFlags(ctypes.byref(self.h),
+                                                          ctypes.c_uint(self.FLAGS)), "create")
+
+    def _check(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"hipEvent{what} failed with HIP error {rc}")
+
+    def record(self, stream):
+        self._check(HipEvent._hip.hipEventRecord(self.h, self._c.c_void_p(stream.cuda_stream)),
+                    "Record")
+
+    def elapsed_ms(self, end):
+        ms = self._c.c_float()
+        self._check(HipEvent._hip.hipEventSynchronize(end.h), "Synchronize")
+        self._check(HipEvent._hip.hipEventElapsedTime(self._c.byref(ms), self.h, end.h),
+                    "ElapsedTime")
+        return ms.value
+
+    def destroy(self):
+        if self.h:
+            self._check(HipEvent._hip.hipEventDestroy(self.h), "Destroy")
+            self.h = self._c.c_void_p()
+
+
 def kernel_source_sha256():
     """Hash of the decode kernel's device code: the text from the kernel's
     signature line to the end of its body in decode.hip."""
@@ -112,8 +153,8 @@ def cpu_baseline(w, budget_s=10.0):
     slots = np.concatenate([per[s] for s in range(w.B)])
     assert len(slots) == len(w.row_seq) and np.all(w.row_pos == np.arange(len(slots)) -
                                                   np.repeat(starts, w.lens))
-    kc, vc = oracle.write_kv(np.zeros((w.num_blocks, w.Hkv, 16, w.D), np.uint16),
-                             np.zeros((w.num_blocks, w.Hkv, w.D, 16), np.uint16),
+    shape = (w.num_blocks, w.Hkv, 16, w.D)
+    kc, vc = oracle.write_kv(np.zeros(shape, np.uint16), np.zeros(shape, np.uint16),
                              w.k_rows, w.v_rows, slots, "bf16", "bf16")
     cap = max(-(-int(L) // 16) for L in w.lens)
     bt, cl = bm.pack(list(range(w.B)), cap)
@@ -157,6 +198,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
     NL = args.layers
 
     _log("bench: generating the GQA batch-256 workload")
@@ -175,7 +217,7 @@ def main():
         per.append(sl)
     slots = torch.from_numpy(np.concatenate(per)).to(dev)
     kc = [torch.zeros(desc.shape, dtype=torch.bfloat16, device=dev) for _ in range(NL)]
-    vc = [torch.zeros(desc.v_shape, dtype=torch.bfloat16, device=dev) for _ in range(NL)]
+    vc = [torch.zeros(desc.shape, dtype=torch.bfloat16, device=dev) for _ in range(NL)]
     k_rows = torch.from_numpy(w.k_rows.view(np.int16)).to(dev).view(torch.bfloat16)
     v_rows = torch.from_numpy(w.v_rows.view(np.int16)).to(dev).view(torch.bfloat16)
     pk.write_kv(desc, kc[0], vc[0], k_rows, v_rows, slots)
@@ -227,13 +269,13 @@ def main():
         buf_ev[b] = ev
         max_len = int(lens.max())
         for l in range(NL):
-            pk.write_kv(desc, kc[l], vc[l], k_new[l], v_new[l], d_slots)
+            pk.write_kv(desc, kc[l], vc[l], k_new[l], v_new[l], d_slots, stream=stream)
             if ev_pairs is not None:
-                ev_pairs[l][0].record()
+                ev_pairs[l][0].record(stream)
             pk.decode(desc, kc[l], vc[l], q[l], out[l], d_bt, d_cl, max_len, float(w.scale),
-                      workspace)
+                      workspace, stream=stream)
             if ev_pairs is not None:
-                ev_pairs[l][1].record()
+                ev_pairs[l][1].record(stream)
         return _kv_bytes(lens, Hkv, D, 2)
 
     _log(f"bench: {NL} layers x {w.num_blocks} blocks, warmup {args.warmup}, steps {args.steps}")
@@ -241,8 +283,7 @@ def main():
         step(i, None)
     torch.cuda.synchronize()
 
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(NL)] for _ in range(args.steps)]
+    evs = [[(HipEvent(), HipEvent()) for _ in range(NL)] for _ in range(args.steps)]
     kv_per_call = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -253,7 +294,11 @@ def main():
     wall = t1 - t0
     assert torch.isfinite(out[0].float()).all(), "non-finite decode output"
 
-    dec_ms = [a.elapsed_time(b) for row in evs for (a, b) in row]
+    dec_ms = [a.elapsed_ms(b) for row in evs for (a, b) in row]
+    for row in evs:
+        for a, b in row:
+            a.destroy()
+            b.destroy()
     mean_dec_s = statistics.mean(dec_ms) / 1e3
     mean_kv = statistics.mean(kv_per_call)
     achieved = mean_kv / mean_dec_s / 1e9

@@ -28,14 +28,11 @@
  *     device arrays (block ids, slots, context lengths) cannot be checked on
  *     the host; out-of-range values there are undefined behaviour.
  *
- * Cache layout (one K and one V tensor, same dtype and size):
- *   K: k_cache[num_blocks][num_kv_heads][16][head_dim] -- element (block b,
- *      kv head g, slot t, dim d) at ((b*Hkv + g)*16 + t)*D + d;
- *   V: v_cache[num_blocks][num_kv_heads][head_dim][16] -- element (b, g, t, d)
- *      at ((b*Hkv + g)*D + d)*16 + t.
- *   Either way one (block, head) tile is 16*D contiguous elements.  The V
- *   tile is stored dims-major so that it is directly the operand of the
- *   matrix instruction that forms P.V on gfx950.
+ * Cache layout (one K and one V tensor, same shape and dtype):
+ *   cache[num_blocks][num_kv_heads][16][head_dim], row-major, so element
+ *   (block b, kv head g, slot t, dim d) is at ((b*Hkv + g)*16 + t)*D + d and
+ *   one (block, head) tile is 16*D contiguous elements; a token's row of one
+ *   head is D contiguous elements, so appending a token writes whole rows.
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H

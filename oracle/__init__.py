@@ -20,14 +20,14 @@ forms, invariants, a library routine); none is "parity unpinned".
 """
 from .formats import (bf16_to_f64, e4m3_to_f64, e4m3_encode, e4m3_all_values,
                       widen_cache)
-from .attention import gather_kv, gather_v, decode, decode_partitioned, merge_partitions
+from .attention import gather_kv, decode, decode_partitioned, merge_partitions
 from .cache_ops import write_kv, copy_blocks
 from .block_manager import RefBlockManager, NoBlocks, UnknownSeq, SeqExists
 from .accounting import kv_cache_bytes, paged_utilisation, contiguous_utilisation
 
 __all__ = [
     "bf16_to_f64", "e4m3_to_f64", "e4m3_encode", "e4m3_all_values", "widen_cache",
-    "gather_kv", "gather_v", "decode", "decode_partitioned", "merge_partitions",
+    "gather_kv", "decode", "decode_partitioned", "merge_partitions",
     "write_kv", "copy_blocks",
     "RefBlockManager", "NoBlocks", "UnknownSeq", "SeqExists",
     "kv_cache_bytes", "paged_utilisation", "contiguous_utilisation",

@@ -19,10 +19,8 @@ sequence's block table.
 
 Readings where the pages are silent:
 
-* Cache layout: two tensors.  K is ``[num_blocks, Hkv, 16, D]``, element
-  (b, g, t, d) at ((b*Hkv + g)*16 + t)*D + d; V is ``[num_blocks, Hkv, D, 16]``,
-  element (b, g, t, d) at ((b*Hkv + g)*D + d)*16 + t.  Either way one
-  (block, KV head) tile is 16*D contiguous elements.
+* Cache layout: two tensors (K and V), each ``[num_blocks, Hkv, 16, D]``;
+  element (b, g, t, d) sits at ((b*Hkv + g)*16 + t)*D + d.
 * Query head h reads KV head floor(h / G), G = Hq / Hkv.
 * Only the first ``context_lens[s]`` positions are attended; slots past that in
   the last block are never read (so garbage there cannot leak in), and table
@@ -52,8 +50,7 @@ def _q64(q: np.ndarray, q_fmt: str) -> np.ndarray:
 
 def gather_kv(cache: np.ndarray, block_table_row: np.ndarray, L: int,
               g: int) -> np.ndarray:
-    """Contiguous [L, D] key rows of KV head g for one sequence, in storage
-    format, from a token-major cache ``[num_blocks, Hkv, 16, D]``.
+    """Contiguous [L, D] rows of KV head g for one sequence, in storage format.
 
     Walks table entries j = 0 .. ceil(L/16)-1, takes physical block
     ``block_table_row[j]`` (all 16 slots of head g), concatenates and keeps
@@ -65,20 +62,6 @@ def gather_kv(cache: np.ndarray, block_table_row: np.ndarray, L: int,
     ids = np.asarray(block_table_row[:n], dtype=np.int64)
     tiles = cache[ids, g, :, :]                  # [n, 16, D]
     return tiles.reshape(n * BLOCK, cache.shape[-1])[:L]
-
-
-def gather_v(cache: np.ndarray, block_table_row: np.ndarray, L: int,
-             g: int) -> np.ndarray:
-    """Contiguous [L, D] value rows of KV head g for one sequence, in storage
-    format, from a dims-major cache ``[num_blocks, Hkv, D, 16]``: the same
-    table walk as ``gather_kv``, each tile transposed back to [16, D]."""
-    n = -(-int(L) // BLOCK)
-    D = cache.shape[2]
-    if n == 0:
-        return cache[:0, g, :, 0].reshape(0, D)
-    ids = np.asarray(block_table_row[:n], dtype=np.int64)
-    tiles = cache[ids, g, :, :].transpose(0, 2, 1)   # [n, 16, D]
-    return tiles.reshape(n * BLOCK, D)[:L]
 
 
 def decode(q: np.ndarray, q_fmt: str, k_cache: np.ndarray, v_cache: np.ndarray,
@@ -113,7 +96,7 @@ def decode(q: np.ndarray, q_fmt: str, k_cache: np.ndarray, v_cache: np.ndarray,
                     weights[(s, h)] = np.zeros(0)
                 continue
             K = widen_cache(gather_kv(k_cache, block_tables[s], L, g), fmt, k_scale)
-            V = widen_cache(gather_v(v_cache, block_tables[s], L, g), fmt, v_scale)
+            V = widen_cache(gather_kv(v_cache, block_tables[s], L, g), fmt, v_scale)
             for h in heads:
                 z = sc * (K @ q64[s, h])
                 m = z.max()
@@ -159,7 +142,7 @@ def decode_partitioned(q: np.ndarray, q_fmt: str, k_cache: np.ndarray,
                 out[s, g * G:(g + 1) * G] = 0.0
                 continue
             K = widen_cache(gather_kv(k_cache, block_tables[s], L, g), fmt, k_scale)
-            V = widen_cache(gather_v(v_cache, block_tables[s], L, g), fmt, v_scale)
+            V = widen_cache(gather_kv(v_cache, block_tables[s], L, g), fmt, v_scale)
             for h in range(g * G, (g + 1) * G):
                 ms, ls, os_ = [], [], []
                 for start in range(0, L, partition):
@@ -191,7 +174,7 @@ def reference_rows(q: np.ndarray, q_fmt: str, k_cache, v_cache, fmt,
             continue
         g = h // G
         K = widen_cache(gather_kv(k_cache, block_tables[s], L, g), fmt, k_scale)
-        V = widen_cache(gather_v(v_cache, block_tables[s], L, g), fmt, v_scale)
+        V = widen_cache(gather_kv(v_cache, block_tables[s], L, g), fmt, v_scale)
         z = sc * (K @ q64[s, h])
         e = np.exp(z - z.max())
         rows.append((e / e.sum()) @ V)

@@ -11,9 +11,8 @@
   Precondition (reading): destinations are distinct and no destination is also
   a source, so the pairs commute.
 
-K caches are ``[num_blocks, Hkv, 16, D]`` and V caches ``[num_blocks, Hkv,
-D, 16]`` arrays in storage format (float32, uint16 bf16 bits, or uint8 E4M3
-codes).  Both functions return new arrays and
+Caches are ``[num_blocks, Hkv, 16, D]`` arrays in storage format (float32,
+uint16 bf16 bits, or uint8 E4M3 codes).  Both functions return new arrays and
 leave every byte they do not write untouched.
 """
 from __future__ import annotations
@@ -41,8 +40,7 @@ def write_kv(k_cache: np.ndarray, v_cache: np.ndarray, k: np.ndarray,
     """Scatter rows ``k[i], v[i]`` ([Hkv, D] each) into slot ``slot_mapping[i]``.
 
     For slot >= 0: block = slot // 16, offset = slot % 16, and for every KV
-    head g: k_cache[block, g, offset, :] = convert(k[i, g, :]) and
-    v_cache[block, g, :, offset] = convert(v[i, g, :]).  Returns the new
+    head g: cache[block, g, offset, :] = convert(row[g, :]).  Returns the new
     (k_cache, v_cache).
     """
     kc = k_cache.copy()
@@ -52,7 +50,7 @@ def write_kv(k_cache: np.ndarray, v_cache: np.ndarray, k: np.ndarray,
     blk = slots[keep] // BLOCK
     off = slots[keep] % BLOCK
     kc[blk, :, off, :] = _convert(np.asarray(k)[keep], src_fmt, fmt, k_scale)
-    vc[blk, :, :, off] = _convert(np.asarray(v)[keep], src_fmt, fmt, v_scale)
+    vc[blk, :, off, :] = _convert(np.asarray(v)[keep], src_fmt, fmt, v_scale)
     return kc, vc
 
 

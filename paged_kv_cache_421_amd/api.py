@@ -30,9 +30,8 @@ def dtype_code(x) -> int:
 
 
 class CacheDesc:
-    """pa_cache_desc: shape and format of a pair of K/V caches: K is
-    ``[num_blocks, num_kv_heads, 16, head_dim]`` (token-major tiles), V is
-    ``[num_blocks, num_kv_heads, head_dim, 16]`` (dims-major tiles)."""
+    """pa_cache_desc: shape and format of a pair of K/V caches, each
+    ``[num_blocks, num_kv_heads, 16, head_dim]``."""
 
     def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, dtype,
                  k_scale: float = 1.0, v_scale: float = 1.0):
@@ -41,13 +40,8 @@ class CacheDesc:
 
     @property
     def shape(self) -> Tuple[int, int, int, int]:
-        """Shape of the K cache."""
+        """Shape of each of the K and V caches."""
         return (self.c.num_blocks, self.c.num_kv_heads, BLOCK_SIZE, self.c.head_dim)
-
-    @property
-    def v_shape(self) -> Tuple[int, int, int, int]:
-        """Shape of the V cache."""
-        return (self.c.num_blocks, self.c.num_kv_heads, self.c.head_dim, BLOCK_SIZE)
 
     @property
     def torch_dtype(self):

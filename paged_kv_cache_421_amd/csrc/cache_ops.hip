@@ -3,14 +3,11 @@
 // write: each decode iteration stores the new token's K and V in its
 // sequence's current block (ybb.press, "vLLM PagedAttention 大模型推理架构深度实战",
 // §6); the destination of each row is a flat slot = block * 16 + offset.
-// K tiles are token-major and V tiles dims-major (the layout the decode
-// kernel's matrix instructions read directly).
 // copy: copy-on-write duplicates a shared block before it is modified
 // (same page, §2.3); a pair copies the whole block of both caches.
 //
 // Both kernels are pure data movement: one lane moves 16 source bytes, so a
-// wave reads 1 KiB per instruction; K rows and copied blocks are written the
-// same way, V elements with a 16-element stride.
+// wave moves 1 KiB per instruction with fully coalesced accesses.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -21,8 +18,8 @@
 namespace pagedkv {
 
 // One lane per 16-byte chunk of a source row [Hkv][D]; grid.y selects K or V.
-// K tiles are token-major ([16][D]): a chunk is one contiguous store.  V
-// tiles are dims-major ([D][16]): a chunk's elements go to 16-element strides.
+// A token's row of one head is contiguous in the cache, so every chunk is
+// one store.
 template <typename SrcChunk, int kElems, int kFmt>
 __global__ void __launch_bounds__(256)
 write_kv_kernel(char* __restrict__ k_cache, char* __restrict__ v_cache,
@@ -41,14 +38,9 @@ write_kv_kernel(char* __restrict__ k_cache, char* __restrict__ v_cache,
   const int c = rem - g * chunks_per_head;
   const int64_t blk = slot / kBlock;
   const int off = static_cast<int>(slot % kBlock);
-  const int64_t tile = (blk * hkv + g) * kBlock * d;          // first element of the tile
+  const int64_t dst_elem = ((blk * hkv + g) * kBlock + off) * d + c * kElems;
   const SrcChunk src = reinterpret_cast<const SrcChunk*>(is_v ? v : k)[idx];
   char* cache = is_v ? v_cache : k_cache;
-  // element i of this chunk (dim c*kElems + i) goes to element dst(i)
-  auto dst = [&](int i) -> int64_t {
-    const int dim = c * kElems + i;
-    return is_v ? tile + static_cast<int64_t>(dim) * kBlock + off : tile + off * d + dim;
-  };
   if constexpr (kFmt == PA_FP8_E4M3) {
     const float inv = is_v ? v_inv : k_inv;
     uint32_t codes[8];
@@ -57,29 +49,13 @@ write_kv_kernel(char* __restrict__ k_cache, char* __restrict__ v_cache,
       codes[2 * i] = e4m3_encode(bf16_lo(src[i]) * inv);
       codes[2 * i + 1] = e4m3_encode(bf16_hi(src[i]) * inv);
     }
-    if (!is_v) {
-      u32x2_t out;
-      out[0] = codes[0] | (codes[1] << 8) | (codes[2] << 16) | (codes[3] << 24);
-      out[1] = codes[4] | (codes[5] << 8) | (codes[6] << 16) | (codes[7] << 24);
-      *reinterpret_cast<u32x2_t*>(cache + dst(0)) = out;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) reinterpret_cast<uint8_t*>(cache)[dst(i)] = static_cast<uint8_t>(codes[i]);
-    }
+    u32x2_t out;
+    out[0] = codes[0] | (codes[1] << 8) | (codes[2] << 16) | (codes[3] << 24);
+    out[1] = codes[4] | (codes[5] << 8) | (codes[6] << 16) | (codes[7] << 24);
+    *reinterpret_cast<u32x2_t*>(cache + dst_elem) = out;
   } else {
     constexpr int kBytes = sizeof(SrcChunk) / kElems;
-    if (!is_v) {
-      *reinterpret_cast<SrcChunk*>(cache + dst(0) * kBytes) = src;
-    } else if constexpr (kBytes == 4) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) reinterpret_cast<uint32_t*>(cache)[dst(i)] = src[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        reinterpret_cast<uint16_t*>(cache)[dst(2 * i)] = static_cast<uint16_t>(src[i] & 0xFFFFu);
-        reinterpret_cast<uint16_t*>(cache)[dst(2 * i + 1)] = static_cast<uint16_t>(src[i] >> 16);
-      }
-    }
+    *reinterpret_cast<SrcChunk*>(cache + dst_elem * kBytes) = src;
   }
 }
 

@@ -27,13 +27,15 @@
 //  * Tiles are read with buffer loads whose range is the tile's valid rows:
 //    slots past the context length read as zero and move no data, and a
 //    slot of the ring with nothing to load has range 0.
-//  * Both products of a tile are MFMAs with the cache tile as the A operand,
-//    read straight from HBM in operand layout.  Logits are formed
-//    transposed, S^T = K q^T (16x16x32 bf16, one per 32 dims, q zero-padded
-//    to 16 heads), which leaves lane (head h, quad) holding S[h][4*quad..+3]
-//    -- exactly the B operand layout of the 16x16x16 bf16 MFMA that forms
-//    O^T = V^T P^T from the dims-major V tile, so P never moves between
-//    lanes.  The running max is moved only when a logit exceeds it by more
+//  * Both products of a tile are MFMAs with the cache tile as the A operand.
+//    Logits are formed transposed, S^T = K q^T (16x16x32 bf16, one per 32
+//    dims, q zero-padded to 16 heads), with K read from HBM straight into
+//    operand layout; this leaves lane (head h, quad) holding
+//    S[h][4*quad..+3] -- exactly the B operand layout of the 16x16x16 bf16
+//    MFMA that forms O^T = V^T P^T, so P never moves between lanes.  That
+//    MFMA wants 4 tokens of one dim per lane, the transpose of how the
+//    token-major V tile is stored: V rows are loaded whole, staged in a
+//    per-wave LDS tile, and read back down its columns.  The running max is moved only when a logit exceeds it by more
 //    than 2^8 (any reference max gives the same softmax): the common path
 //    has no cross-lane step at all.  P is rounded to bf16 once and the sum
 //    takes the rounded values, so the weights applied are exactly
@@ -177,9 +179,12 @@ decode_stream_kernel(StreamArgs a) {
   constexpr int kTileBytes = kBlock * kRowBytes;
   constexpr int kKK = kD / 32;                     // QK MFMA steps over head_dim
   constexpr int kVC = kD / 16;                     // P.V MFMAs (16 dims each)
+  constexpr int kLanesPerRow = kD / 8;             // V: lanes covering one token row
+  constexpr int kRowsPerLoad = 64 / kLanesPerRow;  // V: token rows per load
+  constexpr int kVLoads = kBlock / kRowsPerLoad;   // V: loads per lane
+  constexpr int kVStride = kRowBytes + 16;         // LDS row pitch of the V staging tile
   constexpr int kSlot = kG * (kD + 2);             // floats per partial slot
-  using KChunk = typename std::conditional<kFp8, u32x2_t, u32x4_t>::type;
-  using VChunk = typename std::conditional<kFp8, uint32_t, u32x2_t>::type;
+  using Chunk = typename std::conditional<kFp8, u32x2_t, u32x4_t>::type;
 
   // waves of a work-group are independent (no barriers): a work-group only
   // places kWavesPerGroup waves on one CU together
@@ -276,6 +281,10 @@ decode_stream_kernel(StreamArgs a) {
   // the ends of a piece: a segment's ends or the ends of this wave's range.
   __shared__ u32x4_t s_desc_all[kWavesPerGroup][kCap];
   u32x4_t* s_desc = s_desc_all[wig];
+  // V tile staging (token-major rows, padded pitch): it turns the V tile's
+  // rows into the P.V MFMA's operand, 4 tokens of one dim per lane
+  __shared__ __align__(16) char s_v_all[kWavesPerGroup][kBlock * kVStride];
+  char* s_v = s_v_all[wig];
   int w_s = s_cur, w_g = g0, w_j = j0, w_L = L_cur, w_nb = nb0, w_seg = seg0 + g0 * nb0;
   // lengths for the walk: from Lr for the first 256 sequences, past them
   // from a window of 64 (lane i -> sequence lwin_base + i) loaded on demand
@@ -295,13 +304,15 @@ decode_stream_kernel(StreamArgs a) {
   const int tbl_bytes = B * a.max_blocks * 4;
   const __amdgpu_buffer_rsrc_t tbl_rsrc = make_rsrc(a.block_tables, tbl_bytes);
 
-  // Lane offsets inside a (block, KV head) tile, in bytes.
-  //  K tile [16][D]: MFMA A operand, lane (row, quad) holds token `row`,
+  // Lane offsets inside a (block, KV head) tile [16][D], in bytes.
+  //  K: MFMA A operand of S^T = K q^T, lane (row, quad) holds token `row`,
   //    dims 32*kk + 8*quad .. +7.
-  //  V tile [D][16]: MFMA A operand of P.V, lane (row, quad) holds dim
-  //    16*c + row, tokens 4*quad .. +3.
+  //  V: plain rows, lane l holds token l / kLanesPerRow (+ kRowsPerLoad per
+  //    load), dims 8 * (l % kLanesPerRow) .. +7; they pass through LDS.
   const int k_off = (row * kD + 8 * quad) * kE;               // + 32*kk*kE
-  const int v_off = (row * kBlock + 4 * quad) * kE;           // + 16*c*kBlock*kE
+  const int v_c = lane % kLanesPerRow;
+  const int v_r = lane / kLanesPerRow;
+  const int v_off = (v_r * kD + 8 * v_c) * kE;                // + i*kRowsPerLoad*kRowBytes
 
   // ---- 4. consumer state: online softmax of the current segment piece.
   // Logits are computed transposed (S^T = K q^T), so lane (row, quad) holds
@@ -426,8 +437,8 @@ decode_stream_kernel(StreamArgs a) {
   };
 
   // ring slots: tile data and the segment's q
-  KChunk kt[kNT][kKK];
-  VChunk vt[kNT][kVC];
+  Chunk kt[kNT][kKK];
+  Chunk vt[kNT][kVLoads];
   u32x4_t qs[kNT][kKK];
 
   for (int done = 0; done < n_total;) {
@@ -497,7 +508,7 @@ decode_stream_kernel(StreamArgs a) {
         const uint32_t info = __builtin_amdgcn_readfirstlane(d[1]);
         const int s = __builtin_amdgcn_readfirstlane(static_cast<int>(d[2]));
         k_nrec = static_cast<int>(info & 31u) * kRowBytes;   // rows past the context read 0
-        v_nrec = kTileBytes;                                  // (V columns are masked below)
+        v_nrec = k_nrec;
         tile_off = static_cast<int64_t>(tile) * kTileBytes;
         if (info & 32u) {
           q_off = (static_cast<int64_t>(s) * hq + static_cast<int>((info >> 7) & 511u) * kG) * kD * 2;
@@ -512,16 +523,16 @@ decode_stream_kernel(StreamArgs a) {
 #pragma unroll
       for (int kk = 0; kk < kKK; ++kk) {
         if constexpr (kFp8)
-          kt[slot][kk] = __builtin_bit_cast(KChunk, __builtin_amdgcn_raw_buffer_load_b64(rk, k_off + 32 * kk * kE, 0, kAux));
+          kt[slot][kk] = __builtin_bit_cast(Chunk, __builtin_amdgcn_raw_buffer_load_b64(rk, k_off + 32 * kk * kE, 0, kAux));
         else
           kt[slot][kk] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_off + 32 * kk * kE, 0, kAux);
       }
 #pragma unroll
-      for (int c = 0; c < kVC; ++c) {
+      for (int i = 0; i < kVLoads; ++i) {
         if constexpr (kFp8)
-          vt[slot][c] = __builtin_amdgcn_raw_buffer_load_b32(rv, v_off + 16 * c * kBlock * kE, 0, kAux);
+          vt[slot][i] = __builtin_bit_cast(Chunk, __builtin_amdgcn_raw_buffer_load_b64(rv, v_off + i * kRowsPerLoad * kRowBytes, 0, kAux));
         else
-          vt[slot][c] = __builtin_bit_cast(VChunk, __builtin_amdgcn_raw_buffer_load_b64(rv, v_off + 16 * c * kBlock * kE, 0, kAux));
+          vt[slot][i] = __builtin_amdgcn_raw_buffer_load_b128(rv, v_off + i * kRowsPerLoad * kRowBytes, 0, kAux);
       }
     };
 
@@ -589,27 +600,32 @@ decode_stream_kernel(StreamArgs a) {
         pb[r] = static_cast<__bf16>(__builtin_amdgcn_exp2f(x[r] - m_ref));
         l_part += static_cast<float>(pb[r]);
       }
-      // V columns past the context: zero them (0 * garbage could be NaN)
-      uint32_t vmask_lo = 0xFFFFFFFFu, vmask_hi = 0xFFFFFFFFu;
-      if (valid < kBlock) {
-        const int t0 = 4 * quad;
-        vmask_lo = (t0 + 0 < valid ? 0x0000FFFFu : 0u) | (t0 + 1 < valid ? 0xFFFF0000u : 0u);
-        vmask_hi = (t0 + 2 < valid ? 0x0000FFFFu : 0u) | (t0 + 3 < valid ? 0xFFFF0000u : 0u);
+      // V rows through LDS: rows past the context were read as zeros
+#pragma unroll
+      for (int i = 0; i < kVLoads; ++i) {
+        char* dst = s_v + (v_r + i * kRowsPerLoad) * kVStride + 8 * v_c * kE;
+        if constexpr (kFp8)
+          *reinterpret_cast<u32x2_t*>(dst) = vt[slot][i];
+        else
+          *reinterpret_cast<u32x4_t*>(dst) = vt[slot][i];
       }
+      const char* vsrc = s_v + (4 * quad) * kVStride + row * kE;   // token 4*quad, dim `row`
 #pragma unroll
       for (int c = 0; c < kVC; ++c) {
-        u32x2_t vw;
+        u32x2_t vw;                                                // tokens 4*quad..+3 of dim 16c+row
         if constexpr (kFp8) {
-          const int w0 = static_cast<int>(vt[slot][c]);
-          const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
-          const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
-          vw[0] = __builtin_bit_cast(uint32_t, p0);
-          vw[1] = __builtin_bit_cast(uint32_t, p1);
+          const char* p = vsrc + 16 * c;
+          const uint32_t b0 = static_cast<uint8_t>(p[0]), b1 = static_cast<uint8_t>(p[kVStride]);
+          const uint32_t b2 = static_cast<uint8_t>(p[2 * kVStride]), b3 = static_cast<uint8_t>(p[3 * kVStride]);
+          const int w4 = static_cast<int>(b0 | (b1 << 8) | (b2 << 16) | (b3 << 24));
+          vw[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w4, 1.0f, false));
+          vw[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w4, 1.0f, true));
         } else {
-          vw = vt[slot][c];
+          const uint16_t* p = reinterpret_cast<const uint16_t*>(vsrc + 32 * c);
+          constexpr int kPitch = kVStride / 2;
+          vw[0] = static_cast<uint32_t>(p[0]) | (static_cast<uint32_t>(p[kPitch]) << 16);
+          vw[1] = static_cast<uint32_t>(p[2 * kPitch]) | (static_cast<uint32_t>(p[3 * kPitch]) << 16);
         }
-        vw[0] &= vmask_lo;
-        vw[1] &= vmask_hi;
         oacc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, vw),
                                                            __builtin_bit_cast(s16x4_t, pb),
                                                            oacc[c], 0, 0, 0);
@@ -721,8 +737,7 @@ decode_simple_kernel(const char* __restrict__ k_cache, const char* __restrict__ 
   for (int i = 0; i < kPer; ++i) o[i] = 0.f;
   for (int t = t0; t < t1; ++t) {
     const int64_t id = block_tables[static_cast<int64_t>(s) * max_blocks + t / kBlock];
-    const int64_t tile = (id * hkv + g) * kBlock * kD;       // K [16][D], V [D][16]
-    const int64_t base = tile + (t % kBlock) * kD;
+    const int64_t base = ((id * hkv + g) * kBlock + t % kBlock) * kD;
     float dot = 0.f;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) dot = fmaf(qv[i], elem(k_cache, base + lane + 64 * i), dot);
@@ -735,8 +750,7 @@ decode_simple_kernel(const char* __restrict__ k_cache, const char* __restrict__ 
     l = l * a + p;
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
-      o[i] = fmaf(p, elem(v_cache, tile + static_cast<int64_t>(lane + 64 * i) * kBlock + t % kBlock),
-                  o[i] * a);
+      o[i] = fmaf(p, elem(v_cache, base + lane + 64 * i), o[i] * a);
     m = mn;
   }
   if (nparts == 1) {

@@ -16,14 +16,12 @@ TORCH_STORE = {"f32": torch.int32, "bf16": torch.int16, "fp8": torch.uint8}
 TORCH_VIEW = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
 
 
-def device_cache(num_blocks, Hkv, D, fmt, dev="cuda", v=False):
-    """A K cache [num_blocks, Hkv, 16, D] (V cache [num_blocks, Hkv, D, 16]
-    with v=True) filled with the NaN sentinel of the format."""
+def device_cache(num_blocks, Hkv, D, fmt, dev="cuda"):
+    """[num_blocks, Hkv, 16, D] filled with the NaN sentinel of the format."""
     val = int(SENTINEL[fmt])
     if fmt == "f32":
         val = val - (1 << 32) if val >= (1 << 31) else val
-    shape = (num_blocks, Hkv, D, 16) if v else (num_blocks, Hkv, 16, D)
-    t = torch.full(shape, val, dtype=TORCH_STORE[fmt], device=dev)
+    t = torch.full((num_blocks, Hkv, 16, D), val, dtype=TORCH_STORE[fmt], device=dev)
     return t.view(TORCH_VIEW[fmt])
 
 
@@ -59,7 +57,7 @@ class GpuView:
         self.poison = w.num_blocks
         self.desc = pk.CacheDesc(w.num_blocks + 1, w.Hkv, w.D, w.fmt, w.k_scale, w.v_scale)
         self.kc = device_cache(w.num_blocks + 1, w.Hkv, w.D, w.fmt, dev)
-        self.vc = device_cache(w.num_blocks + 1, w.Hkv, w.D, w.fmt, dev, v=True)
+        self.vc = device_cache(w.num_blocks + 1, w.Hkv, w.D, w.fmt, dev)
         self.bm = pk.BlockManager(w.num_blocks, free_order=w.free_order)
         self.dev = dev
 

@@ -13,13 +13,11 @@ SENTINEL = {"f32": np.uint32(0x7FC0DEAD), "bf16": np.uint16(0x7FC1), "fp8": np.u
 STORE = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}
 
 
-def empty_cache(num_blocks, Hkv, D, fmt, v=False):
-    """A K cache [num_blocks, Hkv, 16, D] (or, with v=True, a V cache
-    [num_blocks, Hkv, D, 16]) filled with a NaN sentinel, in storage format."""
-    shape = (num_blocks, Hkv, D, 16) if v else (num_blocks, Hkv, 16, D)
+def empty_cache(num_blocks, Hkv, D, fmt):
+    """A cache filled with a NaN sentinel, in storage format."""
     if fmt == "f32":
-        return np.full(shape, SENTINEL["f32"], dtype=np.uint32).view(np.float32)
-    return np.full(shape, SENTINEL[fmt], dtype=STORE[fmt])
+        return np.full((num_blocks, Hkv, 16, D), SENTINEL["f32"], dtype=np.uint32).view(np.float32)
+    return np.full((num_blocks, Hkv, 16, D), SENTINEL[fmt], dtype=STORE[fmt])
 
 
 def fill_sequential(w, cap=None):
@@ -36,7 +34,7 @@ def fill_sequential(w, cap=None):
     slots = np.array([per_seq[int(s)][int(p)] for s, p in zip(w.row_seq, w.row_pos)],
                      dtype=np.int64)
     kc = empty_cache(w.num_blocks, w.Hkv, w.D, w.fmt)
-    vc = empty_cache(w.num_blocks, w.Hkv, w.D, w.fmt, v=True)
+    vc = empty_cache(w.num_blocks, w.Hkv, w.D, w.fmt)
     kc, vc = oracle.write_kv(kc, vc, w.k_rows, w.v_rows, slots, w.src_fmt, w.fmt,
                              w.k_scale, w.v_scale)
     if cap is None:
@@ -97,7 +95,7 @@ def fill_cow(w):
     slots = row_slots_cow(w, ps, ss)
     prompt = is_prompt_row(w)
     kc = empty_cache(w.num_blocks, w.Hkv, w.D, w.fmt)
-    vc = empty_cache(w.num_blocks, w.Hkv, w.D, w.fmt, v=True)
+    vc = empty_cache(w.num_blocks, w.Hkv, w.D, w.fmt)
     kc, vc = oracle.write_kv(kc, vc, w.k_rows[prompt], w.v_rows[prompt], slots[prompt],
                              w.src_fmt, w.fmt, w.k_scale, w.v_scale)
     kc, vc = oracle.copy_blocks(kc, vc, pairs)
