@@ -21,6 +21,7 @@ forms, invariants, a library routine); none is "parity unpinned".
 from .formats import (bf16_to_f64, e4m3_to_f64, e4m3_encode, e4m3_all_values,
                       widen_cache)
 from .attention import gather_kv, decode, decode_partitioned, merge_partitions
+from .chunk import decode_chunk, chunk_rows, visible_len
 from .cache_ops import write_kv, copy_blocks
 from .block_manager import RefBlockManager, NoBlocks, UnknownSeq, SeqExists
 from .accounting import kv_cache_bytes, paged_utilisation, contiguous_utilisation
@@ -28,6 +29,7 @@ from .accounting import kv_cache_bytes, paged_utilisation, contiguous_utilisatio
 __all__ = [
     "bf16_to_f64", "e4m3_to_f64", "e4m3_encode", "e4m3_all_values", "widen_cache",
     "gather_kv", "decode", "decode_partitioned", "merge_partitions",
+    "decode_chunk", "chunk_rows", "visible_len",
     "write_kv", "copy_blocks",
     "RefBlockManager", "NoBlocks", "UnknownSeq", "SeqExists",
     "kv_cache_bytes", "paged_utilisation", "contiguous_utilisation",

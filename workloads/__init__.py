@@ -192,6 +192,25 @@ def config3_step(rng: np.random.Generator, B=256, Hq=32, Hkv=8, D=128):
     return k, v, q
 
 
+def chunk_queries(rng: np.random.Generator, B: int, T: int, Hq: int, D: int,
+                  fmt: str = "bf16") -> np.ndarray:
+    """Queries of a chunk of T new tokens per sequence, [B, T, Hq, D]
+    (uniform(-1, 1) float32 for fp32 workloads, N(0, 1) bf16 bits otherwise)."""
+    if fmt == "f32":
+        return _rows(rng, (B, T, Hq, D), "uniform", False)
+    return _rows(rng, (B, T, Hq, D), "normal", True)
+
+
+def config3_chunk_step(rng: np.random.Generator, T: int, B=256, Hq=32, Hkv=8, D=128):
+    """Per-iteration draws of the GQA batch-256 loop when each step brings T
+    new tokens per sequence (chunked prefill or draft verification): the
+    chunk's K and V rows [B, T, Hkv, D], then its queries [B, T, Hq, D]."""
+    k = _rows(rng, (B, T, Hkv, D), "normal", True)
+    v = _rows(rng, (B, T, Hkv, D), "normal", True)
+    q = _rows(rng, (B, T, Hq, D), "normal", True)
+    return k, v, q
+
+
 def config4(seed: int = 4, rows: bool = True) -> Workload:
     """70B-shaped long-context GQA layer, bf16: batch 8, 64 query / 8 KV heads,
     head_dim 128, every context 32768 tokens (2048 blocks, shuffled)."""
