@@ -37,8 +37,15 @@ The JSON line also carries
   * ``cpu_baseline``: the CPU float64 oracle's decode of the same batch on the
     host, single-threaded.
 
+With ``--chunk T`` (T = 2..16) each step brings T new tokens per sequence
+instead of one -- a draft-verification or chunked-prefill step: T appends per
+sequence, pa_write_kv of B*T rows, then pa_decode_chunk with q [B, T, Hq, D]
+(causal inside the chunk).  ``value`` is then query tokens per second per
+layer, and the roofline is pa_decode_chunk's.  The default (T = 1) is the
+decode step above.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers N]
-                      [--no-cpu-baseline] [--copy-calibration MIB]
+                      [--chunk T] [--no-cpu-baseline] [--copy-calibration MIB]
 
 --copy-calibration MIB ends the run with plain device copies of MIB MiB, the
 reference a hardware-counter run scales FETCH_SIZE / WRITE_SIZE by.
@@ -61,10 +68,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+import workloads  # noqa: E402  (seeded input generators; no method arithmetic)
+
 METRIC = "paged decode attention: KV-cache GB/s vs HBM peak; decoded seqs/sec"
+METRIC_CHUNK = ("paged chunk attention (T new tokens per sequence, causal): KV-cache GB/s "
+                "vs HBM peak; query tokens/sec")
 HBM_PEAK_GBPS = 8000.0
 DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_421_amd", "csrc", "decode.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic_gqa8b_b256.txt")
+TRAFFIC_FILE_CHUNK = os.path.join(ROOT, "profiles", "chunk_traffic_gqa8b_b256_t{T}.txt")
 
 
 def _log(msg):
@@ -121,14 +133,15 @@ def kernel_source_sha256():
     return hashlib.sha256(text[a:b].encode()).hexdigest()
 
 
-def _traffic_per_call(kv_bytes):
-    """HBM bytes of one pa_decode call reading ``kv_bytes`` algorithmic KV
-    bytes, from the committed rocprofv3 counter summary (bytes read per
-    algorithmic byte, bytes written per call), if that summary was taken on
-    the current kernel source; else None."""
-    if not os.path.exists(TRAFFIC_FILE):
+def _traffic_per_call(kv_bytes, T=1):
+    """HBM bytes of one pa_decode (pa_decode_chunk for T > 1) call reading
+    ``kv_bytes`` algorithmic KV bytes, from the committed rocprofv3 counter
+    summary (bytes read per algorithmic byte, bytes written per call), if that
+    summary was taken on the current kernel source; else None."""
+    path = TRAFFIC_FILE if T == 1 else TRAFFIC_FILE_CHUNK.format(T=T)
+    if not os.path.exists(path):
         return None
-    text = open(TRAFFIC_FILE).read()
+    text = open(path).read()
     m_src = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
     m_r = re.search(r"fetch_bytes_per_algorithmic_byte:\s*([0-9.eE+]+)", text)
     m_w = re.search(r"write_bytes_per_call:\s*([0-9.eE+]+)", text)
@@ -137,10 +150,12 @@ def _traffic_per_call(kv_bytes):
     return float(m_r.group(1)) * kv_bytes + float(m_w.group(1))
 
 
-def cpu_baseline(w, budget_s=10.0):
+def cpu_baseline(w, budget_s=10.0, T=1):
     """The oracle's decode (gather blocks, textbook fp64 softmax attention) of
     the whole batch at its initial lengths, repeated until ``budget_s``
-    seconds have passed (at least 3 runs); median run time."""
+    seconds have passed (at least 3 runs); median run time.  With T > 1, the
+    oracle's chunk attention, the last T positions of each context being the
+    chunk."""
     import oracle
     from threadpoolctl import threadpool_limits
 
@@ -159,17 +174,25 @@ def cpu_baseline(w, budget_s=10.0):
     cap = max(-(-int(L) // 16) for L in w.lens)
     bt, cl = bm.pack(list(range(w.B)), cap)
     times = []
+    qc = None
+    if T > 1:
+        qc = workloads.chunk_queries(np.random.default_rng(1004), w.B, T, w.Hq, w.D, "bf16")
     with threadpool_limits(limits=1):
         t_all = time.perf_counter()
         while len(times) < 3 or time.perf_counter() - t_all < budget_s:
             t0 = time.perf_counter()
-            oracle.decode(w.q, "bf16", kc, vc, "bf16", bt, cl, w.scale)
+            if T == 1:
+                oracle.decode(w.q, "bf16", kc, vc, "bf16", bt, cl, w.scale)
+            else:
+                oracle.decode_chunk(qc, "bf16", kc, vc, "bf16", bt, cl, w.scale)
             times.append(time.perf_counter() - t0)
     t = statistics.median(times)
-    return {"value": round(w.B / t, 2), "unit": "seqs/s", "cores": 1, "kind": "oracle",
+    what = "256 seqs x 32 heads" if T == 1 else f"256 seqs x {T} chunk tokens x 32 heads"
+    return {"value": round(w.B * T / t, 2), "unit": "seqs/s" if T == 1 else "tokens/s",
+            "cores": 1, "kind": "oracle",
             "kv_gbps": round(_kv_bytes(cl, w.Hkv, w.D, 2) / t / 1e9, 4),
             "host_cores_visible": len(os.sched_getaffinity(0)),
-            "sample": (f"whole batch (256 seqs x 32 heads, sum L {int(cl.sum())}, initial "
+            "sample": (f"whole batch ({what}, sum L {int(cl.sum())}, initial "
                        f"lengths), {len(times)} runs, median {t:.3f} s; numpy float64, "
                        f"BLAS limited to 1 thread")}
 
@@ -177,9 +200,11 @@ def cpu_baseline(w, budget_s=10.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=None, help="default 100 (50 with --chunk)")
+    ap.add_argument("--warmup", type=int, default=None, help="default 10 (5 with --chunk)")
     ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--chunk", type=int, default=1, metavar="T",
+                    help="new tokens per sequence per step (1 = decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     args = ap.parse_args()
@@ -187,9 +212,15 @@ def main():
         print(f"bench.py measures one GPU only (asked for {args.gpus}); the decode path "
               f"has no cross-GPU step in this library", file=sys.stderr)
         sys.exit(2)
-    import workloads
-    if args.steps + args.warmup > workloads.CONFIG3_MAX_APPEND:
-        sys.exit(f"steps + warmup must be <= {workloads.CONFIG3_MAX_APPEND} "
+    T = args.chunk
+    if not 1 <= T <= 16:
+        sys.exit("--chunk must be in 1..16")
+    if args.steps is None:
+        args.steps = 100 if T == 1 else 50
+    if args.warmup is None:
+        args.warmup = 10 if T == 1 else 5
+    if T * (args.steps + args.warmup) > workloads.CONFIG3_MAX_APPEND:
+        sys.exit(f"chunk * (steps + warmup) must be <= {workloads.CONFIG3_MAX_APPEND} "
                  f"(pool headroom for appended tokens)")
 
     import torch
@@ -226,28 +257,34 @@ def main():
         vc[l].copy_(vc[0])
     del k_rows, v_rows, slots
 
-    # ---- per-layer step inputs, resident in HBM
+    # ---- per-layer step inputs, resident in HBM: the new tokens' K/V rows
+    # [B*T, Hkv, D] (sequence-major) and their queries
     rng = np.random.default_rng(1003)
     k_new, v_new, q = [], [], []
     for _ in range(NL):
-        kn, vn, qq = workloads.config3_step(rng, B, Hq, Hkv, D)
+        if T == 1:
+            kn, vn, qq = workloads.config3_step(rng, B, Hq, Hkv, D)
+        else:
+            kn, vn, qq = workloads.config3_chunk_step(rng, T, B, Hq, Hkv, D)
+            kn, vn = kn.reshape(B * T, Hkv, D), vn.reshape(B * T, Hkv, D)
         k_new.append(torch.from_numpy(kn.view(np.int16)).to(dev).view(torch.bfloat16))
         v_new.append(torch.from_numpy(vn.view(np.int16)).to(dev).view(torch.bfloat16))
         q.append(torch.from_numpy(qq.view(np.int16)).to(dev).view(torch.bfloat16))
     out = [torch.empty_like(q[0]) for _ in range(NL)]
 
     total = args.steps + args.warmup
-    max_len_final = int(w.lens.max()) + total
+    max_len_final = int(w.lens.max()) + T * total
     cap = -(-max_len_final // 16)
-    workspace = pk.new_decode_workspace(desc, B, Hq, max_len_final, dev)
+    workspace = pk.new_chunk_workspace(desc, B, Hq, T, max_len_final, dev)
 
     # ---- pinned host staging, triple-buffered against the running GPU
     NBUF = 3
-    h_slots = [torch.empty(B, dtype=torch.int64, pin_memory=True) for _ in range(NBUF)]
+    h_slots = [torch.empty(B * T, dtype=torch.int64, pin_memory=True) for _ in range(NBUF)]
     h_bt = [torch.empty((B, cap), dtype=torch.int32, pin_memory=True) for _ in range(NBUF)]
     h_cl = [torch.empty(B, dtype=torch.int32, pin_memory=True) for _ in range(NBUF)]
     buf_ev = [None] * NBUF
-    d_slots = torch.empty(B, dtype=torch.int64, device=dev)
+    d_slots = torch.empty(B * T, dtype=torch.int64, device=dev)
+    slots_tb = np.empty((T, B), dtype=np.int64)
     d_bt = torch.empty((B, cap), dtype=torch.int32, device=dev)
     d_cl = torch.empty(B, dtype=torch.int32, device=dev)
     ids = np.arange(B, dtype=np.int64)
@@ -257,10 +294,16 @@ def main():
         b = i % NBUF
         if buf_ev[b] is not None:
             buf_ev[b].synchronize()          # the upload that last read buffer b is done
-        sl, pairs = bm.append_batch(ids, slots=h_slots[b].numpy())
-        assert len(pairs) == 0
+        if T == 1:
+            sl, pairs = bm.append_batch(ids, slots=h_slots[b].numpy())
+            assert len(pairs) == 0
+        else:
+            for t in range(T):                   # token t of every sequence
+                sl, pairs = bm.append_batch(ids, slots=slots_tb[t])
+                assert len(pairs) == 0
+            h_slots[b].numpy().reshape(B, T)[:] = slots_tb.T
         bm.pack(ids, cap, block_tables=h_bt[b].numpy(), context_lens=h_cl[b].numpy())
-        lens[:] += 1
+        lens[:] += T
         d_slots.copy_(h_slots[b], non_blocking=True)
         d_bt.copy_(h_bt[b], non_blocking=True)
         d_cl.copy_(h_cl[b], non_blocking=True)
@@ -272,8 +315,12 @@ def main():
             pk.write_kv(desc, kc[l], vc[l], k_new[l], v_new[l], d_slots, stream=stream)
             if ev_pairs is not None:
                 ev_pairs[l][0].record(stream)
-            pk.decode(desc, kc[l], vc[l], q[l], out[l], d_bt, d_cl, max_len, float(w.scale),
-                      workspace, stream=stream)
+            if T == 1:
+                pk.decode(desc, kc[l], vc[l], q[l], out[l], d_bt, d_cl, max_len,
+                          float(w.scale), workspace, stream=stream)
+            else:
+                pk.decode_chunk(desc, kc[l], vc[l], q[l], out[l], d_bt, d_cl, max_len,
+                                float(w.scale), workspace, stream=stream)
             if ev_pairs is not None:
                 ev_pairs[l][1].record(stream)
         return _kv_bytes(lens, Hkv, D, 2)
@@ -303,15 +350,20 @@ def main():
     mean_kv = statistics.mean(kv_per_call)
     achieved = mean_kv / mean_dec_s / 1e9
     steps_s = wall / args.steps
-    traffic = _traffic_per_call(mean_kv)
-    _log(f"bench: pa_decode mean {mean_dec_s * 1e6:.1f} us (p10 "
+    traffic = _traffic_per_call(mean_kv, T)
+    _log(f"bench: {'pa_decode' if T == 1 else 'pa_decode_chunk'} mean {mean_dec_s * 1e6:.1f} us (p10 "
          f"{np.percentile(dec_ms, 10) * 1e3:.1f}, p90 {np.percentile(dec_ms, 90) * 1e3:.1f}), "
          f"{achieved:.0f} GB/s; step {steps_s * 1e3:.3f} ms")
 
+    workload = ("gqa8b-bf16-b256: Llama-3-8B-shaped GQA decode layer, batch 256, "
+                "32 query / 8 KV heads, head_dim 128, bf16 KV in 16-token shuffled "
+                "blocks, lognormal context (median 512, sigma 0.8, [16, 4096])")
+    if T > 1:
+        workload = workload.replace("GQA decode layer", f"GQA layer, {T}-token chunk per sequence")
     res = {
-        "metric": METRIC,
-        "value": round(B * NL * args.steps / wall, 1),
-        "unit": "seqs/s",
+        "metric": METRIC if T == 1 else METRIC_CHUNK,
+        "value": round(B * T * NL * args.steps / wall, 1),
+        "unit": "seqs/s" if T == 1 else "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -322,14 +374,15 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": ("gqa8b-bf16-b256: Llama-3-8B-shaped GQA decode layer, batch 256, "
-                         "32 query / 8 KV heads, head_dim 128, bf16 KV in 16-token shuffled "
-                         "blocks, lognormal context (median 512, sigma 0.8, [16, 4096])"),
+            "workload": workload,
             "global_batch": B,
+            "chunk_tokens": T,
             "layers_per_step": NL,
-            "step": "block-manager append + table upload + per layer pa_write_kv and pa_decode",
-            "value_is": "sequences decoded per second per attention layer",
-            "mean_context_len": round(float(lens.mean()) - args.steps / 2, 1),
+            "step": ("block-manager append + table upload + per layer pa_write_kv and " +
+                     ("pa_decode" if T == 1 else "pa_decode_chunk")),
+            "value_is": ("sequences decoded per second per attention layer" if T == 1 else
+                         "query tokens per second per attention layer"),
+            "mean_context_len": round(float(lens.mean()) - T * args.steps / 2, 1),
             "parallelism": "single GPU",
         },
         "kv_gbps_step": round(mean_kv * NL / steps_s / 1e9, 1),
@@ -337,7 +390,9 @@ def main():
         "decode_us_p10": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
         "decode_us_p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),
         "roofline": {
-            "kernel": "decode_stream_kernel (pa_decode: one persistent kernel)",
+            "kernel": ("decode_stream_kernel (pa_decode: one persistent kernel)" if T == 1 else
+                       "decode_stream_kernel (pa_decode_chunk: one persistent kernel per "
+                       f"{16 // (Hq // Hkv)}-token pass)"),
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
@@ -356,7 +411,7 @@ def main():
         _log(f"bench: copy calibration {n} bytes x 3")
     if not args.no_cpu_baseline:
         _log("bench: timing the CPU oracle")
-        res["cpu_baseline"] = cpu_baseline(w)
+        res["cpu_baseline"] = cpu_baseline(w, T=T)
     print(json.dumps(res), flush=True)
 
 

@@ -64,6 +64,8 @@ typedef enum {
 #define PA_BLOCK_SIZE 16
 /* Context positions per partition of the general (fp32) decode path. */
 #define PA_PARTITION_TOKENS 512
+/* Largest chunk of new tokens per sequence pa_decode_chunk takes. */
+#define PA_MAX_CHUNK 16
 
 typedef struct {
   int32_t num_blocks;    /* physical blocks in each of the K and V caches */
@@ -121,12 +123,17 @@ pa_status pa_copy_blocks(const pa_cache_desc* c, void* k_cache, void* v_cache,
 size_t pa_decode_workspace_bytes(const pa_cache_desc* c, int32_t num_seqs,
                                  int32_t num_q_heads, int32_t max_context_len);
 
+/* The same for pa_decode_chunk with chunk_len new tokens per sequence. */
+size_t pa_decode_chunk_workspace_bytes(const pa_cache_desc* c, int32_t num_seqs,
+                                       int32_t num_q_heads, int32_t chunk_len,
+                                       int32_t max_context_len);
+
 /*
  * pa_decode_workspace_init -- zero-fill `workspace_bytes` bytes of a decode
  * workspace on `stream` (a plain fill kernel, so it may be captured in a
  * graph).  A workspace must be zero-filled once before its first pa_decode
  * (this call, or any other zero fill such as torch.zeros); every pa_decode
- * that completes leaves it zero-filled again.  workspace must be 4-byte
+ * or pa_decode_chunk that completes leaves it zero-filled again.  workspace must be 4-byte
  * aligned.
  */
 pa_status pa_decode_workspace_init(void* workspace, size_t workspace_bytes,
@@ -142,9 +149,10 @@ pa_status pa_decode_workspace_init(void* workspace, size_t workspace_bytes,
  *   which is exact attention, computed blockwise with online-softmax
  *   renormalisation (ybb.press §5.1).  L == 0 gives a zero row.  Only the first
  *   ceil(L/16) table entries and the first L slots are read.
- *   q, out       : [num_seqs][num_q_heads][head_dim] contiguous (device).
- *                  q dtype: F32 with an F32 cache, BF16 with a BF16 or FP8
- *                  cache; out has q's dtype.  Accumulation is fp32.
+ *   q, out       : [num_seqs][num_q_heads][head_dim] contiguous (device),
+ *                  16-byte aligned.  q dtype: F32 with an F32 cache, BF16
+ *                  with a BF16 or FP8 cache; out has q's dtype.
+ *                  Accumulation is fp32.
  *   block_tables : int32 [num_seqs][max_blocks_per_seq] (device).
  *   context_lens : int32 [num_seqs] (device), each in [0, max_context_len].
  *   max_context_len: host-side upper bound on context_lens, sizes the grid.
@@ -157,7 +165,7 @@ pa_status pa_decode_workspace_init(void* workspace, size_t workspace_bytes,
  *                  overlap (different streams) need separate workspaces.
  *   A context is processed in pieces whose partial (max, sum, output) are
  *   merged by the log-sum-exp rule: with a bf16 or fp8 cache, head_dim 64
- *   or 128 and G <= 8, pieces are equal shares of the whole batch's KV
+ *   or 128 and G <= 16, pieces are equal shares of the whole batch's KV
  *   tiles; otherwise pieces are PA_PARTITION_TOKENS-token partitions.
  */
 pa_status pa_decode(const pa_cache_desc* c, const void* k_cache,
@@ -167,6 +175,33 @@ pa_status pa_decode(const pa_cache_desc* c, const void* k_cache,
                     int32_t max_context_len, int32_t num_seqs,
                     int32_t num_q_heads, float scale, void* workspace,
                     size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_chunk -- attention of a chunk of chunk_len = T new tokens per
+ * sequence (1 <= T <= PA_MAX_CHUNK), as in chunked prefill (ybb.press §7.1,
+ * §7.2) and draft-token verification in speculative decoding (ybb.press §9
+ * item 2).  The chunk's K/V rows are already in the cache (pa_write_kv) and
+ * context_lens[s] = L counts them.  Chunk token i sits at position L - T + i
+ * and attends positions 0 .. L - T + i only (causal order inside the chunk):
+ *     out[s][i][h] = sum_{t <= L-T+i} softmax_t(scale * q[s][i][h] . K[t]) V[t]
+ *   with the head map, scales and dtypes of pa_decode.  A token with no
+ *   position to see (L - T + i < 0) gets a zero row.
+ *   q, out    : [num_seqs][chunk_len][num_q_heads][head_dim] contiguous.
+ *   workspace : at least pa_decode_chunk_workspace_bytes(c, num_seqs,
+ *               num_q_heads, chunk_len, max_context_len) bytes, same rules
+ *               as pa_decode's.
+ *   With a bf16 or fp8 cache the KV tiles are streamed once per pass of
+ *   floor(16 / G) chunk tokens (each pass's G * tokens query rows share the
+ *   tile loads); other shapes take the partition path.
+ *   pa_decode is pa_decode_chunk with chunk_len = 1.
+ */
+pa_status pa_decode_chunk(const pa_cache_desc* c, const void* k_cache,
+                          const void* v_cache, const void* q, int32_t q_dtype,
+                          void* out, int32_t chunk_len,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, int32_t max_context_len,
+                          int32_t num_seqs, int32_t num_q_heads, float scale,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Host block manager (plain host memory, no GPU calls).  One owner; not

@@ -7,11 +7,12 @@ marshals arguments -- torch tensors to device pointers, the current HIP stream
 from __future__ import annotations
 
 from ._lib import LIB_PATH, PagedKVError, lib
-from .api import (BLOCK_SIZE, PARTITION_TOKENS, BlockManager, CacheDesc, copy_blocks,
-                  decode, decode_workspace_bytes, decode_workspace_init, dtype_code,
-                  new_decode_workspace, write_kv)
+from .api import (BLOCK_SIZE, MAX_CHUNK, PARTITION_TOKENS, BlockManager, CacheDesc,
+                  chunk_workspace_bytes, copy_blocks, decode, decode_chunk,
+                  decode_workspace_bytes, decode_workspace_init, dtype_code,
+                  new_chunk_workspace, new_decode_workspace, write_kv)
 
-__all__ = ["LIB_PATH", "PagedKVError", "lib", "BLOCK_SIZE", "PARTITION_TOKENS",
-           "BlockManager", "CacheDesc", "copy_blocks", "decode",
-           "decode_workspace_bytes", "decode_workspace_init", "dtype_code",
-           "new_decode_workspace", "write_kv"]
+__all__ = ["LIB_PATH", "PagedKVError", "lib", "BLOCK_SIZE", "MAX_CHUNK", "PARTITION_TOKENS",
+           "BlockManager", "CacheDesc", "chunk_workspace_bytes", "copy_blocks", "decode",
+           "decode_chunk", "decode_workspace_bytes", "decode_workspace_init", "dtype_code",
+           "new_chunk_workspace", "new_decode_workspace", "write_kv"]

@@ -15,6 +15,7 @@ from ._lib import CacheDescC, PagedKVError, check, lib
 
 BLOCK_SIZE = 16
 PARTITION_TOKENS = 512
+MAX_CHUNK = 16
 
 PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 _DTYPES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.uint8: PA_FP8_E4M3,
@@ -146,6 +147,48 @@ def decode(desc: CacheDesc, k_cache: torch.Tensor, v_cache: torch.Tensor, q: tor
                         _dev(block_tables, "block_tables"), block_tables.shape[1],
                         _dev(context_lens, "context_lens"), int(max_context_len), B, Hq,
                         float(scale), ws_ptr, ws_bytes, _stream(stream)))
+    return out
+
+
+def chunk_workspace_bytes(desc: CacheDesc, num_seqs: int, num_q_heads: int, chunk_len: int,
+                          max_context_len: int) -> int:
+    """pa_decode_chunk_workspace_bytes: scratch bytes pa_decode_chunk needs."""
+    return int(lib.pa_decode_chunk_workspace_bytes(ctypes.byref(desc.c), int(num_seqs),
+                                                   int(num_q_heads), int(chunk_len),
+                                                   int(max_context_len)))
+
+
+def new_chunk_workspace(desc: CacheDesc, num_seqs: int, num_q_heads: int, chunk_len: int,
+                        max_context_len: int, device=None) -> torch.Tensor:
+    """A zero-filled uint8 device tensor sized for pa_decode_chunk."""
+    n = chunk_workspace_bytes(desc, num_seqs, num_q_heads, chunk_len, max_context_len)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=device or "cuda")
+    decode_workspace_init(ws)
+    return ws
+
+
+def decode_chunk(desc: CacheDesc, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                 q: torch.Tensor, out: torch.Tensor, block_tables: torch.Tensor,
+                 context_lens: torch.Tensor, max_context_len: int, scale: float,
+                 workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """pa_decode_chunk: attention of T = q.shape[1] new tokens per sequence,
+    causal inside the chunk; q and out are [B, T, Hq, D]."""
+    B, T, Hq, D = q.shape
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must have q's shape and dtype")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
+        raise ValueError("block_tables must be [B, max_blocks] and context_lens [B]")
+    if workspace is None:
+        workspace = new_chunk_workspace(desc, B, Hq, T, max_context_len, q.device)
+    check(lib.pa_decode_chunk(ctypes.byref(desc.c), _dev(k_cache, "k_cache"),
+                              _dev(v_cache, "v_cache"), _dev(q, "q"), dtype_code(q.dtype),
+                              _dev(out, "out"), T, _dev(block_tables, "block_tables"),
+                              block_tables.shape[1], _dev(context_lens, "context_lens"),
+                              int(max_context_len), B, Hq, float(scale),
+                              _dev(workspace, "workspace"),
+                              workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
 
 

@@ -77,6 +77,9 @@ constexpr int kNT = 3;                  // fast path: tiles in flight per wave
 constexpr int kCap = 512;               // fast path: tile descriptors per round (LDS)
 constexpr int kGather = 4;              // fast path: block-id loads in flight per lane
 constexpr int kAuxCoherent = 16;        // buffer cache policy sc1: device-coherent access
+constexpr int kMaxRows = 16;            // fast path: query rows per pass (MFMA columns)
+constexpr float kNoMax = -1e30f;        // running max of a row that has seen no position yet
+constexpr int kOutOfRange = 0x7FFFFF00; // buffer offset past any range: the load reads 0
 
 // DPP controls (GFX9 encoding).
 constexpr int kDppQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]
@@ -152,26 +155,33 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
 
 // ---------------------------------------------------------------------------
 // Fast path.
+// A pass covers `rows` = G * (chunk tokens of the pass) <= 16 query rows per
+// KV head: row n is chunk token t_first + n / G of query head g*G + n % G.
+// Single-token decode is chunk = 1, one pass with rows = G.
 struct StreamArgs {
   const char* k_cache;
   const char* v_cache;
-  const uint16_t* q;          // [B][Hq][D] bf16
-  uint16_t* out;              // [B][Hq][D] bf16
+  const uint16_t* q;          // [B][chunk][Hq][D] bf16
+  uint16_t* out;              // [B][chunk][Hq][D] bf16
   const int32_t* block_tables;
   const int32_t* context_lens;
   uint32_t* counters;         // [B * Hkv], zero between calls
-  float* partials;            // [num_waves][2][kG][kD + 2]
+  float* partials;            // [num_waves][2][rows][kD + 2]
   int num_seqs;
   int hkv;
   int max_blocks;
   int num_waves;
+  int group;                  // G: query heads per KV head
+  int chunk;                  // T: new tokens per sequence
+  int t_first;                // first chunk token of this pass
+  int rows;                   // query rows of this pass (<= kMaxRows)
   float logit_scale;          // scale * k_scale * log2(e)
   float v_scale;
 };
 
-// kD: head_dim; kG: query heads per KV head (1..8); kFp8: E4M3 cache (else
-// bf16); kAux: cache policy bits of the KV loads.
-template <int kD, int kG, bool kFp8, int kAux>
+// kD: head_dim; kFp8: E4M3 cache (else bf16); kAux: cache policy bits of the
+// KV loads.
+template <int kD, bool kFp8, int kAux>
 __global__ void __launch_bounds__(64 * kWavesPerGroup)
 decode_stream_kernel(StreamArgs a) {
   constexpr int kE = kFp8 ? 1 : 2;                 // bytes per cache element
@@ -183,7 +193,7 @@ decode_stream_kernel(StreamArgs a) {
   constexpr int kRowsPerLoad = 64 / kLanesPerRow;  // V: token rows per load
   constexpr int kVLoads = kBlock / kRowsPerLoad;   // V: loads per lane
   constexpr int kVStride = kRowBytes + 16;         // LDS row pitch of the V staging tile
-  constexpr int kSlot = kG * (kD + 2);             // floats per partial slot
+  constexpr int kRowOutBytes = kD * 2;             // one bf16 output row
   using Chunk = typename std::conditional<kFp8, u32x2_t, u32x4_t>::type;
 
   // waves of a work-group are independent (no barriers): a work-group only
@@ -193,7 +203,11 @@ decode_stream_kernel(StreamArgs a) {
   const int lane = threadIdx.x & 63;
   const int B = a.num_seqs;
   const int hkv = a.hkv;
-  const int hq = hkv * kG;
+  const int G = a.group;
+  const int nchunk = a.chunk;
+  const int R = a.rows;
+  const int hq = hkv * G;
+  const int slot_floats = R * (kD + 2);           // floats per partial slot
   const __amdgpu_buffer_rsrc_t lens_rsrc = make_rsrc(a.context_lens, B * 4);
 
   // ---- 1. total tile count; zero rows of empty sequences s = w (mod waves).
@@ -212,8 +226,8 @@ decode_stream_kernel(StreamArgs a) {
       const uint64_t empty = __builtin_amdgcn_ballot_w64(s < B && L[r] == 0 && s % a.num_waves == w);
       for (uint64_t m = empty; m != 0; m &= m - 1) {
         const int se = s0 + 64 * r + __builtin_ctzll(m);
-        uint16_t* orow = a.out + static_cast<int64_t>(se) * hq * kD;
-        for (int i = lane; i < hq * kD / 8; i += 64)
+        uint16_t* orow = a.out + (static_cast<int64_t>(se) * nchunk + a.t_first) * hq * kD;
+        for (int i = lane; i < (R / G) * hq * kD / 8; i += 64)
           reinterpret_cast<u32x4_t*>(orow)[i] = u32x4_t{0u, 0u, 0u, 0u};
       }
     }
@@ -266,16 +280,22 @@ decode_stream_kernel(StreamArgs a) {
 
   // q of a segment travels with each ring slot, loaded straight into the
   // MFMA B-operand layout of S^T = K q^T: lane (row, quad) holds dims
-  // 32*kk + 8*quad .. +7 of head `row`; rows past kG fall outside the
-  // load's range and read as zero.
-  constexpr int kQBytes = kG * kD * 2;
+  // 32*kk + 8*quad .. +7 of query row `row`; rows past R read as zero.
+  // Row `row` is chunk token t_row, query head g*G + h_row; it may see the
+  // context up to L - mshift positions (causal order inside the chunk).
   const int row = lane & 15;
   const int quad = lane >> 4;
-  const int q_lane_off = (row * kD + 8 * quad) * 2;            // + 64*kk
+  const bool row_ok = row < R;
+  const int t_row = a.t_first + (row_ok ? row / G : 0);
+  const int h_row = row_ok ? row - (row / G) * G : 0;
+  const int mshift = nchunk - 1 - t_row;
+  const int q_bytes = ((nchunk - 1) * hq + G) * kD * 2;            // one segment's q rows
+  const int q_lane_off = row_ok ? ((t_row * hq + h_row) * kD + 8 * quad) * 2 : kOutOfRange;  // + 64*kk
 
   // ---- 3. tile descriptors, built in LDS in rounds of up to kCap tiles
   // word 0: tile index block * Hkv + g (the block's position in the table
-  //         while building); word 1: valid rows | first << 5 | last << 6 |
+  //         while building); word 1: rows to the context's end, min(31, L - 16j)
+  //         (the tile's valid rows are min(16, that)) | first << 5 | last << 6 |
   //         g << 7 | blocks of the sequence << 16; word 2: sequence;
   // word 3: list index of the segment's first tile.  "first"/"last" mark
   // the ends of a piece: a segment's ends or the ends of this wave's range.
@@ -285,6 +305,12 @@ decode_stream_kernel(StreamArgs a) {
   // rows into the P.V MFMA's operand, 4 tokens of one dim per lane
   __shared__ __align__(16) char s_v_all[kWavesPerGroup][kBlock * kVStride];
   char* s_v = s_v_all[wig];
+  // output staging: the rows of a finished segment are gathered here so
+  // that each row goes to memory as whole 16-byte pieces, 256 contiguous
+  // bytes per row (partial-line stores are slow on this memory path)
+  constexpr int kOPitch = kRowOutBytes + 16;
+  __shared__ __align__(16) char s_o_all[kWavesPerGroup][kMaxRows * kOPitch];
+  char* s_o = s_o_all[wig];
   int w_s = s_cur, w_g = g0, w_j = j0, w_L = L_cur, w_nb = nb0, w_seg = seg0 + g0 * nb0;
   // lengths for the walk: from Lr for the first 256 sequences, past them
   // from a window of 64 (lane i -> sequence lwin_base + i) loaded on demand
@@ -316,20 +342,41 @@ decode_stream_kernel(StreamArgs a) {
 
   // ---- 4. consumer state: online softmax of the current segment piece.
   // Logits are computed transposed (S^T = K q^T), so lane (row, quad) holds
-  // S[head row][tokens 4*quad + r], r = 0..3 -- which is exactly the layout
+  // S[query row][tokens 4*quad + r], r = 0..3 -- which is exactly the layout
   // of the B operand of the 16x16x16 MFMA that forms P.V.  m_ref is the
-  // reference max of head `row`, the same in its four lanes; l_part is this
-  // lane's share of the exponent sum; oacc[c][r] = O[head row][16*c + 4*quad + r].
+  // reference max of the row, the same in its four lanes (kNoMax while the
+  // row has seen no position: masked logits then still weigh exactly 0);
+  // l_part is this lane's share of the exponent sum; oacc[c][r] =
+  // O[query row][16*c + 4*quad + r].
   bf16x8_t qa[kKK];
-  float m_ref = -INFINITY, l_part = 0.f;
+  float m_ref = kNoMax, l_part = 0.f;
   f32x4_t oacc[kVC];
   int pend_s[2] = {-1, -1}, pend_g[2] = {0, 0}, pend_seg[2] = {0, 0}, pend_nb[2] = {0, 0};
 
   auto slot_ptr = [&](int wave, int seg) -> int64_t {       // byte offset of a partial slot
     const int which = (seg <= wave * per) ? 0 : 1;
-    return static_cast<int64_t>(wave * 2 + which) * kSlot * 4;
+    return static_cast<int64_t>(wave * 2 + which) * slot_floats * 4;
   };
   const __amdgpu_buffer_rsrc_t part_rsrc = make_rsrc(a.partials, 0x7FFFFFFF);
+
+  // Writes the R staged rows of (sequence s, KV head g) to `out`: lane l
+  // moves 16 bytes of row r0 + l / (kD/8) per pass.
+  auto store_rows = [&](int s, int g) {
+    constexpr int kLPR = kRowOutBytes / 16;                // lanes per row
+    constexpr int kRPP = 64 / kLPR;                        // rows per pass
+    const int rr = lane / kLPR;
+    const int ch = lane - rr * kLPR;
+    for (int r0 = 0; r0 < R; r0 += kRPP) {
+      const int n = r0 + rr;
+      if (n < R) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(s_o + n * kOPitch + ch * 16);
+        const int nt = n / G;
+        uint16_t* dst = a.out + ((static_cast<int64_t>(s) * nchunk + a.t_first + nt) * hq +
+                                 g * G + (n - nt * G)) * kD + ch * 8;
+        *reinterpret_cast<u32x4_t*>(dst) = v;
+      }
+    }
+  };
 
   auto finalize = [&](int s, int g, int seg, int nb) {
     float l_tot = l_part;
@@ -338,38 +385,42 @@ decode_stream_kernel(StreamArgs a) {
     const int wf = seg / per;
     const int wl = (seg + nb - 1) / per;
     if (wf == wl) {   // the whole segment was in this wave: write the output
-      if (row < kG) {
-        const float inv = a.v_scale * __builtin_amdgcn_rcpf(l_tot);
-        uint16_t* orow = a.out + (static_cast<int64_t>(s) * hq + g * kG + row) * kD + 4 * quad;
+      if (row_ok) {
+        // a row that saw no position has l = 0 and o = 0: a zero row
+        const float inv = (l_tot > 0.f) ? a.v_scale * __builtin_amdgcn_rcpf(l_tot) : 0.f;
+        char* srow = s_o + row * kOPitch + 8 * quad;
 #pragma unroll
         for (int c = 0; c < kVC; ++c) {
           const bf16x4_t pk = {static_cast<__bf16>(oacc[c][0] * inv), static_cast<__bf16>(oacc[c][1] * inv),
                                static_cast<__bf16>(oacc[c][2] * inv), static_cast<__bf16>(oacc[c][3] * inv)};
-          *reinterpret_cast<bf16x4_t*>(orow + 16 * c) = pk;
+          *reinterpret_cast<bf16x4_t*>(srow + 32 * c) = pk;
         }
       }
+      store_rows(s, g);
       return;
     }
     // A piece of a segment shared with other waves: only the first and the
     // last segment of a range can be shared, so a wave has at most two
-    // pieces, in slots 0 and 1.  Slot layout: o[kG][kD], m[kG], l[kG]
+    // pieces, in slots 0 and 1.  Slot layout (floats): o as [kD/16][4][R][4]
+    // -- lane (row, quad)'s 4 values of dims 16c + 4quad .. +3 at
+    // ((c*4 + quad)*R + row)*4, so every store instruction writes one
+    // contiguous range -- then (m, l) pairs [R][2]
     // (floats).  Pieces are published with device-coherent stores (sc1:
     // written through to the point of coherence of all XCDs); the arrival
     // count follows once they have completed, after the ring has drained.
     // No L2 write-back or invalidation is needed: nothing else is shared.
     const int64_t mine = slot_ptr(w, seg);
     const int which = (seg <= w * per) ? 0 : 1;
-    if (row < kG) {
+    if (row_ok) {
 #pragma unroll
       for (int c = 0; c < kVC; ++c)
         __builtin_amdgcn_raw_buffer_store_b128(
             __builtin_bit_cast(u32x4_t, oacc[c]), part_rsrc,
-            static_cast<int>(mine + (row * kD + 16 * c + 4 * quad) * 4), 0, kAuxCoherent);
+            static_cast<int>(mine + (((c * 4 + quad) * R + row) * 4) * 4), 0, kAuxCoherent);
       if (quad == 0) {
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_ref), part_rsrc,
-                                              static_cast<int>(mine + (kG * kD + row) * 4), 0, kAuxCoherent);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l_tot), part_rsrc,
-                                              static_cast<int>(mine + (kG * kD + kG + row) * 4), 0, kAuxCoherent);
+        const u32x2_t ml = {__float_as_uint(m_ref), __float_as_uint(l_tot)};
+        __builtin_amdgcn_raw_buffer_store_b64(ml, part_rsrc,
+                                              static_cast<int>(mine + (R * kD + 2 * row) * 4), 0, kAuxCoherent);
       }
     }
     pend_s[which] = s;
@@ -380,17 +431,22 @@ decode_stream_kernel(StreamArgs a) {
 
   // The last piece of a segment merges all of them:
   // out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p, computed online.
-  // Lane l handles elements 4*(l + 64*i) .. +3 of the [kG][kD] output.
+  // Lane l handles the 4-float groups l + 64*i of the slot layout above
+  // (group q: row q % R, dims 16*(q / (4R)) + 4*((q / R) % 4) .. +3).  A
+  // piece in which a row saw no position holds m = kNoMax, l = 0, o = 0 and
+  // adds nothing; a row that saw none in any piece gets a zero row.
   auto merge = [&](int s, int g, int seg, int nb) {
     const int wf = seg / per;
     const int wl = (seg + nb - 1) / per;
     uint32_t* ctr = a.counters + static_cast<int64_t>(s) * hkv + g;
-    constexpr int kE4 = (kG * kD / 4 + 63) / 64;          // 4-float groups per lane
+    constexpr int kE4 = (kMaxRows * kD / 4 + 63) / 64;    // 4-float groups per lane, at most
+    const int n_el = R * kD;
+    const int n_grp = n_el / 4;
     float M[kE4], den[kE4];
     f32x4_t num[kE4];
 #pragma unroll
     for (int i = 0; i < kE4; ++i) {
-      M[i] = -INFINITY;
+      M[i] = kNoMax;
       den[i] = 0.f;
       num[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
@@ -400,18 +456,19 @@ decode_stream_kernel(StreamArgs a) {
       float mp[kE4], lp[kE4];
 #pragma unroll
       for (int i = 0; i < kE4; ++i) {
-        const int e = 4 * (lane + 64 * i);
-        const int h = min(e / kD, kG - 1);
-        const int ee = min(e, kG * kD - 4);
+        if (64 * i >= n_grp) break;                        // wave-uniform
+        const int q = min(lane + 64 * i, n_grp - 1);
+        const int r = q % R;
         op[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                part_rsrc, static_cast<int>(sp + ee * 4), 0, kAuxCoherent));
-        mp[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-            part_rsrc, static_cast<int>(sp + (kG * kD + h) * 4), 0, kAuxCoherent));
-        lp[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-            part_rsrc, static_cast<int>(sp + (kG * kD + kG + h) * 4), 0, kAuxCoherent));
+                                                part_rsrc, static_cast<int>(sp + q * 16), 0, kAuxCoherent));
+        const u32x2_t ml = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(
+            part_rsrc, static_cast<int>(sp + (n_el + 2 * r) * 4), 0, kAuxCoherent));
+        mp[i] = __uint_as_float(ml[0]);
+        lp[i] = __uint_as_float(ml[1]);
       }
 #pragma unroll
       for (int i = 0; i < kE4; ++i) {
+        if (64 * i >= n_grp) break;
         const float mn = fmaxf(M[i], mp[i]);
         const float f_old = __builtin_amdgcn_exp2f(M[i] - mn);
         const float f_new = __builtin_amdgcn_exp2f(mp[i] - mn);
@@ -422,17 +479,19 @@ decode_stream_kernel(StreamArgs a) {
       }
     };
     for (int p = wf; p <= wl; ++p) merge_one(p);
-    uint16_t* orow = a.out + (static_cast<int64_t>(s) * hq + g * kG) * kD;
 #pragma unroll
     for (int i = 0; i < kE4; ++i) {
-      const int e = 4 * (lane + 64 * i);
-      if (e < kG * kD) {
-        const float inv = a.v_scale * __builtin_amdgcn_rcpf(den[i]);
+      const int q = lane + 64 * i;
+      if (q < n_grp) {
+        const int r = q % R;
+        const int cq = q / R;                              // c * 4 + quad
+        const float inv = (den[i] > 0.f) ? a.v_scale * __builtin_amdgcn_rcpf(den[i]) : 0.f;
         const bf16x4_t pk = {static_cast<__bf16>(num[i][0] * inv), static_cast<__bf16>(num[i][1] * inv),
                              static_cast<__bf16>(num[i][2] * inv), static_cast<__bf16>(num[i][3] * inv)};
-        *reinterpret_cast<bf16x4_t*>(orow + e) = pk;
+        *reinterpret_cast<bf16x4_t*>(s_o + r * kOPitch + 8 * cq) = pk;
       }
     }
+    store_rows(s, g);
     if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
 
@@ -449,7 +508,7 @@ decode_stream_kernel(StreamArgs a) {
       for (int c = lane; c < span; c += 64) {
         const int j = w_j + c;
         const int gpos = done + pos + c;                     // position in the range
-        const uint32_t valid = static_cast<uint32_t>(min(kBlock, w_L - kBlock * j));
+        const uint32_t valid = static_cast<uint32_t>(min(31, w_L - kBlock * j));
         const uint32_t first = (j == 0 || gpos == 0) ? 1u : 0u;
         const uint32_t last = (j == w_nb - 1 || gpos == n_total - 1) ? 1u : 0u;
         s_desc[pos + c] = u32x4_t{static_cast<uint32_t>(j),
@@ -507,12 +566,12 @@ decode_stream_kernel(StreamArgs a) {
         const uint32_t tile = __builtin_amdgcn_readfirstlane(d[0]);
         const uint32_t info = __builtin_amdgcn_readfirstlane(d[1]);
         const int s = __builtin_amdgcn_readfirstlane(static_cast<int>(d[2]));
-        k_nrec = static_cast<int>(info & 31u) * kRowBytes;   // rows past the context read 0
+        k_nrec = min(static_cast<int>(info & 31u), kBlock) * kRowBytes;   // rows past the context read 0
         v_nrec = k_nrec;
         tile_off = static_cast<int64_t>(tile) * kTileBytes;
         if (info & 32u) {
-          q_off = (static_cast<int64_t>(s) * hq + static_cast<int>((info >> 7) & 511u) * kG) * kD * 2;
-          q_nrec = kQBytes;
+          q_off = (static_cast<int64_t>(s) * nchunk * hq + static_cast<int>((info >> 7) & 511u) * G) * kD * 2;
+          q_nrec = q_bytes;
         }
       }
       const __amdgpu_buffer_rsrc_t rq = make_rsrc(reinterpret_cast<const char*>(a.q) + q_off, q_nrec);
@@ -540,9 +599,9 @@ decode_stream_kernel(StreamArgs a) {
       if (t >= n) return;
       const u32x4_t d = s_desc[t];
       const uint32_t info = __builtin_amdgcn_readfirstlane(d[1]);
-      const int valid = static_cast<int>(info & 31u);
+      const int rows_left = static_cast<int>(info & 31u);   // min(31, L - 16j)
       if (info & 32u) {                                      // a piece starts here
-        m_ref = -INFINITY;
+        m_ref = kNoMax;
         l_part = 0.f;
 #pragma unroll
         for (int c = 0; c < kVC; ++c) oacc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -569,10 +628,11 @@ decode_stream_kernel(StreamArgs a) {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qa[kk], acc, 0, 0, 0);
       }
       float x[4];
+      const int lim = rows_left - mshift;                    // tile rows this query row may see
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         x[r] = acc[r] * a.logit_scale;
-        if (4 * quad + r >= valid) x[r] = -INFINITY;
+        if (4 * quad + r >= lim) x[r] = -INFINITY;
       }
 
       // ---- lazy running max: moved only when a logit exceeds it by more
@@ -686,26 +746,28 @@ zero_fill_kernel(uint32_t* p, int64_t n_words) {
 
 // ---------------------------------------------------------------------------
 // General path: any G, fp32 / bf16 / fp8 cache.  One wave per (partition,
-// query head, sequence); one token at a time, dot product by a wave
+// query row, sequence); one token at a time, dot product by a wave
 // reduction, exact online softmax.  Used for fp32 caches and shapes the fast
-// path does not cover.
+// path does not cover.  Query row y = i * hq + h is chunk token i of query
+// head h; it sees the first L - chunk + 1 + i positions.
 template <int kD, int kFmt, bool kOutF32>
 __global__ void __launch_bounds__(64)
 decode_simple_kernel(const char* __restrict__ k_cache, const char* __restrict__ v_cache,
                      const void* __restrict__ q, const int32_t* __restrict__ block_tables,
                      const int32_t* __restrict__ context_lens, int max_blocks, int hkv,
-                     int group, float logit_scale, float v_scale, PartOut po) {
+                     int group, int hq, int chunk, float logit_scale, float v_scale,
+                     PartOut po) {
   constexpr int kPer = kD / 64;
   const int part = blockIdx.x;
-  const int h = blockIdx.y;
+  const int y = blockIdx.y;
   const int s = blockIdx.z;
-  const int hq = gridDim.y;
+  const int h = y % hq;
   const int g = h / group;
-  const int L = context_lens[s];
+  const int L = max(0, context_lens[s] - chunk + 1 + y / hq);
   const int nparts = (L + kPartTokens - 1) / kPartTokens;
   const int lane = threadIdx.x;
   if (part >= (nparts > 0 ? nparts : 1)) return;
-  const int64_t orow = (static_cast<int64_t>(s) * hq + h) * kD;
+  const int64_t orow = (static_cast<int64_t>(s) * gridDim.y + y) * kD;
   if (L == 0) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) store_out<kOutF32>(po.out, orow + lane + 64 * i, 0.f);
@@ -757,7 +819,7 @@ decode_simple_kernel(const char* __restrict__ k_cache, const char* __restrict__ 
 #pragma unroll
     for (int i = 0; i < kPer; ++i) store_out<kOutF32>(po.out, orow + lane + 64 * i, o[i] / l * v_scale);
   } else {
-    const int64_t r = (static_cast<int64_t>(s) * hq + h) * po.num_parts + part;
+    const int64_t r = (static_cast<int64_t>(s) * gridDim.y + y) * po.num_parts + part;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) po.ws_o[r * kD + lane + 64 * i] = o[i] / l * v_scale;
     if (lane == 0) {
@@ -768,19 +830,18 @@ decode_simple_kernel(const char* __restrict__ k_cache, const char* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp merge of the partitions of one (sequence, query head):
+// Log-sum-exp merge of the partitions of one (sequence, query row):
 //   out = sum_i 2^(m_i - M) l_i o_i / sum_i 2^(m_i - M) l_i,  M = max_i m_i.
 template <int kD, bool kOutF32>
 __global__ void __launch_bounds__(kD)
-reduce_kernel(const int32_t* __restrict__ context_lens, PartOut po) {
-  const int h = blockIdx.x;
+reduce_kernel(const int32_t* __restrict__ context_lens, int hq, int chunk, PartOut po) {
+  const int y = blockIdx.x;
   const int s = blockIdx.y;
-  const int hq = gridDim.x;
-  const int L = context_lens[s];
+  const int L = max(0, context_lens[s] - chunk + 1 + y / hq);
   const int nparts = (L + kPartTokens - 1) / kPartTokens;
   if (nparts <= 1) return;     // written directly by the partition pass
   const int d = threadIdx.x;
-  const int64_t r0 = (static_cast<int64_t>(s) * hq + h) * po.num_parts;
+  const int64_t r0 = (static_cast<int64_t>(s) * gridDim.x + y) * po.num_parts;
   float M = -INFINITY;
   for (int i = 0; i < nparts; ++i) M = fmaxf(M, po.ws_ml[2 * (r0 + i)]);
   float den = 0.f, num = 0.f;
@@ -789,45 +850,29 @@ reduce_kernel(const int32_t* __restrict__ context_lens, PartOut po) {
     den += a;
     num = fmaf(a, po.ws_o[(r0 + i) * kD + d], num);
   }
-  store_out<kOutF32>(po.out, (static_cast<int64_t>(s) * hq + h) * kD + d, num / den);
+  store_out<kOutF32>(po.out, (static_cast<int64_t>(s) * gridDim.x + y) * kD + d, num / den);
 }
 
 template <int kD>
-void launch_simple(int fmt, bool out_f32, dim3 grid, hipStream_t st, const char* kc,
-                   const char* vc, const void* q, const int32_t* bt, const int32_t* cl,
-                   int maxb, int hkv, int G, float ls, float vs, PartOut po) {
+void launch_simple(int fmt, dim3 grid, hipStream_t st, const char* kc, const char* vc,
+                   const void* q, const int32_t* bt, const int32_t* cl, int maxb, int hkv,
+                   int G, int hq, int T, float ls, float vs, PartOut po) {
   if (fmt == PA_F32)
-    decode_simple_kernel<kD, PA_F32, true><<<grid, 64, 0, st>>>(kc, vc, q, bt, cl, maxb, hkv, G, ls, vs, po);
+    decode_simple_kernel<kD, PA_F32, true><<<grid, 64, 0, st>>>(kc, vc, q, bt, cl, maxb, hkv, G, hq, T, ls, vs, po);
   else if (fmt == PA_BF16)
-    decode_simple_kernel<kD, PA_BF16, false><<<grid, 64, 0, st>>>(kc, vc, q, bt, cl, maxb, hkv, G, ls, vs, po);
+    decode_simple_kernel<kD, PA_BF16, false><<<grid, 64, 0, st>>>(kc, vc, q, bt, cl, maxb, hkv, G, hq, T, ls, vs, po);
   else
-    decode_simple_kernel<kD, PA_FP8_E4M3, false><<<grid, 64, 0, st>>>(kc, vc, q, bt, cl, maxb, hkv, G, ls, vs, po);
-  (void)out_f32;
+    decode_simple_kernel<kD, PA_FP8_E4M3, false><<<grid, 64, 0, st>>>(kc, vc, q, bt, cl, maxb, hkv, G, hq, T, ls, vs, po);
 }
 
 
-template <int kD, int kG>
-void launch_stream_g(bool fp8, int nw, hipStream_t st, const StreamArgs& a) {
+template <int kD>
+void launch_stream(bool fp8, int nw, hipStream_t st, const StreamArgs& a) {
   const dim3 grid(nw / kWavesPerGroup), block(64 * kWavesPerGroup);
   if (fp8)
-    decode_stream_kernel<kD, kG, true, kAuxNonTemporal><<<grid, block, kPadLds, st>>>(a);
+    decode_stream_kernel<kD, true, kAuxNonTemporal><<<grid, block, kPadLds, st>>>(a);
   else
-    decode_stream_kernel<kD, kG, false, kAuxNonTemporal><<<grid, block, kPadLds, st>>>(a);
-}
-
-template <int kD>
-void launch_stream(int G, bool fp8, int nw, hipStream_t st, const StreamArgs& a) {
-  switch (G) {
-    case 1: launch_stream_g<kD, 1>(fp8, nw, st, a); break;
-    case 2: launch_stream_g<kD, 2>(fp8, nw, st, a); break;
-    case 3: launch_stream_g<kD, 3>(fp8, nw, st, a); break;
-    case 4: launch_stream_g<kD, 4>(fp8, nw, st, a); break;
-    case 5: launch_stream_g<kD, 5>(fp8, nw, st, a); break;
-    case 6: launch_stream_g<kD, 6>(fp8, nw, st, a); break;
-    case 7: launch_stream_g<kD, 7>(fp8, nw, st, a); break;
-    case 8: launch_stream_g<kD, 8>(fp8, nw, st, a); break;
-    default: break;
-  }
+    decode_stream_kernel<kD, false, kAuxNonTemporal><<<grid, block, kPadLds, st>>>(a);
 }
 
 }  // namespace
@@ -843,9 +888,12 @@ int num_partitions(int32_t max_context_len) {
 }
 
 bool fast_path(int fmt, int q_dtype, int G, int D) {
-  return (fmt == PA_BF16 || fmt == PA_FP8_E4M3) && q_dtype == PA_BF16 && G >= 1 && G <= 8 &&
-         (D == 64 || D == 128);
+  return (fmt == PA_BF16 || fmt == PA_FP8_E4M3) && q_dtype == PA_BF16 && G >= 1 &&
+         G <= kMaxRows && (D == 64 || D == 128);
 }
+
+// Chunk tokens per fast-path pass: as many as fit G rows each in 16 columns.
+int tokens_per_pass(int G, int T) { return std::min(T, std::max(1, kMaxRows / G)); }
 
 // Compute units of the current device (256 on MI355X when it cannot be read).
 int device_cus() {
@@ -866,32 +914,176 @@ int device_cus() {
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-// Fast path workspace: arrival counters, then two partial slots per wave.
-size_t stream_workspace_bytes(int num_seqs, int hkv, int G, int D) {
+// Fast path workspace: arrival counters, then two partial slots per wave of
+// `rows` query rows each.
+size_t stream_workspace_bytes(int num_seqs, int hkv, int rows, int D) {
   const size_t waves = static_cast<size_t>(device_cus()) * kWavesPerCU;
   return align256(static_cast<size_t>(num_seqs) * hkv * sizeof(uint32_t)) +
-         waves * 2 * G * (D + 2) * sizeof(float);
+         waves * 2 * rows * (D + 2) * sizeof(float);
 }
 
-size_t general_workspace_bytes(int num_seqs, int num_q_heads, int D, int max_context_len) {
+size_t general_workspace_bytes(int num_seqs, int num_q_heads, int T, int D, int max_context_len) {
   const int P = num_partitions(max_context_len);
   if (P <= 1) return 0;
-  return static_cast<size_t>(num_seqs) * num_q_heads * P * (D + 2) * sizeof(float);
+  return static_cast<size_t>(num_seqs) * T * num_q_heads * P * (D + 2) * sizeof(float);
+}
+
+size_t workspace_bytes_for(const pa_cache_desc* c, int32_t num_seqs, int32_t num_q_heads,
+                           int32_t T, int32_t max_context_len, const char* fn) {
+  if (check_desc(c, fn) != PA_OK) return 0;
+  if (num_seqs <= 0 || num_q_heads <= 0 || max_context_len <= 0 || T <= 0 ||
+      num_q_heads % c->num_kv_heads != 0)
+    return 0;
+  const int G = num_q_heads / c->num_kv_heads;
+  const int q_dtype = (c->cache_dtype == PA_F32) ? PA_F32 : PA_BF16;
+  if (fast_path(c->cache_dtype, q_dtype, G, c->head_dim))
+    return stream_workspace_bytes(num_seqs, c->num_kv_heads, G * tokens_per_pass(G, T),
+                                  c->head_dim);
+  return general_workspace_bytes(num_seqs, num_q_heads, T, c->head_dim, max_context_len);
+}
+
+// pa_decode (T = 1) and pa_decode_chunk: one implementation.
+pa_status attend(const char* fn, const pa_cache_desc* c, const void* k_cache,
+                 const void* v_cache, const void* q, int32_t q_dtype, void* out, int32_t T,
+                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                 const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs,
+                 int32_t num_q_heads, float scale, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  pa_status st = check_desc(c, fn);
+  if (st != PA_OK) return st;
+  const int hkv = c->num_kv_heads, D = c->head_dim, fmt = c->cache_dtype;
+  if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0 || max_blocks_per_seq < 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (T < 1 || T > PA_MAX_CHUNK)
+    return fail(PA_ERR_INVALID_ARG, "%s: chunk_len %d (1..%d)", fn, T, PA_MAX_CHUNK);
+  if (num_q_heads % hkv != 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: %d query heads not a multiple of %d KV heads", fn,
+                num_q_heads, hkv);
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "%s: scale not finite", fn);
+  const bool combo_ok = (fmt == PA_F32 && q_dtype == PA_F32) ||
+                        (fmt == PA_BF16 && q_dtype == PA_BF16) ||
+                        (fmt == PA_FP8_E4M3 && q_dtype == PA_BF16);
+  if (!combo_ok)
+    return fail(PA_ERR_UNSUPPORTED, "%s: q dtype %d with cache dtype %d", fn, q_dtype, fmt);
+  if (static_cast<int64_t>(max_blocks_per_seq) * kBlock < max_context_len)
+    return fail(PA_ERR_INVALID_ARG, "%s: max_blocks_per_seq %d cannot hold max_context_len %d",
+                fn, max_blocks_per_seq, max_context_len);
+  if (num_seqs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !q || !out || !block_tables || !context_lens)
+    return fail(PA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  const int G = num_q_heads / hkv;
+  const bool fast = fast_path(fmt, q_dtype, G, D);
+  const int tpp = tokens_per_pass(G, T);
+  const int64_t max_tiles = static_cast<int64_t>(hkv) * num_seqs *
+                            ((static_cast<int64_t>(max_context_len) + kBlock - 1) / kBlock);
+  if (fast && (max_tiles >= (int64_t{1} << 30) ||
+               static_cast<int64_t>(max_blocks_per_seq) * 4 >= (int64_t{1} << 31) ||
+               (static_cast<int64_t>(T - 1) * num_q_heads + G) * D * 2 >= (int64_t{1} << 30)))
+    return fail(PA_ERR_UNSUPPORTED, "%s: %lld tiles in one call (limit 2^30)", fn,
+                static_cast<long long>(max_tiles));
+  if (!fast && (num_seqs > 65535 || static_cast<int64_t>(T) * num_q_heads > 65535))
+    return fail(PA_ERR_UNSUPPORTED, "%s: num_seqs / chunk_len * num_q_heads above 65535", fn);
+  if (fast && (reinterpret_cast<uintptr_t>(out) % 16 != 0 || reinterpret_cast<uintptr_t>(q) % 16 != 0))
+    return fail(PA_ERR_INVALID_ARG, "%s: q and out must be 16-byte aligned", fn);
+  const size_t need = fast ? stream_workspace_bytes(num_seqs, hkv, G * tpp, D)
+                           : general_workspace_bytes(num_seqs, num_q_heads, T, D, max_context_len);
+  if (workspace_bytes < need || (need > 0 && !workspace))
+    return fail(PA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes, need %zu", fn,
+                workspace_bytes, need);
+  if (need > 0 && reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: workspace not 16-byte aligned", fn);
+
+  const float kscale = (fmt == PA_FP8_E4M3) ? c->k_scale : 1.f;
+  const float vscale = (fmt == PA_FP8_E4M3) ? c->v_scale : 1.f;
+  const float logit_scale =
+      static_cast<float>(static_cast<double>(scale) * kscale * 1.4426950408889634);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const char* kc = static_cast<const char*>(k_cache);
+  const char* vc = static_cast<const char*>(v_cache);
+
+  if (fast) {
+    if (max_context_len == 0) max_context_len = 1;
+    const int64_t waves_max = static_cast<int64_t>(device_cus()) * kWavesPerCU;
+    const int64_t by_size = (max_tiles + kMinTilesPerWave - 1) / kMinTilesPerWave;
+    const int64_t nw = (std::max<int64_t>(std::min(waves_max, by_size), 1) + kWavesPerGroup - 1) /
+                       kWavesPerGroup * kWavesPerGroup;
+    StreamArgs a;
+    a.k_cache = kc;
+    a.v_cache = vc;
+    a.q = static_cast<const uint16_t*>(q);
+    a.out = static_cast<uint16_t*>(out);
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.counters = static_cast<uint32_t*>(workspace);
+    a.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                          align256(static_cast<size_t>(num_seqs) * hkv * 4));
+    a.num_seqs = num_seqs;
+    a.hkv = hkv;
+    a.max_blocks = max_blocks_per_seq;
+    a.num_waves = static_cast<int>(nw);
+    a.group = G;
+    a.chunk = T;
+    a.logit_scale = logit_scale;
+    a.v_scale = vscale;
+    // one pass per tpp chunk tokens; each pass leaves the counters zeroed
+    for (int t0 = 0; t0 < T; t0 += tpp) {
+      a.t_first = t0;
+      a.rows = G * std::min(tpp, T - t0);
+      if (D == 128) launch_stream<128>(fmt == PA_FP8_E4M3, a.num_waves, s, a);
+      else launch_stream<64>(fmt == PA_FP8_E4M3, a.num_waves, s, a);
+      st = launch_status(fn);
+      if (st != PA_OK) return st;
+    }
+    return PA_OK;
+  }
+
+  const int P = max_context_len > 0 ? num_partitions(max_context_len) : 1;
+  PartOut po;
+  po.out = out;
+  po.num_parts = P;
+  po.ws_o = static_cast<float*>(workspace);
+  po.ws_ml = need ? po.ws_o + static_cast<size_t>(num_seqs) * T * num_q_heads * P * D : nullptr;
+  const int rows = T * num_q_heads;
+  {
+    dim3 grid(P, rows, num_seqs);
+    if (D == 128)
+      launch_simple<128>(fmt, grid, s, kc, vc, q, block_tables, context_lens,
+                         max_blocks_per_seq, hkv, G, num_q_heads, T, logit_scale, vscale, po);
+    else
+      launch_simple<64>(fmt, grid, s, kc, vc, q, block_tables, context_lens,
+                        max_blocks_per_seq, hkv, G, num_q_heads, T, logit_scale, vscale, po);
+  }
+  st = launch_status(fn);
+  if (st != PA_OK) return st;
+  if (P > 1) {
+    dim3 grid(rows, num_seqs);
+    const bool of32 = (q_dtype == PA_F32);
+    if (D == 128) {
+      if (of32) reduce_kernel<128, true><<<grid, 128, 0, s>>>(context_lens, num_q_heads, T, po);
+      else reduce_kernel<128, false><<<grid, 128, 0, s>>>(context_lens, num_q_heads, T, po);
+    } else {
+      if (of32) reduce_kernel<64, true><<<grid, 64, 0, s>>>(context_lens, num_q_heads, T, po);
+      else reduce_kernel<64, false><<<grid, 64, 0, s>>>(context_lens, num_q_heads, T, po);
+    }
+    st = launch_status(fn);
+  }
+  return st;
 }
 
 }  // namespace
 
 extern "C" size_t pa_decode_workspace_bytes(const pa_cache_desc* c, int32_t num_seqs,
                                             int32_t num_q_heads, int32_t max_context_len) {
-  if (check_desc(c, "pa_decode_workspace_bytes") != PA_OK) return 0;
-  if (num_seqs <= 0 || num_q_heads <= 0 || max_context_len <= 0 ||
-      num_q_heads % c->num_kv_heads != 0)
-    return 0;
-  const int G = num_q_heads / c->num_kv_heads;
-  const int q_dtype = (c->cache_dtype == PA_F32) ? PA_F32 : PA_BF16;
-  if (fast_path(c->cache_dtype, q_dtype, G, c->head_dim))
-    return stream_workspace_bytes(num_seqs, c->num_kv_heads, G, c->head_dim);
-  return general_workspace_bytes(num_seqs, num_q_heads, c->head_dim, max_context_len);
+  return workspace_bytes_for(c, num_seqs, num_q_heads, 1, max_context_len,
+                             "pa_decode_workspace_bytes");
+}
+
+extern "C" size_t pa_decode_chunk_workspace_bytes(const pa_cache_desc* c, int32_t num_seqs,
+                                                  int32_t num_q_heads, int32_t chunk_len,
+                                                  int32_t max_context_len) {
+  if (chunk_len < 1 || chunk_len > PA_MAX_CHUNK) return 0;
+  return workspace_bytes_for(c, num_seqs, num_q_heads, chunk_len, max_context_len,
+                             "pa_decode_chunk_workspace_bytes");
 }
 
 extern "C" pa_status pa_decode_workspace_init(void* workspace, size_t workspace_bytes,
@@ -915,109 +1107,19 @@ extern "C" pa_status pa_decode(const pa_cache_desc* c, const void* k_cache, cons
                                const int32_t* context_lens, int32_t max_context_len,
                                int32_t num_seqs, int32_t num_q_heads, float scale,
                                void* workspace, size_t workspace_bytes, void* stream) {
-  pa_status st = check_desc(c, "pa_decode");
-  if (st != PA_OK) return st;
-  const int hkv = c->num_kv_heads, D = c->head_dim, fmt = c->cache_dtype;
-  if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0 || max_blocks_per_seq < 0)
-    return fail(PA_ERR_INVALID_ARG, "pa_decode: negative size");
-  if (num_q_heads % hkv != 0)
-    return fail(PA_ERR_INVALID_ARG, "pa_decode: %d query heads not a multiple of %d KV heads",
-                num_q_heads, hkv);
-  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "pa_decode: scale not finite");
-  const bool combo_ok = (fmt == PA_F32 && q_dtype == PA_F32) ||
-                        (fmt == PA_BF16 && q_dtype == PA_BF16) ||
-                        (fmt == PA_FP8_E4M3 && q_dtype == PA_BF16);
-  if (!combo_ok)
-    return fail(PA_ERR_UNSUPPORTED, "pa_decode: q dtype %d with cache dtype %d", q_dtype, fmt);
-  if (static_cast<int64_t>(max_blocks_per_seq) * kBlock < max_context_len)
-    return fail(PA_ERR_INVALID_ARG,
-                "pa_decode: max_blocks_per_seq %d cannot hold max_context_len %d",
-                max_blocks_per_seq, max_context_len);
-  if (num_seqs == 0) return PA_OK;
-  if (!k_cache || !v_cache || !q || !out || !block_tables || !context_lens)
-    return fail(PA_ERR_INVALID_ARG, "pa_decode: null pointer");
-  const int G = num_q_heads / hkv;
-  const bool fast = fast_path(fmt, q_dtype, G, D);
-  const int64_t max_tiles = static_cast<int64_t>(hkv) * num_seqs *
-                            ((static_cast<int64_t>(max_context_len) + kBlock - 1) / kBlock);
-  if (fast && (max_tiles >= (int64_t{1} << 30) ||
-               static_cast<int64_t>(max_blocks_per_seq) * 4 >= (int64_t{1} << 31)))
-    return fail(PA_ERR_UNSUPPORTED, "pa_decode: %lld tiles in one call (limit 2^30)",
-                static_cast<long long>(max_tiles));
-  if (!fast && (num_seqs > 65535 || num_q_heads > 65535))
-    return fail(PA_ERR_UNSUPPORTED, "pa_decode: num_seqs / num_q_heads above 65535");
-  const size_t need = fast ? stream_workspace_bytes(num_seqs, hkv, G, D)
-                           : general_workspace_bytes(num_seqs, num_q_heads, D, max_context_len);
-  if (workspace_bytes < need || (need > 0 && !workspace))
-    return fail(PA_ERR_WORKSPACE_TOO_SMALL, "pa_decode: workspace %zu bytes, need %zu",
-                workspace_bytes, need);
-  if (need > 0 && reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
-    return fail(PA_ERR_INVALID_ARG, "pa_decode: workspace not 16-byte aligned");
+  return attend("pa_decode", c, k_cache, v_cache, q, q_dtype, out, 1, block_tables,
+                max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads, scale,
+                workspace, workspace_bytes, stream);
+}
 
-  const float kscale = (fmt == PA_FP8_E4M3) ? c->k_scale : 1.f;
-  const float vscale = (fmt == PA_FP8_E4M3) ? c->v_scale : 1.f;
-  const float logit_scale =
-      static_cast<float>(static_cast<double>(scale) * kscale * 1.4426950408889634);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const char* kc = static_cast<const char*>(k_cache);
-  const char* vc = static_cast<const char*>(v_cache);
-
-  if (fast) {
-    if (max_context_len == 0) max_context_len = 1;
-    const int64_t waves_max = static_cast<int64_t>(device_cus()) * kWavesPerCU;
-    const int64_t by_size = (max_tiles + kMinTilesPerWave - 1) / kMinTilesPerWave;
-    // enough waves to cover the empty-sequence duty (one per 64 sequences)
-    const int64_t nw = (std::max<int64_t>(std::min(waves_max, by_size), 1) + kWavesPerGroup - 1) /
-                       kWavesPerGroup * kWavesPerGroup;
-    StreamArgs a;
-    a.k_cache = kc;
-    a.v_cache = vc;
-    a.q = static_cast<const uint16_t*>(q);
-    a.out = static_cast<uint16_t*>(out);
-    a.block_tables = block_tables;
-    a.context_lens = context_lens;
-    a.counters = static_cast<uint32_t*>(workspace);
-    a.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                          align256(static_cast<size_t>(num_seqs) * hkv * 4));
-    a.num_seqs = num_seqs;
-    a.hkv = hkv;
-    a.max_blocks = max_blocks_per_seq;
-    a.num_waves = static_cast<int>(nw);
-    a.logit_scale = logit_scale;
-    a.v_scale = vscale;
-    if (D == 128) launch_stream<128>(G, fmt == PA_FP8_E4M3, a.num_waves, s, a);
-    else launch_stream<64>(G, fmt == PA_FP8_E4M3, a.num_waves, s, a);
-    return launch_status("pa_decode");
-  }
-
-  const int P = max_context_len > 0 ? num_partitions(max_context_len) : 1;
-  PartOut po;
-  po.out = out;
-  po.num_parts = P;
-  po.ws_o = static_cast<float*>(workspace);
-  po.ws_ml = need ? po.ws_o + static_cast<size_t>(num_seqs) * num_q_heads * P * D : nullptr;
-  {
-    dim3 grid(P, num_q_heads, num_seqs);
-    if (D == 128)
-      launch_simple<128>(fmt, fmt == PA_F32, grid, s, kc, vc, q, block_tables, context_lens,
-                         max_blocks_per_seq, hkv, G, logit_scale, vscale, po);
-    else
-      launch_simple<64>(fmt, fmt == PA_F32, grid, s, kc, vc, q, block_tables, context_lens,
-                        max_blocks_per_seq, hkv, G, logit_scale, vscale, po);
-  }
-  st = launch_status("pa_decode (partition pass)");
-  if (st != PA_OK) return st;
-  if (P > 1) {
-    dim3 grid(num_q_heads, num_seqs);
-    const bool of32 = (q_dtype == PA_F32);
-    if (D == 128) {
-      if (of32) reduce_kernel<128, true><<<grid, 128, 0, s>>>(context_lens, po);
-      else reduce_kernel<128, false><<<grid, 128, 0, s>>>(context_lens, po);
-    } else {
-      if (of32) reduce_kernel<64, true><<<grid, 64, 0, s>>>(context_lens, po);
-      else reduce_kernel<64, false><<<grid, 64, 0, s>>>(context_lens, po);
-    }
-    st = launch_status("pa_decode (reduce)");
-  }
-  return st;
+extern "C" pa_status pa_decode_chunk(const pa_cache_desc* c, const void* k_cache,
+                                     const void* v_cache, const void* q, int32_t q_dtype,
+                                     void* out, int32_t chunk_len, const int32_t* block_tables,
+                                     int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                     int32_t max_context_len, int32_t num_seqs,
+                                     int32_t num_q_heads, float scale, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  return attend("pa_decode_chunk", c, k_cache, v_cache, q, q_dtype, out, chunk_len,
+                block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs,
+                num_q_heads, scale, workspace, workspace_bytes, stream);
 }

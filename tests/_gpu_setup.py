@@ -100,6 +100,20 @@ class GpuView:
                   float(w.scale), workspace)
         return out
 
+    def decode_chunk(self, q, max_len=None, workspace=None):
+        """pa_decode_chunk with q [B, T, Hq, D] (generator format)."""
+        w = self.w
+        qd = to_device_rows(q, w.q_fmt, self.dev)
+        out = torch.empty_like(qd)
+        T = q.shape[1]
+        if max_len is None:
+            max_len = int(max(1, int(np.max(self.cl_host)) if len(self.cl_host) else 1))
+        if workspace is None:
+            workspace = pk.new_chunk_workspace(self.desc, w.B, w.Hq, T, max_len, self.dev)
+        pk.decode_chunk(self.desc, self.kc, self.vc, qd, out, self.bt, self.cl, max_len,
+                        float(w.scale), workspace)
+        return out
+
 
 def fill_sequential(view):
     """Sequences 0..B-1 get all their tokens in order; every row but each

@@ -72,10 +72,11 @@ def _small_case(seed, fmt, B, Hq, Hkv, D, max_len, min_len=0, lens=None):
 @pytest.mark.parametrize("fmt,G,D", [
     ("bf16", 1, 128), ("bf16", 4, 128), ("bf16", 8, 128), ("bf16", 3, 64), ("bf16", 5, 128),
     ("bf16", 2, 64), ("fp8", 4, 128), ("fp8", 8, 64), ("fp8", 1, 128),
-    ("f32", 1, 64), ("f32", 4, 128), ("bf16", 16, 128), ("fp8", 12, 64)])
+    ("f32", 1, 64), ("f32", 4, 128), ("bf16", 16, 128), ("fp8", 12, 64), ("bf16", 32, 64)])
 def test_decode_small_ragged(fmt, G, D):
     """Lengths 0..1400: empty, sub-block, ragged last blocks, one to three
-    partitions; G > 8 goes through the general kernel."""
+    partitions; G up to 16 streams tiles, G = 32 and fp32 caches take the
+    partition kernel."""
     Hkv = 2
     lens = np.array([0, 1, 15, 16, 17, 33, 511, 512, 513, 1024, 1400, 700], dtype=np.int32)
     _small_case(100 + G + D, fmt, len(lens), G * Hkv, Hkv, D, 0, lens=lens)

@@ -51,11 +51,17 @@ def test_status_codes_and_messages_on_bad_arguments():
     st = pk.lib.pa_decode(ctypes.byref(d.c), None, None, None, 1, None, None, 2, None, 64,
                           1, 2, 1.0, None, 0, None)
     assert st == -1 and b"max_blocks_per_seq" in pk.lib.pa_last_error()
-    # long contexts need a workspace
-    st = pk.lib.pa_decode(ctypes.byref(d.c), ctypes.c_void_p(1), ctypes.c_void_p(1),
-                          ctypes.c_void_p(1), 1, ctypes.c_void_p(1), ctypes.c_void_p(1), 64,
-                          ctypes.c_void_p(1), 1024, 1, 2, 1.0, None, 0, None)
+    # long contexts need a workspace (fake, never dereferenced pointers; q and
+    # out 16-byte aligned)
+    one, al = ctypes.c_void_p(1), ctypes.c_void_p(256)
+    st = pk.lib.pa_decode(ctypes.byref(d.c), one, one, al, 1, al, one, 64,
+                          one, 1024, 1, 2, 1.0, None, 0, None)
     assert st == -6
+    # q / out must be 16-byte aligned on the bf16 / fp8 path
+    for qp, op in ((ctypes.c_void_p(264), al), (al, ctypes.c_void_p(258))):
+        st = pk.lib.pa_decode(ctypes.byref(d.c), one, one, qp, 1, op, one, 64,
+                              one, 1024, 1, 2, 1.0, None, 0, None)
+        assert st == -1 and b"aligned" in pk.lib.pa_last_error()
     # zero-size calls are no-ops
     assert pk.lib.pa_write_kv(ctypes.byref(d.c), None, None, None, None, 1, None, 0, None) == 0
     assert pk.lib.pa_copy_blocks(ctypes.byref(d.c), None, None, None, 0, None) == 0
@@ -80,6 +86,46 @@ def test_workspace_size_formula():
     # invalid shapes report 0
     assert pk.decode_workspace_bytes(bf, 4, 12, 100) == 0
     assert pk.decode_workspace_bytes(bf, 0, 8, 100) == 0
+
+
+def test_chunk_workspace_size_formula():
+    waves = 256 * 4
+    bf = pk.CacheDesc(64, 8, 128, "bf16")
+    head = 256 * 8 * 4
+    # one pass takes floor(16 / G) chunk tokens: G * tokens rows per slot
+    assert pk.chunk_workspace_bytes(bf, 256, 32, 1, 4096) == pk.decode_workspace_bytes(bf, 256, 32, 4096)
+    assert pk.chunk_workspace_bytes(bf, 256, 32, 4, 4096) == head + waves * 2 * 16 * 130 * 4
+    assert pk.chunk_workspace_bytes(bf, 256, 32, 8, 4096) == head + waves * 2 * 16 * 130 * 4
+    assert pk.chunk_workspace_bytes(bf, 256, 64, 3, 4096) == head + waves * 2 * 16 * 130 * 4
+    assert pk.chunk_workspace_bytes(bf, 256, 8, 5, 4096) == head + waves * 2 * 5 * 130 * 4
+    # G = 16 still takes the streaming path, one token per pass
+    assert pk.chunk_workspace_bytes(pk.CacheDesc(64, 2, 64, "bf16"), 3, 32, 2, 100) == \
+        256 + waves * 2 * 16 * 66 * 4
+    # G = 32 and fp32 caches take the partition path: a record per query row and partition
+    assert pk.chunk_workspace_bytes(pk.CacheDesc(64, 1, 64, "bf16"), 2, 32, 3, 1000) == \
+        2 * 3 * 32 * 2 * 66 * 4
+    f32 = pk.CacheDesc(64, 2, 64, "f32")
+    assert pk.chunk_workspace_bytes(f32, 4, 4, 16, 513) == 4 * 16 * 4 * 2 * 66 * 4
+    assert pk.chunk_workspace_bytes(f32, 4, 4, 16, 512) == 0
+    # chunk lengths outside 1..16
+    assert pk.chunk_workspace_bytes(bf, 4, 32, 0, 100) == 0
+    assert pk.chunk_workspace_bytes(bf, 4, 32, 17, 100) == 0
+
+
+def test_chunk_rejects_bad_chunk_lengths():
+    d = pk.CacheDesc(4, 2, 64, "bf16")
+    one, al = ctypes.c_void_p(1), ctypes.c_void_p(256)
+    for T in (0, 17, -3):
+        st = pk.lib.pa_decode_chunk(ctypes.byref(d.c), one, one, al, 1, al, T, one, 4, one,
+                                    64, 1, 2, 1.0, None, 0, None)
+        assert st == -1 and b"chunk_len" in pk.lib.pa_last_error()
+    # a chunk needs the workspace of its own shape
+    need = pk.chunk_workspace_bytes(d, 1, 4, 4, 64)
+    assert need > pk.decode_workspace_bytes(d, 1, 4, 64)
+    st = pk.lib.pa_decode_chunk(ctypes.byref(d.c), one, one, al, 1, al, 4, one, 4, one,
+                                64, 1, 4, 1.0, ctypes.c_void_p(256),
+                                pk.decode_workspace_bytes(d, 1, 4, 64), None)
+    assert st == -6
 
 
 def test_cache_bytes():
