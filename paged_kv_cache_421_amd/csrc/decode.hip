@@ -207,7 +207,7 @@ decode_stream_kernel(StreamArgs a) {
   const int nchunk = a.chunk;
   const int R = a.rows;
   const int hq = hkv * G;
-  const int slot_floats = R * (kD + 2);           // floats per partial slot
+  const int slot_floats = (R * (kD + 2) + 3) & ~3; // floats per partial slot (16-byte multiple)
   const __amdgpu_buffer_rsrc_t lens_rsrc = make_rsrc(a.context_lens, B * 4);
 
   // ---- 1. total tile count; zero rows of empty sequences s = w (mod waves).
@@ -311,6 +311,11 @@ decode_stream_kernel(StreamArgs a) {
   constexpr int kOPitch = kRowOutBytes + 16;
   __shared__ __align__(16) char s_o_all[kWavesPerGroup][kMaxRows * kOPitch];
   char* s_o = s_o_all[wig];
+  // this wave's (at most two) partial pieces, parked here while the ring
+  // runs and published to the workspace once it has drained
+  constexpr int kSlotBytesMax = kMaxRows * (kD + 2) * 4;
+  __shared__ __align__(16) char s_p_all[kWavesPerGroup][2 * kSlotBytesMax];
+  char* s_p = s_p_all[wig];
   int w_s = s_cur, w_g = g0, w_j = j0, w_L = L_cur, w_nb = nb0, w_seg = seg0 + g0 * nb0;
   // lengths for the walk: from Lr for the first 256 sequences, past them
   // from a window of 64 (lane i -> sequence lwin_base + i) loaded on demand
@@ -401,7 +406,9 @@ decode_stream_kernel(StreamArgs a) {
     }
     // A piece of a segment shared with other waves: only the first and the
     // last segment of a range can be shared, so a wave has at most two
-    // pieces, in slots 0 and 1.  Slot layout (floats): o as [kD/16][4][R][4]
+    // pieces, in slots 0 and 1, kept in LDS until the ring has drained (a
+    // device-coherent store in the middle of the ring would hold up the
+    // loads issued after it).  Slot layout (floats): o as [kD/16][4][R][4]
     // -- lane (row, quad)'s 4 values of dims 16c + 4quad .. +3 at
     // ((c*4 + quad)*R + row)*4, so every store instruction writes one
     // contiguous range -- then (m, l) pairs [R][2]
@@ -409,19 +416,14 @@ decode_stream_kernel(StreamArgs a) {
     // written through to the point of coherence of all XCDs); the arrival
     // count follows once they have completed, after the ring has drained.
     // No L2 write-back or invalidation is needed: nothing else is shared.
-    const int64_t mine = slot_ptr(w, seg);
     const int which = (seg <= w * per) ? 0 : 1;
+    char* lslot = s_p + which * kSlotBytesMax;
     if (row_ok) {
 #pragma unroll
       for (int c = 0; c < kVC; ++c)
-        __builtin_amdgcn_raw_buffer_store_b128(
-            __builtin_bit_cast(u32x4_t, oacc[c]), part_rsrc,
-            static_cast<int>(mine + (((c * 4 + quad) * R + row) * 4) * 4), 0, kAuxCoherent);
-      if (quad == 0) {
-        const u32x2_t ml = {__float_as_uint(m_ref), __float_as_uint(l_tot)};
-        __builtin_amdgcn_raw_buffer_store_b64(ml, part_rsrc,
-                                              static_cast<int>(mine + (R * kD + 2 * row) * 4), 0, kAuxCoherent);
-      }
+        *reinterpret_cast<f32x4_t*>(lslot + (((c * 4 + quad) * R + row) * 4) * 4) = oacc[c];
+      if (quad == 0)
+        *reinterpret_cast<f32x2_t*>(lslot + (R * kD + 2 * row) * 4) = f32x2_t{m_ref, l_tot};
     }
     pend_s[which] = s;
     pend_g[which] = g;
@@ -714,6 +716,17 @@ decode_stream_kernel(StreamArgs a) {
   // this wave has completed; both counters at once), then merge the
   // segments of which this wave holds the last piece
   if (pend_s[0] >= 0 || pend_s[1] >= 0) {
+    // publish the parked pieces: whole 16-byte chunks, device-coherent
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if (pend_s[i] < 0) continue;
+      const int64_t mine = slot_ptr(w, pend_seg[i]);
+      const char* lslot = s_p + i * kSlotBytesMax;
+      for (int off = 16 * lane; off < slot_floats * 4; off += 1024)
+        __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4_t*>(lslot + off),
+                                               part_rsrc, static_cast<int>(mine + off), 0,
+                                               kAuxCoherent);
+    }
     __builtin_amdgcn_s_waitcnt(0);
     uint32_t prev[2] = {0u, 0u};
     if (lane == 0) {
@@ -918,8 +931,9 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 // `rows` query rows each.
 size_t stream_workspace_bytes(int num_seqs, int hkv, int rows, int D) {
   const size_t waves = static_cast<size_t>(device_cus()) * kWavesPerCU;
+  const size_t slot_floats = (static_cast<size_t>(rows) * (D + 2) + 3) & ~static_cast<size_t>(3);
   return align256(static_cast<size_t>(num_seqs) * hkv * sizeof(uint32_t)) +
-         waves * 2 * rows * (D + 2) * sizeof(float);
+         waves * 2 * slot_floats * sizeof(float);
 }
 
 size_t general_workspace_bytes(int num_seqs, int num_q_heads, int T, int D, int max_context_len) {

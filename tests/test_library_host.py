@@ -82,7 +82,8 @@ def test_workspace_size_formula():
     assert pk.decode_workspace_bytes(bf, 256, 32, 4096) == 256 * 8 * 4 + waves * 2 * 4 * 130 * 4
     assert pk.decode_workspace_bytes(bf, 3, 64, 10) == 256 + waves * 2 * 8 * 130 * 4
     fp8 = pk.CacheDesc(64, 2, 64, "fp8", 0.5, 0.5)
-    assert pk.decode_workspace_bytes(fp8, 5, 2, 100) == 256 + waves * 2 * 1 * 66 * 4
+    # slots are padded to whole 16-byte chunks: 1 * 66 floats -> 68
+    assert pk.decode_workspace_bytes(fp8, 5, 2, 100) == 256 + waves * 2 * 68 * 4
     # invalid shapes report 0
     assert pk.decode_workspace_bytes(bf, 4, 12, 100) == 0
     assert pk.decode_workspace_bytes(bf, 0, 8, 100) == 0
@@ -97,7 +98,7 @@ def test_chunk_workspace_size_formula():
     assert pk.chunk_workspace_bytes(bf, 256, 32, 4, 4096) == head + waves * 2 * 16 * 130 * 4
     assert pk.chunk_workspace_bytes(bf, 256, 32, 8, 4096) == head + waves * 2 * 16 * 130 * 4
     assert pk.chunk_workspace_bytes(bf, 256, 64, 3, 4096) == head + waves * 2 * 16 * 130 * 4
-    assert pk.chunk_workspace_bytes(bf, 256, 8, 5, 4096) == head + waves * 2 * 5 * 130 * 4
+    assert pk.chunk_workspace_bytes(bf, 256, 8, 5, 4096) == head + waves * 2 * 652 * 4
     # G = 16 still takes the streaming path, one token per pass
     assert pk.chunk_workspace_bytes(pk.CacheDesc(64, 2, 64, "bf16"), 3, 32, 2, 100) == \
         256 + waves * 2 * 16 * 66 * 4
