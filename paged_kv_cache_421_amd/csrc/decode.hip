@@ -437,7 +437,7 @@ decode_stream_kernel(StreamArgs a) {
   // (group q: row q % R, dims 16*(q / (4R)) + 4*((q / R) % 4) .. +3).  A
   // piece in which a row saw no position holds m = kNoMax, l = 0, o = 0 and
   // adds nothing; a row that saw none in any piece gets a zero row.
-  auto merge = [&](int s, int g, int seg, int nb) {
+  auto merge = [&](int s, int g, int seg, int nb, int own) {
     const int wf = seg / per;
     const int wl = (seg + nb - 1) / per;
     uint32_t* ctr = a.counters + static_cast<int64_t>(s) * hkv + g;
@@ -452,25 +452,10 @@ decode_stream_kernel(StreamArgs a) {
       den[i] = 0.f;
       num[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    auto merge_one = [&](int p) {
-      const int64_t sp = slot_ptr(p, seg);
-      f32x4_t op[kE4];
-      float mp[kE4], lp[kE4];
+    auto combine = [&](const f32x4_t (&op)[kE4], const float (&mp)[kE4], const float (&lp)[kE4]) {
 #pragma unroll
       for (int i = 0; i < kE4; ++i) {
         if (64 * i >= n_grp) break;                        // wave-uniform
-        const int q = min(lane + 64 * i, n_grp - 1);
-        const int r = q % R;
-        op[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                part_rsrc, static_cast<int>(sp + q * 16), 0, kAuxCoherent));
-        const u32x2_t ml = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(
-            part_rsrc, static_cast<int>(sp + (n_el + 2 * r) * 4), 0, kAuxCoherent));
-        mp[i] = __uint_as_float(ml[0]);
-        lp[i] = __uint_as_float(ml[1]);
-      }
-#pragma unroll
-      for (int i = 0; i < kE4; ++i) {
-        if (64 * i >= n_grp) break;
         const float mn = fmaxf(M[i], mp[i]);
         const float f_old = __builtin_amdgcn_exp2f(M[i] - mn);
         const float f_new = __builtin_amdgcn_exp2f(mp[i] - mn);
@@ -480,7 +465,51 @@ decode_stream_kernel(StreamArgs a) {
         M[i] = mn;
       }
     };
-    for (int p = wf; p <= wl; ++p) merge_one(p);
+    // Pieces are combined in wave order whoever merges, so the result does
+    // not depend on which piece arrived last.  Two are loaded at a time;
+    // this wave's own piece comes from its LDS slot (its workspace load has
+    // an empty range, as has a second piece past the last).
+    const char* own_slot = s_p + own * kSlotBytesMax;
+    auto from_lds = [&](f32x4_t (&op)[kE4], float (&mp)[kE4], float (&lp)[kE4]) {
+#pragma unroll
+      for (int i = 0; i < kE4; ++i) {
+        if (64 * i >= n_grp) break;
+        const int q = min(lane + 64 * i, n_grp - 1);
+        op[i] = *reinterpret_cast<const f32x4_t*>(own_slot + q * 16);
+        const f32x2_t ml = *reinterpret_cast<const f32x2_t*>(own_slot + (n_el + 2 * (q % R)) * 4);
+        mp[i] = ml[0];
+        lp[i] = ml[1];
+      }
+    };
+    for (int p0 = wf; p0 <= wl; p0 += 2) {
+      f32x4_t oa[kE4], ob[kE4];
+      float ma[kE4], la[kE4], mb[kE4], lb[kE4];
+      const bool has_b = p0 + 1 <= wl;
+      const bool ga = p0 != w;
+      const bool gb = has_b && p0 + 1 != w;
+      const char* base = reinterpret_cast<const char*>(a.partials);
+      const __amdgpu_buffer_rsrc_t ra = make_rsrc(base + slot_ptr(p0, seg), ga ? slot_floats * 4 : 0);
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(base + (has_b ? slot_ptr(p0 + 1, seg) : 0),
+                                                  gb ? slot_floats * 4 : 0);
+#pragma unroll
+      for (int i = 0; i < kE4; ++i) {
+        if (64 * i >= n_grp) break;
+        const int q = min(lane + 64 * i, n_grp - 1);
+        const int mo = (n_el + 2 * (q % R)) * 4;
+        oa[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, q * 16, 0, kAuxCoherent));
+        ob[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rb, q * 16, 0, kAuxCoherent));
+        const u32x2_t mla = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(ra, mo, 0, kAuxCoherent));
+        const u32x2_t mlb = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rb, mo, 0, kAuxCoherent));
+        ma[i] = __uint_as_float(mla[0]);
+        la[i] = __uint_as_float(mla[1]);
+        mb[i] = __uint_as_float(mlb[0]);
+        lb[i] = __uint_as_float(mlb[1]);
+      }
+      if (!ga) from_lds(oa, ma, la);
+      if (has_b && !gb) from_lds(ob, mb, lb);
+      combine(oa, ma, la);
+      if (has_b) combine(ob, mb, lb);
+    }
 #pragma unroll
     for (int i = 0; i < kE4; ++i) {
       const int q = lane + 64 * i;
@@ -743,7 +772,7 @@ decode_stream_kernel(StreamArgs a) {
       const int wl = (pend_seg[i] + pend_nb[i] - 1) / per;
       if (static_cast<uint32_t>(readlane_i(static_cast<int>(prev[i]), 0)) ==
           static_cast<uint32_t>(wl - wf))                      // the last piece
-        merge(pend_s[i], pend_g[i], pend_seg[i], pend_nb[i]);
+        merge(pend_s[i], pend_g[i], pend_seg[i], pend_nb[i], i);
     }
   }
 }
