@@ -10,6 +10,8 @@
   block -- all KV heads, all 16 slots -- of both caches, byte for byte.
   Precondition (reading): destinations are distinct and no destination is also
   a source, so the pairs commute.
+* ``swap_blocks``: the same whole-block copies between two pools, the device
+  cache and a host pool, for swapping sequences out and back in.
 
 Caches are ``[num_blocks, Hkv, 16, D]`` arrays in storage format (float32,
 uint16 bf16 bits, or uint8 E4M3 codes).  Both functions return new arrays and
@@ -62,3 +64,17 @@ def copy_blocks(k_cache: np.ndarray, v_cache: np.ndarray, pairs) -> tuple:
         kc[dst] = k_cache[src]
         vc[dst] = v_cache[src]
     return kc, vc
+
+
+def swap_blocks(src_k: np.ndarray, src_v: np.ndarray, dst_k: np.ndarray, dst_v: np.ndarray,
+                pairs) -> tuple:
+    """Block copies between two pools (device cache and host pool, either way):
+    for each (s, d), dst[d] = src[s] for both caches, whole blocks, byte for
+    byte (ybb.press §3.2: a swapped-out sequence's KV moves to CPU memory and
+    back).  Returns new destination arrays; the sources are unchanged."""
+    kd = dst_k.copy()
+    vd = dst_v.copy()
+    for s, d in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
+        kd[d] = src_k[s]
+        vd[d] = src_v[s]
+    return kd, vd
