@@ -44,8 +44,17 @@ sequence, pa_write_kv of B*T rows, then pa_decode_chunk with q [B, T, Hq, D]
 layer, and the roofline is pa_decode_chunk's.  The default (T = 1) is the
 decode step above.
 
+With ``--swap`` the step is a swap-out and swap-in of 64 of the 256
+sequences of one layer's cache (block manager pa_bm_swap_out / _in, then
+pa_swap_blocks between the device cache and a pinned host pool); ``value``
+is the bytes moved per second over both directions, and the roofline is
+the host link (PCIe 5.0 x16, 63 GB/s per direction).  A plain contiguous
+copy of the same bytes (the DMA engines, hipMemcpyAsync) is timed beside it
+as context.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers N]
-                      [--chunk T] [--no-cpu-baseline] [--copy-calibration MIB]
+                      [--chunk T | --swap] [--no-cpu-baseline]
+                      [--copy-calibration MIB]
 
 --copy-calibration MIB ends the run with plain device copies of MIB MiB, the
 reference a hardware-counter run scales FETCH_SIZE / WRITE_SIZE by.
@@ -74,6 +83,8 @@ METRIC = "paged decode attention: KV-cache GB/s vs HBM peak; decoded seqs/sec"
 METRIC_CHUNK = ("paged chunk attention (T new tokens per sequence, causal): KV-cache GB/s "
                 "vs HBM peak; query tokens/sec")
 HBM_PEAK_GBPS = 8000.0
+PCIE5_X16_GBPS = 63.0        # 32 GT/s x 16 lanes x 128/130 / 8, per direction
+METRIC_SWAP = "paged KV swap: device<->pinned host block copy GB/s vs host link peak"
 DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_421_amd", "csrc", "decode.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic_gqa8b_b256.txt")
 TRAFFIC_FILE_CHUNK = os.path.join(ROOT, "profiles", "chunk_traffic_gqa8b_b256_t{T}.txt")
@@ -197,6 +208,144 @@ def cpu_baseline(w, budget_s=10.0, T=1):
                        f"BLAS limited to 1 thread")}
 
 
+def swap_cpu_baseline(kc, vc, pairs, budget_s=10.0):
+    """The oracle's swap_blocks (numpy whole-block copies) over the same
+    pairs, on host arrays, until ``budget_s`` seconds have passed."""
+    import oracle
+    hk = np.zeros((int(pairs[:, 1].max()) + 1,) + kc.shape[1:], kc.dtype)
+    hv = np.zeros_like(hk)
+    times = []
+    t_all = time.perf_counter()
+    while len(times) < 3 or time.perf_counter() - t_all < budget_s:
+        t0 = time.perf_counter()
+        oracle.swap_blocks(kc, vc, hk, hv, pairs)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    nbytes = len(pairs) * 2 * kc[0].nbytes
+    return {"value": round(nbytes / t / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": (f"{len(pairs)} block pairs ({nbytes / 1e6:.0f} MB, K and V) between numpy "
+                       f"arrays in host memory, {len(times)} runs, median {t:.3f} s")}
+
+
+def run_swap(args):
+    """Swap 64 of the 256 sequences of the GQA batch-256 cache out to a
+    pinned host pool and back, ``steps`` times."""
+    import torch
+    import paged_kv_cache_421_amd as pk
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    steps = args.steps or 20
+    warm = args.warmup if args.warmup is not None else 3
+    w = workloads.config3(rows=False)
+    B, Hkv, D = w.B, w.Hkv, w.D
+    group = np.arange(0, B, 4, dtype=np.int64)           # 64 sequences, every 4th
+    need = int(sum(-(-int(w.lens[s]) // 16) for s in group))
+    H = need + 16
+    desc = pk.CacheDesc(w.num_blocks, Hkv, D, "bf16")
+    bm = pk.BlockManager(w.num_blocks, free_order=w.free_order, num_host_blocks=H)
+    for s in range(B):
+        bm.add_seq(s)
+        bm.append_tokens(s, int(w.lens[s]))
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    kc = torch.randn(desc.shape, device=dev, generator=g).to(torch.bfloat16)
+    vc = torch.randn(desc.shape, device=dev, generator=g).to(torch.bfloat16)
+    hk = torch.empty((H,) + tuple(desc.shape[1:]), dtype=torch.bfloat16, pin_memory=True)
+    hv = torch.empty_like(hk, pin_memory=True)
+    block_bytes = Hkv * 16 * D * 2
+    pairs_dev = torch.empty((max(H, w.num_blocks), 2), dtype=torch.int32, device=dev)
+    _log(f"bench: swap {len(group)} sequences = {need} blocks = {need * 2 * block_bytes / 1e6:.0f} MB "
+         f"each way, {steps} steps")
+
+    def one(out, evs):
+        pairs = bm.swap_out(group) if out else bm.swap_in(group)
+        n = len(pairs)
+        pairs_dev[:n].copy_(torch.from_numpy(pairs), non_blocking=False)
+        if evs is not None:
+            evs[0].record(stream)
+        if out:
+            pk.swap_blocks(desc, kc, vc, hk, hv, pairs_dev[:n], stream=stream)
+        else:
+            pk.swap_blocks(desc, hk, hv, kc, vc, pairs_dev[:n], stream=stream)
+        if evs is not None:
+            evs[1].record(stream)
+        return n * 2 * block_bytes
+
+    for _ in range(warm):
+        one(True, None)
+        one(False, None)
+    torch.cuda.synchronize()
+    ev_out = [(HipEvent(), HipEvent()) for _ in range(steps)]
+    ev_in = [(HipEvent(), HipEvent()) for _ in range(steps)]
+    moved = 0
+    t0 = time.perf_counter()
+    for i in range(steps):
+        moved += one(True, ev_out[i])
+        moved += one(False, ev_in[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_out = statistics.mean(a.elapsed_ms(b) for a, b in ev_out) / 1e3
+    t_in = statistics.mean(a.elapsed_ms(b) for a, b in ev_in) / 1e3
+    for a, b in ev_out + ev_in:
+        a.destroy()
+        b.destroy()
+    per_dir = need * 2 * block_bytes
+    gbps_out, gbps_in = per_dir / t_out / 1e9, per_dir / t_in / 1e9
+    # context: the DMA engines on one contiguous buffer of the same size
+    src = torch.empty(per_dir // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty(per_dir // 2, dtype=torch.bfloat16, pin_memory=True)
+    dma = {}
+    for name, (a, b) in (("d2h", (dst, src)), ("h2d", (src, dst))):
+        a.copy_(b, non_blocking=True)
+        torch.cuda.synchronize()
+        e0, e1 = HipEvent(), HipEvent()
+        e0.record(stream)
+        for _ in range(5):
+            a.copy_(b, non_blocking=True)
+        e1.record(stream)
+        dma[name] = round(5 * per_dir / (e0.elapsed_ms(e1) / 1e3) / 1e9, 2)
+        e0.destroy()
+        e1.destroy()
+    _log(f"bench: swap out {t_out * 1e6:.0f} us ({gbps_out:.1f} GB/s), in {t_in * 1e6:.0f} us "
+         f"({gbps_in:.1f} GB/s); DMA contiguous copy d2h {dma['d2h']} h2d {dma['h2d']} GB/s")
+    mean_gbps = 2 * per_dir / (t_out + t_in) / 1e9
+    res = {
+        "metric": METRIC_SWAP,
+        "value": round(moved / wall / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": steps, "warmup": warm,
+        "ms_per_step": round(wall / steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": ("gqa8b-bf16-b256 cache (Llama-3-8B-shaped layer, 8 KV heads, "
+                                "head_dim 128, 16-token shuffled blocks): swap out and back in "
+                                f"{len(group)} of 256 sequences ({need} blocks, "
+                                f"{per_dir / 1e6:.0f} MB K+V each way) to a pinned host pool"),
+                   "step": "pa_bm_swap_out + pa_swap_blocks (device->host), pa_bm_swap_in + "
+                           "pa_swap_blocks (host->device)",
+                   "value_is": "bytes moved per second over the timed steps, both directions, "
+                               "host bookkeeping and pair uploads included",
+                   "parallelism": "single GPU"},
+        "swap_out_gbps": round(gbps_out, 2), "swap_in_gbps": round(gbps_in, 2),
+        "dma_contiguous_gbps": dma,
+        "roofline": {"kernel": "copy_blocks_kernel (pa_swap_blocks)", "bound": "pcie",
+                     "achieved": round(mean_gbps, 2), "peak": PCIE5_X16_GBPS, "unit": "GB/s",
+                     "frac": round(mean_gbps / PCIE5_X16_GBPS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        _log("bench: timing the CPU oracle")
+        nb = 512
+        rng = np.random.default_rng(5)
+        kh = rng.integers(0, 2**16, (nb,) + tuple(desc.shape[1:]), dtype=np.uint16)
+        vh = rng.integers(0, 2**16, (nb,) + tuple(desc.shape[1:]), dtype=np.uint16)
+        pr = np.stack([rng.permutation(nb), rng.permutation(nb)], 1).astype(np.int64)
+        res["cpu_baseline"] = swap_cpu_baseline(kh, vh, pr)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -205,6 +354,8 @@ def main():
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--chunk", type=int, default=1, metavar="T",
                     help="new tokens per sequence per step (1 = decode)")
+    ap.add_argument("--swap", action="store_true",
+                    help="measure swapping sequences out to pinned host memory and back")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     args = ap.parse_args()
@@ -212,6 +363,8 @@ def main():
         print(f"bench.py measures one GPU only (asked for {args.gpus}); the decode path "
               f"has no cross-GPU step in this library", file=sys.stderr)
         sys.exit(2)
+    if args.swap:
+        return run_swap(args)
     T = args.chunk
     if not 1 <= T <= 16:
         sys.exit("--chunk must be in 1..16")

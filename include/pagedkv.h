@@ -52,7 +52,8 @@ typedef enum {
   PA_ERR_UNKNOWN_SEQ = -4,        /* block manager: no such sequence id */
   PA_ERR_SEQ_EXISTS = -5,         /* block manager: id already in use */
   PA_ERR_WORKSPACE_TOO_SMALL = -6,
-  PA_ERR_HIP = -7                 /* a HIP runtime call or launch failed */
+  PA_ERR_HIP = -7,                /* a HIP runtime call or launch failed */
+  PA_ERR_SWAPPED = -8             /* block manager: sequence is in the other pool */
 } pa_status;
 
 typedef enum {
@@ -219,6 +220,11 @@ typedef struct pa_bm pa_bm;
 /* NULL on invalid arguments (see pa_last_error). */
 pa_bm* pa_bm_create(int32_t num_blocks, int32_t block_size,
                     const int32_t* free_order);
+/* The same with a pool of num_host_blocks host blocks for swapping
+ * (host_free_order: a permutation of 0..num_host_blocks-1, NULL = 0,1,...). */
+pa_bm* pa_bm_create_ex(int32_t num_blocks, int32_t block_size,
+                       const int32_t* free_order, int32_t num_host_blocks,
+                       const int32_t* host_free_order);
 void pa_bm_destroy(pa_bm* bm);
 
 pa_status pa_bm_add_seq(pa_bm* bm, int64_t seq_id);
@@ -250,6 +256,52 @@ pa_status pa_bm_length(const pa_bm* bm, int64_t seq_id, int32_t* len);
  * context_lens[n].  Host memory. */
 pa_status pa_bm_pack(const pa_bm* bm, const int64_t* seq_ids, int32_t n,
                      int32_t* block_tables, int32_t cap, int32_t* context_lens);
+
+/* ---------------------------------------------------------------------------
+ * Swapping (ybb.press §3.2: when device memory runs short the KV cache of
+ * low-priority sequences moves to CPU memory and is resumed later; §6: the
+ * scheduler swaps sequences out and in; §9 item 5: it stays in host memory).
+ *
+ * pa_bm_swap_out moves the sequences seq_ids[0..n-1] to the host pool: every
+ * distinct device block they reference, in walk order (sequences as listed,
+ * each table in logical order), gets one host block popped from the host
+ * pool, and pairs[k] = (device block, host block) is the k-th copy to make
+ * (pa_swap_blocks, device cache -> host pool).  Each table entry then names
+ * the host copy; each device block loses the set's references and returns
+ * to the device pool, in walk order, when its count reaches zero -- a block
+ * also used by sequences outside the set stays on the device for them.
+ * pa_bm_swap_in is the mirror (pairs = (host block, device block)).
+ * pairs: int32 [pairs_cap][2] host array; *num_pairs receives the count.
+ * All or nothing: PA_ERR_NO_BLOCKS when the destination pool is short,
+ * PA_ERR_SWAPPED when a sequence is already in the destination pool,
+ * PA_ERR_INVALID_ARG for a repeated id or a pairs buffer that is too small.
+ * A swapped-out sequence cannot append, fork or be packed (PA_ERR_SWAPPED);
+ * pa_bm_free_seq releases its host blocks.
+ * ------------------------------------------------------------------------- */
+pa_status pa_bm_swap_out(pa_bm* bm, const int64_t* seq_ids, int32_t n,
+                         int32_t* pairs, int32_t pairs_cap, int32_t* num_pairs);
+pa_status pa_bm_swap_in(pa_bm* bm, const int64_t* seq_ids, int32_t n,
+                        int32_t* pairs, int32_t pairs_cap, int32_t* num_pairs);
+int32_t pa_bm_num_free_host(const pa_bm* bm);
+/* Reference count of a host block, -1 if out of range. */
+int32_t pa_bm_host_refcount(const pa_bm* bm, int32_t block);
+/* *swapped = 1 if the sequence is in the host pool, else 0. */
+pa_status pa_bm_is_swapped(const pa_bm* bm, int64_t seq_id, int32_t* swapped);
+
+/*
+ * pa_swap_blocks -- whole-block copies between two pools with the layout of
+ * `c`: for each pairs[i] = (s, d), block d of dst_k / dst_v receives block s
+ * of src_k / src_v, byte for byte (every KV head, all 16 slots).  Each pool
+ * pointer is device memory or pinned host memory (hipHostMalloc); the call
+ * checks that the GPU can address all four (PA_ERR_INVALID_ARG otherwise,
+ * e.g. for pageable host memory).  pairs: int32 [num_pairs][2] in device or
+ * pinned host memory.  Destinations must be distinct; the two pools must not
+ * overlap.  The copy is a kernel on `stream` (it reads or writes host memory
+ * over the host link directly).  num_pairs <= 65535 per call.
+ */
+pa_status pa_swap_blocks(const pa_cache_desc* c, const void* src_k, const void* src_v,
+                         void* dst_k, void* dst_v, const int32_t* pairs,
+                         int32_t num_pairs, void* stream);
 
 #ifdef __cplusplus
 }

@@ -38,6 +38,13 @@ SIGNATURES = {
     "pa_decode": (c_i32, [P_desc, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_vp, c_i32,
                           c_i32, c_i32, c_f32, c_vp, c_sz, c_vp]),
     "pa_bm_create": (c_vp, [c_i32, c_i32, c_vp]),
+    "pa_bm_create_ex": (c_vp, [c_i32, c_i32, c_vp, c_i32, c_vp]),
+    "pa_bm_swap_out": (c_i32, [c_vp, c_vp, c_i32, c_vp, c_i32, c_vp]),
+    "pa_bm_swap_in": (c_i32, [c_vp, c_vp, c_i32, c_vp, c_i32, c_vp]),
+    "pa_bm_num_free_host": (c_i32, [c_vp]),
+    "pa_bm_host_refcount": (c_i32, [c_vp, c_i32]),
+    "pa_bm_is_swapped": (c_i32, [c_vp, c_i64, c_vp]),
+    "pa_swap_blocks": (c_i32, [P_desc, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp]),
     "pa_bm_destroy": (None, [c_vp]),
     "pa_bm_add_seq": (c_i32, [c_vp, c_i64]),
     "pa_bm_fork": (c_i32, [c_vp, c_i64, c_i64]),
@@ -53,7 +60,7 @@ SIGNATURES = {
 
 STATUS = {0: "PA_OK", -1: "PA_ERR_INVALID_ARG", -2: "PA_ERR_UNSUPPORTED",
           -3: "PA_ERR_NO_BLOCKS", -4: "PA_ERR_UNKNOWN_SEQ", -5: "PA_ERR_SEQ_EXISTS",
-          -6: "PA_ERR_WORKSPACE_TOO_SMALL", -7: "PA_ERR_HIP"}
+          -6: "PA_ERR_WORKSPACE_TOO_SMALL", -7: "PA_ERR_HIP", -8: "PA_ERR_SWAPPED"}
 
 
 class PagedKVError(RuntimeError):

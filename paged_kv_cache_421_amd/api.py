@@ -196,26 +196,81 @@ def _ptr(a: np.ndarray) -> ctypes.c_void_p:
     return ctypes.c_void_p(a.ctypes.data)
 
 
-class BlockManager:
-    """Host block manager (pa_bm_*): FIFO free pool, refcounts, copy-on-write."""
+def _pool(t: torch.Tensor, name: str) -> ctypes.c_void_p:
+    if not (t.is_cuda or t.is_pinned()):
+        raise ValueError(f"{name} must be a device tensor or pinned host memory")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
 
-    def __init__(self, num_blocks: int, free_order: Optional[Sequence[int]] = None):
-        self._order = None
-        ptr = ctypes.c_void_p(0)
+
+def swap_blocks(desc: CacheDesc, src_k: torch.Tensor, src_v: torch.Tensor,
+                dst_k: torch.Tensor, dst_v: torch.Tensor, pairs: torch.Tensor,
+                stream=None) -> None:
+    """pa_swap_blocks: whole-block copies dst[d] = src[s] for each (s, d) of
+    ``pairs`` (int32 [n, 2]); pools and pairs are device tensors or pinned
+    host tensors (``pin_memory=True``)."""
+    if pairs.dtype != torch.int32:
+        raise ValueError("pairs must be int32")
+    n = pairs.numel() // 2
+    check(lib.pa_swap_blocks(ctypes.byref(desc.c), _pool(src_k, "src_k"), _pool(src_v, "src_v"),
+                             _pool(dst_k, "dst_k"), _pool(dst_v, "dst_v"),
+                             _pool(pairs, "pairs"), n, _stream(stream)))
+
+
+class BlockManager:
+    """Host block manager (pa_bm_*): FIFO free pools (device, and host for
+    swapping), refcounts, copy-on-write."""
+
+    def __init__(self, num_blocks: int, free_order: Optional[Sequence[int]] = None,
+                 num_host_blocks: int = 0, host_free_order: Optional[Sequence[int]] = None):
+        self._lib = lib                      # kept alive for __del__ at interpreter exit
+        self._order = self._horder = None
+        ptr = hptr = ctypes.c_void_p(0)
         if free_order is not None:
             self._order = np.ascontiguousarray(free_order, dtype=np.int32)
             ptr = _ptr(self._order)
-        h = lib.pa_bm_create(int(num_blocks), BLOCK_SIZE, ptr)
+        if host_free_order is not None:
+            self._horder = np.ascontiguousarray(host_free_order, dtype=np.int32)
+            hptr = _ptr(self._horder)
+        h = lib.pa_bm_create_ex(int(num_blocks), BLOCK_SIZE, ptr, int(num_host_blocks), hptr)
         if not h:
             raise PagedKVError(-1, lib.pa_last_error().decode())
         self._h = ctypes.c_void_p(h)
         self.num_blocks = int(num_blocks)
+        self.num_host_blocks = int(num_host_blocks)
 
     def __del__(self):
         h = getattr(self, "_h", None)
         if h:
-            lib.pa_bm_destroy(h)
+            self._lib.pa_bm_destroy(h)
             self._h = None
+
+    def _move(self, fn, seq_ids, cap: int) -> np.ndarray:
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        pairs = np.empty((max(cap, 1), 2), dtype=np.int32)
+        n = ctypes.c_int32()
+        check(fn(self._h, _ptr(ids), len(ids), _ptr(pairs), cap, ctypes.byref(n)))
+        return pairs[:n.value].copy()
+
+    def swap_out(self, seq_ids) -> np.ndarray:
+        """pa_bm_swap_out: (device block, host block) pairs, int32 [k, 2]."""
+        return self._move(lib.pa_bm_swap_out, seq_ids, self.num_host_blocks)
+
+    def swap_in(self, seq_ids) -> np.ndarray:
+        """pa_bm_swap_in: (host block, device block) pairs, int32 [k, 2]."""
+        return self._move(lib.pa_bm_swap_in, seq_ids, self.num_blocks)
+
+    def num_free_host(self) -> int:
+        return int(lib.pa_bm_num_free_host(self._h))
+
+    def host_refcount(self, block: int) -> int:
+        return int(lib.pa_bm_host_refcount(self._h, int(block)))
+
+    def is_swapped(self, seq: int) -> bool:
+        v = ctypes.c_int32()
+        check(lib.pa_bm_is_swapped(self._h, int(seq), ctypes.byref(v)))
+        return bool(v.value)
 
     def add_seq(self, seq: int) -> None:
         check(lib.pa_bm_add_seq(self._h, int(seq)))

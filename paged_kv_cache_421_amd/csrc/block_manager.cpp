@@ -7,6 +7,16 @@
 // sequence needs a new block (§6); shared blocks are reference counted and
 // a sequence about to modify a shared block copies it first (§2.3).
 //
+// Swapping: when device memory runs short, the KV of low-priority sequences
+// moves to CPU memory and comes back later (§3.2; the scheduler swaps
+// sequences out and in under memory pressure, §6; swapped-out KV stays in
+// host memory, §9 item 5).  A second FIFO pool of host blocks holds them:
+// swap_out of a set of sequences gives every distinct device block they
+// reference one host block, in walk order (sequences as listed, tables in
+// logical order), and emits the (device, host) copy pairs; each device
+// block loses the set's references and returns to the device pool, in the
+// same walk order, when its count reaches zero.  swap_in is the mirror.
+//
 // The queue discipline, the choice of which sharer copies (the one that
 // appends, while the block is still shared) and the all-or-nothing rule make
 // the tables reproducible; they are readings, the pages fix none of them.
@@ -27,16 +37,41 @@ namespace {
 constexpr int32_t kBlock = PA_BLOCK_SIZE;
 
 struct Seq {
-  std::vector<int32_t> table;  // logical -> physical block
+  std::vector<int32_t> table;  // logical -> physical block (host block if on_host)
   int32_t len = 0;             // tokens appended so far
+  bool on_host = false;        // swapped out
+};
+
+// A FIFO free pool with reference counts.
+struct Pool {
+  std::deque<int32_t> free_q;
+  std::vector<int32_t> ref;
+
+  bool init(int32_t n, const int32_t* order) {
+    ref.assign(n, 0);
+    free_q.clear();
+    if (!order) {
+      for (int32_t i = 0; i < n; ++i) free_q.push_back(i);
+      return true;
+    }
+    std::vector<char> seen(n, 0);
+    for (int32_t i = 0; i < n; ++i) {
+      const int32_t b = order[i];
+      if (b < 0 || b >= n || seen[b]) return false;
+      seen[b] = 1;
+      free_q.push_back(b);
+    }
+    return true;
+  }
 };
 
 }  // namespace
 
 struct pa_bm {
   int32_t num_blocks = 0;
-  std::deque<int32_t> free_q;
-  std::vector<int32_t> ref;
+  int32_t num_host_blocks = 0;
+  Pool dev;
+  Pool host;
   std::unordered_map<int64_t, Seq> seqs;
 
   // Blocks an append of n tokens to `s` takes from the pool.
@@ -44,14 +79,14 @@ struct pa_bm {
     if (n <= 0) return 0;
     const int64_t p = s.len;
     int64_t fresh = (p + n + kBlock - 1) / kBlock - (p + kBlock - 1) / kBlock;
-    int64_t cow = (p % kBlock != 0 && ref[s.table.back()] > 1) ? 1 : 0;
+    int64_t cow = (p % kBlock != 0 && dev.ref[s.table.back()] > 1) ? 1 : 0;
     return fresh + cow;
   }
 
   int32_t pop() {
-    int32_t b = free_q.front();
-    free_q.pop_front();
-    ref[b] = 1;
+    int32_t b = dev.free_q.front();
+    dev.free_q.pop_front();
+    dev.ref[b] = 1;
     return b;
   }
 
@@ -60,10 +95,10 @@ struct pa_bm {
     const int32_t p = s.len;
     if (p % kBlock == 0) {
       s.table.push_back(pop());
-    } else if (ref[s.table.back()] > 1) {
+    } else if (dev.ref[s.table.back()] > 1) {
       const int32_t old = s.table.back();
       const int32_t b = pop();
-      ref[old] -= 1;
+      dev.ref[old] -= 1;
       s.table.back() = b;
       *cow_src = old;
       *cow_dst = b;
@@ -75,10 +110,11 @@ struct pa_bm {
 
 extern "C" {
 
-pa_bm* pa_bm_create(int32_t num_blocks, int32_t block_size,
-                    const int32_t* free_order) {
-  if (num_blocks < 0) {
-    fail(PA_ERR_INVALID_ARG, "pa_bm_create: num_blocks %d < 0", num_blocks);
+pa_bm* pa_bm_create_ex(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                       int32_t num_host_blocks, const int32_t* host_free_order) {
+  if (num_blocks < 0 || num_host_blocks < 0) {
+    fail(PA_ERR_INVALID_ARG, "pa_bm_create: num_blocks %d, num_host_blocks %d", num_blocks,
+         num_host_blocks);
     return nullptr;
   }
   if (block_size != kBlock) {
@@ -92,25 +128,25 @@ pa_bm* pa_bm_create(int32_t num_blocks, int32_t block_size,
     return nullptr;
   }
   bm->num_blocks = num_blocks;
-  bm->ref.assign(num_blocks, 0);
-  if (free_order) {
-    std::vector<char> seen(num_blocks, 0);
-    for (int32_t i = 0; i < num_blocks; ++i) {
-      const int32_t b = free_order[i];
-      if (b < 0 || b >= num_blocks || seen[b]) {
-        delete bm;
-        fail(PA_ERR_INVALID_ARG,
-             "pa_bm_create: free_order is not a permutation (entry %d = %d)",
-             i, b);
-        return nullptr;
-      }
-      seen[b] = 1;
-      bm->free_q.push_back(b);
-    }
-  } else {
-    for (int32_t i = 0; i < num_blocks; ++i) bm->free_q.push_back(i);
+  bm->num_host_blocks = num_host_blocks;
+  if (!bm->dev.init(num_blocks, free_order)) {
+    delete bm;
+    fail(PA_ERR_INVALID_ARG, "pa_bm_create: free_order is not a permutation of 0..%d",
+         num_blocks - 1);
+    return nullptr;
+  }
+  if (!bm->host.init(num_host_blocks, host_free_order)) {
+    delete bm;
+    fail(PA_ERR_INVALID_ARG, "pa_bm_create: host_free_order is not a permutation of 0..%d",
+         num_host_blocks - 1);
+    return nullptr;
   }
   return bm;
+}
+
+pa_bm* pa_bm_create(int32_t num_blocks, int32_t block_size,
+                    const int32_t* free_order) {
+  return pa_bm_create_ex(num_blocks, block_size, free_order, 0, nullptr);
 }
 
 void pa_bm_destroy(pa_bm* bm) { delete bm; }
@@ -133,8 +169,11 @@ pa_status pa_bm_fork(pa_bm* bm, int64_t parent_id, int64_t child_id) {
   if (bm->seqs.count(child_id))
     return fail(PA_ERR_SEQ_EXISTS, "pa_bm_fork: child %lld exists",
                 (long long)child_id);
+  if (it->second.on_host)
+    return fail(PA_ERR_SWAPPED, "pa_bm_fork: parent %lld is swapped out",
+                (long long)parent_id);
   Seq child = it->second;  // copy before emplace may rehash
-  for (int32_t b : child.table) bm->ref[b] += 1;
+  for (int32_t b : child.table) bm->dev.ref[b] += 1;
   bm->seqs.emplace(child_id, std::move(child));
   return PA_OK;
 }
@@ -151,13 +190,16 @@ pa_status pa_bm_append_tokens(pa_bm* bm, int64_t seq_id, int32_t n,
     return fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_append_tokens: unknown sequence %lld",
                 (long long)seq_id);
   Seq& s = it->second;
+  if (s.on_host)
+    return fail(PA_ERR_SWAPPED, "pa_bm_append_tokens: sequence %lld is swapped out",
+                (long long)seq_id);
   if (static_cast<int64_t>(s.len) + n > INT32_MAX)
     return fail(PA_ERR_INVALID_ARG, "pa_bm_append_tokens: length overflow");
   const int64_t need = bm->blocks_needed(s, n);
-  if (need > static_cast<int64_t>(bm->free_q.size()))
+  if (need > static_cast<int64_t>(bm->dev.free_q.size()))
     return fail(PA_ERR_NO_BLOCKS,
                 "pa_bm_append_tokens: sequence %lld needs %lld blocks, %zu free",
-                (long long)seq_id, (long long)need, bm->free_q.size());
+                (long long)seq_id, (long long)need, bm->dev.free_q.size());
   *cow_src = -1;
   *cow_dst = -1;
   for (int32_t i = 0; i < n; ++i) slots[i] = bm->append_one(s, cow_src, cow_dst);
@@ -190,6 +232,9 @@ pa_status pa_bm_append_batch(pa_bm* bm, const int64_t* seq_ids, int32_t n,
       return fail(PA_ERR_INVALID_ARG, "pa_bm_append_batch: sequence %lld listed twice",
                   (long long)seq_ids[i]);
     ss[i] = &it->second;
+    if (ss[i]->on_host)
+      return fail(PA_ERR_SWAPPED, "pa_bm_append_batch: sequence %lld is swapped out",
+                  (long long)seq_ids[i]);
     if (ss[i]->len == INT32_MAX)
       return fail(PA_ERR_INVALID_ARG, "pa_bm_append_batch: length overflow");
   }
@@ -202,16 +247,16 @@ pa_status pa_bm_append_batch(pa_bm* bm, const int64_t* seq_ids, int32_t n,
       need += 1;
     } else {
       const int32_t last = s.table.back();
-      const int32_t r = bm->ref[last] + ref_delta[last];
+      const int32_t r = bm->dev.ref[last] + ref_delta[last];
       if (r > 1) {
         need += 1;
         ref_delta[last] -= 1;
       }
     }
   }
-  if (need > static_cast<int64_t>(bm->free_q.size()))
+  if (need > static_cast<int64_t>(bm->dev.free_q.size()))
     return fail(PA_ERR_NO_BLOCKS, "pa_bm_append_batch: batch needs %lld blocks, %zu free",
-                (long long)need, bm->free_q.size());
+                (long long)need, bm->dev.free_q.size());
   int32_t np = 0;
   for (int32_t i = 0; i < n; ++i) {
     int32_t src = -1, dst = -1;
@@ -232,20 +277,113 @@ pa_status pa_bm_free_seq(pa_bm* bm, int64_t seq_id) {
   if (it == bm->seqs.end())
     return fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_free_seq: unknown sequence %lld",
                 (long long)seq_id);
+  Pool& pool = it->second.on_host ? bm->host : bm->dev;
   for (int32_t b : it->second.table) {
-    if (--bm->ref[b] == 0) bm->free_q.push_back(b);
+    if (--pool.ref[b] == 0) pool.free_q.push_back(b);
   }
   bm->seqs.erase(it);
   return PA_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// swap_out (to_host) / swap_in of a set of sequences; all or nothing.
+pa_status move_seqs(pa_bm* bm, const int64_t* seq_ids, int32_t n, bool to_host,
+                    int32_t* pairs, int32_t pairs_cap, int32_t* num_pairs, const char* fn) {
+  if (!bm || !num_pairs || n < 0 || pairs_cap < 0 || (n > 0 && !seq_ids) ||
+      (pairs_cap > 0 && !pairs))
+    return fail(PA_ERR_INVALID_ARG, "%s: bad argument", fn);
+  std::vector<Seq*> ss(n);
+  std::unordered_set<int64_t> seen;
+  for (int32_t i = 0; i < n; ++i)      // a repeated id is reported before anything else
+    if (!seen.insert(seq_ids[i]).second)
+      return fail(PA_ERR_INVALID_ARG, "%s: sequence %lld listed twice", fn,
+                  (long long)seq_ids[i]);
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = bm->seqs.find(seq_ids[i]);
+    if (it == bm->seqs.end())
+      return fail(PA_ERR_UNKNOWN_SEQ, "%s: unknown sequence %lld", fn, (long long)seq_ids[i]);
+    if (it->second.on_host == to_host)
+      return fail(PA_ERR_SWAPPED, "%s: sequence %lld is already %s", fn, (long long)seq_ids[i],
+                  to_host ? "swapped out" : "on the device");
+    ss[i] = &it->second;
+  }
+  Pool& src = to_host ? bm->dev : bm->host;
+  Pool& dst = to_host ? bm->host : bm->dev;
+  std::vector<int32_t> order;
+  std::unordered_map<int32_t, int32_t> mapping;
+  for (Seq* s : ss)
+    for (int32_t b : s->table)
+      if (mapping.emplace(b, -1).second) order.push_back(b);
+  if (order.size() > dst.free_q.size())
+    return fail(PA_ERR_NO_BLOCKS, "%s: %zu blocks to move, %zu free", fn, order.size(),
+                dst.free_q.size());
+  if (static_cast<int64_t>(order.size()) > pairs_cap)
+    return fail(PA_ERR_INVALID_ARG, "%s: pairs buffer holds %d pairs, %zu needed", fn,
+                pairs_cap, order.size());
+  for (size_t k = 0; k < order.size(); ++k) {
+    const int32_t d = dst.free_q.front();
+    dst.free_q.pop_front();
+    dst.ref[d] = 0;
+    mapping[order[k]] = d;
+    pairs[2 * k] = order[k];
+    pairs[2 * k + 1] = d;
+  }
+  for (Seq* s : ss) {
+    for (int32_t& b : s->table) {
+      const int32_t d = mapping[b];
+      dst.ref[d] += 1;
+      if (--src.ref[b] == 0) src.free_q.push_back(b);
+      b = d;
+    }
+    s->on_host = to_host;
+  }
+  *num_pairs = static_cast<int32_t>(order.size());
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_bm_swap_out(pa_bm* bm, const int64_t* seq_ids, int32_t n, int32_t* pairs,
+                         int32_t pairs_cap, int32_t* num_pairs) {
+  return move_seqs(bm, seq_ids, n, true, pairs, pairs_cap, num_pairs, "pa_bm_swap_out");
+}
+
+pa_status pa_bm_swap_in(pa_bm* bm, const int64_t* seq_ids, int32_t n, int32_t* pairs,
+                        int32_t pairs_cap, int32_t* num_pairs) {
+  return move_seqs(bm, seq_ids, n, false, pairs, pairs_cap, num_pairs, "pa_bm_swap_in");
+}
+
+int32_t pa_bm_num_free_host(const pa_bm* bm) {
+  return bm ? static_cast<int32_t>(bm->host.free_q.size()) : -1;
+}
+
+int32_t pa_bm_host_refcount(const pa_bm* bm, int32_t block) {
+  if (!bm || block < 0 || block >= bm->num_host_blocks) return -1;
+  return bm->host.ref[block];
+}
+
+pa_status pa_bm_is_swapped(const pa_bm* bm, int64_t seq_id, int32_t* swapped) {
+  if (!bm || !swapped) return fail(PA_ERR_INVALID_ARG, "pa_bm_is_swapped: null argument");
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end())
+    return fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_is_swapped: unknown sequence %lld",
+                (long long)seq_id);
+  *swapped = it->second.on_host ? 1 : 0;
+  return PA_OK;
+}
+
 int32_t pa_bm_num_free(const pa_bm* bm) {
-  return bm ? static_cast<int32_t>(bm->free_q.size()) : -1;
+  return bm ? static_cast<int32_t>(bm->dev.free_q.size()) : -1;
 }
 
 int32_t pa_bm_refcount(const pa_bm* bm, int32_t block) {
   if (!bm || block < 0 || block >= bm->num_blocks) return -1;
-  return bm->ref[block];
+  return bm->dev.ref[block];
 }
 
 pa_status pa_bm_length(const pa_bm* bm, int64_t seq_id, int32_t* len) {
@@ -267,6 +405,9 @@ pa_status pa_bm_pack(const pa_bm* bm, const int64_t* seq_ids, int32_t n,
     auto it = bm->seqs.find(seq_ids[i]);
     if (it == bm->seqs.end())
       return fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_pack: unknown sequence %lld",
+                  (long long)seq_ids[i]);
+    if (it->second.on_host)
+      return fail(PA_ERR_SWAPPED, "pa_bm_pack: sequence %lld is swapped out",
                   (long long)seq_ids[i]);
     if (static_cast<int64_t>(it->second.table.size()) > cap)
       return fail(PA_ERR_INVALID_ARG, "pa_bm_pack: sequence %lld has %zu blocks > cap %d",

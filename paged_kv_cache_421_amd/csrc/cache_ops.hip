@@ -1,12 +1,15 @@
-// pa_write_kv and pa_copy_blocks for gfx950.
+// pa_write_kv, pa_copy_blocks and pa_swap_blocks for gfx950.
 //
 // write: each decode iteration stores the new token's K and V in its
 // sequence's current block (ybb.press, "vLLM PagedAttention 大模型推理架构深度实战",
 // §6); the destination of each row is a flat slot = block * 16 + offset.
 // copy: copy-on-write duplicates a shared block before it is modified
 // (same page, §2.3); a pair copies the whole block of both caches.
+// swap: the same whole-block copies between the device cache and a pinned
+// host pool, when sequences are swapped out under memory pressure and back
+// in (same page, §3.2, §6, §9 item 5).
 //
-// Both kernels are pure data movement: one lane moves 16 source bytes, so a
+// All kernels are pure data movement: one lane moves 16 source bytes, so a
 // wave moves 1 KiB per instruction with fully coalesced accesses.
 #include <hip/hip_runtime.h>
 
@@ -59,17 +62,21 @@ write_kv_kernel(char* __restrict__ k_cache, char* __restrict__ v_cache,
   }
 }
 
-// One lane per 16-byte chunk of a block; grid.y = pair, grid.z = K or V.
+// Whole-block copies from one pool to another (the same pool for
+// copy-on-write; device cache and pinned host pool for swapping).  One lane
+// per 16-byte chunk of a block; grid.y = pair, grid.z = K or V.
 __global__ void __launch_bounds__(256)
-copy_blocks_kernel(char* __restrict__ k_cache, char* __restrict__ v_cache,
+copy_blocks_kernel(const char* __restrict__ src_k, const char* __restrict__ src_v,
+                   char* __restrict__ dst_k, char* __restrict__ dst_v,
                    const int32_t* __restrict__ pairs, int64_t block_bytes) {
   const int64_t chunk = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (chunk * 16 >= block_bytes) return;
-  const int32_t src = pairs[2 * blockIdx.y];
-  const int32_t dst = pairs[2 * blockIdx.y + 1];
-  char* cache = blockIdx.z ? v_cache : k_cache;
-  const u32x4_t x = *reinterpret_cast<const u32x4_t*>(cache + src * block_bytes + chunk * 16);
-  *reinterpret_cast<u32x4_t*>(cache + dst * block_bytes + chunk * 16) = x;
+  const int64_t src = pairs[2 * blockIdx.y];
+  const int64_t dst = pairs[2 * blockIdx.y + 1];
+  const char* from = blockIdx.z ? src_v : src_k;
+  char* to = blockIdx.z ? dst_v : dst_k;
+  const u32x4_t x = *reinterpret_cast<const u32x4_t*>(from + src * block_bytes + chunk * 16);
+  *reinterpret_cast<u32x4_t*>(to + dst * block_bytes + chunk * 16) = x;
 }
 
 int dtype_bytes(int dt) {
@@ -177,6 +184,59 @@ extern "C" pa_status pa_copy_blocks(const pa_cache_desc* c, void* k_cache, void*
   const int64_t chunks = block_bytes / 16;
   dim3 grid(static_cast<unsigned>((chunks + 255) / 256), num_pairs, 2);
   copy_blocks_kernel<<<grid, 256, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const char*>(k_cache), static_cast<const char*>(v_cache),
       static_cast<char*>(k_cache), static_cast<char*>(v_cache), pairs, block_bytes);
   return launch_status("pa_copy_blocks");
+}
+
+namespace {
+
+// True if the GPU can address `p`: device memory, or host memory allocated
+// pinned (hipHostMalloc) or managed.  Pageable host memory is not.
+bool gpu_addressable(const void* p) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();     // the query leaves its error behind
+    return false;
+  }
+  switch (attr.type) {
+    case hipMemoryTypeDevice:
+    case hipMemoryTypeManaged:
+    case hipMemoryTypeUnified:
+      return true;
+    case hipMemoryTypeHost:
+      return attr.devicePointer != nullptr;
+    default:
+      return false;
+  }
+}
+
+}  // namespace
+
+extern "C" pa_status pa_swap_blocks(const pa_cache_desc* c, const void* src_k,
+                                    const void* src_v, void* dst_k, void* dst_v,
+                                    const int32_t* pairs, int32_t num_pairs, void* stream) {
+  pa_status st = check_desc(c, "pa_swap_blocks");
+  if (st != PA_OK) return st;
+  if (num_pairs < 0) return fail(PA_ERR_INVALID_ARG, "pa_swap_blocks: num_pairs < 0");
+  if (num_pairs == 0) return PA_OK;
+  if (num_pairs > 65535)
+    return fail(PA_ERR_UNSUPPORTED, "pa_swap_blocks: %d pairs (at most 65535 per call)",
+                num_pairs);
+  if (!src_k || !src_v || !dst_k || !dst_v || !pairs)
+    return fail(PA_ERR_INVALID_ARG, "pa_swap_blocks: null pointer");
+  const void* ptrs[5] = {src_k, src_v, dst_k, dst_v, pairs};
+  const char* names[5] = {"src_k", "src_v", "dst_k", "dst_v", "pairs"};
+  for (int i = 0; i < 5; ++i)
+    if (!gpu_addressable(ptrs[i]))
+      return fail(PA_ERR_INVALID_ARG,
+                  "pa_swap_blocks: %s is not device or pinned host memory", names[i]);
+  const int64_t block_bytes = static_cast<int64_t>(c->num_kv_heads) * kBlock * c->head_dim *
+                              dtype_bytes(c->cache_dtype);
+  const int64_t chunks = block_bytes / 16;
+  dim3 grid(static_cast<unsigned>((chunks + 255) / 256), num_pairs, 2);
+  copy_blocks_kernel<<<grid, 256, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const char*>(src_k), static_cast<const char*>(src_v),
+      static_cast<char*>(dst_k), static_cast<char*>(dst_v), pairs, block_bytes);
+  return launch_status("pa_swap_blocks");
 }

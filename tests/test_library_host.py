@@ -302,3 +302,89 @@ def test_cpp_batch_is_all_or_nothing():
     assert bm.length(0) == 16 and bm.length(1) == 0 and bm.num_free() == 1
     with pytest.raises(pk.PagedKVError):
         bm.append_batch(np.array([0, 0]))
+
+
+_ERR_SWAP = {-1: "ValueError", -3: "NoBlocks", -4: "UnknownSeq", -5: "SeqExists", -8: "Swapped"}
+
+
+def _apply_swap(bm, op, args):
+    try:
+        if op == "add":
+            bm.add_seq(args[0])
+            return None, None
+        if op == "fork":
+            bm.fork(*args)
+            return None, None
+        if op == "free":
+            bm.free_seq(args[0])
+            return None, None
+        if op in ("out", "in"):
+            pairs = (bm.swap_out if op == "out" else bm.swap_in)(list(args))
+            return None, [tuple(int(x) for x in p) for p in pairs]
+        sl, pr = bm.append_tokens(*args)
+        return None, (list(sl), pr)
+    except (oracle.NoBlocks, oracle.UnknownSeq, oracle.SeqExists, oracle.Swapped,
+            ValueError) as e:
+        return type(e).__name__, None
+    except pk.PagedKVError as e:
+        return _ERR_SWAP[e.status], None
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_cpp_manager_matches_oracle_with_swapping(seed):
+    rng = np.random.default_rng(seed)
+    N, H = 64, 48
+    order, horder = rng.permutation(N), rng.permutation(H)
+    ref = oracle.RefBlockManager(N, free_order=order, num_host_blocks=H, host_free_order=horder)
+    cpp = pk.BlockManager(N, free_order=order, num_host_blocks=H, host_free_order=horder)
+    live, nxt = [], 0
+    for step in range(3000):
+        r = int(rng.integers(0, 12))
+        pick = live[int(rng.integers(len(live)))] if live else 0
+        if r == 0 or not live:
+            op, args = "add", (nxt,)
+        elif r == 1:
+            op, args = "fork", (pick, nxt)
+        elif r == 2:
+            op, args = "free", (pick,)
+        elif r in (3, 4, 5):
+            k = int(rng.integers(1, min(len(live), 4) + 1))
+            group = [live[i] for i in rng.choice(len(live), size=k, replace=False)]
+            if rng.integers(0, 10) == 0:
+                group.append(group[0])            # a repeated id is an argument error
+            op, args = ("out" if r < 5 else "in"), tuple(group)
+        else:
+            op, args = "append", (pick, int(rng.integers(0, 40)))
+        e1, r1 = _apply_swap(ref, op, args)
+        e2, r2 = _apply_swap(cpp, op, args)
+        assert (e1, r1) == (e2, r2), (step, op, args)
+        if e1 is None:
+            if op in ("add", "fork"):
+                live.append(nxt)
+                nxt += 1
+            elif op == "free":
+                live.remove(pick)
+        assert ref.num_free() == cpp.num_free() and ref.num_free_host() == cpp.num_free_host()
+        dev = [s for s in live if not ref.is_swapped(s)]
+        assert [cpp.is_swapped(s) for s in live] == [ref.is_swapped(s) for s in live]
+        assert _cpp_tables(cpp, dev) == {s: (ref.table(s), ref.length(s)) for s in dev}
+        if step % 97 == 0:
+            ref.check_invariants()
+            assert [cpp.refcount(b) for b in range(N)] == ref.ref
+            assert [cpp.host_refcount(b) for b in range(H)] == ref.host_ref
+    for s in live:
+        ref.free_seq(s)
+        cpp.free_seq(s)
+    assert cpp.num_free() == N and cpp.num_free_host() == H
+    assert list(ref.free) == _drain(cpp, N)
+
+
+def test_swap_blocks_rejects_pageable_host_memory():
+    """The pool pointers are checked before any launch: a pageable host
+    buffer would fault inside the kernel, so it is refused."""
+    d = pk.CacheDesc(4, 2, 64, "bf16")
+    buf = np.zeros(4096, dtype=np.uint8)
+    p = ctypes.c_void_p(buf.ctypes.data)
+    st = pk.lib.pa_swap_blocks(ctypes.byref(d.c), p, p, p, p, p, 1, None)
+    assert st == -1 and b"pinned" in pk.lib.pa_last_error()
+    assert pk.lib.pa_swap_blocks(ctypes.byref(d.c), p, p, p, p, p, 0, None) == 0
