@@ -23,7 +23,7 @@ from .formats import (bf16_to_f64, e4m3_to_f64, e4m3_encode, e4m3_all_values,
 from .attention import gather_kv, decode, decode_partitioned, merge_partitions
 from .chunk import decode_chunk, chunk_rows, visible_len
 from .cache_ops import write_kv, copy_blocks, swap_blocks
-from .block_manager import RefBlockManager, NoBlocks, UnknownSeq, SeqExists, Swapped
+from .block_manager import RefBlockManager, NoBlocks, UnknownSeq, SeqExists, Swapped, block_key
 from .accounting import kv_cache_bytes, paged_utilisation, contiguous_utilisation
 
 __all__ = [
@@ -31,6 +31,6 @@ __all__ = [
     "gather_kv", "decode", "decode_partitioned", "merge_partitions",
     "decode_chunk", "chunk_rows", "visible_len",
     "write_kv", "copy_blocks", "swap_blocks",
-    "RefBlockManager", "NoBlocks", "UnknownSeq", "SeqExists", "Swapped",
+    "RefBlockManager", "NoBlocks", "UnknownSeq", "SeqExists", "Swapped", "block_key",
     "kv_cache_bytes", "paged_utilisation", "contiguous_utilisation",
 ]

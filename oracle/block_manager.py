@@ -55,15 +55,61 @@ host link).  Readings:
 * Both are all-or-nothing: too few free blocks in the destination pool
   raise ``NoBlocks`` and change nothing; so does listing a sequence twice
   or one that is not where the call expects it (``Swapped``).
+
+Prefix caching (explore.n1n.ai, "vLLM 深度解析", section "vLLM 生态的核心功能
+亮点": requests that share a system prompt or documents reuse that prefix's
+cached KV instead of recomputing it; ybb.press §7.3: automatic prefix caching
+finds identical prefixes across requests and shares their KV blocks, e.g.
+earlier turns of a chat; gheillcoat.github.io, "概念-vLLM", section 3: shared
+prefixes such as the system prompt are cached automatically; unionyoga.cn,
+section "在真实架构中扮演什么角色？": block-cache hit rate is a monitored
+figure, target above 95%).  Readings:
+
+* Once enabled, a full block written through the token-id calls gets a key:
+  FNV-1a 64 (the published Fowler-Noll-Vo hash) over the 8 little-endian
+  bytes of its parent's key (0 for a sequence's first block) followed by its
+  16 token ids as 4-byte little-endian integers.  The first block with a key
+  is registered for it; the key chain makes the key depend on the whole
+  prefix.
+* ``add_seq_prompt(seq, tokens)``: the longest run of the prompt's leading
+  full blocks whose keys are registered -- and whose stored parent key and
+  tokens match, so a hash collision is never shared -- is reused (each
+  block gains a reference); the caller need not write those tokens' KV
+  (``num_cached``).  The rest of the prompt is appended.  Queried blocks =
+  the prompt's full blocks; hit blocks = the reused ones.
+* A registered block whose count drops to zero is not freed but becomes
+  evictable, most recently released last; a hit revives it.  Allocation
+  takes the free queue first, then evicts the least recently released
+  block (dropping its registration).  Capacity checks count both.
+* Appending without token ids stops a sequence's blocks being registered.
 """
 from __future__ import annotations
 
-from collections import deque
-from typing import Dict, List, Optional, Tuple
+from collections import OrderedDict, deque
+from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 
 BLOCK = 16
+
+FNV_OFFSET = 0xCBF29CE484222325
+FNV_PRIME = 0x100000001B3
+MASK64 = (1 << 64) - 1
+
+
+def fnv1a64(data: bytes) -> int:
+    """FNV-1a, 64-bit: for each byte, h ^= byte, then h *= prime (mod 2^64)."""
+    h = FNV_OFFSET
+    for byte in data:
+        h ^= byte
+        h = (h * FNV_PRIME) & MASK64
+    return h
+
+
+def block_key(parent: int, tokens: Sequence[int]) -> int:
+    """FNV-1a 64 over parent key (8 bytes LE) then the token ids (4 bytes LE each)."""
+    return fnv1a64(int(parent).to_bytes(8, "little") + b"".join(
+        int(t).to_bytes(4, "little", signed=True) for t in tokens))
 
 
 class NoBlocks(RuntimeError):
@@ -104,10 +150,48 @@ class RefBlockManager:
         self.tables: Dict[int, List[int]] = {}
         self.lens: Dict[int, int] = {}
         self.on_host: Dict[int, bool] = {}
+        # prefix caching
+        self.caching = False
+        self.cache: Dict[int, int] = {}                 # key -> block
+        self.bkey: Dict[int, int] = {}                  # registered block -> key
+        self.bmeta: Dict[int, Tuple[int, tuple]] = {}   # registered block -> (parent key, tokens)
+        self.lru: "OrderedDict[int, None]" = OrderedDict()   # evictable, oldest release first
+        self.toks: Dict[int, Optional[List[int]]] = {}  # token ids (None: not tracked)
+        self.last_key: Dict[int, int] = {}
+        self.queried = 0
+        self.hits = 0
+
+    def enable_prefix_caching(self) -> None:
+        self.caching = True
+
+    def available(self) -> int:
+        return len(self.free) + len(self.lru)
+
+    def cache_stats(self):
+        """(queried blocks, hit blocks, registered blocks, evictable blocks)."""
+        return self.queried, self.hits, len(self.cache), len(self.lru)
+
+    def _pop(self) -> int:
+        if self.free:
+            b = self.free.popleft()
+        else:
+            b, _ = self.lru.popitem(last=False)
+            del self.cache[self.bkey.pop(b)]
+            del self.bmeta[b]
+        self.ref[b] = 1
+        return b
+
+    def _release(self, b: int) -> None:
+        """A device block's count reached zero."""
+        if b in self.bkey:
+            self.lru[b] = None
+        else:
+            self.free.append(b)
 
     # -- queries -----------------------------------------------------------
     def num_free(self) -> int:
-        return len(self.free)
+        """Blocks an allocation can take: free plus evictable."""
+        return self.available()
 
     def refcount(self, block: int) -> int:
         return self.ref[block]
@@ -147,6 +231,8 @@ class RefBlockManager:
         self.tables[seq] = []
         self.lens[seq] = 0
         self.on_host[seq] = False
+        self.toks[seq] = [] if self.caching else None
+        self.last_key[seq] = 0
 
     def fork(self, parent: int, child: int) -> None:
         t = self._get_dev(parent)
@@ -155,6 +241,8 @@ class RefBlockManager:
         self.tables[child] = list(t)
         self.lens[child] = self.lens[parent]
         self.on_host[child] = False
+        self.toks[child] = None if self.toks[parent] is None else list(self.toks[parent])
+        self.last_key[child] = self.last_key[parent]
         for b in t:
             self.ref[b] += 1
 
@@ -166,19 +254,87 @@ class RefBlockManager:
         return new + cow
 
     def append_tokens(self, seq: int, n: int) -> Tuple[List[int], Optional[Tuple[int, int]]]:
-        """Append n tokens; returns (slots, copy pair or None)."""
+        """Append n tokens; returns (slots, copy pair or None).  Their ids are
+        unknown, so the sequence's blocks stop being registered."""
+        return self._append(seq, n, None)
+
+    def append_token_ids(self, seq: int, tokens) -> Tuple[List[int], Optional[Tuple[int, int]]]:
+        """Append tokens with their ids (full blocks get registered)."""
+        return self._append(seq, len(tokens), [int(t) for t in tokens])
+
+    def _append(self, seq, n, ids):
         self._get_dev(seq)
         if n < 0:
             raise ValueError("n must be >= 0")
-        if self._blocks_needed(seq, n) > len(self.free):
+        if self._blocks_needed(seq, n) > self.available():
             raise NoBlocks(seq)
+        if ids is None and n > 0:
+            self.toks[seq] = None
         slots, pair = [], None
-        for _ in range(n):
+        for i in range(n):
             s, cp = self._append_one(seq)
             slots.append(s)
             if cp is not None:
                 pair = cp
+            if ids is not None:
+                self._note_token(seq, ids[i])
         return slots, pair
+
+    def _note_token(self, seq: int, tok: int) -> None:
+        tk = self.toks[seq]
+        if tk is None:
+            return
+        tk.append(tok)
+        if len(tk) % BLOCK == 0:                     # a block just filled
+            blk = tuple(tk[-BLOCK:])
+            key = block_key(self.last_key[seq], blk)
+            b = self.tables[seq][len(tk) // BLOCK - 1]
+            if key not in self.cache and b not in self.bkey:
+                self.cache[key] = b
+                self.bkey[b] = key
+                self.bmeta[b] = (self.last_key[seq], blk)
+            self.last_key[seq] = key
+
+    def add_seq_prompt(self, seq: int, tokens) -> Tuple[List[int], int]:
+        """New sequence with a prompt: reuse the longest cached run of its
+        leading full blocks, append the rest.  Returns (slots, num_cached)."""
+        if seq in self.tables:
+            raise SeqExists(seq)
+        tokens = [int(t) for t in tokens]
+        hits: List[int] = []
+        parent = 0
+        if self.caching:
+            for k in range(len(tokens) // BLOCK):
+                blk = tuple(tokens[BLOCK * k:BLOCK * (k + 1)])
+                key = block_key(parent, blk)
+                b = self.cache.get(key)
+                if b is None or self.bmeta[b] != (parent, blk):
+                    break
+                hits.append(b)
+                parent = key
+        revived = sum(1 for b in hits if self.ref[b] == 0)
+        need = -(-len(tokens) // BLOCK) - len(hits)
+        if need > self.available() - revived:
+            raise NoBlocks(seq)
+        self.add_seq(seq)
+        if self.caching:
+            self.queried += len(tokens) // BLOCK
+            self.hits += len(hits)
+        t = self.tables[seq]
+        for b in hits:
+            if self.ref[b] == 0:
+                del self.lru[b]
+            self.ref[b] += 1
+            t.append(b)
+        nc = BLOCK * len(hits)
+        self.lens[seq] = nc
+        if self.toks[seq] is not None:
+            self.toks[seq] = tokens[:nc]
+        self.last_key[seq] = parent
+        slots = [t[p // BLOCK] * BLOCK + p % BLOCK for p in range(nc)]
+        more, pair = self.append_token_ids(seq, tokens[nc:])
+        assert pair is None
+        return slots + more, nc
 
     def append_slot(self, seq: int) -> Tuple[int, Optional[Tuple[int, int]]]:
         slots, pair = self.append_tokens(seq, 1)
@@ -189,13 +345,11 @@ class RefBlockManager:
         p = self.lens[seq]
         pair = None
         if p % BLOCK == 0:
-            b = self.free.popleft()
-            self.ref[b] = 1
+            b = self._pop()
             t.append(b)
         elif self.ref[t[-1]] > 1:
             old = t[-1]
-            b = self.free.popleft()
-            self.ref[b] = 1
+            b = self._pop()
             self.ref[old] -= 1
             t[-1] = b
             pair = (old, b)
@@ -205,15 +359,20 @@ class RefBlockManager:
 
     def free_seq(self, seq: int) -> None:
         t = self._get(seq)
-        ref, free = ((self.host_ref, self.host_free) if self.on_host[seq]
-                     else (self.ref, self.free))
         for b in t:
-            ref[b] -= 1
-            if ref[b] == 0:
-                free.append(b)
+            if self.on_host[seq]:
+                self.host_ref[b] -= 1
+                if self.host_ref[b] == 0:
+                    self.host_free.append(b)
+            else:
+                self.ref[b] -= 1
+                if self.ref[b] == 0:
+                    self._release(b)
         del self.tables[seq]
         del self.lens[seq]
         del self.on_host[seq]
+        del self.toks[seq]
+        del self.last_key[seq]
 
     # -- swapping ----------------------------------------------------------
     def _move(self, seqs, to_host: bool) -> List[Tuple[int, int]]:
@@ -224,19 +383,21 @@ class RefBlockManager:
             self._get(s)
             if self.on_host[s] == to_host:
                 raise Swapped(s)
-        src_ref, dst_ref, src_free, dst_free = (
-            (self.ref, self.host_ref, self.free, self.host_free) if to_host else
-            (self.host_ref, self.ref, self.host_free, self.free))
+        src_ref, dst_ref = (self.ref, self.host_ref) if to_host else (self.host_ref, self.ref)
         order: List[int] = []
         for s in seqs:
             for b in self.tables[s]:
                 if b not in order:
                     order.append(b)
-        if len(order) > len(dst_free):
+        room = len(self.host_free) if to_host else self.available()
+        if len(order) > room:
             raise NoBlocks(seqs)
         mapping = {}
         for b in order:
-            mapping[b] = dst_free.popleft()
+            if to_host:
+                mapping[b] = self.host_free.popleft()
+            else:
+                mapping[b] = self._pop()
             dst_ref[mapping[b]] = 0
         for s in seqs:
             t = self.tables[s]
@@ -244,7 +405,10 @@ class RefBlockManager:
                 dst_ref[mapping[b]] += 1
                 src_ref[b] -= 1
                 if src_ref[b] == 0:
-                    src_free.append(b)
+                    if to_host:
+                        self._release(b)
+                    else:
+                        self.host_free.append(b)
                 t[j] = mapping[b]
             self.on_host[s] = to_host
         return [(b, mapping[b]) for b in order]
@@ -282,8 +446,11 @@ class RefBlockManager:
                     for b in t:
                         occ[b] += 1
             assert occ == ref, "refcount != table occurrences"
-            free = set(fq)
-            assert len(free) == len(fq), "duplicate in free queue"
+            free = set(fq) | (set() if host else set(self.lru))
+            assert len(free) == len(fq) + (0 if host else len(self.lru)), "duplicate in free pools"
             used = {b for b in range(n) if ref[b] > 0}
             assert not (free & used), "block both free and referenced"
             assert free | used == set(range(n)), "block lost"
+        assert set(self.lru) <= set(self.bkey), "evictable block not registered"
+        assert all(self.cache[k] == b for b, k in self.bkey.items()), "registry out of sync"
+        assert len(self.cache) == len(self.bkey)
