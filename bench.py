@@ -52,8 +52,16 @@ the host link (PCIe 5.0 x16, 63 GB/s per direction).  A plain contiguous
 copy of the same bytes (the DMA engines, hipMemcpyAsync) is timed beside it
 as context.
 
+With ``--prefix`` the batch is 256 requests sharing a 2048-token system
+prompt, each with its own 64..512-token question, built with prefix
+caching (the prompt's blocks are stored once and shared); the step is the
+decode step above.  The roofline takes the unique KV bytes a call reads
+(shared blocks once), the logical bytes (every sequence's whole context)
+are reported beside them, with the block manager's hit rate and that of a
+simulated multi-turn chat.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers N]
-                      [--chunk T | --swap] [--no-cpu-baseline]
+                      [--chunk T | --swap | --prefix] [--no-cpu-baseline]
                       [--copy-calibration MIB]
 
 --copy-calibration MIB ends the run with plain device copies of MIB MiB, the
@@ -84,6 +92,8 @@ METRIC_CHUNK = ("paged chunk attention (T new tokens per sequence, causal): KV-c
                 "vs HBM peak; query tokens/sec")
 HBM_PEAK_GBPS = 8000.0
 PCIE5_X16_GBPS = 63.0        # 32 GT/s x 16 lanes x 128/130 / 8, per direction
+METRIC_PREFIX = ("paged decode with prefix caching: unique KV GB/s vs HBM peak; decoded "
+                 "seqs/sec; block-cache hit rate")
 METRIC_SWAP = "paged KV swap: device<->pinned host block copy GB/s vs host link peak"
 DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_421_amd", "csrc", "decode.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic_gqa8b_b256.txt")
@@ -346,6 +356,168 @@ def run_swap(args):
     print(json.dumps(res), flush=True)
 
 
+def chat_hit_rate(seed=11, conversations=64, turns=8):
+    """Host-only: multi-turn chats through the library's block manager with
+    prefix caching.  Turn k's prompt is the whole conversation so far plus a
+    new user message (64..256 tokens); the answer (128..512 tokens) is
+    appended with its ids; the request then ends and its blocks become
+    evictable.  Returns (hit rate, queried blocks, microseconds per prompt
+    lookup)."""
+    import paged_kv_cache_421_amd as pk
+    rng = np.random.default_rng(seed)
+    bm = pk.BlockManager(1 << 16)
+    bm.enable_prefix_caching()
+    hist = [np.zeros(0, np.int32) for _ in range(conversations)]
+    sid, t_lookup, n_lookup = 0, 0.0, 0
+    for _ in range(turns):
+        for c in range(conversations):
+            prompt = np.concatenate([hist[c], rng.integers(0, 32000, int(rng.integers(64, 257)))])
+            t0 = time.perf_counter()
+            bm.add_seq_prompt(sid, prompt)
+            t_lookup += time.perf_counter() - t0
+            n_lookup += 1
+            ans = rng.integers(0, 32000, int(rng.integers(128, 513)))
+            bm.append_token_ids(sid, ans)
+            bm.free_seq(sid)
+            hist[c] = np.concatenate([prompt, ans]).astype(np.int32)
+            sid += 1
+    q, h, _, _ = bm.cache_stats()
+    return h / q, q, t_lookup / n_lookup * 1e6
+
+
+def run_prefix(args):
+    """256 requests sharing a 2048-token prompt, decoded step by step."""
+    import torch
+    import paged_kv_cache_421_amd as pk
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    steps = args.steps or 100
+    warm = args.warmup if args.warmup is not None else 10
+    NL = args.layers
+    P = 2048
+    w = workloads.prefix_batch(9, 256, P, 64, 512, rows=False)
+    B, Hq, Hkv, D = w.B, w.Hq, w.Hkv, w.D
+    nb = w.num_blocks + B * (-(-(steps + warm) // 16) + 1)
+    desc = pk.CacheDesc(nb, Hkv, D, "bf16")
+    bm = pk.BlockManager(nb, free_order=np.r_[w.free_order, np.arange(w.num_blocks, nb)])
+    bm.enable_prefix_caching()
+    kc = [torch.empty(desc.shape, dtype=torch.bfloat16, device=dev) for _ in range(NL)]
+    vc = [torch.empty(desc.shape, dtype=torch.bfloat16, device=dev) for _ in range(NL)]
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    written = 0
+    for r in range(B):
+        slots, nc = bm.add_seq_prompt(r, w.prompt(r))
+        n = len(slots) - nc
+        sm = torch.from_numpy(np.ascontiguousarray(slots[nc:], dtype=np.int64)).to(dev)
+        for l in range(NL):
+            k = torch.randn((n, Hkv, D), device=dev, generator=g).to(torch.bfloat16)
+            v = torch.randn((n, Hkv, D), device=dev, generator=g).to(torch.bfloat16)
+            pk.write_kv(desc, kc[l], vc[l], k, v, sm, stream=stream)
+        written += n
+    queried, hits, registered, _ = bm.cache_stats()
+    lens = np.array([len(w.prompt(r)) for r in range(B)], dtype=np.int64)
+    _log(f"bench: prefix batch: {B} requests, prompt {P} shared, hit rate {hits / queried:.4f}, "
+         f"{written} of {int(lens.sum())} prompt rows written")
+    rng = np.random.default_rng(1003)
+    k_new, v_new, q = [], [], []
+    for _ in range(NL):
+        kn, vn, qq = workloads.config3_step(rng, B, Hq, Hkv, D)
+        k_new.append(torch.from_numpy(kn.view(np.int16)).to(dev).view(torch.bfloat16))
+        v_new.append(torch.from_numpy(vn.view(np.int16)).to(dev).view(torch.bfloat16))
+        q.append(torch.from_numpy(qq.view(np.int16)).to(dev).view(torch.bfloat16))
+    out = [torch.empty_like(q[0]) for _ in range(NL)]
+    max_len_final = int(lens.max()) + steps + warm
+    cap = -(-max_len_final // 16)
+    workspace = pk.new_decode_workspace(desc, B, Hq, max_len_final, dev)
+    h_slots = torch.empty(B, dtype=torch.int64, pin_memory=True)
+    h_bt = torch.empty((B, cap), dtype=torch.int32, pin_memory=True)
+    h_cl = torch.empty(B, dtype=torch.int32, pin_memory=True)
+    d_slots = torch.empty(B, dtype=torch.int64, device=dev)
+    d_bt = torch.empty((B, cap), dtype=torch.int32, device=dev)
+    d_cl = torch.empty(B, dtype=torch.int32, device=dev)
+    ids = np.arange(B, dtype=np.int64)
+    nfull = P // 16
+
+    def step(ev_pairs):
+        torch.cuda.current_stream().synchronize()        # host buffers are reused
+        sl, pairs = bm.append_batch(ids, slots=h_slots.numpy())
+        assert len(pairs) == 0
+        bm.pack(ids, cap, block_tables=h_bt.numpy(), context_lens=h_cl.numpy())
+        lens[:] += 1
+        d_slots.copy_(h_slots, non_blocking=True)
+        d_bt.copy_(h_bt, non_blocking=True)
+        d_cl.copy_(h_cl, non_blocking=True)
+        max_len = int(lens.max())
+        for l in range(NL):
+            pk.write_kv(desc, kc[l], vc[l], k_new[l], v_new[l], d_slots, stream=stream)
+            if ev_pairs is not None:
+                ev_pairs[l][0].record(stream)
+            pk.decode(desc, kc[l], vc[l], q[l], out[l], d_bt, d_cl, max_len, float(w.scale),
+                      workspace, stream=stream)
+            if ev_pairs is not None:
+                ev_pairs[l][1].record(stream)
+        logical = int(lens.sum()) * Hkv * D * 4
+        unique = (16 * nfull + int((lens - 16 * nfull).sum())) * Hkv * D * 4
+        return logical, unique
+
+    for _ in range(warm):
+        step(None)
+    torch.cuda.synchronize()
+    evs = [[(HipEvent(), HipEvent()) for _ in range(NL)] for _ in range(steps)]
+    per = []
+    t0 = time.perf_counter()
+    for i in range(steps):
+        per.append(step(evs[i]))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec_ms = [a.elapsed_ms(b) for row in evs for (a, b) in row]
+    for row in evs:
+        for a, b in row:
+            a.destroy()
+            b.destroy()
+    mean_s = statistics.mean(dec_ms) / 1e3
+    logical = statistics.mean(p[0] for p in per)
+    unique = statistics.mean(p[1] for p in per)
+    ach = unique / mean_s / 1e9
+    chat_rate, chat_q, lookup_us = chat_hit_rate()
+    _log(f"bench: pa_decode mean {mean_s * 1e6:.1f} us: unique {unique / 1e9:.3f} GB "
+         f"({ach:.0f} GB/s), logical {logical / 1e9:.3f} GB ({logical / mean_s / 1e9:.0f} GB/s); "
+         f"chat hit rate {chat_rate:.4f}")
+    res = {
+        "metric": METRIC_PREFIX,
+        "value": round(B * NL * steps / wall, 1),
+        "unit": "seqs/s",
+        "n_gpus": 1, "steps": steps, "warmup": warm,
+        "ms_per_step": round(wall / steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": ("prefix-shared GQA batch: Llama-3-8B-shaped layer (32 query / 8 KV "
+                                "heads, head_dim 128, bf16), 256 requests sharing a 2048-token "
+                                "system prompt plus their own 64..512-token questions, built "
+                                "through prefix caching"),
+                   "layers_per_step": NL,
+                   "step": "block-manager append + table upload + per layer pa_write_kv and pa_decode",
+                   "value_is": "sequences decoded per second per attention layer",
+                   "parallelism": "single GPU"},
+        "block_cache_hit_rate": round(hits / queried, 4),
+        "prompt_rows_written": written, "prompt_rows_total": int(lens.sum() - B * (steps + warm)),
+        "unique_kv_gb": round(unique / 1e9, 4), "logical_kv_gb": round(logical / 1e9, 4),
+        "logical_kv_gbps": round(logical / mean_s / 1e9, 1),
+        "decode_us_mean": round(mean_s * 1e6, 2),
+        "chat_sim": {"hit_rate": round(chat_rate, 4), "queried_blocks": chat_q,
+                     "conversations": 64, "turns": 8,
+                     "us_per_prompt_lookup": round(lookup_us, 2)},
+        "roofline": {"kernel": "decode_stream_kernel (pa_decode over shared prompt blocks)",
+                     "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -356,6 +528,8 @@ def main():
                     help="new tokens per sequence per step (1 = decode)")
     ap.add_argument("--swap", action="store_true",
                     help="measure swapping sequences out to pinned host memory and back")
+    ap.add_argument("--prefix", action="store_true",
+                    help="decode a batch that shares a system prompt through prefix caching")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     args = ap.parse_args()
@@ -365,6 +539,8 @@ def main():
         sys.exit(2)
     if args.swap:
         return run_swap(args)
+    if args.prefix:
+        return run_prefix(args)
     T = args.chunk
     if not 1 <= T <= 16:
         sys.exit("--chunk must be in 1..16")

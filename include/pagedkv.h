@@ -247,6 +247,7 @@ pa_status pa_bm_append_batch(pa_bm* bm, const int64_t* seq_ids, int32_t n,
                              int32_t* num_pairs);
 pa_status pa_bm_free_seq(pa_bm* bm, int64_t seq_id);
 
+/* Blocks an allocation can take (free, plus evictable with prefix caching). */
 int32_t pa_bm_num_free(const pa_bm* bm);
 /* Reference count of `block`, or -1 if out of range. */
 int32_t pa_bm_refcount(const pa_bm* bm, int32_t block);
@@ -287,6 +288,39 @@ int32_t pa_bm_num_free_host(const pa_bm* bm);
 int32_t pa_bm_host_refcount(const pa_bm* bm, int32_t block);
 /* *swapped = 1 if the sequence is in the host pool, else 0. */
 pa_status pa_bm_is_swapped(const pa_bm* bm, int64_t seq_id, int32_t* swapped);
+
+/* ---------------------------------------------------------------------------
+ * Prefix caching (explore.n1n.ai, "vLLM 深度解析", section "vLLM 生态的核心功能
+ * 亮点": requests sharing a system prompt or documents reuse its cached KV;
+ * ybb.press §7.3: automatic prefix caching shares the KV blocks of
+ * identical prefixes across requests; gheillcoat.github.io, "概念-vLLM",
+ * section 3).  Off until pa_bm_enable_prefix_caching.
+ *
+ * A full block written with token ids (pa_bm_add_seq_prompt,
+ * pa_bm_append_token_ids) is registered under a key: FNV-1a 64 over its
+ * parent block's key (8 bytes little-endian, 0 for a first block) then its
+ * 16 token ids (4 bytes little-endian each), so the key covers the whole
+ * prefix.  pa_bm_add_seq_prompt creates a sequence with tokens[0..n-1]: the
+ * longest run of leading full blocks whose key, parent key and ids all match
+ * a registered block is reused (each gains a reference); *num_cached
+ * receives that many tokens -- their KV is already in the cache, the caller
+ * writes only tokens num_cached..n-1 -- and the rest are appended.  slots[n]
+ * receives every token's slot.  A registered block whose count drops to
+ * zero is kept as evictable rather than freed; allocation takes free blocks
+ * first, then evicts the least recently released evictable block, and a hit
+ * revives one.  pa_bm_num_free counts free plus evictable blocks.
+ * pa_bm_append_tokens / pa_bm_append_batch (ids unknown) stop registering a
+ * sequence's later blocks.  All calls are all-or-nothing as above.
+ * ------------------------------------------------------------------------- */
+pa_status pa_bm_enable_prefix_caching(pa_bm* bm);
+pa_status pa_bm_add_seq_prompt(pa_bm* bm, int64_t seq_id, const int32_t* tokens,
+                               int32_t n, int64_t* slots, int32_t* num_cached);
+pa_status pa_bm_append_token_ids(pa_bm* bm, int64_t seq_id, const int32_t* tokens,
+                                 int32_t n, int64_t* slots, int32_t* cow_src,
+                                 int32_t* cow_dst);
+/* Prompt full blocks looked up, blocks reused, registered and evictable blocks. */
+pa_status pa_bm_cache_stats(const pa_bm* bm, int64_t* queried_blocks, int64_t* hit_blocks,
+                            int32_t* registered_blocks, int32_t* evictable_blocks);
 
 /*
  * pa_swap_blocks -- whole-block copies between two pools with the layout of

@@ -261,6 +261,35 @@ class BlockManager:
         """pa_bm_swap_in: (host block, device block) pairs, int32 [k, 2]."""
         return self._move(lib.pa_bm_swap_in, seq_ids, self.num_blocks)
 
+    def enable_prefix_caching(self) -> None:
+        check(lib.pa_bm_enable_prefix_caching(self._h))
+
+    def add_seq_prompt(self, seq: int, tokens):
+        """pa_bm_add_seq_prompt: (slots int64 [n], num_cached)."""
+        toks = np.ascontiguousarray(tokens, dtype=np.int32)
+        slots = np.empty(max(len(toks), 1), dtype=np.int64)
+        nc = ctypes.c_int32()
+        check(lib.pa_bm_add_seq_prompt(self._h, int(seq), _ptr(toks), len(toks), _ptr(slots),
+                                       ctypes.byref(nc)))
+        return slots[:len(toks)], nc.value
+
+    def append_token_ids(self, seq: int, tokens):
+        """pa_bm_append_token_ids: (slots, copy pair or None)."""
+        toks = np.ascontiguousarray(tokens, dtype=np.int32)
+        slots = np.empty(max(len(toks), 1), dtype=np.int64)
+        src, dst = ctypes.c_int32(), ctypes.c_int32()
+        check(lib.pa_bm_append_token_ids(self._h, int(seq), _ptr(toks), len(toks), _ptr(slots),
+                                         ctypes.byref(src), ctypes.byref(dst)))
+        return slots[:len(toks)], (None if src.value < 0 else (src.value, dst.value))
+
+    def cache_stats(self):
+        """(queried blocks, hit blocks, registered blocks, evictable blocks)."""
+        q, h = ctypes.c_int64(), ctypes.c_int64()
+        r, e = ctypes.c_int32(), ctypes.c_int32()
+        check(lib.pa_bm_cache_stats(self._h, ctypes.byref(q), ctypes.byref(h), ctypes.byref(r),
+                                    ctypes.byref(e)))
+        return q.value, h.value, r.value, e.value
+
     def num_free_host(self) -> int:
         return int(lib.pa_bm_num_free_host(self._h))
 

@@ -17,11 +17,24 @@
 // block loses the set's references and returns to the device pool, in the
 // same walk order, when its count reaches zero.  swap_in is the mirror.
 //
+// Prefix caching: requests that share a prompt reuse its cached KV blocks
+// instead of recomputing them (explore.n1n.ai, "vLLM 深度解析", section
+// "vLLM 生态的核心功能亮点"; ybb.press §7.3; gheillcoat.github.io, "概念-vLLM",
+// section 3).  A full block written with token ids is keyed by FNV-1a 64 over
+// its parent's key (8 bytes, little-endian; 0 for a first block) and its 16
+// ids (4 bytes each, little-endian); a prompt reuses the longest run of its
+// leading full blocks whose key, parent key and ids all match.  A registered
+// block whose count drops to zero becomes evictable (least recently released
+// first) instead of free; allocation takes free blocks first, then evicts.
+//
 // The queue discipline, the choice of which sharer copies (the one that
 // appends, while the block is still shared) and the all-or-nothing rule make
 // the tables reproducible; they are readings, the pages fix none of them.
+#include <array>
 #include <cstdint>
 #include <deque>
+#include <iterator>
+#include <list>
 #include <new>
 #include <unordered_map>
 #include <unordered_set>
@@ -40,7 +53,31 @@ struct Seq {
   std::vector<int32_t> table;  // logical -> physical block (host block if on_host)
   int32_t len = 0;             // tokens appended so far
   bool on_host = false;        // swapped out
+  bool track = false;          // token ids known (prefix caching)
+  std::vector<int32_t> toks;   // token ids, when tracked
+  uint64_t last_key = 0;       // key of the last full block
 };
+
+using BlockTokens = std::array<int32_t, kBlock>;
+
+uint64_t fnv1a64_bytes(uint64_t h, const unsigned char* p, size_t n) {
+  for (size_t i = 0; i < n; ++i) {
+    h ^= p[i];
+    h *= 0x100000001B3ull;
+  }
+  return h;
+}
+
+// Key of a full block: FNV-1a 64 over the parent key then the token ids.
+uint64_t block_key(uint64_t parent, const int32_t* toks) {
+  unsigned char buf[8 + 4 * kBlock];
+  for (int i = 0; i < 8; ++i) buf[i] = static_cast<unsigned char>(parent >> (8 * i));
+  for (int t = 0; t < kBlock; ++t) {
+    const uint32_t v = static_cast<uint32_t>(toks[t]);
+    for (int i = 0; i < 4; ++i) buf[8 + 4 * t + i] = static_cast<unsigned char>(v >> (8 * i));
+  }
+  return fnv1a64_bytes(0xCBF29CE484222325ull, buf, sizeof(buf));
+}
 
 // A FIFO free pool with reference counts.
 struct Pool {
@@ -74,6 +111,31 @@ struct pa_bm {
   Pool host;
   std::unordered_map<int64_t, Seq> seqs;
 
+  // prefix cache (device blocks)
+  bool caching = false;
+  std::unordered_map<uint64_t, int32_t> cache;   // key -> block
+  std::vector<char> registered;                  // per block
+  std::vector<uint64_t> bkey, bparent;
+  std::vector<BlockTokens> btok;
+  std::list<int32_t> lru;                        // evictable, oldest release first
+  std::vector<std::list<int32_t>::iterator> lru_pos;
+  std::vector<char> in_lru;
+  int64_t queried = 0, hits = 0;
+
+  void init_cache_state() {
+    registered.assign(num_blocks, 0);
+    bkey.assign(num_blocks, 0);
+    bparent.assign(num_blocks, 0);
+    btok.assign(num_blocks, BlockTokens{});
+    lru_pos.assign(num_blocks, lru.end());
+    in_lru.assign(num_blocks, 0);
+  }
+
+  // Blocks an allocation can take: free plus evictable.
+  int64_t available() const {
+    return static_cast<int64_t>(dev.free_q.size()) + static_cast<int64_t>(lru.size());
+  }
+
   // Blocks an append of n tokens to `s` takes from the pool.
   int64_t blocks_needed(const Seq& s, int64_t n) const {
     if (n <= 0) return 0;
@@ -83,11 +145,55 @@ struct pa_bm {
     return fresh + cow;
   }
 
+  // A device block for a new use (count 1): free first, else evict.
   int32_t pop() {
-    int32_t b = dev.free_q.front();
-    dev.free_q.pop_front();
+    int32_t b;
+    if (!dev.free_q.empty()) {
+      b = dev.free_q.front();
+      dev.free_q.pop_front();
+    } else {
+      b = lru.front();
+      lru.pop_front();
+      in_lru[b] = 0;
+      cache.erase(bkey[b]);
+      registered[b] = 0;
+    }
     dev.ref[b] = 1;
     return b;
+  }
+
+  // A device block's count reached zero.
+  void release(int32_t b) {
+    if (registered[b]) {
+      lru.push_back(b);
+      lru_pos[b] = std::prev(lru.end());
+      in_lru[b] = 1;
+    } else {
+      dev.free_q.push_back(b);
+    }
+  }
+
+  void revive(int32_t b) {
+    lru.erase(lru_pos[b]);
+    in_lru[b] = 0;
+  }
+
+  // Records a token id; registers the block it completes.
+  void note_token(Seq& s, int32_t tok) {
+    if (!s.track) return;
+    s.toks.push_back(tok);
+    if (s.toks.size() % kBlock != 0) return;
+    const int32_t* blk = s.toks.data() + s.toks.size() - kBlock;
+    const uint64_t key = block_key(s.last_key, blk);
+    const int32_t b = s.table[s.toks.size() / kBlock - 1];
+    if (!cache.count(key) && !registered[b]) {
+      cache.emplace(key, b);
+      registered[b] = 1;
+      bkey[b] = key;
+      bparent[b] = s.last_key;
+      for (int i = 0; i < kBlock; ++i) btok[b][i] = blk[i];
+    }
+    s.last_key = key;
   }
 
   // Appends one token; the caller has checked that blocks are available.
@@ -141,6 +247,7 @@ pa_bm* pa_bm_create_ex(int32_t num_blocks, int32_t block_size, const int32_t* fr
          num_host_blocks - 1);
     return nullptr;
   }
+  bm->init_cache_state();
   return bm;
 }
 
@@ -156,7 +263,9 @@ pa_status pa_bm_add_seq(pa_bm* bm, int64_t seq_id) {
   if (bm->seqs.count(seq_id))
     return fail(PA_ERR_SEQ_EXISTS, "pa_bm_add_seq: sequence %lld exists",
                 (long long)seq_id);
-  bm->seqs.emplace(seq_id, Seq{});
+  Seq s;
+  s.track = bm->caching;
+  bm->seqs.emplace(seq_id, std::move(s));
   return PA_OK;
 }
 
@@ -178,31 +287,129 @@ pa_status pa_bm_fork(pa_bm* bm, int64_t parent_id, int64_t child_id) {
   return PA_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Appends n tokens (ids: their token ids, or null when unknown); all or nothing.
+pa_status append_n(pa_bm* bm, int64_t seq_id, int32_t n, const int32_t* ids, int64_t* slots,
+                   int32_t* cow_src, int32_t* cow_dst, const char* fn) {
+  if (!bm || !cow_src || !cow_dst || (n > 0 && !slots))
+    return fail(PA_ERR_INVALID_ARG, "%s: null argument", fn);
+  if (n < 0) return fail(PA_ERR_INVALID_ARG, "%s: n = %d < 0", fn, n);
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end())
+    return fail(PA_ERR_UNKNOWN_SEQ, "%s: unknown sequence %lld", fn, (long long)seq_id);
+  Seq& s = it->second;
+  if (s.on_host)
+    return fail(PA_ERR_SWAPPED, "%s: sequence %lld is swapped out", fn, (long long)seq_id);
+  if (static_cast<int64_t>(s.len) + n > INT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "%s: length overflow", fn);
+  const int64_t need = bm->blocks_needed(s, n);
+  if (need > bm->available())
+    return fail(PA_ERR_NO_BLOCKS, "%s: sequence %lld needs %lld blocks, %lld available", fn,
+                (long long)seq_id, (long long)need, (long long)bm->available());
+  if (!ids && n > 0) {
+    s.track = false;
+    s.toks.clear();
+  }
+  *cow_src = -1;
+  *cow_dst = -1;
+  for (int32_t i = 0; i < n; ++i) {
+    slots[i] = bm->append_one(s, cow_src, cow_dst);
+    if (ids) bm->note_token(s, ids[i]);
+  }
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 pa_status pa_bm_append_tokens(pa_bm* bm, int64_t seq_id, int32_t n,
                               int64_t* slots, int32_t* cow_src,
                               int32_t* cow_dst) {
-  if (!bm || !cow_src || !cow_dst || (n > 0 && !slots))
-    return fail(PA_ERR_INVALID_ARG, "pa_bm_append_tokens: null argument");
-  if (n < 0)
-    return fail(PA_ERR_INVALID_ARG, "pa_bm_append_tokens: n = %d < 0", n);
-  auto it = bm->seqs.find(seq_id);
-  if (it == bm->seqs.end())
-    return fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_append_tokens: unknown sequence %lld",
+  return append_n(bm, seq_id, n, nullptr, slots, cow_src, cow_dst, "pa_bm_append_tokens");
+}
+
+pa_status pa_bm_append_token_ids(pa_bm* bm, int64_t seq_id, const int32_t* tokens, int32_t n,
+                                 int64_t* slots, int32_t* cow_src, int32_t* cow_dst) {
+  if (n > 0 && !tokens)
+    return fail(PA_ERR_INVALID_ARG, "pa_bm_append_token_ids: null tokens");
+  return append_n(bm, seq_id, n, tokens, slots, cow_src, cow_dst, "pa_bm_append_token_ids");
+}
+
+pa_status pa_bm_enable_prefix_caching(pa_bm* bm) {
+  if (!bm) return fail(PA_ERR_INVALID_ARG, "pa_bm_enable_prefix_caching: null manager");
+  bm->caching = true;
+  return PA_OK;
+}
+
+pa_status pa_bm_add_seq_prompt(pa_bm* bm, int64_t seq_id, const int32_t* tokens, int32_t n,
+                               int64_t* slots, int32_t* num_cached) {
+  if (!bm || !num_cached || n < 0 || (n > 0 && (!tokens || !slots)))
+    return fail(PA_ERR_INVALID_ARG, "pa_bm_add_seq_prompt: bad argument");
+  if (bm->seqs.count(seq_id))
+    return fail(PA_ERR_SEQ_EXISTS, "pa_bm_add_seq_prompt: sequence %lld exists",
                 (long long)seq_id);
-  Seq& s = it->second;
-  if (s.on_host)
-    return fail(PA_ERR_SWAPPED, "pa_bm_append_tokens: sequence %lld is swapped out",
-                (long long)seq_id);
-  if (static_cast<int64_t>(s.len) + n > INT32_MAX)
-    return fail(PA_ERR_INVALID_ARG, "pa_bm_append_tokens: length overflow");
-  const int64_t need = bm->blocks_needed(s, n);
-  if (need > static_cast<int64_t>(bm->dev.free_q.size()))
-    return fail(PA_ERR_NO_BLOCKS,
-                "pa_bm_append_tokens: sequence %lld needs %lld blocks, %zu free",
-                (long long)seq_id, (long long)need, bm->dev.free_q.size());
-  *cow_src = -1;
-  *cow_dst = -1;
-  for (int32_t i = 0; i < n; ++i) slots[i] = bm->append_one(s, cow_src, cow_dst);
+  // the longest run of leading full blocks found in the cache
+  std::vector<int32_t> hit;
+  uint64_t parent = 0;
+  if (bm->caching) {
+    for (int32_t k = 0; k < n / kBlock; ++k) {
+      const int32_t* blk = tokens + static_cast<int64_t>(k) * kBlock;
+      const uint64_t key = block_key(parent, blk);
+      auto c = bm->cache.find(key);
+      if (c == bm->cache.end()) break;
+      const int32_t b = c->second;
+      bool same = bm->bparent[b] == parent;
+      for (int i = 0; i < kBlock && same; ++i) same = bm->btok[b][i] == blk[i];
+      if (!same) break;
+      hit.push_back(b);
+      parent = key;
+    }
+  }
+  int64_t revived = 0;
+  for (int32_t b : hit) revived += bm->dev.ref[b] == 0 ? 1 : 0;
+  const int64_t need = (static_cast<int64_t>(n) + kBlock - 1) / kBlock - static_cast<int64_t>(hit.size());
+  if (need > bm->available() - revived)
+    return fail(PA_ERR_NO_BLOCKS, "pa_bm_add_seq_prompt: prompt needs %lld new blocks, %lld available",
+                (long long)need, (long long)(bm->available() - revived));
+  Seq s;
+  s.track = bm->caching;
+  if (bm->caching) {
+    bm->queried += n / kBlock;
+    bm->hits += static_cast<int64_t>(hit.size());
+  }
+  for (int32_t b : hit) {
+    if (bm->dev.ref[b] == 0) bm->revive(b);
+    bm->dev.ref[b] += 1;
+    s.table.push_back(b);
+  }
+  const int32_t nc = kBlock * static_cast<int32_t>(hit.size());
+  s.len = nc;
+  if (s.track) s.toks.assign(tokens, tokens + nc);
+  s.last_key = parent;
+  for (int32_t p = 0; p < nc; ++p)
+    slots[p] = static_cast<int64_t>(s.table[p / kBlock]) * kBlock + p % kBlock;
+  Seq& stored = bm->seqs.emplace(seq_id, std::move(s)).first->second;
+  int32_t cs = -1, cd = -1;
+  for (int32_t p = nc; p < n; ++p) {
+    slots[p] = bm->append_one(stored, &cs, &cd);
+    bm->note_token(stored, tokens[p]);
+  }
+  *num_cached = nc;
+  return PA_OK;
+}
+
+pa_status pa_bm_cache_stats(const pa_bm* bm, int64_t* queried_blocks, int64_t* hit_blocks,
+                            int32_t* registered_blocks, int32_t* evictable_blocks) {
+  if (!bm || !queried_blocks || !hit_blocks || !registered_blocks || !evictable_blocks)
+    return fail(PA_ERR_INVALID_ARG, "pa_bm_cache_stats: null argument");
+  *queried_blocks = bm->queried;
+  *hit_blocks = bm->hits;
+  *registered_blocks = static_cast<int32_t>(bm->cache.size());
+  *evictable_blocks = static_cast<int32_t>(bm->lru.size());
   return PA_OK;
 }
 
@@ -254,12 +461,14 @@ pa_status pa_bm_append_batch(pa_bm* bm, const int64_t* seq_ids, int32_t n,
       }
     }
   }
-  if (need > static_cast<int64_t>(bm->dev.free_q.size()))
-    return fail(PA_ERR_NO_BLOCKS, "pa_bm_append_batch: batch needs %lld blocks, %zu free",
-                (long long)need, bm->dev.free_q.size());
+  if (need > bm->available())
+    return fail(PA_ERR_NO_BLOCKS, "pa_bm_append_batch: batch needs %lld blocks, %lld available",
+                (long long)need, (long long)bm->available());
   int32_t np = 0;
   for (int32_t i = 0; i < n; ++i) {
     int32_t src = -1, dst = -1;
+    ss[i]->track = false;                // token ids unknown
+    ss[i]->toks.clear();
     slots[i] = bm->append_one(*ss[i], &src, &dst);
     if (src >= 0) {
       cow_pairs[2 * np] = src;
@@ -277,9 +486,12 @@ pa_status pa_bm_free_seq(pa_bm* bm, int64_t seq_id) {
   if (it == bm->seqs.end())
     return fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_free_seq: unknown sequence %lld",
                 (long long)seq_id);
-  Pool& pool = it->second.on_host ? bm->host : bm->dev;
   for (int32_t b : it->second.table) {
-    if (--pool.ref[b] == 0) pool.free_q.push_back(b);
+    if (it->second.on_host) {
+      if (--bm->host.ref[b] == 0) bm->host.free_q.push_back(b);
+    } else if (--bm->dev.ref[b] == 0) {
+      bm->release(b);
+    }
   }
   bm->seqs.erase(it);
   return PA_OK;
@@ -317,15 +529,21 @@ pa_status move_seqs(pa_bm* bm, const int64_t* seq_ids, int32_t n, bool to_host,
   for (Seq* s : ss)
     for (int32_t b : s->table)
       if (mapping.emplace(b, -1).second) order.push_back(b);
-  if (order.size() > dst.free_q.size())
-    return fail(PA_ERR_NO_BLOCKS, "%s: %zu blocks to move, %zu free", fn, order.size(),
-                dst.free_q.size());
+  const int64_t room = to_host ? static_cast<int64_t>(bm->host.free_q.size()) : bm->available();
+  if (static_cast<int64_t>(order.size()) > room)
+    return fail(PA_ERR_NO_BLOCKS, "%s: %zu blocks to move, %lld available", fn, order.size(),
+                (long long)room);
   if (static_cast<int64_t>(order.size()) > pairs_cap)
     return fail(PA_ERR_INVALID_ARG, "%s: pairs buffer holds %d pairs, %zu needed", fn,
                 pairs_cap, order.size());
   for (size_t k = 0; k < order.size(); ++k) {
-    const int32_t d = dst.free_q.front();
-    dst.free_q.pop_front();
+    int32_t d;
+    if (to_host) {
+      d = dst.free_q.front();
+      dst.free_q.pop_front();
+    } else {
+      d = bm->pop();
+    }
     dst.ref[d] = 0;
     mapping[order[k]] = d;
     pairs[2 * k] = order[k];
@@ -335,7 +553,10 @@ pa_status move_seqs(pa_bm* bm, const int64_t* seq_ids, int32_t n, bool to_host,
     for (int32_t& b : s->table) {
       const int32_t d = mapping[b];
       dst.ref[d] += 1;
-      if (--src.ref[b] == 0) src.free_q.push_back(b);
+      if (--src.ref[b] == 0) {
+        if (to_host) bm->release(b);
+        else src.free_q.push_back(b);
+      }
       b = d;
     }
     s->on_host = to_host;
@@ -378,7 +599,7 @@ pa_status pa_bm_is_swapped(const pa_bm* bm, int64_t seq_id, int32_t* swapped) {
 }
 
 int32_t pa_bm_num_free(const pa_bm* bm) {
-  return bm ? static_cast<int32_t>(bm->dev.free_q.size()) : -1;
+  return bm ? static_cast<int32_t>(bm->available()) : -1;
 }
 
 int32_t pa_bm_refcount(const pa_bm* bm, int32_t block) {

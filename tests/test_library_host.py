@@ -388,3 +388,83 @@ def test_swap_blocks_rejects_pageable_host_memory():
     st = pk.lib.pa_swap_blocks(ctypes.byref(d.c), p, p, p, p, p, 1, None)
     assert st == -1 and b"pinned" in pk.lib.pa_last_error()
     assert pk.lib.pa_swap_blocks(ctypes.byref(d.c), p, p, p, p, p, 0, None) == 0
+
+
+def _apply_prefix(bm, op, args):
+    try:
+        if op == "prompt":
+            slots, nc = bm.add_seq_prompt(*args)
+            return None, ([int(x) for x in slots], int(nc))
+        if op == "ids":
+            slots, pair = bm.append_token_ids(*args)
+            return None, ([int(x) for x in slots], pair)
+        if op == "plain":
+            slots, pair = bm.append_tokens(*args)
+            return None, ([int(x) for x in slots], pair)
+        if op == "free":
+            bm.free_seq(args[0])
+            return None, None
+        if op == "fork":
+            bm.fork(*args)
+            return None, None
+        if op in ("out", "in"):
+            pairs = (bm.swap_out if op == "out" else bm.swap_in)(list(args))
+            return None, [tuple(int(x) for x in p) for p in pairs]
+    except (oracle.NoBlocks, oracle.UnknownSeq, oracle.SeqExists, oracle.Swapped,
+            ValueError) as e:
+        return type(e).__name__, None
+    except pk.PagedKVError as e:
+        return _ERR_SWAP[e.status], None
+    raise AssertionError(op)
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3, 4])
+def test_cpp_prefix_cache_matches_oracle_under_random_scripts(seed):
+    rng = np.random.default_rng(seed)
+    N, H = 80, 40
+    order = rng.permutation(N)
+    ref = oracle.RefBlockManager(N, free_order=order, num_host_blocks=H)
+    cpp = pk.BlockManager(N, free_order=order, num_host_blocks=H)
+    ref.enable_prefix_caching()
+    cpp.enable_prefix_caching()
+    prefixes = [[int(x) for x in rng.integers(-5, 40, int(rng.integers(0, 90)))] for _ in range(5)]
+    live, nxt = [], 0
+    for step in range(2500):
+        r = int(rng.integers(0, 12))
+        pick = live[int(rng.integers(len(live)))] if live else 0
+        if r <= 3 or not live:
+            toks = prefixes[int(rng.integers(0, 5))] + [int(x) for x in rng.integers(-5, 40, int(rng.integers(0, 30)))]
+            op, args = "prompt", (nxt, toks)
+        elif r == 4:
+            op, args = "free", (pick,)
+        elif r == 5:
+            op, args = "fork", (pick, nxt)
+        elif r == 6:
+            op, args = "out", (pick,)
+        elif r == 7:
+            op, args = "in", (pick,)
+        elif r == 8:
+            op, args = "plain", (pick, int(rng.integers(0, 20)))
+        else:
+            op, args = "ids", (pick, [int(x) for x in rng.integers(-5, 40, int(rng.integers(0, 25)))])
+        e1, r1 = _apply_prefix(ref, op, args)
+        e2, r2 = _apply_prefix(cpp, op, args)
+        assert (e1, r1) == (e2, r2), (step, op, args)
+        if e1 is None:
+            if op in ("prompt", "fork"):
+                live.append(nxt)
+                nxt += 1
+            elif op == "free":
+                live.remove(pick)
+        assert ref.num_free() == cpp.num_free()
+        assert ref.cache_stats() == cpp.cache_stats(), step
+        dev = [s for s in live if not ref.is_swapped(s)]
+        assert _cpp_tables(cpp, dev, cap=200) == {s: (ref.table(s), ref.length(s)) for s in dev}
+        if step % 50 == 0:
+            ref.check_invariants()
+            assert [cpp.refcount(b) for b in range(N)] == ref.ref
+    for s in live:
+        ref.free_seq(s)
+        cpp.free_seq(s)
+    assert cpp.num_free() == ref.num_free() == N
+    assert ref.cache_stats() == cpp.cache_stats()

@@ -322,3 +322,67 @@ def small_random(seed: int, B: int, Hq: int, Hkv: int, D: int, fmt: str,
     return Workload(f"small-{fmt}-s{seed}", seed, B, Hq, Hkv, D, fmt,
                     "f32" if fmt == "f32" else "bf16", lens, nb, perm, k, v,
                     rs, rp, q, np.float32(1.0 / math.sqrt(D)), ks, vs)
+
+
+@dataclasses.dataclass
+class PrefixWorkload:
+    """Requests that share a system prompt (retrieval-augmented generation,
+    chat with a common system prompt): request r's prompt is the shared
+    prefix tokens followed by its own question tokens.  KV rows of a prefix
+    position are the same for every request (the KV of a position depends on
+    the tokens before it, and those are shared), question rows are drawn per
+    request."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    fmt: str
+    prefix_ids: np.ndarray           # int32 [P]
+    question_ids: List[np.ndarray]   # int32 [Q_r] per request
+    prefix_k: np.ndarray             # [P, Hkv, D] source rows
+    prefix_v: np.ndarray
+    question_k: List[np.ndarray]     # [Q_r, Hkv, D] per request
+    question_v: List[np.ndarray]
+    q: np.ndarray                    # [B, Hq, D]
+    num_blocks: int
+    free_order: np.ndarray
+    scale: np.float32
+
+    def prompt(self, r: int) -> np.ndarray:
+        return np.concatenate([self.prefix_ids, self.question_ids[r]]).astype(np.int32)
+
+    def rows(self, r: int):
+        return (np.concatenate([self.prefix_k, self.question_k[r]]),
+                np.concatenate([self.prefix_v, self.question_v[r]]))
+
+
+def prefix_batch(seed: int, B: int, prefix: int, qmin: int, qmax: int, Hq: int = 32,
+                 Hkv: int = 8, D: int = 128, fmt: str = "bf16", vocab: int = 32000,
+                 rows: bool = True) -> PrefixWorkload:
+    """Draw order: prefix ids, question lengths U{qmin..qmax}, question ids,
+    pool permutation, prefix K, prefix V, per request question K then V, q.
+    The pool holds every request's private blocks plus the prefix once,
+    times 1.25, plus 2 blocks per request of headroom."""
+    rng = np.random.default_rng(seed)
+    pid = rng.integers(0, vocab, prefix).astype(np.int32)
+    qlen = rng.integers(qmin, qmax + 1, B)
+    qid = [rng.integers(0, vocab, int(n)).astype(np.int32) for n in qlen]
+    full = prefix // BLOCK
+    need = full + sum(-(-(prefix + int(n)) // BLOCK) - full for n in qlen)
+    nb = int(math.ceil(1.25 * need)) + 2 * B
+    perm = rng.permutation(nb).astype(np.int32)
+    bf16 = fmt != "f32"
+    if rows:
+        pk_ = _rows(rng, (prefix, Hkv, D), "normal", bf16)
+        pv_ = _rows(rng, (prefix, Hkv, D), "normal", bf16)
+        qk, qv = [], []
+        for n in qlen:
+            qk.append(_rows(rng, (int(n), Hkv, D), "normal", bf16))
+            qv.append(_rows(rng, (int(n), Hkv, D), "normal", bf16))
+        q = _rows(rng, (B, Hq, D), "normal", bf16)
+    else:
+        pk_ = pv_ = q = None
+        qk = qv = []
+    return PrefixWorkload(f"prefix-{fmt}-b{B}-p{prefix}", B, Hq, Hkv, D, fmt, pid, qid, pk_, pv_,
+                          qk, qv, q, nb, perm, np.float32(1.0 / math.sqrt(D)))
