@@ -163,3 +163,68 @@ def test_pins_catch_a_planted_off_by_one_in_the_visible_length(monkeypatch):
                         lambda L, T_, i: max(0, int(L) - int(T_) + int(i)))
     wrong = oracle.chunk.decode_chunk(q, "f32", kc, vc, "f32", bt, cl, w.scale)
     assert np.abs(wrong - right).max() > 1e-3
+
+
+# ---------------------------------------------------------------- sliding window
+@pytest.mark.parametrize("W,T", [(1, 1), (5, 1), (17, 3), (40, 4), (1000, 2)])
+def test_window_matches_torch_sdpa_with_band_mask(W, T):
+    """SDPA over the generator's rows with the band mask: chunk token i (at
+    position p = L - T + i) sees t iff p - W < t <= p."""
+    G = 2
+    w = workloads.small_random(90 + W, 4, 4, 2, 32, "f32", 120, T)
+    q = workloads.chunk_queries(np.random.default_rng(W), w.B, T, w.Hq, w.D, "f32")
+    bm, kc, vc, bt, cl, _ = fill_sequential(w)
+    out = oracle.decode_chunk(q, "f32", kc, vc, "f32", bt, cl, w.scale, window=W)
+    for s in range(w.B):
+        L = int(cl[s])
+        kr, vr = contiguous_rows(w, s)
+        K = torch.from_numpy(np.asarray(kr, np.float64)).permute(1, 0, 2).repeat_interleave(G, 0)
+        V = torch.from_numpy(np.asarray(vr, np.float64)).permute(1, 0, 2).repeat_interleave(G, 0)
+        Q = torch.from_numpy(np.asarray(q[s], np.float64)).permute(1, 0, 2)
+        p = (L - T + torch.arange(T))[:, None]
+        t = torch.arange(L)[None, :]
+        mask = (t <= p) & (t > p - W)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            Q.unsqueeze(0), K.unsqueeze(0), V.unsqueeze(0), attn_mask=mask,
+            scale=float(w.scale)).squeeze(0).permute(1, 0, 2).numpy()
+        np.testing.assert_allclose(out[s], ref, rtol=0, atol=1e-12)
+
+
+def test_window_of_one_returns_the_tokens_own_value_row():
+    T = 3
+    w, q = _chunk_case(91, fmt="f32", T=T, lens=np.array([3, 20, 33]))
+    bm, kc, vc, bt, cl, _ = fill_sequential(w)
+    out = oracle.decode_chunk(q, "f32", kc, vc, "f32", bt, cl, w.scale, window=1)
+    G = w.Hq // w.Hkv
+    for s in range(w.B):
+        _, vr = contiguous_rows(w, s)
+        for i in range(T):
+            p = int(cl[s]) - T + i
+            for h in range(w.Hq):
+                np.testing.assert_array_equal(out[s, i, h], np.float64(vr[p, h // G]))
+
+
+def test_window_covering_the_context_changes_nothing_and_sampled_rows_agree():
+    T = 2
+    w, q = _chunk_case(92, fmt="bf16", B=4, Hq=8, Hkv=2, D=16, T=T, max_len=60)
+    bm, kc, vc, bt, cl, _ = fill_sequential(w)
+    full = oracle.decode_chunk(q, "bf16", kc, vc, "bf16", bt, cl, w.scale)
+    wide = oracle.decode_chunk(q, "bf16", kc, vc, "bf16", bt, cl, w.scale, window=60)
+    np.testing.assert_array_equal(full, wide)
+    narrow = oracle.decode_chunk(q, "bf16", kc, vc, "bf16", bt, cl, w.scale, window=9)
+    picks = [(0, 0, 0), (1, 1, 7), (3, 0, 2)]
+    rows = oracle.chunk_rows(q, "bf16", kc, vc, "bf16", bt, cl, w.scale, picks=picks, window=9)
+    for r, (s, i, h) in zip(rows, picks):
+        np.testing.assert_array_equal(r, narrow[s, i, h])
+
+
+def test_pins_catch_a_planted_off_by_one_in_the_window(monkeypatch):
+    T, W = 2, 7
+    w = workloads.small_random(93, 3, 4, 2, 16, "f32", 50, 20)
+    q = workloads.chunk_queries(np.random.default_rng(93), w.B, T, w.Hq, w.D, "f32")
+    bm, kc, vc, bt, cl, _ = fill_sequential(w)
+    right = oracle.decode_chunk(q, "f32", kc, vc, "f32", bt, cl, w.scale, window=W)
+    monkeypatch.setattr(oracle.chunk, "window_start",
+                        lambda n, window: max(0, int(n) - int(window) + 1))
+    wrong = oracle.chunk.decode_chunk(q, "f32", kc, vc, "f32", bt, cl, w.scale, window=W)
+    assert np.abs(wrong - right).max() > 1e-3
