@@ -60,9 +60,14 @@ decode step above.  The roofline takes the unique KV bytes a call reads
 are reported beside them, with the block manager's hit rate and that of a
 simulated multi-turn chat.
 
+With ``--window W`` the decode (or chunk) step attends only the last W
+positions of each context (pa_decode_window); the roofline's algorithmic
+bytes are then the positions the window keeps, min(L, W + T - 1) per
+sequence.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers N]
-                      [--chunk T | --swap | --prefix] [--no-cpu-baseline]
-                      [--copy-calibration MIB]
+                      [--chunk T | --swap | --prefix] [--window W]
+                      [--no-cpu-baseline] [--copy-calibration MIB]
 
 --copy-calibration MIB ends the run with plain device copies of MIB MiB, the
 reference a hardware-counter run scales FETCH_SIZE / WRITE_SIZE by.
@@ -528,6 +533,8 @@ def main():
                     help="new tokens per sequence per step (1 = decode)")
     ap.add_argument("--swap", action="store_true",
                     help="measure swapping sequences out to pinned host memory and back")
+    ap.add_argument("--window", type=int, default=0, metavar="W",
+                    help="sliding window of W positions (0: none)")
     ap.add_argument("--prefix", action="store_true",
                     help="decode a batch that shares a system prompt through prefix caching")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -644,14 +651,18 @@ def main():
             pk.write_kv(desc, kc[l], vc[l], k_new[l], v_new[l], d_slots, stream=stream)
             if ev_pairs is not None:
                 ev_pairs[l][0].record(stream)
-            if T == 1:
+            if T == 1 and not args.window:
                 pk.decode(desc, kc[l], vc[l], q[l], out[l], d_bt, d_cl, max_len,
                           float(w.scale), workspace, stream=stream)
             else:
-                pk.decode_chunk(desc, kc[l], vc[l], q[l], out[l], d_bt, d_cl, max_len,
-                                float(w.scale), workspace, stream=stream)
+                qq = q[l] if T > 1 else q[l].view(B, 1, Hq, D)
+                oo = out[l] if T > 1 else out[l].view(B, 1, Hq, D)
+                pk.decode_chunk(desc, kc[l], vc[l], qq, oo, d_bt, d_cl, max_len,
+                                float(w.scale), workspace, stream=stream, window=args.window)
             if ev_pairs is not None:
                 ev_pairs[l][1].record(stream)
+        if args.window:
+            return _kv_bytes(np.minimum(lens, args.window + T - 1), Hkv, D, 2)
         return _kv_bytes(lens, Hkv, D, 2)
 
     _log(f"bench: {NL} layers x {w.num_blocks} blocks, warmup {args.warmup}, steps {args.steps}")
@@ -679,7 +690,7 @@ def main():
     mean_kv = statistics.mean(kv_per_call)
     achieved = mean_kv / mean_dec_s / 1e9
     steps_s = wall / args.steps
-    traffic = _traffic_per_call(mean_kv, T)
+    traffic = None if args.window else _traffic_per_call(mean_kv, T)
     _log(f"bench: {'pa_decode' if T == 1 else 'pa_decode_chunk'} mean {mean_dec_s * 1e6:.1f} us (p10 "
          f"{np.percentile(dec_ms, 10) * 1e3:.1f}, p90 {np.percentile(dec_ms, 90) * 1e3:.1f}), "
          f"{achieved:.0f} GB/s; step {steps_s * 1e3:.3f} ms")
@@ -689,6 +700,8 @@ def main():
                 "blocks, lognormal context (median 512, sigma 0.8, [16, 4096])")
     if T > 1:
         workload = workload.replace("GQA decode layer", f"GQA layer, {T}-token chunk per sequence")
+    if args.window:
+        workload += f", sliding window of {args.window} positions"
     res = {
         "metric": METRIC if T == 1 else METRIC_CHUNK,
         "value": round(B * T * NL * args.steps / wall, 1),
@@ -719,7 +732,8 @@ def main():
         "decode_us_p10": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
         "decode_us_p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),
         "roofline": {
-            "kernel": ("decode_stream_kernel (pa_decode: one persistent kernel)" if T == 1 else
+            "kernel": ("decode_stream_kernel (pa_decode_window)" if args.window else
+                       "decode_stream_kernel (pa_decode: one persistent kernel)" if T == 1 else
                        "decode_stream_kernel (pa_decode_chunk: one persistent kernel per "
                        f"{16 // (Hq // Hkv)}-token pass)"),
             "bound": "hbm",
@@ -738,7 +752,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         _log(f"bench: copy calibration {n} bytes x 3")
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.window:
         _log("bench: timing the CPU oracle")
         res["cpu_baseline"] = cpu_baseline(w, T=T)
     print(json.dumps(res), flush=True)

@@ -204,6 +204,24 @@ pa_status pa_decode_chunk(const pa_cache_desc* c, const void* k_cache,
                           int32_t num_seqs, int32_t num_q_heads, float scale,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * pa_decode_window -- pa_decode_chunk with a sliding window (ybb.press §7.2:
+ * sliding-window attention for long contexts): with window = W > 0 a token
+ * at position p attends only positions max(0, p - W + 1) .. p (its own and
+ * the W - 1 before it), so a chunk token i of a length-L context sees
+ * max(0, L - T + i + 1 - W) .. L - T + i.  window = 0 is no window.  Blocks
+ * wholly before every chunk token's window are not read.  Same arguments,
+ * workspace (pa_decode_chunk_workspace_bytes) and errors as pa_decode_chunk;
+ * window < 0 is PA_ERR_INVALID_ARG.
+ */
+pa_status pa_decode_window(const pa_cache_desc* c, const void* k_cache,
+                           const void* v_cache, const void* q, int32_t q_dtype,
+                           void* out, int32_t chunk_len, int32_t window,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t max_context_len,
+                           int32_t num_seqs, int32_t num_q_heads, float scale,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Host block manager (plain host memory, no GPU calls).  One owner; not
  * thread-safe.  Policy: the free pool is a FIFO queue initialised from

@@ -33,6 +33,8 @@ SIGNATURES = {
     "pa_decode_workspace_bytes": (c_sz, [P_desc, c_i32, c_i32, c_i32]),
     "pa_decode_workspace_init": (c_i32, [c_vp, c_sz, c_vp]),
     "pa_decode_chunk_workspace_bytes": (c_sz, [P_desc, c_i32, c_i32, c_i32, c_i32]),
+    "pa_decode_window": (c_i32, [P_desc, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32, c_vp, c_i32,
+                                 c_vp, c_i32, c_i32, c_i32, c_f32, c_vp, c_sz, c_vp]),
     "pa_decode_chunk": (c_i32, [P_desc, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_vp, c_i32, c_vp,
                                 c_i32, c_i32, c_i32, c_f32, c_vp, c_sz, c_vp]),
     "pa_decode": (c_i32, [P_desc, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_vp, c_i32,

@@ -170,9 +170,11 @@ def new_chunk_workspace(desc: CacheDesc, num_seqs: int, num_q_heads: int, chunk_
 def decode_chunk(desc: CacheDesc, k_cache: torch.Tensor, v_cache: torch.Tensor,
                  q: torch.Tensor, out: torch.Tensor, block_tables: torch.Tensor,
                  context_lens: torch.Tensor, max_context_len: int, scale: float,
-                 workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """pa_decode_chunk: attention of T = q.shape[1] new tokens per sequence,
-    causal inside the chunk; q and out are [B, T, Hq, D]."""
+                 workspace: Optional[torch.Tensor] = None, stream=None,
+                 window: int = 0) -> torch.Tensor:
+    """pa_decode_chunk (pa_decode_window when ``window`` > 0): attention of
+    T = q.shape[1] new tokens per sequence, causal inside the chunk; q and
+    out are [B, T, Hq, D]."""
     B, T, Hq, D = q.shape
     if out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("out must have q's shape and dtype")
@@ -182,6 +184,15 @@ def decode_chunk(desc: CacheDesc, k_cache: torch.Tensor, v_cache: torch.Tensor,
         raise ValueError("block_tables must be [B, max_blocks] and context_lens [B]")
     if workspace is None:
         workspace = new_chunk_workspace(desc, B, Hq, T, max_context_len, q.device)
+    if window:
+        check(lib.pa_decode_window(ctypes.byref(desc.c), _dev(k_cache, "k_cache"),
+                                   _dev(v_cache, "v_cache"), _dev(q, "q"), dtype_code(q.dtype),
+                                   _dev(out, "out"), T, int(window),
+                                   _dev(block_tables, "block_tables"), block_tables.shape[1],
+                                   _dev(context_lens, "context_lens"), int(max_context_len), B,
+                                   Hq, float(scale), _dev(workspace, "workspace"),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+        return out
     check(lib.pa_decode_chunk(ctypes.byref(desc.c), _dev(k_cache, "k_cache"),
                               _dev(v_cache, "v_cache"), _dev(q, "q"), dtype_code(q.dtype),
                               _dev(out, "out"), T, _dev(block_tables, "block_tables"),

@@ -80,6 +80,8 @@ constexpr int kAuxCoherent = 16;        // buffer cache policy sc1: device-coher
 constexpr int kMaxRows = 16;            // fast path: query rows per pass (MFMA columns)
 constexpr float kNoMax = -1e30f;        // running max of a row that has seen no position yet
 constexpr int kOutOfRange = 0x7FFFFF00; // buffer offset past any range: the load reads 0
+constexpr int kSeqBits = 26;            // descriptor word 2: sequence | window start << 26
+constexpr uint32_t kSeqMask = (1u << kSeqBits) - 1;
 
 // DPP controls (GFX9 encoding).
 constexpr int kDppQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]
@@ -173,6 +175,7 @@ struct StreamArgs {
   int num_waves;
   int group;                  // G: query heads per KV head
   int chunk;                  // T: new tokens per sequence
+  int window;                 // W > 0: attend only the last W positions; 0: all
   int t_first;                // first chunk token of this pass
   int rows;                   // query rows of this pass (<= kMaxRows)
   float logit_scale;          // scale * k_scale * log2(e)
@@ -208,6 +211,11 @@ decode_stream_kernel(StreamArgs a) {
   const int R = a.rows;
   const int hq = hkv * G;
   const int slot_floats = (R * (kD + 2) + 3) & ~3; // floats per partial slot (16-byte multiple)
+  // With a window, a (sequence, KV head) segment covers the blocks from the
+  // one holding the first chunk token's window start to the last.
+  const int win = a.window;
+  auto first_blk = [&](int L) -> int { return win > 0 ? max(0, L - nchunk + 1 - win) / kBlock : 0; };
+  auto tiles_of = [&](int L) -> int { return (L + kBlock - 1) / kBlock - first_blk(L); };
   const __amdgpu_buffer_rsrc_t lens_rsrc = make_rsrc(a.context_lens, B * 4);
 
   // ---- 1. total tile count; zero rows of empty sequences s = w (mod waves).
@@ -222,7 +230,7 @@ decode_stream_kernel(StreamArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int s = s0 + 64 * r + lane;
-      c += (L[r] + kBlock - 1) / kBlock;
+      c += tiles_of(L[r]);
       const uint64_t empty = __builtin_amdgcn_ballot_w64(s < B && L[r] == 0 && s % a.num_waves == w);
       for (uint64_t m = empty; m != 0; m &= m - 1) {
         const int se = s0 + 64 * r + __builtin_ctzll(m);
@@ -252,7 +260,7 @@ decode_stream_kernel(StreamArgs a) {
   {
     int base = 0;
     auto scan64 = [&](int s0, int L) {
-      const int c = hkv * ((L + kBlock - 1) / kBlock);
+      const int c = hkv * tiles_of(L);
       const int incl = wave_incl_scan(c, lane);
       const uint64_t m = __builtin_amdgcn_ballot_w64(base + incl > t_begin);
       if (m != 0) {
@@ -273,9 +281,9 @@ decode_stream_kernel(StreamArgs a) {
   }
   if (s_cur < 0 || L_cur <= 0) return;   // lengths changed under us: nothing safe to do
   // tile t_begin is block j0 of KV head g0 of sequence s_cur
-  const int nb0 = (L_cur + kBlock - 1) / kBlock;
+  const int nb0 = tiles_of(L_cur);
   const int g0 = off / nb0;
-  const int j0 = off - g0 * nb0;
+  const int j0 = first_blk(L_cur) + (off - g0 * nb0);
   const int n_total = min(per, T - t_begin);
 
   // q of a segment travels with each ring slot, loaded straight into the
@@ -296,9 +304,12 @@ decode_stream_kernel(StreamArgs a) {
   // word 0: tile index block * Hkv + g (the block's position in the table
   //         while building); word 1: rows to the context's end, min(31, L - 16j)
   //         (the tile's valid rows are min(16, that)) | first << 5 | last << 6 |
-  //         g << 7 | blocks of the sequence << 16; word 2: sequence;
-  // word 3: list index of the segment's first tile.  "first"/"last" mark
-  // the ends of a piece: a segment's ends or the ends of this wave's range.
+  //         g << 7 | tiles of the segment << 16; word 2: sequence | window code
+  // << 26 (0 without a window, else 17 + the first chunk token's window
+  // start relative to the segment's first block, clamped at -16); word 3:
+  // list index of the
+  // segment's first tile.  "first"/"last" mark the ends of a piece: a
+  // segment's ends or the ends of this wave's range.
   __shared__ u32x4_t s_desc_all[kWavesPerGroup][kCap];
   u32x4_t* s_desc = s_desc_all[wig];
   // V tile staging (token-major rows, padded pitch): it turns the V tile's
@@ -316,7 +327,15 @@ decode_stream_kernel(StreamArgs a) {
   constexpr int kSlotBytesMax = kMaxRows * (kD + 2) * 4;
   __shared__ __align__(16) char s_p_all[kWavesPerGroup][2 * kSlotBytesMax];
   char* s_p = s_p_all[wig];
-  int w_s = s_cur, w_g = g0, w_j = j0, w_L = L_cur, w_nb = nb0, w_seg = seg0 + g0 * nb0;
+  int w_s = s_cur, w_g = g0, w_j = j0, w_L = L_cur, w_nb = (L_cur + kBlock - 1) / kBlock;
+  int w_jf = first_blk(L_cur), w_seg = seg0 + g0 * nb0;
+  // The first chunk token's window starts at L - T + 1 - W; a row of chunk
+  // token t starts t later.  Code = that start relative to the segment's
+  // first block, clamped at -16 (rows then cut nothing), plus 17: 1..32.
+  auto lo_code = [&](int L, int jf) -> uint32_t {
+    return win > 0 ? static_cast<uint32_t>(max(L - nchunk + 1 - win - kBlock * jf, -kBlock) + kBlock + 1)
+                   : 0u;
+  };
   // lengths for the walk: from Lr for the first 256 sequences, past them
   // from a window of 64 (lane i -> sequence lwin_base + i) loaded on demand
   int lwin_base = -1, lwin = 0;
@@ -536,23 +555,23 @@ decode_stream_kernel(StreamArgs a) {
     // pass 1: walk the pieces of this round, one lane per tile
     for (int pos = 0; pos < n;) {
       const int span = min(w_nb - w_j, n - pos);
+      const uint32_t word2 = static_cast<uint32_t>(w_s) | (lo_code(w_L, w_jf) << kSeqBits);
       for (int c = lane; c < span; c += 64) {
         const int j = w_j + c;
         const int gpos = done + pos + c;                     // position in the range
         const uint32_t valid = static_cast<uint32_t>(min(31, w_L - kBlock * j));
-        const uint32_t first = (j == 0 || gpos == 0) ? 1u : 0u;
+        const uint32_t first = (j == w_jf || gpos == 0) ? 1u : 0u;
         const uint32_t last = (j == w_nb - 1 || gpos == n_total - 1) ? 1u : 0u;
         s_desc[pos + c] = u32x4_t{static_cast<uint32_t>(j),
                                   valid | (first << 5) | (last << 6) |
                                       (static_cast<uint32_t>(w_g) << 7) |
-                                      (static_cast<uint32_t>(w_nb) << 16),
-                                  static_cast<uint32_t>(w_s), static_cast<uint32_t>(w_seg)};
+                                      (static_cast<uint32_t>(w_nb - w_jf) << 16),
+                                  word2, static_cast<uint32_t>(w_seg)};
       }
       pos += span;
       w_j += span;
       if (w_j == w_nb) {                                     // next segment
-        w_seg += w_nb;
-        w_j = 0;
+        w_seg += w_nb - w_jf;
         if (++w_g == hkv) {                                  // next non-empty sequence
           w_g = 0;
           do {
@@ -560,7 +579,9 @@ decode_stream_kernel(StreamArgs a) {
             w_L = (w_s < B) ? len_of(w_s) : 0;
           } while (w_L == 0 && w_s + 1 < B);
           w_nb = (w_L + kBlock - 1) / kBlock;
+          w_jf = first_blk(w_L);
         }
+        w_j = w_jf;
       }
     }
     // pass 2: block ids from the tables, independent loads per lane
@@ -573,7 +594,7 @@ decode_stream_kernel(StreamArgs a) {
         if (e < n) {
           const u32x4_t d = s_desc[e];
           ids[r] = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(
-              tbl_rsrc, (static_cast<int>(d[2]) * a.max_blocks + static_cast<int>(d[0])) * 4, 0, 0));
+              tbl_rsrc, (static_cast<int>(d[2] & kSeqMask) * a.max_blocks + static_cast<int>(d[0])) * 4, 0, 0));
         }
       }
 #pragma unroll
@@ -596,7 +617,7 @@ decode_stream_kernel(StreamArgs a) {
         const u32x4_t d = s_desc[t];
         const uint32_t tile = __builtin_amdgcn_readfirstlane(d[0]);
         const uint32_t info = __builtin_amdgcn_readfirstlane(d[1]);
-        const int s = __builtin_amdgcn_readfirstlane(static_cast<int>(d[2]));
+        const int s = __builtin_amdgcn_readfirstlane(static_cast<int>(d[2] & kSeqMask));
         k_nrec = min(static_cast<int>(info & 31u), kBlock) * kRowBytes;   // rows past the context read 0
         v_nrec = k_nrec;
         tile_off = static_cast<int64_t>(tile) * kTileBytes;
@@ -660,10 +681,18 @@ decode_stream_kernel(StreamArgs a) {
       }
       float x[4];
       const int lim = rows_left - mshift;                    // tile rows this query row may see
+      // window start: tile rows below `lo` are cut (never, without a window)
+      const uint32_t wcode =
+          static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(d[2]))) >> kSeqBits;
+      int lo = -kBlock;
+      if (wcode != 0u) {
+        const int j_local = t_begin + done + t - __builtin_amdgcn_readfirstlane(static_cast<int>(d[3]));
+        lo = static_cast<int>(wcode) - (kBlock + 1) + t_row - kBlock * j_local;
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         x[r] = acc[r] * a.logit_scale;
-        if (4 * quad + r >= lim) x[r] = -INFINITY;
+        if (4 * quad + r >= lim || 4 * quad + r < lo) x[r] = -INFINITY;
       }
 
       // ---- lazy running max: moved only when a logit exceeds it by more
@@ -723,7 +752,7 @@ decode_stream_kernel(StreamArgs a) {
       }
 
       if (info & 64u)                                        // a piece ends here
-        finalize(__builtin_amdgcn_readfirstlane(static_cast<int>(d[2])),
+        finalize(__builtin_amdgcn_readfirstlane(static_cast<int>(d[2] & kSeqMask)),
                  static_cast<int>((info >> 7) & 511u),
                  __builtin_amdgcn_readfirstlane(static_cast<int>(d[3])),
                  static_cast<int>(info >> 16));
@@ -791,14 +820,15 @@ zero_fill_kernel(uint32_t* p, int64_t n_words) {
 // query row, sequence); one token at a time, dot product by a wave
 // reduction, exact online softmax.  Used for fp32 caches and shapes the fast
 // path does not cover.  Query row y = i * hq + h is chunk token i of query
-// head h; it sees the first L - chunk + 1 + i positions.
+// head h; it sees positions below n = L - chunk + 1 + i, from max(0, n - W)
+// with a window of W > 0.  A partition with nothing to see records l = 0.
 template <int kD, int kFmt, bool kOutF32>
 __global__ void __launch_bounds__(64)
 decode_simple_kernel(const char* __restrict__ k_cache, const char* __restrict__ v_cache,
                      const void* __restrict__ q, const int32_t* __restrict__ block_tables,
                      const int32_t* __restrict__ context_lens, int max_blocks, int hkv,
-                     int group, int hq, int chunk, float logit_scale, float v_scale,
-                     PartOut po) {
+                     int group, int hq, int chunk, int window, float logit_scale,
+                     float v_scale, PartOut po) {
   constexpr int kPer = kD / 64;
   const int part = blockIdx.x;
   const int y = blockIdx.y;
@@ -834,8 +864,8 @@ decode_simple_kernel(const char* __restrict__ k_cache, const char* __restrict__ 
     else
       qv[i] = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(q)[orow + lane + 64 * i]) << 16);
   }
-  const int t0 = part * kPartTokens;
-  const int t1 = min(L, t0 + kPartTokens);
+  const int t0 = max(part * kPartTokens, window > 0 ? L - window : 0);
+  const int t1 = min(L, part * kPartTokens + kPartTokens);
   float m = -INFINITY, l = 0.f, o[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) o[i] = 0.f;
@@ -857,13 +887,14 @@ decode_simple_kernel(const char* __restrict__ k_cache, const char* __restrict__ 
       o[i] = fmaf(p, elem(v_cache, base + lane + 64 * i), o[i] * a);
     m = mn;
   }
+  const float inv = (l > 0.f) ? v_scale / l : 0.f;
   if (nparts == 1) {
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) store_out<kOutF32>(po.out, orow + lane + 64 * i, o[i] / l * v_scale);
+    for (int i = 0; i < kPer; ++i) store_out<kOutF32>(po.out, orow + lane + 64 * i, o[i] * inv);
   } else {
     const int64_t r = (static_cast<int64_t>(s) * gridDim.y + y) * po.num_parts + part;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) po.ws_o[r * kD + lane + 64 * i] = o[i] / l * v_scale;
+    for (int i = 0; i < kPer; ++i) po.ws_o[r * kD + lane + 64 * i] = o[i] * inv;
     if (lane == 0) {
       po.ws_ml[2 * r] = m;
       po.ws_ml[2 * r + 1] = l;
@@ -888,7 +919,8 @@ reduce_kernel(const int32_t* __restrict__ context_lens, int hq, int chunk, PartO
   for (int i = 0; i < nparts; ++i) M = fmaxf(M, po.ws_ml[2 * (r0 + i)]);
   float den = 0.f, num = 0.f;
   for (int i = 0; i < nparts; ++i) {
-    const float a = __builtin_amdgcn_exp2f(po.ws_ml[2 * (r0 + i)] - M) * po.ws_ml[2 * (r0 + i) + 1];
+    const float li = po.ws_ml[2 * (r0 + i) + 1];
+    const float a = (li > 0.f) ? __builtin_amdgcn_exp2f(po.ws_ml[2 * (r0 + i)] - M) * li : 0.f;
     den += a;
     num = fmaf(a, po.ws_o[(r0 + i) * kD + d], num);
   }
@@ -898,13 +930,13 @@ reduce_kernel(const int32_t* __restrict__ context_lens, int hq, int chunk, PartO
 template <int kD>
 void launch_simple(int fmt, dim3 grid, hipStream_t st, const char* kc, const char* vc,
                    const void* q, const int32_t* bt, const int32_t* cl, int maxb, int hkv,
-                   int G, int hq, int T, float ls, float vs, PartOut po) {
+                   int G, int hq, int T, int W, float ls, float vs, PartOut po) {
   if (fmt == PA_F32)
-    decode_simple_kernel<kD, PA_F32, true><<<grid, 64, 0, st>>>(kc, vc, q, bt, cl, maxb, hkv, G, hq, T, ls, vs, po);
+    decode_simple_kernel<kD, PA_F32, true><<<grid, 64, 0, st>>>(kc, vc, q, bt, cl, maxb, hkv, G, hq, T, W, ls, vs, po);
   else if (fmt == PA_BF16)
-    decode_simple_kernel<kD, PA_BF16, false><<<grid, 64, 0, st>>>(kc, vc, q, bt, cl, maxb, hkv, G, hq, T, ls, vs, po);
+    decode_simple_kernel<kD, PA_BF16, false><<<grid, 64, 0, st>>>(kc, vc, q, bt, cl, maxb, hkv, G, hq, T, W, ls, vs, po);
   else
-    decode_simple_kernel<kD, PA_FP8_E4M3, false><<<grid, 64, 0, st>>>(kc, vc, q, bt, cl, maxb, hkv, G, hq, T, ls, vs, po);
+    decode_simple_kernel<kD, PA_FP8_E4M3, false><<<grid, 64, 0, st>>>(kc, vc, q, bt, cl, maxb, hkv, G, hq, T, W, ls, vs, po);
 }
 
 
@@ -985,9 +1017,11 @@ size_t workspace_bytes_for(const pa_cache_desc* c, int32_t num_seqs, int32_t num
   return general_workspace_bytes(num_seqs, num_q_heads, T, c->head_dim, max_context_len);
 }
 
-// pa_decode (T = 1) and pa_decode_chunk: one implementation.
+// pa_decode (T = 1, no window), pa_decode_chunk and pa_decode_window: one
+// implementation.
 pa_status attend(const char* fn, const pa_cache_desc* c, const void* k_cache,
                  const void* v_cache, const void* q, int32_t q_dtype, void* out, int32_t T,
+                 int32_t W,
                  const int32_t* block_tables, int32_t max_blocks_per_seq,
                  const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs,
                  int32_t num_q_heads, float scale, void* workspace, size_t workspace_bytes,
@@ -999,6 +1033,7 @@ pa_status attend(const char* fn, const pa_cache_desc* c, const void* k_cache,
     return fail(PA_ERR_INVALID_ARG, "%s: negative size", fn);
   if (T < 1 || T > PA_MAX_CHUNK)
     return fail(PA_ERR_INVALID_ARG, "%s: chunk_len %d (1..%d)", fn, T, PA_MAX_CHUNK);
+  if (W < 0) return fail(PA_ERR_INVALID_ARG, "%s: window %d < 0", fn, W);
   if (num_q_heads % hkv != 0)
     return fail(PA_ERR_INVALID_ARG, "%s: %d query heads not a multiple of %d KV heads", fn,
                 num_q_heads, hkv);
@@ -1019,7 +1054,7 @@ pa_status attend(const char* fn, const pa_cache_desc* c, const void* k_cache,
   const int tpp = tokens_per_pass(G, T);
   const int64_t max_tiles = static_cast<int64_t>(hkv) * num_seqs *
                             ((static_cast<int64_t>(max_context_len) + kBlock - 1) / kBlock);
-  if (fast && (max_tiles >= (int64_t{1} << 30) ||
+  if (fast && (max_tiles >= (int64_t{1} << 30) || num_seqs > static_cast<int32_t>(kSeqMask) ||
                static_cast<int64_t>(max_blocks_per_seq) * 4 >= (int64_t{1} << 31) ||
                (static_cast<int64_t>(T - 1) * num_q_heads + G) * D * 2 >= (int64_t{1} << 30)))
     return fail(PA_ERR_UNSUPPORTED, "%s: %lld tiles in one call (limit 2^30)", fn,
@@ -1066,6 +1101,7 @@ pa_status attend(const char* fn, const pa_cache_desc* c, const void* k_cache,
     a.num_waves = static_cast<int>(nw);
     a.group = G;
     a.chunk = T;
+    a.window = W;
     a.logit_scale = logit_scale;
     a.v_scale = vscale;
     // one pass per tpp chunk tokens; each pass leaves the counters zeroed
@@ -1091,10 +1127,10 @@ pa_status attend(const char* fn, const pa_cache_desc* c, const void* k_cache,
     dim3 grid(P, rows, num_seqs);
     if (D == 128)
       launch_simple<128>(fmt, grid, s, kc, vc, q, block_tables, context_lens,
-                         max_blocks_per_seq, hkv, G, num_q_heads, T, logit_scale, vscale, po);
+                         max_blocks_per_seq, hkv, G, num_q_heads, T, W, logit_scale, vscale, po);
     else
       launch_simple<64>(fmt, grid, s, kc, vc, q, block_tables, context_lens,
-                        max_blocks_per_seq, hkv, G, num_q_heads, T, logit_scale, vscale, po);
+                        max_blocks_per_seq, hkv, G, num_q_heads, T, W, logit_scale, vscale, po);
   }
   st = launch_status(fn);
   if (st != PA_OK) return st;
@@ -1150,7 +1186,7 @@ extern "C" pa_status pa_decode(const pa_cache_desc* c, const void* k_cache, cons
                                const int32_t* context_lens, int32_t max_context_len,
                                int32_t num_seqs, int32_t num_q_heads, float scale,
                                void* workspace, size_t workspace_bytes, void* stream) {
-  return attend("pa_decode", c, k_cache, v_cache, q, q_dtype, out, 1, block_tables,
+  return attend("pa_decode", c, k_cache, v_cache, q, q_dtype, out, 1, 0, block_tables,
                 max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads, scale,
                 workspace, workspace_bytes, stream);
 }
@@ -1162,7 +1198,19 @@ extern "C" pa_status pa_decode_chunk(const pa_cache_desc* c, const void* k_cache
                                      int32_t max_context_len, int32_t num_seqs,
                                      int32_t num_q_heads, float scale, void* workspace,
                                      size_t workspace_bytes, void* stream) {
-  return attend("pa_decode_chunk", c, k_cache, v_cache, q, q_dtype, out, chunk_len,
+  return attend("pa_decode_chunk", c, k_cache, v_cache, q, q_dtype, out, chunk_len, 0,
+                block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs,
+                num_q_heads, scale, workspace, workspace_bytes, stream);
+}
+
+extern "C" pa_status pa_decode_window(const pa_cache_desc* c, const void* k_cache,
+                                      const void* v_cache, const void* q, int32_t q_dtype,
+                                      void* out, int32_t chunk_len, int32_t window,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* context_lens, int32_t max_context_len,
+                                      int32_t num_seqs, int32_t num_q_heads, float scale,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  return attend("pa_decode_window", c, k_cache, v_cache, q, q_dtype, out, chunk_len, window,
                 block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs,
                 num_q_heads, scale, workspace, workspace_bytes, stream);
 }

@@ -100,8 +100,8 @@ class GpuView:
                   float(w.scale), workspace)
         return out
 
-    def decode_chunk(self, q, max_len=None, workspace=None):
-        """pa_decode_chunk with q [B, T, Hq, D] (generator format)."""
+    def decode_chunk(self, q, max_len=None, workspace=None, window=0):
+        """pa_decode_chunk (pa_decode_window if window) with q [B, T, Hq, D]."""
         w = self.w
         qd = to_device_rows(q, w.q_fmt, self.dev)
         out = torch.empty_like(qd)
@@ -111,7 +111,7 @@ class GpuView:
         if workspace is None:
             workspace = pk.new_chunk_workspace(self.desc, w.B, w.Hq, T, max_len, self.dev)
         pk.decode_chunk(self.desc, self.kc, self.vc, qd, out, self.bt, self.cl, max_len,
-                        float(w.scale), workspace)
+                        float(w.scale), workspace, window=window)
         return out
 
 

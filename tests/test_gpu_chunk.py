@@ -154,3 +154,40 @@ def test_chunk_gqa_batch256_sampled_rows():
     err = np.abs(got - ref).max()
     assert err <= TOL["bf16"], err
     _say(f"  max abs err {err:.3e}")
+
+
+# ---------------------------------------------------------------- sliding window
+def _small_window(seed, fmt, G, D, T, W, Hkv=2, lens=None):
+    w, q, view, (kc, vc, bt, cl) = _build(seed, fmt, len(lens), G * Hkv, Hkv, D, T, lens=lens)
+    out = view.decode_chunk(q, window=W)
+    torch.cuda.synchronize()
+    ref = oracle.decode_chunk(q, w.q_fmt, kc, vc, w.fmt, bt, cl, w.scale, w.k_scale, w.v_scale,
+                              window=W)
+    err = _check(out, ref, w.fmt)
+    _say(f"  window {W}: max abs err {err:.3e}")
+    return out, view, w, q
+
+
+@pytest.mark.parametrize("fmt,G,D,T,W", [
+    ("bf16", 4, 128, 1, 1), ("bf16", 4, 128, 1, 15), ("bf16", 4, 128, 1, 16),
+    ("bf16", 4, 128, 1, 17), ("bf16", 4, 128, 1, 100), ("bf16", 4, 128, 1, 5000),
+    ("bf16", 4, 128, 4, 33), ("bf16", 4, 128, 7, 20), ("bf16", 1, 128, 16, 64),
+    ("fp8", 8, 64, 2, 40), ("f32", 2, 64, 3, 600), ("bf16", 32, 64, 2, 700)])
+def test_window_small_ragged(fmt, G, D, T, W):
+    """Windows below, at and above a block, longer than every context, with
+    chunks (the window and the causal cut together), fp8, and the partition
+    path (fp32, G = 32) whose partitions may see nothing."""
+    Hkv = 1 if G == 32 else 2
+    _small_window(900 + W + T, fmt, G, D, T, W, Hkv=Hkv, lens=LENS)
+
+
+def test_window_long_contexts_split_across_many_waves():
+    _small_window(950, "bf16", 8, 128, 2, 3000, lens=np.array([20000, 9000, 2999, 3001], np.int32))
+
+
+def test_window_wider_than_contexts_equals_no_window_bitwise():
+    w, q, view, _ = _build(951, "bf16", 7, 8, 2, 128, 3, lens=LENS[:7])
+    a = view.decode_chunk(q)
+    b = view.decode_chunk(q, window=100000)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
