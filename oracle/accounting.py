@@ -6,7 +6,8 @@
   Hkv x head_dim rather than the model's hidden width.
 * Paged utilisation: only the last block of each sequence can hold unused
   slots (explore.n1n.ai, "vLLM 深度解析", 映射机制详解), so the fraction of
-  allocated slots holding tokens is sum L / (16 * sum ceil(L / 16)).
+  allocated slots holding tokens is sum L / (bs * sum ceil(L / bs)), bs the
+  block size (16 unless stated).
 * Contiguous reservation, the scheme paging replaces: every sequence reserves
   ``max_len`` slots up front (explore.n1n.ai, section on KV-cache
   fragmentation), so the used fraction is sum L / (B * max_len).
@@ -23,9 +24,9 @@ def kv_cache_bytes(batch: int, seq_len: int, layers: int, width: int,
     return int(batch) * int(seq_len) * int(layers) * int(width) * 2 * int(elem_bytes)
 
 
-def paged_utilisation(lens) -> float:
+def paged_utilisation(lens, block_size: int = BLOCK) -> float:
     L = np.asarray(lens, dtype=np.int64)
-    slots = BLOCK * int(np.sum(-(-L // BLOCK)))
+    slots = int(block_size) * int(np.sum(-(-L // int(block_size))))
     return float(L.sum()) / slots if slots else 1.0
 
 

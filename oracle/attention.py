@@ -52,16 +52,17 @@ def gather_kv(cache: np.ndarray, block_table_row: np.ndarray, L: int,
               g: int) -> np.ndarray:
     """Contiguous [L, D] rows of KV head g for one sequence, in storage format.
 
-    Walks table entries j = 0 .. ceil(L/16)-1, takes physical block
-    ``block_table_row[j]`` (all 16 slots of head g), concatenates and keeps
-    the first L rows.
+    Walks table entries j = 0 .. ceil(L/bs)-1 (bs = the cache's tokens per
+    block, 16 unless stated), takes physical block ``block_table_row[j]``
+    (all bs slots of head g), concatenates and keeps the first L rows.
     """
-    n = -(-int(L) // BLOCK)
+    bs = cache.shape[2]                          # tokens per block
+    n = -(-int(L) // bs)
     if n == 0:
         return cache[:0, g, :, :].reshape(0, cache.shape[-1])
     ids = np.asarray(block_table_row[:n], dtype=np.int64)
-    tiles = cache[ids, g, :, :]                  # [n, 16, D]
-    return tiles.reshape(n * BLOCK, cache.shape[-1])[:L]
+    tiles = cache[ids, g, :, :]                  # [n, bs, D]
+    return tiles.reshape(n * bs, cache.shape[-1])[:L]
 
 
 def decode(q: np.ndarray, q_fmt: str, k_cache: np.ndarray, v_cache: np.ndarray,

@@ -3,17 +3,17 @@
 * ``write_kv``: after attention, each decode iteration stores the new token's
   K and V into its sequence's current block (ybb.press, "vLLM PagedAttention
   大模型推理架构深度实战", §6 decode loop).  The destination of token i is given
-  as a flat slot number ``slot_mapping[i]`` = physical block * 16 + offset
+  as a flat slot number ``slot_mapping[i]`` = physical block * block_size + offset
   (reading: the pages fix no form; a negative slot means "skip this row").
 * ``copy_blocks``: copy-on-write duplicates a shared block before a sequence
   modifies it (ybb.press, §2.3).  Every (src, dst) pair copies the whole
-  block -- all KV heads, all 16 slots -- of both caches, byte for byte.
+  block -- all KV heads, all slots -- of both caches, byte for byte.
   Precondition (reading): destinations are distinct and no destination is also
   a source, so the pairs commute.
 * ``swap_blocks``: the same whole-block copies between two pools, the device
   cache and a host pool, for swapping sequences out and back in.
 
-Caches are ``[num_blocks, Hkv, 16, D]`` arrays in storage format (float32,
+Caches are ``[num_blocks, Hkv, block_size, D]`` arrays (block_size 16 unless stated) in storage format (float32,
 uint16 bf16 bits, or uint8 E4M3 codes).  Both functions return new arrays and
 leave every byte they do not write untouched.
 """
@@ -41,16 +41,18 @@ def write_kv(k_cache: np.ndarray, v_cache: np.ndarray, k: np.ndarray,
              k_scale: float = 1.0, v_scale: float = 1.0):
     """Scatter rows ``k[i], v[i]`` ([Hkv, D] each) into slot ``slot_mapping[i]``.
 
-    For slot >= 0: block = slot // 16, offset = slot % 16, and for every KV
-    head g: cache[block, g, offset, :] = convert(row[g, :]).  Returns the new
+    For slot >= 0: block = slot // bs, offset = slot % bs (bs = the cache's
+    tokens per block, 16 unless stated), and for every KV head g:
+    cache[block, g, offset, :] = convert(row[g, :]).  Returns the new
     (k_cache, v_cache).
     """
     kc = k_cache.copy()
     vc = v_cache.copy()
     slots = np.asarray(slot_mapping, dtype=np.int64)
     keep = slots >= 0
-    blk = slots[keep] // BLOCK
-    off = slots[keep] % BLOCK
+    bs = k_cache.shape[2]                        # tokens per block
+    blk = slots[keep] // bs
+    off = slots[keep] % bs
     kc[blk, :, off, :] = _convert(np.asarray(k)[keep], src_fmt, fmt, k_scale)
     vc[blk, :, off, :] = _convert(np.asarray(v)[keep], src_fmt, fmt, v_scale)
     return kc, vc
