@@ -65,9 +65,16 @@ positions of each context (pa_decode_window); the roofline's algorithmic
 bytes are then the positions the window keeps, min(L, W + T - 1) per
 sequence.
 
+With ``--block-size BS`` (8, 32 or 64) the caches use BS-token blocks (the
+pool re-sized for them, with its own seeded free order); the JSON line adds
+the paged utilisation and the simulated chat's block-cache hit rate at that
+block size.  Blocks of 32 and 64 stream as 2 and 4 tiles; 8-token blocks
+take the partition path.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers N]
                       [--chunk T | --swap | --prefix] [--window W]
-                      [--no-cpu-baseline] [--copy-calibration MIB]
+                      [--block-size BS] [--no-cpu-baseline]
+                      [--copy-calibration MIB]
 
 --copy-calibration MIB ends the run with plain device copies of MIB MiB, the
 reference a hardware-counter run scales FETCH_SIZE / WRITE_SIZE by.
@@ -361,7 +368,7 @@ def run_swap(args):
     print(json.dumps(res), flush=True)
 
 
-def chat_hit_rate(seed=11, conversations=64, turns=8):
+def chat_hit_rate(seed=11, conversations=64, turns=8, block_size=16):
     """Host-only: multi-turn chats through the library's block manager with
     prefix caching.  Turn k's prompt is the whole conversation so far plus a
     new user message (64..256 tokens); the answer (128..512 tokens) is
@@ -370,7 +377,7 @@ def chat_hit_rate(seed=11, conversations=64, turns=8):
     lookup)."""
     import paged_kv_cache_421_amd as pk
     rng = np.random.default_rng(seed)
-    bm = pk.BlockManager(1 << 16)
+    bm = pk.BlockManager((1 << 20) // block_size, block_size=block_size)
     bm.enable_prefix_caching()
     hist = [np.zeros(0, np.int32) for _ in range(conversations)]
     sid, t_lookup, n_lookup = 0, 0.0, 0
@@ -533,6 +540,8 @@ def main():
                     help="new tokens per sequence per step (1 = decode)")
     ap.add_argument("--swap", action="store_true",
                     help="measure swapping sequences out to pinned host memory and back")
+    ap.add_argument("--block-size", type=int, default=16, metavar="BS",
+                    help="tokens per cache block: 8, 16, 32 or 64")
     ap.add_argument("--window", type=int, default=0, metavar="W",
                     help="sliding window of W positions (0: none)")
     ap.add_argument("--prefix", action="store_true",
@@ -571,11 +580,17 @@ def main():
     _log("bench: generating the GQA batch-256 workload")
     w = workloads.config3()
     B, Hq, Hkv, D = w.B, w.Hq, w.Hkv, w.D
-    desc = pk.CacheDesc(w.num_blocks, Hkv, D, "bf16")
+    bs = args.block_size
+    if bs == 16:
+        n_blocks, order = w.num_blocks, w.free_order
+    else:        # the same token capacity in bs-token blocks, one more per sequence
+        n_blocks = -(-w.num_blocks * 16 // bs) + B
+        order = np.random.default_rng(3000 + bs).permutation(n_blocks).astype(np.int32)
+    desc = pk.CacheDesc(n_blocks, Hkv, D, "bf16", block_size=bs)
 
     # ---- caches of layer 0 through the library's own write path; the other
     # layers get copies (distinct HBM, same contents)
-    bm = pk.BlockManager(w.num_blocks, free_order=w.free_order)
+    bm = pk.BlockManager(n_blocks, free_order=order, block_size=bs)
     per = []
     for s in range(B):
         bm.add_seq(s)
@@ -610,7 +625,7 @@ def main():
 
     total = args.steps + args.warmup
     max_len_final = int(w.lens.max()) + T * total
-    cap = -(-max_len_final // 16)
+    cap = -(-max_len_final // bs)
     workspace = pk.new_chunk_workspace(desc, B, Hq, T, max_len_final, dev)
 
     # ---- pinned host staging, triple-buffered against the running GPU
@@ -665,7 +680,7 @@ def main():
             return _kv_bytes(np.minimum(lens, args.window + T - 1), Hkv, D, 2)
         return _kv_bytes(lens, Hkv, D, 2)
 
-    _log(f"bench: {NL} layers x {w.num_blocks} blocks, warmup {args.warmup}, steps {args.steps}")
+    _log(f"bench: {NL} layers x {n_blocks} blocks of {bs}, warmup {args.warmup}, steps {args.steps}")
     for i in range(args.warmup):
         step(i, None)
     torch.cuda.synchronize()
@@ -690,7 +705,7 @@ def main():
     mean_kv = statistics.mean(kv_per_call)
     achieved = mean_kv / mean_dec_s / 1e9
     steps_s = wall / args.steps
-    traffic = None if args.window else _traffic_per_call(mean_kv, T)
+    traffic = None if (args.window or bs != 16) else _traffic_per_call(mean_kv, T)
     _log(f"bench: {'pa_decode' if T == 1 else 'pa_decode_chunk'} mean {mean_dec_s * 1e6:.1f} us (p10 "
          f"{np.percentile(dec_ms, 10) * 1e3:.1f}, p90 {np.percentile(dec_ms, 90) * 1e3:.1f}), "
          f"{achieved:.0f} GB/s; step {steps_s * 1e3:.3f} ms")
@@ -702,6 +717,8 @@ def main():
         workload = workload.replace("GQA decode layer", f"GQA layer, {T}-token chunk per sequence")
     if args.window:
         workload += f", sliding window of {args.window} positions"
+    if bs != 16:
+        workload = workload.replace("16-token shuffled blocks", f"{bs}-token shuffled blocks")
     res = {
         "metric": METRIC if T == 1 else METRIC_CHUNK,
         "value": round(B * T * NL * args.steps / wall, 1),
@@ -728,6 +745,8 @@ def main():
             "parallelism": "single GPU",
         },
         "kv_gbps_step": round(mean_kv * NL / steps_s / 1e9, 1),
+        "block_size": bs,
+        "paged_utilisation": round(float(lens.sum()) / (bs * float(np.sum(-(-lens // bs)))), 4),
         "decode_us_mean": round(mean_dec_s * 1e6, 2),
         "decode_us_p10": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
         "decode_us_p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),
@@ -752,7 +771,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         _log(f"bench: copy calibration {n} bytes x 3")
-    if not args.no_cpu_baseline and not args.window:
+    if bs != 16:
+        rate, _, _ = chat_hit_rate(block_size=bs)
+        res["chat_sim_hit_rate"] = round(rate, 4)
+    if not args.no_cpu_baseline and not args.window and bs == 16:
         _log("bench: timing the CPU oracle")
         res["cpu_baseline"] = cpu_baseline(w, T=T)
     print(json.dumps(res), flush=True)

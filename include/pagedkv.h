@@ -3,12 +3,14 @@
  * attention for AMD Instinct MI355X (gfx950).
  *
  * What the library does (sources are web pages on vLLM / PagedAttention):
- *   - The KV cache is split into fixed 16-token blocks that need not be
+ *   - The KV cache is split into fixed-size blocks (16 tokens by default;
+ *     8, 32 or 64 may be chosen to suit request lengths, unionyoga.cn,
+ *     section "在真实架构中扮演什么角色？") that need not be
  *     contiguous; each sequence owns a block table from logical to physical
  *     block (explore.n1n.ai, "vLLM 深度解析：PagedAttention 如何让大模型推理更快、
  *     更省钱", 映射机制详解; ybb.press, "vLLM PagedAttention 大模型推理架构深度
  *     实战", §2.2).
- *   - The attention kernel walks ceil(len / 16) table entries of a sequence
+ *   - The attention kernel walks ceil(len / block_size) table entries of a sequence
  *     and reads the blocks they name (unionyoga.cn, "vLLM：重塑大模型推理性能的
  *     关键引擎", PagedAttention section, kernel sketch).
  *   - Each decode iteration writes the new token's K/V into its block and
@@ -28,11 +30,12 @@
  *     device arrays (block ids, slots, context lengths) cannot be checked on
  *     the host; out-of-range values there are undefined behaviour.
  *
- * Cache layout (one K and one V tensor, same shape and dtype):
- *   cache[num_blocks][num_kv_heads][16][head_dim], row-major, so element
- *   (block b, kv head g, slot t, dim d) is at ((b*Hkv + g)*16 + t)*D + d and
- *   one (block, head) tile is 16*D contiguous elements; a token's row of one
+ * Cache layout (one K and one V tensor, same shape and dtype; bs = block_size):
+ *   cache[num_blocks][num_kv_heads][bs][head_dim], row-major, so element
+ *   (block b, kv head g, slot t, dim d) is at ((b*Hkv + g)*bs + t)*D + d and
+ *   one (block, head) tile is bs*D contiguous elements; a token's row of one
  *   head is D contiguous elements, so appending a token writes whole rows.
+ *   Below, "16" in slot and table formulas stands for the block size.
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H
@@ -70,7 +73,9 @@ typedef enum {
 
 typedef struct {
   int32_t num_blocks;    /* physical blocks in each of the K and V caches */
-  int32_t block_size;    /* tokens per block; must be PA_BLOCK_SIZE */
+  int32_t block_size;    /* tokens per block: 8, 16 (PA_BLOCK_SIZE), 32 or 64;
+                            decode streams tiles of 16 tokens, so 8-token blocks
+                            take the partition path */
   int32_t num_kv_heads;  /* Hkv >= 1 */
   int32_t head_dim;      /* D: 64 or 128 */
   int32_t cache_dtype;   /* pa_dtype of both caches */
@@ -92,9 +97,9 @@ size_t pa_cache_bytes(const pa_cache_desc* c);
  * into its block" step of each decode iteration, ybb.press §6).
  *   k, v          : [num_tokens][num_kv_heads][head_dim] contiguous, dtype
  *                   src_dtype (device).
- *   slot_mapping  : int64 [num_tokens] (device); slot = block * 16 + offset;
+ *   slot_mapping  : int64 [num_tokens] (device); slot = block * bs + offset;
  *                   a negative slot skips that row.  Non-negative slots must
- *                   be distinct and < num_blocks * 16.
+ *                   be distinct and < num_blocks * bs.
  *   Supported (src_dtype -> cache_dtype): F32 -> F32, BF16 -> BF16 (bit
  *   copies) and BF16 -> FP8_E4M3 (code = round-to-nearest-even of
  *   min(|x * fp32(1/scale)|, 448) with x's sign; NaN -> 0x7F).
@@ -108,7 +113,7 @@ pa_status pa_write_kv(const pa_cache_desc* c, void* k_cache, void* v_cache,
 /*
  * pa_copy_blocks -- copy-on-write block duplication (ybb.press §2.3).
  *   pairs : int32 [num_pairs][2] (device), each (src, dst): the whole block
- *           -- every KV head, all 16 slots -- of both caches is copied byte
+ *           -- every KV head, all bs slots -- of both caches is copied byte
  *           for byte from src to dst.  Destinations must be distinct and none
  *           may also be a source (the block manager never emits otherwise).
  */

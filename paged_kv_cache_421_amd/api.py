@@ -32,17 +32,22 @@ def dtype_code(x) -> int:
 
 class CacheDesc:
     """pa_cache_desc: shape and format of a pair of K/V caches, each
-    ``[num_blocks, num_kv_heads, 16, head_dim]``."""
+    ``[num_blocks, num_kv_heads, block_size, head_dim]`` (block_size 8, 16,
+    32 or 64; 16 by default)."""
 
     def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, dtype,
-                 k_scale: float = 1.0, v_scale: float = 1.0):
-        self.c = CacheDescC(int(num_blocks), BLOCK_SIZE, int(num_kv_heads), int(head_dim),
+                 k_scale: float = 1.0, v_scale: float = 1.0, block_size: int = BLOCK_SIZE):
+        self.c = CacheDescC(int(num_blocks), int(block_size), int(num_kv_heads), int(head_dim),
                             dtype_code(dtype), float(k_scale), float(v_scale))
+
+    @property
+    def block_size(self) -> int:
+        return int(self.c.block_size)
 
     @property
     def shape(self) -> Tuple[int, int, int, int]:
         """Shape of each of the K and V caches."""
-        return (self.c.num_blocks, self.c.num_kv_heads, BLOCK_SIZE, self.c.head_dim)
+        return (self.c.num_blocks, self.c.num_kv_heads, self.c.block_size, self.c.head_dim)
 
     @property
     def torch_dtype(self):
@@ -234,7 +239,8 @@ class BlockManager:
     swapping), refcounts, copy-on-write."""
 
     def __init__(self, num_blocks: int, free_order: Optional[Sequence[int]] = None,
-                 num_host_blocks: int = 0, host_free_order: Optional[Sequence[int]] = None):
+                 num_host_blocks: int = 0, host_free_order: Optional[Sequence[int]] = None,
+                 block_size: int = BLOCK_SIZE):
         self._lib = lib                      # kept alive for __del__ at interpreter exit
         self._order = self._horder = None
         ptr = hptr = ctypes.c_void_p(0)
@@ -244,12 +250,13 @@ class BlockManager:
         if host_free_order is not None:
             self._horder = np.ascontiguousarray(host_free_order, dtype=np.int32)
             hptr = _ptr(self._horder)
-        h = lib.pa_bm_create_ex(int(num_blocks), BLOCK_SIZE, ptr, int(num_host_blocks), hptr)
+        h = lib.pa_bm_create_ex(int(num_blocks), int(block_size), ptr, int(num_host_blocks), hptr)
         if not h:
             raise PagedKVError(-1, lib.pa_last_error().decode())
         self._h = ctypes.c_void_p(h)
         self.num_blocks = int(num_blocks)
         self.num_host_blocks = int(num_host_blocks)
+        self.block_size = int(block_size)
 
     def __del__(self):
         h = getattr(self, "_h", None)

@@ -47,7 +47,7 @@ using pagedkv::fail;
 
 namespace {
 
-constexpr int32_t kBlock = PA_BLOCK_SIZE;
+constexpr int32_t kMaxBlock = 64;        // largest block size accepted
 
 struct Seq {
   std::vector<int32_t> table;  // logical -> physical block (host block if on_host)
@@ -58,8 +58,6 @@ struct Seq {
   uint64_t last_key = 0;       // key of the last full block
 };
 
-using BlockTokens = std::array<int32_t, kBlock>;
-
 uint64_t fnv1a64_bytes(uint64_t h, const unsigned char* p, size_t n) {
   for (size_t i = 0; i < n; ++i) {
     h ^= p[i];
@@ -68,15 +66,15 @@ uint64_t fnv1a64_bytes(uint64_t h, const unsigned char* p, size_t n) {
   return h;
 }
 
-// Key of a full block: FNV-1a 64 over the parent key then the token ids.
-uint64_t block_key(uint64_t parent, const int32_t* toks) {
-  unsigned char buf[8 + 4 * kBlock];
+// Key of a full block of n tokens: FNV-1a 64 over the parent key then the ids.
+uint64_t block_key(uint64_t parent, const int32_t* toks, int n) {
+  unsigned char buf[8 + 4 * kMaxBlock];
   for (int i = 0; i < 8; ++i) buf[i] = static_cast<unsigned char>(parent >> (8 * i));
-  for (int t = 0; t < kBlock; ++t) {
+  for (int t = 0; t < n; ++t) {
     const uint32_t v = static_cast<uint32_t>(toks[t]);
     for (int i = 0; i < 4; ++i) buf[8 + 4 * t + i] = static_cast<unsigned char>(v >> (8 * i));
   }
-  return fnv1a64_bytes(0xCBF29CE484222325ull, buf, sizeof(buf));
+  return fnv1a64_bytes(0xCBF29CE484222325ull, buf, 8 + 4 * static_cast<size_t>(n));
 }
 
 // A FIFO free pool with reference counts.
@@ -105,6 +103,7 @@ struct Pool {
 }  // namespace
 
 struct pa_bm {
+  int32_t bs = PA_BLOCK_SIZE;                    // tokens per block
   int32_t num_blocks = 0;
   int32_t num_host_blocks = 0;
   Pool dev;
@@ -116,7 +115,7 @@ struct pa_bm {
   std::unordered_map<uint64_t, int32_t> cache;   // key -> block
   std::vector<char> registered;                  // per block
   std::vector<uint64_t> bkey, bparent;
-  std::vector<BlockTokens> btok;
+  std::vector<int32_t> btok;                     // [block][bs] ids of registered blocks
   std::list<int32_t> lru;                        // evictable, oldest release first
   std::vector<std::list<int32_t>::iterator> lru_pos;
   std::vector<char> in_lru;
@@ -126,7 +125,7 @@ struct pa_bm {
     registered.assign(num_blocks, 0);
     bkey.assign(num_blocks, 0);
     bparent.assign(num_blocks, 0);
-    btok.assign(num_blocks, BlockTokens{});
+    btok.assign(static_cast<size_t>(num_blocks) * bs, 0);
     lru_pos.assign(num_blocks, lru.end());
     in_lru.assign(num_blocks, 0);
   }
@@ -140,8 +139,8 @@ struct pa_bm {
   int64_t blocks_needed(const Seq& s, int64_t n) const {
     if (n <= 0) return 0;
     const int64_t p = s.len;
-    int64_t fresh = (p + n + kBlock - 1) / kBlock - (p + kBlock - 1) / kBlock;
-    int64_t cow = (p % kBlock != 0 && dev.ref[s.table.back()] > 1) ? 1 : 0;
+    int64_t fresh = (p + n + bs - 1) / bs - (p + bs - 1) / bs;
+    int64_t cow = (p % bs != 0 && dev.ref[s.table.back()] > 1) ? 1 : 0;
     return fresh + cow;
   }
 
@@ -182,16 +181,16 @@ struct pa_bm {
   void note_token(Seq& s, int32_t tok) {
     if (!s.track) return;
     s.toks.push_back(tok);
-    if (s.toks.size() % kBlock != 0) return;
-    const int32_t* blk = s.toks.data() + s.toks.size() - kBlock;
-    const uint64_t key = block_key(s.last_key, blk);
-    const int32_t b = s.table[s.toks.size() / kBlock - 1];
+    if (s.toks.size() % bs != 0) return;
+    const int32_t* blk = s.toks.data() + s.toks.size() - bs;
+    const uint64_t key = block_key(s.last_key, blk, bs);
+    const int32_t b = s.table[s.toks.size() / bs - 1];
     if (!cache.count(key) && !registered[b]) {
       cache.emplace(key, b);
       registered[b] = 1;
       bkey[b] = key;
       bparent[b] = s.last_key;
-      for (int i = 0; i < kBlock; ++i) btok[b][i] = blk[i];
+      for (int i = 0; i < bs; ++i) btok[static_cast<size_t>(b) * bs + i] = blk[i];
     }
     s.last_key = key;
   }
@@ -199,7 +198,7 @@ struct pa_bm {
   // Appends one token; the caller has checked that blocks are available.
   int64_t append_one(Seq& s, int32_t* cow_src, int32_t* cow_dst) {
     const int32_t p = s.len;
-    if (p % kBlock == 0) {
+    if (p % bs == 0) {
       s.table.push_back(pop());
     } else if (dev.ref[s.table.back()] > 1) {
       const int32_t old = s.table.back();
@@ -210,7 +209,7 @@ struct pa_bm {
       *cow_dst = b;
     }
     s.len = p + 1;
-    return static_cast<int64_t>(s.table[p / kBlock]) * kBlock + p % kBlock;
+    return static_cast<int64_t>(s.table[p / bs]) * bs + p % bs;
   }
 };
 
@@ -223,9 +222,8 @@ pa_bm* pa_bm_create_ex(int32_t num_blocks, int32_t block_size, const int32_t* fr
          num_host_blocks);
     return nullptr;
   }
-  if (block_size != kBlock) {
-    fail(PA_ERR_UNSUPPORTED, "pa_bm_create: block_size %d (only %d)",
-         block_size, kBlock);
+  if (block_size != 8 && block_size != 16 && block_size != 32 && block_size != 64) {
+    fail(PA_ERR_UNSUPPORTED, "pa_bm_create: block_size %d (8, 16, 32 or 64)", block_size);
     return nullptr;
   }
   pa_bm* bm = new (std::nothrow) pa_bm;
@@ -233,6 +231,7 @@ pa_bm* pa_bm_create_ex(int32_t num_blocks, int32_t block_size, const int32_t* fr
     fail(PA_ERR_INVALID_ARG, "pa_bm_create: out of host memory");
     return nullptr;
   }
+  bm->bs = block_size;
   bm->num_blocks = num_blocks;
   bm->num_host_blocks = num_host_blocks;
   if (!bm->dev.init(num_blocks, free_order)) {
@@ -356,14 +355,14 @@ pa_status pa_bm_add_seq_prompt(pa_bm* bm, int64_t seq_id, const int32_t* tokens,
   std::vector<int32_t> hit;
   uint64_t parent = 0;
   if (bm->caching) {
-    for (int32_t k = 0; k < n / kBlock; ++k) {
-      const int32_t* blk = tokens + static_cast<int64_t>(k) * kBlock;
-      const uint64_t key = block_key(parent, blk);
+    for (int32_t k = 0; k < n / bm->bs; ++k) {
+      const int32_t* blk = tokens + static_cast<int64_t>(k) * bm->bs;
+      const uint64_t key = block_key(parent, blk, bm->bs);
       auto c = bm->cache.find(key);
       if (c == bm->cache.end()) break;
       const int32_t b = c->second;
       bool same = bm->bparent[b] == parent;
-      for (int i = 0; i < kBlock && same; ++i) same = bm->btok[b][i] == blk[i];
+      for (int i = 0; i < bm->bs && same; ++i) same = bm->btok[static_cast<size_t>(b) * bm->bs + i] == blk[i];
       if (!same) break;
       hit.push_back(b);
       parent = key;
@@ -371,14 +370,14 @@ pa_status pa_bm_add_seq_prompt(pa_bm* bm, int64_t seq_id, const int32_t* tokens,
   }
   int64_t revived = 0;
   for (int32_t b : hit) revived += bm->dev.ref[b] == 0 ? 1 : 0;
-  const int64_t need = (static_cast<int64_t>(n) + kBlock - 1) / kBlock - static_cast<int64_t>(hit.size());
+  const int64_t need = (static_cast<int64_t>(n) + bm->bs - 1) / bm->bs - static_cast<int64_t>(hit.size());
   if (need > bm->available() - revived)
     return fail(PA_ERR_NO_BLOCKS, "pa_bm_add_seq_prompt: prompt needs %lld new blocks, %lld available",
                 (long long)need, (long long)(bm->available() - revived));
   Seq s;
   s.track = bm->caching;
   if (bm->caching) {
-    bm->queried += n / kBlock;
+    bm->queried += n / bm->bs;
     bm->hits += static_cast<int64_t>(hit.size());
   }
   for (int32_t b : hit) {
@@ -386,12 +385,12 @@ pa_status pa_bm_add_seq_prompt(pa_bm* bm, int64_t seq_id, const int32_t* tokens,
     bm->dev.ref[b] += 1;
     s.table.push_back(b);
   }
-  const int32_t nc = kBlock * static_cast<int32_t>(hit.size());
+  const int32_t nc = bm->bs * static_cast<int32_t>(hit.size());
   s.len = nc;
   if (s.track) s.toks.assign(tokens, tokens + nc);
   s.last_key = parent;
   for (int32_t p = 0; p < nc; ++p)
-    slots[p] = static_cast<int64_t>(s.table[p / kBlock]) * kBlock + p % kBlock;
+    slots[p] = static_cast<int64_t>(s.table[p / bm->bs]) * bm->bs + p % bm->bs;
   Seq& stored = bm->seqs.emplace(seq_id, std::move(s)).first->second;
   int32_t cs = -1, cd = -1;
   for (int32_t p = nc; p < n; ++p) {
@@ -450,7 +449,7 @@ pa_status pa_bm_append_batch(pa_bm* bm, const int64_t* seq_ids, int32_t n,
   std::unordered_map<int32_t, int32_t> ref_delta;
   for (int32_t i = 0; i < n; ++i) {
     const Seq& s = *ss[i];
-    if (s.len % kBlock == 0) {
+    if (s.len % bm->bs == 0) {
       need += 1;
     } else {
       const int32_t last = s.table.back();

@@ -28,7 +28,7 @@ __global__ void __launch_bounds__(256)
 write_kv_kernel(char* __restrict__ k_cache, char* __restrict__ v_cache,
                 const char* __restrict__ k, const char* __restrict__ v,
                 const int64_t* __restrict__ slot_mapping, int64_t num_chunks,
-                int chunks_per_row, int chunks_per_head, int hkv, int d,
+                int chunks_per_row, int chunks_per_head, int hkv, int d, int bs,
                 float k_inv, float v_inv) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= num_chunks) return;
@@ -39,9 +39,9 @@ write_kv_kernel(char* __restrict__ k_cache, char* __restrict__ v_cache,
   if (slot < 0) return;
   const int g = rem / chunks_per_head;
   const int c = rem - g * chunks_per_head;
-  const int64_t blk = slot / kBlock;
-  const int off = static_cast<int>(slot % kBlock);
-  const int64_t dst_elem = ((blk * hkv + g) * kBlock + off) * d + c * kElems;
+  const int64_t blk = slot / bs;
+  const int off = static_cast<int>(slot % bs);
+  const int64_t dst_elem = ((blk * hkv + g) * bs + off) * d + c * kElems;
   const SrcChunk src = reinterpret_cast<const SrcChunk*>(is_v ? v : k)[idx];
   char* cache = is_v ? v_cache : k_cache;
   if constexpr (kFmt == PA_FP8_E4M3) {
@@ -90,8 +90,8 @@ int dtype_bytes(int dt) {
 
 pa_status check_desc(const pa_cache_desc* c, const char* fn) {
   if (!c) return fail(PA_ERR_INVALID_ARG, "%s: null cache descriptor", fn);
-  if (c->block_size != kBlock)
-    return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d (only %d)", fn, c->block_size, kBlock);
+  if (c->block_size != 8 && c->block_size != 16 && c->block_size != 32 && c->block_size != 64)
+    return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d (8, 16, 32 or 64)", fn, c->block_size);
   if (c->num_blocks < 0 || c->num_kv_heads <= 0)
     return fail(PA_ERR_INVALID_ARG, "%s: num_blocks %d, num_kv_heads %d", fn,
                 c->num_blocks, c->num_kv_heads);
@@ -118,7 +118,7 @@ using namespace pagedkv;
 
 extern "C" size_t pa_cache_bytes(const pa_cache_desc* c) {
   if (check_desc(c, "pa_cache_bytes") != PA_OK) return 0;
-  return static_cast<size_t>(c->num_blocks) * c->num_kv_heads * kBlock * c->head_dim *
+  return static_cast<size_t>(c->num_blocks) * c->num_kv_heads * c->block_size * c->head_dim *
          dtype_bytes(c->cache_dtype);
 }
 
@@ -156,15 +156,15 @@ extern "C" pa_status pa_write_kv(const pa_cache_desc* c, void* k_cache, void* v_
   if (c->cache_dtype == PA_FP8_E4M3) {
     write_kv_kernel<u32x4_t, 8, PA_FP8_E4M3><<<grid, 256, 0, s>>>(
         kc, vc, kk, vv, slot_mapping, num_chunks, chunks_per_row, chunks_per_head, hkv, d,
-        k_inv, v_inv);
+        c->block_size, k_inv, v_inv);
   } else if (src_dtype == PA_BF16) {
     write_kv_kernel<u32x4_t, 8, PA_BF16><<<grid, 256, 0, s>>>(
         kc, vc, kk, vv, slot_mapping, num_chunks, chunks_per_row, chunks_per_head, hkv, d,
-        k_inv, v_inv);
+        c->block_size, k_inv, v_inv);
   } else {
     write_kv_kernel<u32x4_t, 4, PA_F32><<<grid, 256, 0, s>>>(
         kc, vc, kk, vv, slot_mapping, num_chunks, chunks_per_row, chunks_per_head, hkv, d,
-        k_inv, v_inv);
+        c->block_size, k_inv, v_inv);
   }
   return launch_status("pa_write_kv");
 }
@@ -179,8 +179,8 @@ extern "C" pa_status pa_copy_blocks(const pa_cache_desc* c, void* k_cache, void*
     return fail(PA_ERR_UNSUPPORTED, "pa_copy_blocks: %d pairs (at most 65535 per call)",
                 num_pairs);
   if (!k_cache || !v_cache || !pairs) return fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: null pointer");
-  const int64_t block_bytes = static_cast<int64_t>(c->num_kv_heads) * kBlock * c->head_dim *
-                              dtype_bytes(c->cache_dtype);
+  const int64_t block_bytes = static_cast<int64_t>(c->num_kv_heads) * c->block_size *
+                              c->head_dim * dtype_bytes(c->cache_dtype);
   const int64_t chunks = block_bytes / 16;
   dim3 grid(static_cast<unsigned>((chunks + 255) / 256), num_pairs, 2);
   copy_blocks_kernel<<<grid, 256, 0, static_cast<hipStream_t>(stream)>>>(
@@ -231,8 +231,8 @@ extern "C" pa_status pa_swap_blocks(const pa_cache_desc* c, const void* src_k,
     if (!gpu_addressable(ptrs[i]))
       return fail(PA_ERR_INVALID_ARG,
                   "pa_swap_blocks: %s is not device or pinned host memory", names[i]);
-  const int64_t block_bytes = static_cast<int64_t>(c->num_kv_heads) * kBlock * c->head_dim *
-                              dtype_bytes(c->cache_dtype);
+  const int64_t block_bytes = static_cast<int64_t>(c->num_kv_heads) * c->block_size *
+                              c->head_dim * dtype_bytes(c->cache_dtype);
   const int64_t chunks = block_bytes / 16;
   dim3 grid(static_cast<unsigned>((chunks + 255) / 256), num_pairs, 2);
   copy_blocks_kernel<<<grid, 256, 0, static_cast<hipStream_t>(stream)>>>(

@@ -80,6 +80,7 @@ constexpr int kAuxCoherent = 16;        // buffer cache policy sc1: device-coher
 constexpr int kMaxRows = 16;            // fast path: query rows per pass (MFMA columns)
 constexpr float kNoMax = -1e30f;        // running max of a row that has seen no position yet
 constexpr int kOutOfRange = 0x7FFFFF00; // buffer offset past any range: the load reads 0
+constexpr int kTile = 16;               // fast path: tokens per MFMA tile (a block holds 1, 2 or 4)
 constexpr int kSeqBits = 26;            // descriptor word 2: sequence | window start << 26
 constexpr uint32_t kSeqMask = (1u << kSeqBits) - 1;
 
@@ -176,6 +177,7 @@ struct StreamArgs {
   int group;                  // G: query heads per KV head
   int chunk;                  // T: new tokens per sequence
   int window;                 // W > 0: attend only the last W positions; 0: all
+  int sub_shift;              // log2(block size / 16): tiles per block = 1 << sub_shift
   int t_first;                // first chunk token of this pass
   int rows;                   // query rows of this pass (<= kMaxRows)
   float logit_scale;          // scale * k_scale * log2(e)
@@ -189,12 +191,12 @@ __global__ void __launch_bounds__(64 * kWavesPerGroup)
 decode_stream_kernel(StreamArgs a) {
   constexpr int kE = kFp8 ? 1 : 2;                 // bytes per cache element
   constexpr int kRowBytes = kD * kE;
-  constexpr int kTileBytes = kBlock * kRowBytes;
+  constexpr int kTileBytes = kTile * kRowBytes;
   constexpr int kKK = kD / 32;                     // QK MFMA steps over head_dim
   constexpr int kVC = kD / 16;                     // P.V MFMAs (16 dims each)
   constexpr int kLanesPerRow = kD / 8;             // V: lanes covering one token row
   constexpr int kRowsPerLoad = 64 / kLanesPerRow;  // V: token rows per load
-  constexpr int kVLoads = kBlock / kRowsPerLoad;   // V: loads per lane
+  constexpr int kVLoads = kTile / kRowsPerLoad;   // V: loads per lane
   constexpr int kVStride = kRowBytes + 16;         // LDS row pitch of the V staging tile
   constexpr int kRowOutBytes = kD * 2;             // one bf16 output row
   using Chunk = typename std::conditional<kFp8, u32x2_t, u32x4_t>::type;
@@ -214,8 +216,8 @@ decode_stream_kernel(StreamArgs a) {
   // With a window, a (sequence, KV head) segment covers the blocks from the
   // one holding the first chunk token's window start to the last.
   const int win = a.window;
-  auto first_blk = [&](int L) -> int { return win > 0 ? max(0, L - nchunk + 1 - win) / kBlock : 0; };
-  auto tiles_of = [&](int L) -> int { return (L + kBlock - 1) / kBlock - first_blk(L); };
+  auto first_blk = [&](int L) -> int { return win > 0 ? max(0, L - nchunk + 1 - win) / kTile : 0; };
+  auto tiles_of = [&](int L) -> int { return (L + kTile - 1) / kTile - first_blk(L); };
   const __amdgpu_buffer_rsrc_t lens_rsrc = make_rsrc(a.context_lens, B * 4);
 
   // ---- 1. total tile count; zero rows of empty sequences s = w (mod waves).
@@ -314,7 +316,7 @@ decode_stream_kernel(StreamArgs a) {
   u32x4_t* s_desc = s_desc_all[wig];
   // V tile staging (token-major rows, padded pitch): it turns the V tile's
   // rows into the P.V MFMA's operand, 4 tokens of one dim per lane
-  __shared__ __align__(16) char s_v_all[kWavesPerGroup][kBlock * kVStride];
+  __shared__ __align__(16) char s_v_all[kWavesPerGroup][kTile * kVStride];
   char* s_v = s_v_all[wig];
   // output staging: the rows of a finished segment are gathered here so
   // that each row goes to memory as whole 16-byte pieces, 256 contiguous
@@ -327,13 +329,13 @@ decode_stream_kernel(StreamArgs a) {
   constexpr int kSlotBytesMax = kMaxRows * (kD + 2) * 4;
   __shared__ __align__(16) char s_p_all[kWavesPerGroup][2 * kSlotBytesMax];
   char* s_p = s_p_all[wig];
-  int w_s = s_cur, w_g = g0, w_j = j0, w_L = L_cur, w_nb = (L_cur + kBlock - 1) / kBlock;
+  int w_s = s_cur, w_g = g0, w_j = j0, w_L = L_cur, w_nb = (L_cur + kTile - 1) / kTile;
   int w_jf = first_blk(L_cur), w_seg = seg0 + g0 * nb0;
   // The first chunk token's window starts at L - T + 1 - W; a row of chunk
   // token t starts t later.  Code = that start relative to the segment's
   // first block, clamped at -16 (rows then cut nothing), plus 17: 1..32.
   auto lo_code = [&](int L, int jf) -> uint32_t {
-    return win > 0 ? static_cast<uint32_t>(max(L - nchunk + 1 - win - kBlock * jf, -kBlock) + kBlock + 1)
+    return win > 0 ? static_cast<uint32_t>(max(L - nchunk + 1 - win - kTile * jf, -kTile) + kTile + 1)
                    : 0u;
   };
   // lengths for the walk: from Lr for the first 256 sequences, past them
@@ -559,7 +561,7 @@ decode_stream_kernel(StreamArgs a) {
       for (int c = lane; c < span; c += 64) {
         const int j = w_j + c;
         const int gpos = done + pos + c;                     // position in the range
-        const uint32_t valid = static_cast<uint32_t>(min(31, w_L - kBlock * j));
+        const uint32_t valid = static_cast<uint32_t>(min(31, w_L - kTile * j));
         const uint32_t first = (j == w_jf || gpos == 0) ? 1u : 0u;
         const uint32_t last = (j == w_nb - 1 || gpos == n_total - 1) ? 1u : 0u;
         s_desc[pos + c] = u32x4_t{static_cast<uint32_t>(j),
@@ -578,7 +580,7 @@ decode_stream_kernel(StreamArgs a) {
             ++w_s;
             w_L = (w_s < B) ? len_of(w_s) : 0;
           } while (w_L == 0 && w_s + 1 < B);
-          w_nb = (w_L + kBlock - 1) / kBlock;
+          w_nb = (w_L + kTile - 1) / kTile;
           w_jf = first_blk(w_L);
         }
         w_j = w_jf;
@@ -594,15 +596,18 @@ decode_stream_kernel(StreamArgs a) {
         if (e < n) {
           const u32x4_t d = s_desc[e];
           ids[r] = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(
-              tbl_rsrc, (static_cast<int>(d[2] & kSeqMask) * a.max_blocks + static_cast<int>(d[0])) * 4, 0, 0));
+              tbl_rsrc, (static_cast<int>(d[2] & kSeqMask) * a.max_blocks +
+                         static_cast<int>(d[0] >> a.sub_shift)) * 4, 0, 0));
         }
       }
 #pragma unroll
       for (int r = 0; r < kGather; ++r) {
         const int e = e0 + 64 * r + lane;
         if (e < n) {
+          // tile j of the sequence is sub-tile j % (tiles per block) of its block
           const uint32_t g = (s_desc[e][1] >> 7) & 511u;
-          s_desc[e][0] = static_cast<uint32_t>(ids[r]) * static_cast<uint32_t>(hkv) + g;
+          const uint32_t u = s_desc[e][0] & ((1u << a.sub_shift) - 1u);
+          s_desc[e][0] = ((static_cast<uint32_t>(ids[r]) * static_cast<uint32_t>(hkv) + g) << a.sub_shift) + u;
         }
       }
     }
@@ -618,7 +623,7 @@ decode_stream_kernel(StreamArgs a) {
         const uint32_t tile = __builtin_amdgcn_readfirstlane(d[0]);
         const uint32_t info = __builtin_amdgcn_readfirstlane(d[1]);
         const int s = __builtin_amdgcn_readfirstlane(static_cast<int>(d[2] & kSeqMask));
-        k_nrec = min(static_cast<int>(info & 31u), kBlock) * kRowBytes;   // rows past the context read 0
+        k_nrec = min(static_cast<int>(info & 31u), kTile) * kRowBytes;   // rows past the context read 0
         v_nrec = k_nrec;
         tile_off = static_cast<int64_t>(tile) * kTileBytes;
         if (info & 32u) {
@@ -684,10 +689,10 @@ decode_stream_kernel(StreamArgs a) {
       // window start: tile rows below `lo` are cut (never, without a window)
       const uint32_t wcode =
           static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(d[2]))) >> kSeqBits;
-      int lo = -kBlock;
+      int lo = -kTile;
       if (wcode != 0u) {
         const int j_local = t_begin + done + t - __builtin_amdgcn_readfirstlane(static_cast<int>(d[3]));
-        lo = static_cast<int>(wcode) - (kBlock + 1) + t_row - kBlock * j_local;
+        lo = static_cast<int>(wcode) - (kTile + 1) + t_row - kTile * j_local;
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -827,7 +832,7 @@ __global__ void __launch_bounds__(64)
 decode_simple_kernel(const char* __restrict__ k_cache, const char* __restrict__ v_cache,
                      const void* __restrict__ q, const int32_t* __restrict__ block_tables,
                      const int32_t* __restrict__ context_lens, int max_blocks, int hkv,
-                     int group, int hq, int chunk, int window, float logit_scale,
+                     int bs, int group, int hq, int chunk, int window, float logit_scale,
                      float v_scale, PartOut po) {
   constexpr int kPer = kD / 64;
   const int part = blockIdx.x;
@@ -870,8 +875,8 @@ decode_simple_kernel(const char* __restrict__ k_cache, const char* __restrict__ 
 #pragma unroll
   for (int i = 0; i < kPer; ++i) o[i] = 0.f;
   for (int t = t0; t < t1; ++t) {
-    const int64_t id = block_tables[static_cast<int64_t>(s) * max_blocks + t / kBlock];
-    const int64_t base = ((id * hkv + g) * kBlock + t % kBlock) * kD;
+    const int64_t id = block_tables[static_cast<int64_t>(s) * max_blocks + t / bs];
+    const int64_t base = ((id * hkv + g) * bs + t % bs) * kD;
     float dot = 0.f;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) dot = fmaf(qv[i], elem(k_cache, base + lane + 64 * i), dot);
@@ -929,14 +934,14 @@ reduce_kernel(const int32_t* __restrict__ context_lens, int hq, int chunk, PartO
 
 template <int kD>
 void launch_simple(int fmt, dim3 grid, hipStream_t st, const char* kc, const char* vc,
-                   const void* q, const int32_t* bt, const int32_t* cl, int maxb, int hkv,
+                   const void* q, const int32_t* bt, const int32_t* cl, int maxb, int hkv, int bs,
                    int G, int hq, int T, int W, float ls, float vs, PartOut po) {
   if (fmt == PA_F32)
-    decode_simple_kernel<kD, PA_F32, true><<<grid, 64, 0, st>>>(kc, vc, q, bt, cl, maxb, hkv, G, hq, T, W, ls, vs, po);
+    decode_simple_kernel<kD, PA_F32, true><<<grid, 64, 0, st>>>(kc, vc, q, bt, cl, maxb, hkv, bs, G, hq, T, W, ls, vs, po);
   else if (fmt == PA_BF16)
-    decode_simple_kernel<kD, PA_BF16, false><<<grid, 64, 0, st>>>(kc, vc, q, bt, cl, maxb, hkv, G, hq, T, W, ls, vs, po);
+    decode_simple_kernel<kD, PA_BF16, false><<<grid, 64, 0, st>>>(kc, vc, q, bt, cl, maxb, hkv, bs, G, hq, T, W, ls, vs, po);
   else
-    decode_simple_kernel<kD, PA_FP8_E4M3, false><<<grid, 64, 0, st>>>(kc, vc, q, bt, cl, maxb, hkv, G, hq, T, W, ls, vs, po);
+    decode_simple_kernel<kD, PA_FP8_E4M3, false><<<grid, 64, 0, st>>>(kc, vc, q, bt, cl, maxb, hkv, bs, G, hq, T, W, ls, vs, po);
 }
 
 
@@ -961,9 +966,9 @@ int num_partitions(int32_t max_context_len) {
   return (max_context_len + kPartTokens - 1) / kPartTokens;
 }
 
-bool fast_path(int fmt, int q_dtype, int G, int D) {
+bool fast_path(int fmt, int q_dtype, int G, int D, int bs) {
   return (fmt == PA_BF16 || fmt == PA_FP8_E4M3) && q_dtype == PA_BF16 && G >= 1 &&
-         G <= kMaxRows && (D == 64 || D == 128);
+         G <= kMaxRows && (D == 64 || D == 128) && bs % kTile == 0;
 }
 
 // Chunk tokens per fast-path pass: as many as fit G rows each in 16 columns.
@@ -1011,7 +1016,7 @@ size_t workspace_bytes_for(const pa_cache_desc* c, int32_t num_seqs, int32_t num
     return 0;
   const int G = num_q_heads / c->num_kv_heads;
   const int q_dtype = (c->cache_dtype == PA_F32) ? PA_F32 : PA_BF16;
-  if (fast_path(c->cache_dtype, q_dtype, G, c->head_dim))
+  if (fast_path(c->cache_dtype, q_dtype, G, c->head_dim, c->block_size))
     return stream_workspace_bytes(num_seqs, c->num_kv_heads, G * tokens_per_pass(G, T),
                                   c->head_dim);
   return general_workspace_bytes(num_seqs, num_q_heads, T, c->head_dim, max_context_len);
@@ -1043,18 +1048,20 @@ pa_status attend(const char* fn, const pa_cache_desc* c, const void* k_cache,
                         (fmt == PA_FP8_E4M3 && q_dtype == PA_BF16);
   if (!combo_ok)
     return fail(PA_ERR_UNSUPPORTED, "%s: q dtype %d with cache dtype %d", fn, q_dtype, fmt);
-  if (static_cast<int64_t>(max_blocks_per_seq) * kBlock < max_context_len)
+  const int bs = c->block_size;
+  if (static_cast<int64_t>(max_blocks_per_seq) * bs < max_context_len)
     return fail(PA_ERR_INVALID_ARG, "%s: max_blocks_per_seq %d cannot hold max_context_len %d",
                 fn, max_blocks_per_seq, max_context_len);
   if (num_seqs == 0) return PA_OK;
   if (!k_cache || !v_cache || !q || !out || !block_tables || !context_lens)
     return fail(PA_ERR_INVALID_ARG, "%s: null pointer", fn);
   const int G = num_q_heads / hkv;
-  const bool fast = fast_path(fmt, q_dtype, G, D);
+  const bool fast = fast_path(fmt, q_dtype, G, D, bs);
   const int tpp = tokens_per_pass(G, T);
   const int64_t max_tiles = static_cast<int64_t>(hkv) * num_seqs *
-                            ((static_cast<int64_t>(max_context_len) + kBlock - 1) / kBlock);
+                            ((static_cast<int64_t>(max_context_len) + kTile - 1) / kTile);
   if (fast && (max_tiles >= (int64_t{1} << 30) || num_seqs > static_cast<int32_t>(kSeqMask) ||
+               static_cast<int64_t>(c->num_blocks) * hkv * (bs / kTile) >= (int64_t{1} << 32) ||
                static_cast<int64_t>(max_blocks_per_seq) * 4 >= (int64_t{1} << 31) ||
                (static_cast<int64_t>(T - 1) * num_q_heads + G) * D * 2 >= (int64_t{1} << 30)))
     return fail(PA_ERR_UNSUPPORTED, "%s: %lld tiles in one call (limit 2^30)", fn,
@@ -1102,6 +1109,7 @@ pa_status attend(const char* fn, const pa_cache_desc* c, const void* k_cache,
     a.group = G;
     a.chunk = T;
     a.window = W;
+    a.sub_shift = bs == 64 ? 2 : bs == 32 ? 1 : 0;
     a.logit_scale = logit_scale;
     a.v_scale = vscale;
     // one pass per tpp chunk tokens; each pass leaves the counters zeroed
@@ -1127,10 +1135,10 @@ pa_status attend(const char* fn, const pa_cache_desc* c, const void* k_cache,
     dim3 grid(P, rows, num_seqs);
     if (D == 128)
       launch_simple<128>(fmt, grid, s, kc, vc, q, block_tables, context_lens,
-                         max_blocks_per_seq, hkv, G, num_q_heads, T, W, logit_scale, vscale, po);
+                         max_blocks_per_seq, hkv, bs, G, num_q_heads, T, W, logit_scale, vscale, po);
     else
       launch_simple<64>(fmt, grid, s, kc, vc, q, block_tables, context_lens,
-                        max_blocks_per_seq, hkv, G, num_q_heads, T, W, logit_scale, vscale, po);
+                        max_blocks_per_seq, hkv, bs, G, num_q_heads, T, W, logit_scale, vscale, po);
   }
   st = launch_status(fn);
   if (st != PA_OK) return st;

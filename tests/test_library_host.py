@@ -418,13 +418,13 @@ def _apply_prefix(bm, op, args):
     raise AssertionError(op)
 
 
-@pytest.mark.parametrize("seed", [1, 2, 3, 4])
-def test_cpp_prefix_cache_matches_oracle_under_random_scripts(seed):
+@pytest.mark.parametrize("seed,bs", [(1, 16), (2, 16), (3, 16), (4, 16), (5, 8), (6, 32), (7, 64)])
+def test_cpp_prefix_cache_matches_oracle_under_random_scripts(seed, bs):
     rng = np.random.default_rng(seed)
-    N, H = 80, 40
+    N, H = 80 if bs <= 16 else 200, 40 if bs <= 16 else 100
     order = rng.permutation(N)
-    ref = oracle.RefBlockManager(N, free_order=order, num_host_blocks=H)
-    cpp = pk.BlockManager(N, free_order=order, num_host_blocks=H)
+    ref = oracle.RefBlockManager(N, free_order=order, num_host_blocks=H, block_size=bs)
+    cpp = pk.BlockManager(N, free_order=order, num_host_blocks=H, block_size=bs)
     ref.enable_prefix_caching()
     cpp.enable_prefix_caching()
     prefixes = [[int(x) for x in rng.integers(-5, 40, int(rng.integers(0, 90)))] for _ in range(5)]
