@@ -35,7 +35,11 @@ The JSON line also carries
     ``traffic`` is the HBM bytes per call from the committed rocprofv3
     counter summary, when that was taken on the current kernel source;
   * ``cpu_baseline``: the CPU float64 oracle's decode of the same batch on the
-    host, single-threaded.
+    host, single-threaded;
+  * ``stream_read_probe``: context for the roofline fraction -- the rate
+    pa_read_probe streams a 4 GiB buffer at with the decode kernel's load
+    form, in address order and in 4 KiB chunks visited in a seeded random
+    order (the paged pattern), and decode's fraction of the latter.
 
 With ``--chunk T`` (T = 2..16) each step brings T new tokens per sequence
 instead of one -- a draft-verification or chunked-prefill step: T appends per
@@ -181,6 +185,32 @@ def _traffic_per_call(kv_bytes, T=1):
     if not (m_src and m_r and m_w) or m_src.group(1) != kernel_source_sha256():
         return None
     return float(m_r.group(1)) * kv_bytes + float(m_w.group(1))
+
+
+def stream_read_probe(dev, stream, gib=4, reps=3):
+    """GB/s of pa_read_probe over a ``gib`` GiB buffer: (in order, random 4 KiB)."""
+    import torch
+    import paged_kv_cache_421_amd as pk
+    n = gib << 30
+    buf = torch.empty(n, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    order = torch.randperm(n // 4096, device=dev, generator=g).to(torch.int32)
+    sink = pk.read_probe(buf, stream=stream)
+    out = []
+    for o in (None, order):
+        pk.read_probe(buf, o, sink, stream=stream)             # warm
+        e0, e1 = HipEvent(), HipEvent()
+        e0.record(stream)
+        for _ in range(reps):
+            pk.read_probe(buf, o, sink, stream=stream)
+        e1.record(stream)
+        out.append(round(reps * n / (e0.elapsed_ms(e1) / 1e3) / 1e9, 1))
+        e0.destroy()
+        e1.destroy()
+    del buf, order, sink
+    return out[0], out[1]
 
 
 def cpu_baseline(w, budget_s=10.0, T=1):
@@ -763,6 +793,11 @@ def main():
             "traffic": None if traffic is None else round(traffic / mean_dec_s / 1e9, 1),
         },
     }
+    if T == 1 and not args.window and bs == 16:
+        seq_gbps, rnd_gbps = stream_read_probe(dev, stream)
+        res["stream_read_probe"] = {"in_order_gbps": seq_gbps, "random_4k_gbps": rnd_gbps,
+                                    "decode_frac_of_random_4k": round(achieved / rnd_gbps, 4)}
+        _log(f"bench: read probe {seq_gbps} GB/s in order, {rnd_gbps} GB/s random 4 KiB chunks")
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)

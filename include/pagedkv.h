@@ -360,6 +360,22 @@ pa_status pa_swap_blocks(const pa_cache_desc* c, const void* src_k, const void* 
                          void* dst_k, void* dst_v, const int32_t* pairs,
                          int32_t num_pairs, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Diagnostics (not part of the attention path).
+ *
+ * pa_read_probe -- reads floor(bytes / 4096) chunks of 4 KiB of the device
+ * buffer `buf` with the decode kernel's load form (16-byte non-temporal
+ * buffer loads), 8 waves per compute unit: in address order, or, with
+ * chunk_order (int32 [chunks], device memory, each < chunks), chunk c taken
+ * from offset chunk_order[c] * 4096 -- the scattered pattern of paged
+ * blocks.  Timing a call gives the streaming-read rate decode's bandwidth is
+ * compared with.  sink: device scratch of pa_read_probe_sink_bytes(num_cus)
+ * bytes (its contents are meaningless).
+ * ------------------------------------------------------------------------- */
+size_t pa_read_probe_sink_bytes(int32_t num_cus);
+pa_status pa_read_probe(const void* buf, size_t bytes, const int32_t* chunk_order,
+                        void* sink, int32_t num_cus, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -208,6 +208,20 @@ def decode_chunk(desc: CacheDesc, k_cache: torch.Tensor, v_cache: torch.Tensor,
     return out
 
 
+def read_probe(buf: torch.Tensor, chunk_order: Optional[torch.Tensor] = None,
+               sink: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """pa_read_probe: stream ``buf`` (device) in 4 KiB chunks, in order or in
+    ``chunk_order`` (int32 device tensor).  Returns the sink tensor."""
+    cus = torch.cuda.get_device_properties(buf.device).multi_processor_count
+    if sink is None:
+        sink = torch.empty(lib.pa_read_probe_sink_bytes(cus) // 4, dtype=torch.int32,
+                           device=buf.device)
+    order = ctypes.c_void_p(0) if chunk_order is None else _dev(chunk_order, "chunk_order")
+    check(lib.pa_read_probe(_dev(buf, "buf"), buf.numel() * buf.element_size(), order,
+                            _dev(sink, "sink"), cus, _stream(stream)))
+    return sink
+
+
 def _ptr(a: np.ndarray) -> ctypes.c_void_p:
     return ctypes.c_void_p(a.ctypes.data)
 
