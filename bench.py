@@ -59,10 +59,14 @@ as context.
 With ``--prefix`` the batch is 256 requests sharing a 2048-token system
 prompt, each with its own 64..512-token question, built with prefix
 caching (the prompt's blocks are stored once and shared); the step is the
-decode step above.  The roofline takes the unique KV bytes a call reads
-(shared blocks once), the logical bytes (every sequence's whole context)
-are reported beside them, with the block manager's hit rate and that of a
-simulated multi-turn chat.
+decode step above, with the block manager's shared-prefix groups and
+pa_decode_shared_prefix (the prompt attended once per KV head for all 256
+requests, then each request's own blocks) unless ``--prefix-path plain``
+asks for pa_decode over every whole context.  The roofline takes the unique
+KV bytes a call reads (shared blocks once) over the whole call; the logical
+bytes (every sequence's whole context) are reported beside them, with the
+other path's time on the final batch, the block manager's hit rate and that
+of a simulated multi-turn chat.
 
 With ``--window W`` the decode (or chunk) step attends only the last W
 positions of each context (pa_decode_window); the roofline's algorithmic
@@ -474,7 +478,9 @@ def run_prefix(args):
     out = [torch.empty_like(q[0]) for _ in range(NL)]
     max_len_final = int(lens.max()) + steps + warm
     cap = -(-max_len_final // 16)
+    cascade = args.prefix_path == "cascade"
     workspace = pk.new_decode_workspace(desc, B, Hq, max_len_final, dev)
+    sp_workspace = pk.new_shared_prefix_workspace(desc, B, Hq, cap, max_len_final, dev)
     h_slots = torch.empty(B, dtype=torch.int64, pin_memory=True)
     h_bt = torch.empty((B, cap), dtype=torch.int32, pin_memory=True)
     h_cl = torch.empty(B, dtype=torch.int32, pin_memory=True)
@@ -483,6 +489,14 @@ def run_prefix(args):
     d_cl = torch.empty(B, dtype=torch.int32, device=dev)
     ids = np.arange(B, dtype=np.int64)
     nfull = P // 16
+
+    def attend(l, groups, max_len):
+        if groups is not None:
+            pk.decode_shared_prefix(desc, kc[l], vc[l], q[l], out[l], d_bt, d_cl, max_len,
+                                    float(w.scale), groups, sp_workspace, stream=stream)
+        else:
+            pk.decode(desc, kc[l], vc[l], q[l], out[l], d_bt, d_cl, max_len, float(w.scale),
+                      workspace, stream=stream)
 
     def step(ev_pairs):
         torch.cuda.current_stream().synchronize()        # host buffers are reused
@@ -494,12 +508,12 @@ def run_prefix(args):
         d_bt.copy_(h_bt, non_blocking=True)
         d_cl.copy_(h_cl, non_blocking=True)
         max_len = int(lens.max())
+        groups = bm.shared_prefix_groups(ids) if cascade else None
         for l in range(NL):
             pk.write_kv(desc, kc[l], vc[l], k_new[l], v_new[l], d_slots, stream=stream)
             if ev_pairs is not None:
                 ev_pairs[l][0].record(stream)
-            pk.decode(desc, kc[l], vc[l], q[l], out[l], d_bt, d_cl, max_len, float(w.scale),
-                      workspace, stream=stream)
+            attend(l, groups, max_len)
             if ev_pairs is not None:
                 ev_pairs[l][1].record(stream)
         logical = int(lens.sum()) * Hkv * D * 4
@@ -525,10 +539,27 @@ def run_prefix(args):
     logical = statistics.mean(p[0] for p in per)
     unique = statistics.mean(p[1] for p in per)
     ach = unique / mean_s / 1e9
+    # the other path on the final batch, for comparison (not the timed value)
+    final_groups = bm.shared_prefix_groups(ids)
+    other = []
+    for _ in range(3):
+        for l in range(NL):
+            a, b = HipEvent(), HipEvent()
+            a.record(stream)
+            attend(l, None if cascade else final_groups, int(lens.max()))
+            b.record(stream)
+            other.append((a, b))
+    torch.cuda.synchronize()
+    other_us = statistics.mean(a.elapsed_ms(b) for a, b in other[NL:]) * 1e3
+    for a, b in other:
+        a.destroy()
+        b.destroy()
+    name = "pa_decode_shared_prefix" if cascade else "pa_decode"
+    other_name = "pa_decode" if cascade else "pa_decode_shared_prefix"
     chat_rate, chat_q, lookup_us = chat_hit_rate()
-    _log(f"bench: pa_decode mean {mean_s * 1e6:.1f} us: unique {unique / 1e9:.3f} GB "
+    _log(f"bench: {name} mean {mean_s * 1e6:.1f} us: unique {unique / 1e9:.3f} GB "
          f"({ach:.0f} GB/s), logical {logical / 1e9:.3f} GB ({logical / mean_s / 1e9:.0f} GB/s); "
-         f"chat hit rate {chat_rate:.4f}")
+         f"{other_name} on the final batch {other_us:.1f} us; chat hit rate {chat_rate:.4f}")
     res = {
         "metric": METRIC_PREFIX,
         "value": round(B * NL * steps / wall, 1),
@@ -542,7 +573,9 @@ def run_prefix(args):
                                 "system prompt plus their own 64..512-token questions, built "
                                 "through prefix caching"),
                    "layers_per_step": NL,
-                   "step": "block-manager append + table upload + per layer pa_write_kv and pa_decode",
+                   "step": ("block-manager append + table upload" +
+                            (" + shared-prefix groups" if cascade else "") +
+                            f" + per layer pa_write_kv and {name}"),
                    "value_is": "sequences decoded per second per attention layer",
                    "parallelism": "single GPU"},
         "block_cache_hit_rate": round(hits / queried, 4),
@@ -550,10 +583,15 @@ def run_prefix(args):
         "unique_kv_gb": round(unique / 1e9, 4), "logical_kv_gb": round(logical / 1e9, 4),
         "logical_kv_gbps": round(logical / mean_s / 1e9, 1),
         "decode_us_mean": round(mean_s * 1e6, 2),
+        "decode_path": name,
+        "other_path": {"name": other_name, "us_on_final_batch": round(other_us, 2)},
         "chat_sim": {"hit_rate": round(chat_rate, 4), "queried_blocks": chat_q,
                      "conversations": 64, "turns": 8,
                      "us_per_prompt_lookup": round(lookup_us, 2)},
-        "roofline": {"kernel": "decode_stream_kernel (pa_decode over shared prompt blocks)",
+        "roofline": {"kernel": ("shared_prefix_prep_kernel + shared_prefix_kernel + "
+                               "decode_stream_kernel (pa_decode_shared_prefix, whole call)"
+                               if cascade else
+                               "decode_stream_kernel (pa_decode over shared prompt blocks)"),
                      "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None},
     }
@@ -576,6 +614,8 @@ def main():
                     help="sliding window of W positions (0: none)")
     ap.add_argument("--prefix", action="store_true",
                     help="decode a batch that shares a system prompt through prefix caching")
+    ap.add_argument("--prefix-path", choices=("cascade", "plain"), default="cascade",
+                    help="with --prefix: pa_decode_shared_prefix (default) or pa_decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     args = ap.parse_args()

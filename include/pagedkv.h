@@ -345,6 +345,50 @@ pa_status pa_bm_append_token_ids(pa_bm* bm, int64_t seq_id, const int32_t* token
 pa_status pa_bm_cache_stats(const pa_bm* bm, int64_t* queried_blocks, int64_t* hit_blocks,
                             int32_t* registered_blocks, int32_t* evictable_blocks);
 
+/* ---------------------------------------------------------------------------
+ * Shared prefixes: attention over a prompt prefix that several sequences
+ * share is computed once for all of them (prefix caching makes such
+ * sharing common: explore.n1n.ai, "vLLM 深度解析", section "vLLM 生态的核心功能
+ * 亮点"; ybb.press §7.3).
+ *
+ * pa_bm_shared_prefix_groups -- runs of adjacent sequences of seq_ids (in
+ * that order) whose tables start with the same block, as groups[k] =
+ * (index in seq_ids of the first member, member count, shared blocks):
+ * shared = the longest common run of leading table entries that leaves
+ * every member at least one more token (shared * block_size < length).
+ * Runs of one sequence or with nothing shared are left out.  groups: host
+ * int32 [cap][3]; *num_groups receives the count (PA_ERR_INVALID_ARG if it
+ * would exceed cap).
+ *
+ * pa_decode_shared_prefix -- pa_decode for a batch in which groups[k] =
+ * (first, count, shared) says sequences first .. first+count-1 hold the
+ * same valid block ids in their first `shared` table entries (host array,
+ * at most 32 disjoint groups; a member no longer than shared * block_size
+ * sees only its own length of them).  The result is pa_decode's (up to
+ * rounding order); the prefix is attended once per
+ * (group, KV head) on MFMA with all members' query rows and folded into each
+ * row by the log-sum-exp rule, then the suffixes are decoded as usual.
+ * Needs the bf16 / fp8 fast path (head_dim 64 or 128, G <= 16, block size a
+ * multiple of 16), single-token decode.  workspace: zero-filled before first
+ * use, 256-byte aligned, pa_decode_shared_prefix_workspace_bytes(...) bytes;
+ * it holds suffix tables and lengths and per-row prefix records besides
+ * pa_decode's scratch.  num_groups = 0 is pa_decode.
+ * ------------------------------------------------------------------------- */
+pa_status pa_bm_shared_prefix_groups(const pa_bm* bm, const int64_t* seq_ids, int32_t n,
+                                     int32_t* groups, int32_t cap, int32_t* num_groups);
+size_t pa_decode_shared_prefix_workspace_bytes(const pa_cache_desc* c, int32_t num_seqs,
+                                               int32_t num_q_heads,
+                                               int32_t max_blocks_per_seq,
+                                               int32_t max_context_len);
+pa_status pa_decode_shared_prefix(const pa_cache_desc* c, const void* k_cache,
+                                  const void* v_cache, const void* q, int32_t q_dtype,
+                                  void* out, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                  int32_t max_context_len, int32_t num_seqs,
+                                  int32_t num_q_heads, float scale, const int32_t* groups,
+                                  int32_t num_groups, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 /*
  * pa_swap_blocks -- whole-block copies between two pools with the layout of
  * `c`: for each pairs[i] = (s, d), block d of dst_k / dst_v receives block s

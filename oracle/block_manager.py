@@ -428,6 +428,37 @@ class RefBlockManager:
         """Move the listed sequences back to device blocks; (host, device) pairs."""
         return self._move(seqs, False)
 
+    # -- shared prefixes ---------------------------------------------------
+    def shared_prefix_groups(self, seq_ids) -> List[Tuple[int, int, int]]:
+        """Runs of adjacent sequences (in the given order) whose tables start
+        with the same block, as (index of the first, count, shared blocks):
+        shared = the longest common run of leading table entries that are
+        full blocks and leave every member at least one more token
+        (shared * bs < L).  Runs of one sequence, or with no shared block,
+        are left out.  Reading: the pages say requests with a common prefix
+        share its blocks; attention over such a prefix is computed once for
+        all of them."""
+        ids = [int(s) for s in seq_ids]
+        out = []
+        i = 0
+        while i < len(ids):
+            t0 = self._get_dev(ids[i])
+            j = i + 1
+            while j < len(ids) and self._get_dev(ids[j])[:1] == t0[:1] and t0:
+                j += 1
+            if j - i >= 2:
+                m = min((self.lens[ids[k]] - 1) // self.bs for k in range(i, j))
+                for k in range(i + 1, j):
+                    t = self.tables[ids[k]]
+                    c = 0
+                    while c < min(len(t), len(t0)) and t[c] == t0[c]:
+                        c += 1
+                    m = min(m, c)
+                if m >= 1:
+                    out.append((i, j - i, m))
+            i = j
+        return out
+
     # -- packing -----------------------------------------------------------
     def pack(self, seq_ids, cap: int):
         """block_tables int32 [n, cap] padded with -1, context_lens int32 [n]."""

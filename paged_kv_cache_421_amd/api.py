@@ -208,6 +208,46 @@ def decode_chunk(desc: CacheDesc, k_cache: torch.Tensor, v_cache: torch.Tensor,
     return out
 
 
+def shared_prefix_workspace_bytes(desc: CacheDesc, num_seqs: int, num_q_heads: int,
+                                  max_blocks_per_seq: int, max_context_len: int) -> int:
+    return int(lib.pa_decode_shared_prefix_workspace_bytes(
+        ctypes.byref(desc.c), int(num_seqs), int(num_q_heads), int(max_blocks_per_seq),
+        int(max_context_len)))
+
+
+def new_shared_prefix_workspace(desc: CacheDesc, num_seqs: int, num_q_heads: int,
+                                max_blocks_per_seq: int, max_context_len: int,
+                                device=None) -> torch.Tensor:
+    n = shared_prefix_workspace_bytes(desc, num_seqs, num_q_heads, max_blocks_per_seq,
+                                      max_context_len)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=device or "cuda")
+    decode_workspace_init(ws)
+    return ws
+
+
+def decode_shared_prefix(desc: CacheDesc, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                         q: torch.Tensor, out: torch.Tensor, block_tables: torch.Tensor,
+                         context_lens: torch.Tensor, max_context_len: int, scale: float,
+                         groups, workspace: Optional[torch.Tensor] = None,
+                         stream=None) -> torch.Tensor:
+    """pa_decode_shared_prefix: pa_decode, with the shared prefix of each
+    group (host int32 [k, 3] of (first, count, shared blocks)) attended once."""
+    B, Hq, D = q.shape
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must have q's shape and dtype")
+    grp = np.ascontiguousarray(groups, dtype=np.int32).reshape(-1, 3)
+    if workspace is None:
+        workspace = new_shared_prefix_workspace(desc, B, Hq, block_tables.shape[1],
+                                                max_context_len, q.device)
+    check(lib.pa_decode_shared_prefix(
+        ctypes.byref(desc.c), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(q, "q"),
+        dtype_code(q.dtype), _dev(out, "out"), _dev(block_tables, "block_tables"),
+        block_tables.shape[1], _dev(context_lens, "context_lens"), int(max_context_len), B, Hq,
+        float(scale), _ptr(grp), len(grp), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
 def read_probe(buf: torch.Tensor, chunk_order: Optional[torch.Tensor] = None,
                sink: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """pa_read_probe: stream ``buf`` (device) in 4 KiB chunks, in order or in
@@ -321,6 +361,16 @@ class BlockManager:
         check(lib.pa_bm_cache_stats(self._h, ctypes.byref(q), ctypes.byref(h), ctypes.byref(r),
                                     ctypes.byref(e)))
         return q.value, h.value, r.value, e.value
+
+    def shared_prefix_groups(self, seq_ids) -> np.ndarray:
+        """pa_bm_shared_prefix_groups: int32 [k, 3] of (first index, count, shared blocks)."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        cap = max(len(ids) // 2, 1)
+        out = np.empty((cap, 3), dtype=np.int32)
+        n = ctypes.c_int32()
+        check(lib.pa_bm_shared_prefix_groups(self._h, _ptr(ids), len(ids), _ptr(out), cap,
+                                             ctypes.byref(n)))
+        return out[:n.value].copy()
 
     def num_free_host(self) -> int:
         return int(lib.pa_bm_num_free_host(self._h))

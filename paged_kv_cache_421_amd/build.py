@@ -24,9 +24,14 @@ ARCH = os.environ.get("PAGEDKV_ARCH", "gfx950")
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 CXX = shutil.which("g++") or "g++"
 
-# Packed fp32 instructions are disabled for all device code.
+# Packed fp32 instructions are disabled for all device code.  MFMA results
+# are kept in VGPRs (the accumulator registers are left for spills): the
+# kernels rescale their accumulators with ordinary vector arithmetic, which
+# cannot read accumulator registers, so the default placement copies every
+# accumulator out and back on each tile.
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
              "-I", CSRC, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-mllvm", "-amdgpu-mfma-vgpr-form",
              "-Wall", "-Wno-unused-function"]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wextra"]
 

@@ -31,6 +31,7 @@
 // appends, while the block is still shared) and the all-or-nothing rule make
 // the tables reproducible; they are readings, the pages fix none of them.
 #include <array>
+#include <algorithm>
 #include <cstdint>
 #include <deque>
 #include <iterator>
@@ -398,6 +399,51 @@ pa_status pa_bm_add_seq_prompt(pa_bm* bm, int64_t seq_id, const int32_t* tokens,
     bm->note_token(stored, tokens[p]);
   }
   *num_cached = nc;
+  return PA_OK;
+}
+
+pa_status pa_bm_shared_prefix_groups(const pa_bm* bm, const int64_t* seq_ids, int32_t n,
+                                     int32_t* groups, int32_t cap, int32_t* num_groups) {
+  if (!bm || !num_groups || n < 0 || cap < 0 || (n > 0 && !seq_ids) || (cap > 0 && !groups))
+    return fail(PA_ERR_INVALID_ARG, "pa_bm_shared_prefix_groups: bad argument");
+  std::vector<const Seq*> ss(n);
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = bm->seqs.find(seq_ids[i]);
+    if (it == bm->seqs.end())
+      return fail(PA_ERR_UNKNOWN_SEQ, "pa_bm_shared_prefix_groups: unknown sequence %lld",
+                  (long long)seq_ids[i]);
+    if (it->second.on_host)
+      return fail(PA_ERR_SWAPPED, "pa_bm_shared_prefix_groups: sequence %lld is swapped out",
+                  (long long)seq_ids[i]);
+    ss[i] = &it->second;
+  }
+  int32_t k = 0;
+  for (int32_t i = 0; i < n;) {
+    const std::vector<int32_t>& t0 = ss[i]->table;
+    int32_t j = i + 1;
+    while (j < n && !t0.empty() && !ss[j]->table.empty() && ss[j]->table[0] == t0[0]) ++j;
+    if (j - i >= 2) {
+      int32_t m = INT32_MAX;
+      for (int32_t r = i; r < j; ++r) m = std::min(m, (ss[r]->len - 1) / bm->bs);
+      for (int32_t r = i + 1; r < j; ++r) {
+        const std::vector<int32_t>& t = ss[r]->table;
+        int32_t c = 0;
+        const int32_t lim = static_cast<int32_t>(std::min(t.size(), t0.size()));
+        while (c < lim && t[c] == t0[c]) ++c;
+        m = std::min(m, c);
+      }
+      if (m >= 1) {
+        if (k >= cap)
+          return fail(PA_ERR_INVALID_ARG, "pa_bm_shared_prefix_groups: more than %d groups", cap);
+        groups[3 * k] = i;
+        groups[3 * k + 1] = j - i;
+        groups[3 * k + 2] = m;
+        ++k;
+      }
+    }
+    i = j;
+  }
+  *num_groups = k;
   return PA_OK;
 }
 

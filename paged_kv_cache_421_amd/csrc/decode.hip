@@ -51,9 +51,12 @@
 // plus a separate log-sum-exp reduce kernel.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <mutex>
 #include <type_traits>
+#include <utility>
+#include <vector>
 
 #include "device_common.h"
 #include "status.h"
@@ -137,6 +140,20 @@ __device__ __forceinline__ int wave_sum(int x) {
   for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d);
   return __builtin_amdgcn_readfirstlane(x);
 }
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations, then for the other waves; global loads stay in flight (a
+// full __syncthreads also waits for every outstanding global access).  The
+// memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Maximum over the 64 lanes of a wave, as a wave-uniform value.
+__device__ __forceinline__ int wave_max_int(int x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x = max(x, __shfl_xor(x, d));
+  return __builtin_amdgcn_readfirstlane(x);
+}
 
 // Result of one (partition, query head or KV head, sequence) of the general
 // path: either the final output rows, or partial results for the reduce.
@@ -178,6 +195,13 @@ struct StreamArgs {
   int chunk;                  // T: new tokens per sequence
   int window;                 // W > 0: attend only the last W positions; 0: all
   int sub_shift;              // log2(block size / 16): tiles per block = 1 << sub_shift
+  // shared prefixes (null when unused): a sequence with prefix_len[s] > 0
+  // has the attention over its first prefix_len[s] positions in
+  // prefix_rec[(s*Hq + h)*(kD + 4)]: unnormalised o[kD], max m (log2 units),
+  // sum l, 2 floats of padding (16-byte rows); the tables and lengths this
+  // kernel reads are the suffixes'.
+  const int32_t* prefix_len;
+  const float* prefix_rec;
   int t_first;                // first chunk token of this pass
   int rows;                   // query rows of this pass (<= kMaxRows)
   float logit_scale;          // scale * k_scale * log2(e)
@@ -237,8 +261,25 @@ decode_stream_kernel(StreamArgs a) {
       for (uint64_t m = empty; m != 0; m &= m - 1) {
         const int se = s0 + 64 * r + __builtin_ctzll(m);
         uint16_t* orow = a.out + (static_cast<int64_t>(se) * nchunk + a.t_first) * hq * kD;
-        for (int i = lane; i < (R / G) * hq * kD / 8; i += 64)
-          reinterpret_cast<u32x4_t*>(orow)[i] = u32x4_t{0u, 0u, 0u, 0u};
+        if (a.prefix_len != nullptr && a.prefix_len[se] > 0) {
+          // all of it is shared prefix (single-token decode): its record alone
+          for (int i = lane; i < hq * kD / 8; i += 64) {
+            const int h = i / (kD / 8), d0 = 8 * i - h * kD;
+            const float* rec = a.prefix_rec + (static_cast<int64_t>(se) * hq + h) * (kD + 4);
+            const float lp = rec[kD + 1];
+            const float inv = lp > 0.f ? a.v_scale * __builtin_amdgcn_rcpf(lp) : 0.f;
+            const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(rec + d0);
+            const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(rec + d0 + 4);
+            const bf16x8_t v = {static_cast<__bf16>(x0[0] * inv), static_cast<__bf16>(x0[1] * inv),
+                                static_cast<__bf16>(x0[2] * inv), static_cast<__bf16>(x0[3] * inv),
+                                static_cast<__bf16>(x1[0] * inv), static_cast<__bf16>(x1[1] * inv),
+                                static_cast<__bf16>(x1[2] * inv), static_cast<__bf16>(x1[3] * inv)};
+            reinterpret_cast<u32x4_t*>(orow)[i] = __builtin_bit_cast(u32x4_t, v);
+          }
+        } else {
+          for (int i = lane; i < (R / G) * hq * kD / 8; i += 64)
+            reinterpret_cast<u32x4_t*>(orow)[i] = u32x4_t{0u, 0u, 0u, 0u};
+        }
       }
     }
     return wave_sum(c);
@@ -411,7 +452,21 @@ decode_stream_kernel(StreamArgs a) {
     const int wf = seg / per;
     const int wl = (seg + nb - 1) / per;
     if (wf == wl) {   // the whole segment was in this wave: write the output
+      const bool has_prefix = a.prefix_len != nullptr && a.prefix_len[s] > 0;
       if (row_ok) {
+        if (has_prefix) {                                    // fold in the shared prefix
+          const float* rec = a.prefix_rec + (static_cast<int64_t>(s) * hq + g * G + h_row) * (kD + 4);
+          const float mp = rec[kD], lp = rec[kD + 1];
+          const float mn = fmaxf(m_ref, mp);
+          const float fa = __builtin_amdgcn_exp2f(m_ref - mn), fb = __builtin_amdgcn_exp2f(mp - mn);
+          l_tot = l_tot * fa + lp * fb;
+#pragma unroll
+          for (int c = 0; c < kVC; ++c) {
+            const f32x4_t po = *reinterpret_cast<const f32x4_t*>(rec + 16 * c + 4 * quad);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) oacc[c][r] = oacc[c][r] * fa + po[r] * fb;
+          }
+        }
         // a row that saw no position has l = 0 and o = 0: a zero row
         const float inv = (l_tot > 0.f) ? a.v_scale * __builtin_amdgcn_rcpf(l_tot) : 0.f;
         char* srow = s_o + row * kOPitch + 8 * quad;
@@ -530,6 +585,27 @@ decode_stream_kernel(StreamArgs a) {
       if (has_b && !gb) from_lds(ob, mb, lb);
       combine(oa, ma, la);
       if (has_b) combine(ob, mb, lb);
+    }
+    if (a.prefix_len != nullptr && a.prefix_len[s] > 0) {     // fold in the shared prefix
+#pragma unroll
+      for (int i = 0; i < kE4; ++i) {
+        const int q = lane + 64 * i;
+        if (q < n_grp) {
+          const int r = q % R;
+          const int cq = q / R;
+          const int nt = r / G;
+          const float* rec = a.prefix_rec + ((static_cast<int64_t>(s) * nchunk + a.t_first + nt) * hq +
+                                             g * G + (r - nt * G)) * (kD + 4);
+          const float mp = rec[kD], lp = rec[kD + 1];
+          const f32x4_t po = *reinterpret_cast<const f32x4_t*>(rec + 4 * cq);
+          const float mn = fmaxf(M[i], mp);
+          const float fa = __builtin_amdgcn_exp2f(M[i] - mn), fb = __builtin_amdgcn_exp2f(mp - mn);
+          den[i] = den[i] * fa + lp * fb;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) num[i][e] = num[i][e] * fa + po[e] * fb;
+          M[i] = mn;
+        }
+      }
     }
 #pragma unroll
     for (int i = 0; i < kE4; ++i) {
@@ -819,6 +895,358 @@ zero_fill_kernel(uint32_t* p, int64_t n_words) {
     p[i] = 0u;
 }
 
+// ---------------------------------------------------------------------------
+// Shared prefixes.  Sequences first .. first+count-1 of a group share the
+// physical blocks of their first `shared` table entries (a prompt reused
+// through prefix caching).  Attention over those positions is one dense
+// contraction per KV head -- every member's query rows against the same K
+// and V -- so it is computed once per group, on MFMA, with many query rows
+// per tile, and folded into each row's result by the log-sum-exp rule.
+constexpr int kMaxGroups = 32;
+constexpr int kPrefixWaves = 4;    // waves (16 query rows each) per workgroup
+constexpr int kMaxSplits = 8;      // position ranges of a prefix (one record each)
+
+struct PrefixGroups {
+  int num;
+  int first[kMaxGroups];
+  int count[kMaxGroups];
+  int shared[kMaxGroups];          // blocks
+  int wg_begin[kMaxGroups + 1];    // prefix sum of row workgroups: ceil(count * G / 64)
+};
+
+__device__ __forceinline__ int group_of_seq(const PrefixGroups& gr, int s) {
+  for (int i = 0; i < gr.num; ++i)
+    if (s >= gr.first[i] && s < gr.first[i] + gr.count[i]) return i;
+  return -1;
+}
+
+// Suffix tables and lengths of every sequence (grouped ones drop their
+// shared blocks), and prefix_len[s] = shared positions it sees.  One thread
+// per table entry.
+__global__ void __launch_bounds__(256)
+shared_prefix_prep_kernel(const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
+                          int32_t* __restrict__ suf_tables, int32_t* __restrict__ suf_lens,
+                          int32_t* __restrict__ prefix_len, int num_seqs, int max_blocks, int bs,
+                          PrefixGroups gr) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= static_cast<int64_t>(num_seqs) * max_blocks) return;
+  const int s = static_cast<int>(idx / max_blocks);
+  const int j = static_cast<int>(idx - static_cast<int64_t>(s) * max_blocks);
+  const int gi = group_of_seq(gr, s);
+  const int m = gi >= 0 ? gr.shared[gi] : 0;
+  const int64_t row = static_cast<int64_t>(s) * max_blocks;
+  suf_tables[row + j] = (j + m < max_blocks) ? tables[row + j + m] : -1;
+  if (j == 0) {
+    const int L = lens[s];
+    const int p = min(m * bs, max(L, 0));     // a member no longer than the prefix is all prefix
+    suf_lens[s] = L - p;
+    prefix_len[s] = p;
+  }
+}
+
+struct PrefixArgs {
+  const char* k_cache;
+  const char* v_cache;
+  const uint16_t* q;            // [B][Hq][D] bf16
+  const int32_t* block_tables;
+  const int32_t* prefix_len;    // [B]: positions of the prefix each member sees
+  float* rec;                   // [splits][B*Hq][D+4]: o, m, l, padding
+  uint32_t* counters;           // [Hkv * workgroups]: split arrivals, zero between calls
+  int64_t split_stride;         // floats between the splits' records
+  int num_seqs;
+  int hkv;
+  int group;                    // G
+  int max_blocks;
+  int sub_shift;
+  int splits;
+  float logit_scale;
+  PrefixGroups gr;
+};
+
+// One workgroup of 4 waves per (KV head g, 64 query rows of a group, split
+// of the prefix's positions): rows are (member, head) pairs, member-major,
+// 16 per wave.  Each 16-token K and V tile is loaded once per workgroup,
+// 16 bytes per thread, into LDS (two stages; four tiles in flight in
+// registers) and read there by all four waves.  Workgroups are dispatched
+// round-robin over the chip's 8 XCDs, so with g = block index mod Hkv all
+// workgroups of a head run on the same XCD(s) and share its tiles in L2.
+// A split writes one (o, m, l) record per row; with several splits, the
+// last of a row block's splits to finish merges them into split 0's record
+// (device-coherent stores, then an arrival counter, as in the decode
+// kernel), so the decode kernel folds one record per row.  Workgroups of
+// one group start their walk of the prefix at different tiles, so that the
+// first reads of a tile, which miss L2, are spread over the prefix instead
+// of all waiting on the same lines.
+template <int kD, bool kFp8>
+__global__ void __launch_bounds__(64 * kPrefixWaves)
+shared_prefix_kernel(PrefixArgs a) {
+  constexpr int kE = kFp8 ? 1 : 2;
+  constexpr int kRowBytes = kD * kE;
+  constexpr int kTileBytes = kTile * kRowBytes;
+  constexpr int kKK = kD / 32;
+  constexpr int kVC = kD / 16;
+  constexpr int kPitch = kRowBytes + 16;            // LDS row pitch (K and V)
+  constexpr int kStage = 2 * kTile * kPitch;        // K rows, then V rows
+  constexpr int kThreads = 64 * kPrefixWaves;
+  constexpr int kKPieces = kTileBytes / 16;         // 16-byte pieces of a K (or V) tile
+  constexpr int kPer = (2 * kKPieces + kThreads - 1) / kThreads;
+  constexpr int kRing = 8;
+  constexpr int kIdCap = 1024;
+  static_assert(kKPieces % 64 == 0 && kIdCap % kRing == 0, "wave-uniform pieces, whole rings");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6) & (kPrefixWaves - 1);   // < 4, known
+  const int hkv = a.hkv, G = a.group, hq = hkv * G;
+  const int g = static_cast<int>(blockIdx.x) % hkv;
+  const int rest = static_cast<int>(blockIdx.x) / hkv;
+  const int sp = rest % a.splits;
+  const int wg = rest / a.splits;
+  int gi = 0;
+  while (gi + 1 < a.gr.num && wg >= a.gr.wg_begin[gi + 1]) ++gi;
+  const int first = a.gr.first[gi], count = a.gr.count[gi];
+  const int row = lane & 15, quad = lane >> 4;
+  const int ri = ((wg - a.gr.wg_begin[gi]) * kPrefixWaves + wv) * 16 + row;   // row in the group
+  const int member = ri / G;
+  const bool row_ok = member < count;
+  const int h = ri - member * G;
+  const int s = first + (row_ok ? member : 0);
+  const int lim = row_ok ? a.prefix_len[s] : 0;               // positions this row sees
+
+  // positions up to the longest member's share; rows past a shorter
+  // member's share are masked, slots past the longest read as zero
+  int span = 0;
+  for (int i = lane; i < count; i += 64) span = max(span, a.prefix_len[first + i]);
+  span = wave_max_int(span);
+  const int ntiles = (span + kTile - 1) / kTile;
+  const int per = (ntiles + a.splits - 1) / a.splits;
+  const int tb = min(ntiles, sp * per), te = min(ntiles, tb + per);
+  const int hi = min(lim, kTile * te);                        // this row's end in this split
+  const int wg_local = wg - a.gr.wg_begin[gi];
+  const int wg_count = a.gr.wg_begin[gi + 1] - a.gr.wg_begin[gi];
+
+  // q rows in the B-operand layout of S^T = K q^T (rows past the group read 0)
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.q), 0, a.num_seqs * hq * kD * 2, kRsrcWord3);
+  const int q_off = row_ok ? ((s * hq + g * G + h) * kD + 8 * quad) * 2 : kOutOfRange;
+  bf16x8_t qa[kKK];
+#pragma unroll
+  for (int kk = 0; kk < kKK; ++kk)
+    qa[kk] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rq, q_off + 64 * kk, 0, 0));
+
+  __shared__ uint32_t s_tile[kIdCap];
+  __shared__ __align__(16) char s_kv[2][kStage];
+  const int32_t* trow = a.block_tables + static_cast<int64_t>(first) * a.max_blocks;
+
+  float m_ref = kNoMax, l_part = 0.f;
+  f32x4_t oacc[kVC];
+#pragma unroll
+  for (int c = 0; c < kVC; ++c) oacc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  u32x4_t buf[kRing][kPer];
+
+  for (int c0 = tb; c0 < te; c0 += kIdCap) {
+    const int n = min(kIdCap, te - c0);
+    const int rot = static_cast<int>(static_cast<int64_t>(wg_local) * n / wg_count);
+    // walk position t holds tile c0 + (t + rot) mod n
+    auto tile_at = [&](int t) -> int { return c0 + (t + rot < n ? t + rot : t + rot - n); };
+    __syncthreads();                                   // the previous round's ids are read
+    for (int e = tid; e < n; e += kThreads) {
+      const int j = tile_at(e);
+      const uint32_t id = static_cast<uint32_t>(trow[j >> a.sub_shift]);
+      s_tile[e] = ((id * static_cast<uint32_t>(hkv) + static_cast<uint32_t>(g)) << a.sub_shift) +
+                  (static_cast<uint32_t>(j) & ((1u << a.sub_shift) - 1u));
+    }
+    __syncthreads();
+    // Load j of a thread is piece p = tid + 256j of the tile pair: K bytes
+    // 16p for p < kKPieces, V bytes 16(p - kKPieces) below 2 kKPieces, none
+    // past that.  Which one is the same for a whole wave, so every thread
+    // issues the same loads, unconditionally (past the end or the tile's
+    // rows the load reads 0), and the waits before the LDS writes count.
+    auto issue = [&](int slot, int t) {
+      const bool live = t < n;
+      const uint32_t tile = __builtin_amdgcn_readfirstlane(live ? s_tile[t] : 0u);
+      const int rows = live ? min(kTile, span - kTile * tile_at(t)) : 0;
+      const int64_t off = static_cast<int64_t>(tile) * kTileBytes;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int pw = 64 * wv + kThreads * j;                    // the wave's first piece
+        const bool is_k = pw < kKPieces;
+        const int nrec = pw < 2 * kKPieces ? rows * kRowBytes : 0;
+        const __amdgpu_buffer_rsrc_t r = make_rsrc((is_k ? a.k_cache : a.v_cache) + off, nrec);
+        const int b = 16 * (pw + lane - (is_k ? 0 : kKPieces));
+        buf[slot][j] = __builtin_amdgcn_raw_buffer_load_b128(r, b, 0, 0);
+      }
+    };
+    auto stage = [&](int slot, char* dst) {
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int pw = 64 * wv + kThreads * j;
+        if (pw < 2 * kKPieces) {
+          const int kv = pw < kKPieces ? 0 : 1;
+          const int b = 16 * (pw + lane - kv * kKPieces);          // byte in the tile
+          const int r = b / kRowBytes;
+          *reinterpret_cast<u32x4_t*>(dst + (kv * kTile + r) * kPitch + (b - r * kRowBytes)) =
+              buf[slot][j];
+        }
+      }
+    };
+    auto compute = [&](const char* st, int t) {
+      const char* sk = st + row * kPitch + 8 * quad * kE;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < kKK; ++kk) {
+        bf16x8_t kb;
+        if constexpr (kFp8) {
+          const u32x2_t wv2 = *reinterpret_cast<const u32x2_t*>(sk + 32 * kk);
+          const int w0 = static_cast<int>(wv2[0]), w1 = static_cast<int>(wv2[1]);
+          const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+          const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+          const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+          const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+          kb = bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        } else {
+          kb = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(sk + 64 * kk));
+        }
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qa[kk], acc, 0, 0, 0);
+      }
+      float x[4];
+      const int p0 = kTile * (t < n ? tile_at(t) : te) + 4 * quad;   // position of x[0]
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[r] = p0 + r < hi ? acc[r] * a.logit_scale : -INFINITY;
+      const float xm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      if (__builtin_amdgcn_ballot_w64(xm > m_ref + kRescaleSlack) != 0) {
+        float mt = xm;
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float mn = (mt > m_ref + kRescaleSlack) ? mt : m_ref;
+        const float alpha = __builtin_amdgcn_exp2f(m_ref - mn);
+        l_part *= alpha;
+#pragma unroll
+        for (int c = 0; c < kVC; ++c)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) oacc[c][r] *= alpha;
+        m_ref = mn;
+      }
+      bf16x4_t pb;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pb[r] = static_cast<__bf16>(__builtin_amdgcn_exp2f(x[r] - m_ref));
+        l_part += static_cast<float>(pb[r]);
+      }
+      const char* vsrc = st + (kTile + 4 * quad) * kPitch + row * kE;   // token 4*quad, dim `row`
+#pragma unroll
+      for (int c = 0; c < kVC; ++c) {
+        u32x2_t vw;
+        if constexpr (kFp8) {
+          const char* p = vsrc + 16 * c;
+          const uint32_t b0 = static_cast<uint8_t>(p[0]), b1 = static_cast<uint8_t>(p[kPitch]);
+          const uint32_t b2 = static_cast<uint8_t>(p[2 * kPitch]), b3 = static_cast<uint8_t>(p[3 * kPitch]);
+          const int w4 = static_cast<int>(b0 | (b1 << 8) | (b2 << 16) | (b3 << 24));
+          vw[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w4, 1.0f, false));
+          vw[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w4, 1.0f, true));
+        } else {
+          const uint16_t* p = reinterpret_cast<const uint16_t*>(vsrc + 32 * c);
+          constexpr int kP2 = kPitch / 2;
+          vw[0] = static_cast<uint32_t>(p[0]) | (static_cast<uint32_t>(p[kP2]) << 16);
+          vw[1] = static_cast<uint32_t>(p[2 * kP2]) | (static_cast<uint32_t>(p[3 * kP2]) << 16);
+        }
+        oacc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, vw),
+                                                           __builtin_bit_cast(s16x4_t, pb),
+                                                           oacc[c], 0, 0, 0);
+      }
+    };
+    // tile t: registers (slot t mod kRing) -> LDS stage t mod 2 -> MFMA.
+    // One barrier per tile: a thread writing stage t mod 2 has passed
+    // tile t-1's barrier, so every wave is done with tile t-2 that used it.
+    // The barrier waits for the LDS writes only (lgkmcnt), not for the
+    // loads in flight.  Rounds run whole rings: tiles t >= n read zeros and
+    // their positions (at or past this split's end) are masked.
+    // (issued in slot order, which the loop's waits count on)
+#pragma unroll
+    for (int k = 0; k < kRing; ++k) {
+      issue(k, k);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int t0 = 0; t0 < n; t0 += kRing) {
+#pragma unroll
+      for (int k = 0; k < kRing; ++k) {
+        const int t = t0 + k;
+        char* st = s_kv[t & 1];
+        stage(k, st);
+        issue(k, t + kRing);
+        lds_barrier();
+        compute(st, t);
+      }
+    }
+  }
+  float l_tot = l_part;
+  l_tot += __shfl_xor(l_tot, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  const int64_t row_off = (static_cast<int64_t>(s) * hq + g * G + h) * (kD + 4);
+  if (a.splits == 1) {
+    if (row_ok) {
+      float* rec = a.rec + row_off;
+#pragma unroll
+      for (int c = 0; c < kVC; ++c) *reinterpret_cast<f32x4_t*>(rec + 16 * c + 4 * quad) = oacc[c];
+      if (quad == 0) {
+        rec[kD] = m_ref;
+        rec[kD + 1] = l_tot;
+      }
+    }
+    return;
+  }
+  // publish this split's records (device-coherent), count the arrival
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.rec, 0x7FFFFFFF);
+  const int64_t mine = (sp * a.split_stride + row_off) * 4;            // bytes
+  if (row_ok) {
+#pragma unroll
+    for (int c = 0; c < kVC; ++c)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, oacc[c]), rr,
+                                             static_cast<int>(mine + (16 * c + 4 * quad) * 4), 0,
+                                             kAuxCoherent);
+    if (quad == 0)
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{__float_as_uint(m_ref), __float_as_uint(l_tot)},
+                                            rr, static_cast<int>(mine + kD * 4), 0, kAuxCoherent);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __shared__ uint32_t s_prev;
+  __syncthreads();
+  uint32_t* ctr = a.counters + static_cast<int64_t>(wg) * hkv + g;
+  if (tid == 0)
+    s_prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (s_prev != static_cast<uint32_t>(a.splits - 1)) return;
+  // the last split: merge every split's record of each row into split 0's
+  if (row_ok) {
+    float M = m_ref, Ls = l_tot;
+    for (int k = 0; k < a.splits; ++k) {
+      if (k == sp) continue;
+      const int off = static_cast<int>((k * a.split_stride + row_off) * 4);
+      const u32x2_t ml = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rr, off + kD * 4, 0, kAuxCoherent));
+      const float mk = __uint_as_float(ml[0]), lk = __uint_as_float(ml[1]);
+      const float mn = fmaxf(M, mk);
+      const float fa = __builtin_amdgcn_exp2f(M - mn), fb = __builtin_amdgcn_exp2f(mk - mn);
+#pragma unroll
+      for (int c = 0; c < kVC; ++c) {
+        const f32x4_t o = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                           rr, off + (16 * c + 4 * quad) * 4, 0, kAuxCoherent));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) oacc[c][r] = oacc[c][r] * fa + o[r] * fb;
+      }
+      Ls = Ls * fa + lk * fb;
+      M = mn;
+    }
+    float* rec = a.rec + row_off;
+#pragma unroll
+    for (int c = 0; c < kVC; ++c) *reinterpret_cast<f32x4_t*>(rec + 16 * c + 4 * quad) = oacc[c];
+    if (quad == 0) {
+      rec[kD] = M;
+      rec[kD + 1] = Ls;
+    }
+  }
+  if (tid == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 
 // ---------------------------------------------------------------------------
 // General path: any G, fp32 / bf16 / fp8 cache.  One wave per (partition,
@@ -1030,7 +1458,8 @@ pa_status attend(const char* fn, const pa_cache_desc* c, const void* k_cache,
                  const int32_t* block_tables, int32_t max_blocks_per_seq,
                  const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs,
                  int32_t num_q_heads, float scale, void* workspace, size_t workspace_bytes,
-                 void* stream) {
+                 void* stream, const int32_t* prefix_len = nullptr,
+                 const float* prefix_rec = nullptr) {
   pa_status st = check_desc(c, fn);
   if (st != PA_OK) return st;
   const int hkv = c->num_kv_heads, D = c->head_dim, fmt = c->cache_dtype;
@@ -1110,6 +1539,8 @@ pa_status attend(const char* fn, const pa_cache_desc* c, const void* k_cache,
     a.chunk = T;
     a.window = W;
     a.sub_shift = bs == 64 ? 2 : bs == 32 ? 1 : 0;
+    a.prefix_len = prefix_len;
+    a.prefix_rec = prefix_rec;
     a.logit_scale = logit_scale;
     a.v_scale = vscale;
     // one pass per tpp chunk tokens; each pass leaves the counters zeroed
@@ -1221,4 +1652,153 @@ extern "C" pa_status pa_decode_window(const pa_cache_desc* c, const void* k_cach
   return attend("pa_decode_window", c, k_cache, v_cache, q, q_dtype, out, chunk_len, window,
                 block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs,
                 num_q_heads, scale, workspace, workspace_bytes, stream);
+}
+
+namespace {
+
+// Row workgroups of a launch: each group rounds its count * G rows up to
+// whole workgroups, at most one partial one per group.
+int64_t max_prefix_wgs(int32_t B, int G) {
+  return (static_cast<int64_t>(B) * G + 16 * kPrefixWaves - 1) / (16 * kPrefixWaves) + kMaxGroups;
+}
+
+struct SharedPrefixLayout {
+  size_t stream, tables, lens, plen, counters, recs, total;
+  int64_t split_stride;         // floats
+};
+
+SharedPrefixLayout shared_prefix_layout(const pa_cache_desc* c, int32_t B, int32_t Hq,
+                                        int32_t max_blocks) {
+  SharedPrefixLayout L{};
+  const int G = Hq / c->num_kv_heads;
+  L.stream = align256(stream_workspace_bytes(B, c->num_kv_heads, G, c->head_dim));
+  L.tables = L.stream;
+  L.lens = L.tables + align256(static_cast<size_t>(B) * max_blocks * 4);
+  L.plen = L.lens + align256(static_cast<size_t>(B) * 4);
+  L.counters = L.plen + align256(static_cast<size_t>(B) * 4);
+  L.recs = L.counters + align256(static_cast<size_t>(c->num_kv_heads) * max_prefix_wgs(B, G) * 4);
+  L.split_stride = static_cast<int64_t>(B) * Hq * (c->head_dim + 4);
+  L.total = L.recs + static_cast<size_t>(L.split_stride) * kMaxSplits * 4;
+  return L;
+}
+
+}  // namespace
+
+extern "C" size_t pa_decode_shared_prefix_workspace_bytes(const pa_cache_desc* c, int32_t num_seqs,
+                                                          int32_t num_q_heads,
+                                                          int32_t max_blocks_per_seq,
+                                                          int32_t max_context_len) {
+  if (check_desc(c, "pa_decode_shared_prefix_workspace_bytes") != PA_OK) return 0;
+  if (num_seqs <= 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0 || max_context_len <= 0 ||
+      num_q_heads % c->num_kv_heads != 0)
+    return 0;
+  const int G = num_q_heads / c->num_kv_heads;
+  const int q_dtype = (c->cache_dtype == PA_F32) ? PA_F32 : PA_BF16;
+  if (!fast_path(c->cache_dtype, q_dtype, G, c->head_dim, c->block_size)) return 0;
+  return shared_prefix_layout(c, num_seqs, num_q_heads, max_blocks_per_seq).total;
+}
+
+extern "C" pa_status pa_decode_shared_prefix(
+    const pa_cache_desc* c, const void* k_cache, const void* v_cache, const void* q,
+    int32_t q_dtype, void* out, const int32_t* block_tables, int32_t max_blocks_per_seq,
+    const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+    float scale, const int32_t* groups, int32_t num_groups, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  const char* fn = "pa_decode_shared_prefix";
+  if (num_groups < 0 || num_groups > kMaxGroups)
+    return fail(PA_ERR_INVALID_ARG, "%s: num_groups %d (0..%d)", fn, num_groups, kMaxGroups);
+  if (num_groups == 0)
+    return attend(fn, c, k_cache, v_cache, q, q_dtype, out, 1, 0, block_tables,
+                  max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads,
+                  scale, workspace, workspace_bytes, stream);
+  pa_status st = check_desc(c, fn);
+  if (st != PA_OK) return st;
+  if (!groups) return fail(PA_ERR_INVALID_ARG, "%s: null groups", fn);
+  if (num_seqs <= 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0 ||
+      num_q_heads % c->num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: bad batch shape", fn);
+  const int hkv = c->num_kv_heads, D = c->head_dim, G = num_q_heads / hkv, bs = c->block_size;
+  if (!fast_path(c->cache_dtype, q_dtype, G, D, bs))
+    return fail(PA_ERR_UNSUPPORTED, "%s: needs a bf16 or fp8 cache with bf16 q, head_dim 64 or "
+                "128, G <= 16 and a block size that is a multiple of 16", fn);
+  if (static_cast<int64_t>(num_seqs) * num_q_heads * D * 2 >= (int64_t{1} << 31) ||
+      static_cast<int64_t>(num_seqs) * num_q_heads * (D + 4) * 4 * kMaxSplits >= (int64_t{1} << 31))
+    return fail(PA_ERR_UNSUPPORTED, "%s: q or the prefix records larger than 2 GiB", fn);
+  PrefixGroups gr{};
+  gr.num = num_groups;
+  std::vector<std::pair<int, int>> spans;
+  int rb = 0, max_tiles = 0;
+  for (int i = 0; i < num_groups; ++i) {
+    const int f = groups[3 * i], n = groups[3 * i + 1], m = groups[3 * i + 2];
+    if (f < 0 || n < 1 || m < 1 || static_cast<int64_t>(f) + n > num_seqs || m > max_blocks_per_seq)
+      return fail(PA_ERR_INVALID_ARG, "%s: group %d = (%d, %d, %d) out of range", fn, i, f, n, m);
+    gr.first[i] = f;
+    gr.count[i] = n;
+    gr.shared[i] = m;
+    gr.wg_begin[i] = rb;
+    rb += (n * G + 16 * kPrefixWaves - 1) / (16 * kPrefixWaves);
+    max_tiles = std::max(max_tiles, m * (bs / kTile));
+    spans.emplace_back(f, f + n);
+  }
+  gr.wg_begin[num_groups] = rb;
+  std::sort(spans.begin(), spans.end());
+  for (size_t i = 1; i < spans.size(); ++i)
+    if (spans[i].first < spans[i - 1].second)
+      return fail(PA_ERR_INVALID_ARG, "%s: groups overlap", fn);
+  const SharedPrefixLayout L = shared_prefix_layout(c, num_seqs, num_q_heads, max_blocks_per_seq);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(PA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes, need %zu", fn,
+                workspace_bytes, L.total);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: workspace not 256-byte aligned", fn);
+  if (!k_cache || !v_cache || !q || !out || !block_tables || !context_lens)
+    return fail(PA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* suf_tables = reinterpret_cast<int32_t*>(ws + L.tables);
+  int32_t* suf_lens = reinterpret_cast<int32_t*>(ws + L.lens);
+  int32_t* plen = reinterpret_cast<int32_t*>(ws + L.plen);
+  float* recs = reinterpret_cast<float*>(ws + L.recs);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const int64_t entries = static_cast<int64_t>(num_seqs) * max_blocks_per_seq;
+  shared_prefix_prep_kernel<<<static_cast<unsigned>((entries + 255) / 256), 256, 0, hs>>>(
+      block_tables, context_lens, suf_tables, suf_lens, plen, num_seqs, max_blocks_per_seq, bs, gr);
+  st = launch_status(fn);
+  if (st != PA_OK) return st;
+  const float kscale = (c->cache_dtype == PA_FP8_E4M3) ? c->k_scale : 1.f;
+  PrefixArgs pa;
+  pa.k_cache = static_cast<const char*>(k_cache);
+  pa.v_cache = static_cast<const char*>(v_cache);
+  pa.q = static_cast<const uint16_t*>(q);
+  pa.block_tables = block_tables;
+  pa.prefix_len = plen;
+  pa.rec = recs;
+  pa.counters = reinterpret_cast<uint32_t*>(ws + L.counters);
+  // splits of the prefix: enough workgroups for two per CU, each split at
+  // least 8 tiles
+  const int64_t wgs = static_cast<int64_t>(rb) * hkv;
+  int splits = static_cast<int>(std::min<int64_t>(kMaxSplits, (2 * device_cus() + wgs - 1) / wgs));
+  splits = std::max(1, std::min(splits, max_tiles / 8));
+  pa.splits = splits;
+  pa.split_stride = L.split_stride;
+  pa.num_seqs = num_seqs;
+  pa.hkv = hkv;
+  pa.group = G;
+  pa.max_blocks = max_blocks_per_seq;
+  pa.sub_shift = bs == 64 ? 2 : bs == 32 ? 1 : 0;
+  pa.logit_scale = static_cast<float>(static_cast<double>(scale) * kscale * 1.4426950408889634);
+  pa.gr = gr;
+  const unsigned grid = static_cast<unsigned>(wgs * splits);
+  const bool fp8 = c->cache_dtype == PA_FP8_E4M3;
+  if (D == 128) {
+    if (fp8) shared_prefix_kernel<128, true><<<grid, 64 * kPrefixWaves, 0, hs>>>(pa);
+    else shared_prefix_kernel<128, false><<<grid, 64 * kPrefixWaves, 0, hs>>>(pa);
+  } else {
+    if (fp8) shared_prefix_kernel<64, true><<<grid, 64 * kPrefixWaves, 0, hs>>>(pa);
+    else shared_prefix_kernel<64, false><<<grid, 64 * kPrefixWaves, 0, hs>>>(pa);
+  }
+  st = launch_status(fn);
+  if (st != PA_OK) return st;
+  return attend(fn, c, k_cache, v_cache, q, q_dtype, out, 1, 0, suf_tables, max_blocks_per_seq,
+                suf_lens, max_context_len, num_seqs, num_q_heads, scale, workspace, L.stream,
+                stream, plen, recs);
 }

@@ -16,12 +16,12 @@ TORCH_STORE = {"f32": torch.int32, "bf16": torch.int16, "fp8": torch.uint8}
 TORCH_VIEW = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
 
 
-def device_cache(num_blocks, Hkv, D, fmt, dev="cuda"):
-    """[num_blocks, Hkv, 16, D] filled with the NaN sentinel of the format."""
+def device_cache(num_blocks, Hkv, D, fmt, dev="cuda", bs=16):
+    """[num_blocks, Hkv, bs, D] filled with the NaN sentinel of the format."""
     val = int(SENTINEL[fmt])
     if fmt == "f32":
         val = val - (1 << 32) if val >= (1 << 31) else val
-    t = torch.full((num_blocks, Hkv, 16, D), val, dtype=TORCH_STORE[fmt], device=dev)
+    t = torch.full((num_blocks, Hkv, bs, D), val, dtype=TORCH_STORE[fmt], device=dev)
     return t.view(TORCH_VIEW[fmt])
 
 

@@ -13,11 +13,11 @@ SENTINEL = {"f32": np.uint32(0x7FC0DEAD), "bf16": np.uint16(0x7FC1), "fp8": np.u
 STORE = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}
 
 
-def empty_cache(num_blocks, Hkv, D, fmt):
+def empty_cache(num_blocks, Hkv, D, fmt, bs=16):
     """A cache filled with a NaN sentinel, in storage format."""
     if fmt == "f32":
-        return np.full((num_blocks, Hkv, 16, D), SENTINEL["f32"], dtype=np.uint32).view(np.float32)
-    return np.full((num_blocks, Hkv, 16, D), SENTINEL[fmt], dtype=STORE[fmt])
+        return np.full((num_blocks, Hkv, bs, D), SENTINEL["f32"], dtype=np.uint32).view(np.float32)
+    return np.full((num_blocks, Hkv, bs, D), SENTINEL[fmt], dtype=STORE[fmt])
 
 
 def fill_sequential(w, cap=None):

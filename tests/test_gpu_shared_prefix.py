@@ -1,0 +1,204 @@
+"""GPU parity of pa_decode_shared_prefix through the C ABI: a batch of
+requests built with prefix caching, in which runs of adjacent requests share
+a system prompt's blocks, decoded with each run's prefix attended once.  The
+result matches the oracle's textbook attention over every request's whole
+context, and pa_decode's output, within the format's tolerance; with no
+groups it is pa_decode's bit for bit; repeated calls are bit-identical."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests import _oracle_setup as osu
+from tests._gpu_setup import cache_to_numpy, device_cache, out_to_f64, to_device_rows
+
+pk = pytest.importorskip("paged_kv_cache_421_amd")
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "fp8": 6e-2}
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _fp8_scales(ws):
+    allk = np.concatenate([x for w in ws for x in [w.prefix_k] + w.question_k])
+    allv = np.concatenate([x for w in ws for x in [w.prefix_v] + w.question_v])
+    return (float(np.abs(workloads.bf16_bits_to_f32(allk)).max() / 448.0),
+            float(np.abs(workloads.bf16_bits_to_f32(allv)).max() / 448.0))
+
+
+class Batch:
+    """Requests (workload index, request index) in batch order, built by the
+    library's manager with prefix caching and by the oracle's; their caches
+    must agree bit for bit."""
+
+    def __init__(self, ws, order, fmt, bs, seed):
+        self.ws, self.order, self.fmt, self.bs = ws, order, fmt, bs
+        w0 = ws[0]
+        self.Hq, self.Hkv, self.D = w0.Hq, w0.Hkv, w0.D
+        self.scale = w0.scale
+        self.ks, self.vs = _fp8_scales(ws) if fmt == "fp8" else (1.0, 1.0)
+        nb = sum(w.num_blocks for w in ws)
+        free = np.random.default_rng(seed).permutation(nb).astype(np.int32)
+        self.desc = pk.CacheDesc(nb, self.Hkv, self.D, fmt, self.ks, self.vs, block_size=bs)
+        self.kc = device_cache(nb, self.Hkv, self.D, fmt, bs=bs)
+        self.vc = device_cache(nb, self.Hkv, self.D, fmt, bs=bs)
+        self.kc_o = osu.empty_cache(nb, self.Hkv, self.D, fmt, bs=bs)
+        self.vc_o = osu.empty_cache(nb, self.Hkv, self.D, fmt, bs=bs)
+        self.bm = pk.BlockManager(nb, free_order=free, block_size=bs)
+        self.ref = oracle.RefBlockManager(nb, free_order=free, block_size=bs)
+        self.bm.enable_prefix_caching()
+        self.ref.enable_prefix_caching()
+        qs, ks, vs, ss = [], [], [], []
+        for sid, (wi, r) in enumerate(order):
+            w = ws[wi]
+            prompt = w.prompt(r)
+            slots, nc = self.bm.add_seq_prompt(sid, prompt)
+            rslots, rnc = self.ref.add_seq_prompt(sid, prompt)
+            assert nc == rnc and list(slots) == list(rslots)
+            k, v = w.rows(r)          # rows of cached positions are not written again
+            ks.append(k[nc:])
+            vs.append(v[nc:])
+            ss.append(np.asarray(slots[nc:], dtype=np.int64))
+            qs.append(w.q[r])
+        k, v, sm = np.concatenate(ks), np.concatenate(vs), np.concatenate(ss)
+        pk.write_kv(self.desc, self.kc, self.vc, to_device_rows(k, "bf16"),
+                    to_device_rows(v, "bf16"), torch.from_numpy(sm).cuda())
+        self.kc_o, self.vc_o = oracle.write_kv(self.kc_o, self.vc_o, k, v, sm, "bf16", fmt,
+                                               self.ks, self.vs)
+        self.q = np.stack(qs)
+        self.B = len(order)
+        cap = max(-(-len(ws[wi].prompt(r)) // bs) for wi, r in order)
+        self.bt, self.cl = self.bm.pack(np.arange(self.B), cap)
+        bt_o, cl_o = self.ref.pack(list(range(self.B)), cap)
+        np.testing.assert_array_equal(self.bt, bt_o)
+        np.testing.assert_array_equal(self.cl, cl_o)
+        torch.cuda.synchronize()
+        assert np.array_equal(cache_to_numpy(self.kc, fmt).view(np.uint8), self.kc_o.view(np.uint8))
+        assert np.array_equal(cache_to_numpy(self.vc, fmt).view(np.uint8), self.vc_o.view(np.uint8))
+        self.groups = self.bm.shared_prefix_groups(np.arange(self.B))
+        assert [tuple(g) for g in self.groups.tolist()] == \
+            self.ref.shared_prefix_groups(range(self.B))
+
+    def device(self, cl=None):
+        cl = self.cl if cl is None else cl
+        return (to_device_rows(self.q, "bf16"), torch.from_numpy(self.bt.astype(np.int32)).cuda(),
+                torch.from_numpy(np.asarray(cl, np.int32)).cuda(), int(np.max(cl)))
+
+    def shared(self, groups, cl=None, workspace=None):
+        q, bt, cl_d, ml = self.device(cl)
+        out = torch.empty_like(q)
+        pk.decode_shared_prefix(self.desc, self.kc, self.vc, q, out, bt, cl_d, ml,
+                                float(self.scale), groups, workspace=workspace)
+        return out
+
+    def plain(self, cl=None):
+        q, bt, cl_d, ml = self.device(cl)
+        out = torch.empty_like(q)
+        pk.decode(self.desc, self.kc, self.vc, q, out, bt, cl_d, ml, float(self.scale))
+        return out
+
+    def oracle(self, cl=None):
+        cl = self.cl if cl is None else cl
+        return oracle.decode(self.q, "bf16", self.kc_o, self.vc_o, self.fmt, self.bt, cl,
+                             self.scale, self.ks, self.vs)
+
+
+def _workloads(seed, Hq, Hkv, D, prefixes, counts, qmax=90):
+    return [workloads.prefix_batch(seed + i, n, p, 1, qmax, Hq=Hq, Hkv=Hkv, D=D)
+            for i, (p, n) in enumerate(zip(prefixes, counts))]
+
+
+@pytest.mark.parametrize("fmt,bs,D,Hq,Hkv", [("bf16", 16, 128, 8, 2), ("fp8", 32, 128, 16, 2),
+                                             ("bf16", 64, 64, 32, 2), ("bf16", 16, 64, 4, 4)])
+def test_shared_prefix_decode_matches_oracle_and_decode(fmt, bs, D, Hq, Hkv):
+    ws = _workloads(900 + bs + D, Hq, Hkv, D, (300, 100, 40), (5, 4, 1))
+    # two runs that share a prompt, then requests left alone: one that
+    # shares the first prompt but is not adjacent to its run, one with a
+    # prompt of its own, another stray one of the first
+    order = [(0, 0), (0, 1), (0, 2), (1, 0), (1, 1), (1, 2), (1, 3), (0, 3), (2, 0), (0, 4)]
+    _say(f"shared prefix {fmt} bs={bs} D={D} G={Hq // Hkv}")
+    b = Batch(ws, order, fmt, bs, 31)
+    expect = [(0, 3, min(300 // bs, (int(min(b.cl[:3])) - 1) // bs)),
+              (3, 4, min(100 // bs, (int(min(b.cl[3:7])) - 1) // bs))]
+    assert [tuple(g) for g in b.groups.tolist()] == [g for g in expect if g[2] >= 1]
+    _say(f"  groups {b.groups.tolist()}, lens {b.cl.tolist()}")
+    ws_t = pk.new_shared_prefix_workspace(b.desc, b.B, Hq, b.bt.shape[1], int(b.cl.max()))
+    out = b.shared(b.groups, workspace=ws_t)
+    again = b.shared(b.groups, workspace=ws_t)
+    plain = b.plain()
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), again.view(torch.int16))
+    ref = b.oracle()
+    got = out_to_f64(out)
+    assert np.all(np.isfinite(got))
+    err = np.abs(got - ref).max()
+    diff = np.abs(got - out_to_f64(plain)).max()
+    _say(f"  max abs err vs oracle {err:.3e}, vs pa_decode {diff:.3e}")
+    assert err <= TOL[fmt] and diff <= TOL[fmt]
+    # no groups: pa_decode itself
+    none = b.shared(np.zeros((0, 3), np.int32))
+    torch.cuda.synchronize()
+    assert torch.equal(none.view(torch.int16), plain.view(torch.int16))
+
+
+def test_members_no_longer_than_the_shared_blocks():
+    """A group whose shared run covers a member's whole context (its suffix is
+    empty) or more (the member sees only its own length of the prefix); a
+    member of length 0 gets a zero row."""
+    ws = _workloads(950, 8, 2, 128, (300,), (6,))
+    b = Batch(ws, [(0, r) for r in range(6)], "bf16", 16, 5)
+    cl = b.cl.copy()
+    cl[1] = 288            # exactly the 18 shared blocks
+    cl[2] = 200            # inside them
+    cl[4] = 0
+    groups = np.array([[0, 6, 18]], np.int32)
+    _say(f"short members: lens {cl.tolist()}")
+    out = b.shared(groups, cl=cl)
+    torch.cuda.synchronize()
+    got = out_to_f64(out)
+    ref = b.oracle(cl=cl)
+    err = np.abs(got - ref).max()
+    _say(f"  max abs err {err:.3e}")
+    assert err <= TOL["bf16"]
+    assert np.all(got[4] == 0)
+
+
+def test_many_groups_and_row_blocks():
+    """32 groups (the most one call takes), G = 16 so every member fills a
+    16-row block, and groups of 2 to 5 members."""
+    rng = np.random.default_rng(4)
+    counts = [int(x) for x in rng.integers(2, 6, 32)]
+    ws = _workloads(1000, 32, 2, 128, [int(x) for x in rng.integers(16, 200, 32)], counts, qmax=40)
+    order = [(i, r) for i, n in enumerate(counts) for r in range(n)]
+    b = Batch(ws, order, "bf16", 16, 9)
+    assert len(b.groups) == 32            # every prompt has a full block
+    _say(f"32 prompts: {len(b.groups)} groups over {b.B} requests")
+    out = b.shared(b.groups)
+    torch.cuda.synchronize()
+    err = np.abs(out_to_f64(out) - b.oracle()).max()
+    _say(f"  max abs err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+def test_bench_sized_batch_sampled():
+    """256 requests sharing a 2048-token prompt, questions of 64..512 tokens
+    (the prefix benchmark's batch): every row against pa_decode, sampled
+    requests against the oracle."""
+    w = workloads.prefix_batch(9, 256, 2048, 64, 512)
+    b = Batch([w], [(0, r) for r in range(256)], "bf16", 16, 3)
+    assert b.groups.tolist() == [[0, 256, 128]]
+    out = b.shared(b.groups)
+    plain = b.plain()
+    torch.cuda.synchronize()
+    got = out_to_f64(out)
+    diff = np.abs(got - out_to_f64(plain)).max()
+    seqs = [0, 1, 77, 128, 255]
+    ref = oracle.decode(b.q, "bf16", b.kc_o, b.vc_o, "bf16", b.bt, b.cl, b.scale, seqs=seqs)
+    err = np.abs(got[seqs] - ref[seqs]).max()
+    _say(f"bench batch: max abs diff vs pa_decode {diff:.3e}, vs oracle (5 requests) {err:.3e}")
+    assert diff <= TOL["bf16"] and err <= TOL["bf16"]

@@ -463,8 +463,74 @@ def test_cpp_prefix_cache_matches_oracle_under_random_scripts(seed, bs):
         if step % 50 == 0:
             ref.check_invariants()
             assert [cpp.refcount(b) for b in range(N)] == ref.ref
+        if step % 25 == 0 and dev:
+            ids = sorted(dev, key=lambda s: (ref.table(s)[:1], s))
+            assert [tuple(g) for g in cpp.shared_prefix_groups(ids).tolist()] == \
+                ref.shared_prefix_groups(ids), step
     for s in live:
         ref.free_seq(s)
         cpp.free_seq(s)
     assert cpp.num_free() == ref.num_free() == N
     assert ref.cache_stats() == cpp.cache_stats()
+
+
+def test_shared_prefix_groups_errors():
+    bm = pk.BlockManager(16, num_host_blocks=4)
+    bm.add_seq(0)
+    bm.append_tokens(0, 40)
+    bm.fork(0, 1)
+    assert bm.shared_prefix_groups([0, 1]).tolist() == [[0, 2, 2]]
+    with pytest.raises(pk.PagedKVError) as e:
+        bm.shared_prefix_groups([0, 7])
+    assert e.value.status == -4
+    bm.swap_out([1])
+    with pytest.raises(pk.PagedKVError) as e:
+        bm.shared_prefix_groups([0, 1])
+    assert e.value.status == -8
+    bm.swap_in([1])                       # back in on blocks of its own
+    assert bm.shared_prefix_groups([0, 1]).tolist() == []
+    n = ctypes.c_int32()
+    g = np.zeros((1, 3), np.int32)
+    bm2 = pk.BlockManager(16)
+    for s in (0, 2):
+        bm2.add_seq(s)
+        bm2.append_tokens(s, 20)
+        bm2.fork(s, s + 1)
+    ids = np.arange(4, dtype=np.int64)
+    st = pk.lib.pa_bm_shared_prefix_groups(bm2._h, ids.ctypes.data, 4, g.ctypes.data, 1,
+                                           ctypes.byref(n))
+    assert st == -1 and b"groups" in pk.lib.pa_last_error()
+
+
+def test_shared_prefix_decode_validates_groups_on_the_host():
+    """Every rejection happens before a launch (fake, never dereferenced,
+    suitably aligned pointers)."""
+    d = pk.CacheDesc(64, 2, 128, "bf16")
+    B, Hq, mb = 6, 8, 8
+    ws_bytes = pk.shared_prefix_workspace_bytes(d, B, Hq, mb, 128)
+    assert ws_bytes > 0
+    one, al = ctypes.c_void_p(256), ctypes.c_void_p(4096)
+
+    def call(groups, desc=d, ws=al, nbytes=ws_bytes, ng=None):
+        g = np.ascontiguousarray(groups, np.int32).reshape(-1, 3)
+        return pk.lib.pa_decode_shared_prefix(
+            ctypes.byref(desc.c), one, one, al, 1, al, one, mb, one, 128, B, Hq, 1.0,
+            g.ctypes.data if len(g) else None, len(g) if ng is None else ng, ws, nbytes, None)
+
+    assert call([[0, 7, 1]]) == -1                       # past the batch
+    assert call([[0, 2, 9]]) == -1                       # more shared blocks than the table
+    assert call([[0, 3, 1], [2, 2, 1]]) == -1 and b"overlap" in pk.lib.pa_last_error()
+    assert call([[0, 1, 0]]) == -1                       # nothing shared
+    assert call([[0, 2, 1]] * 33, ng=33) == -1           # too many groups
+    assert call([[0, 2, 1]], nbytes=ws_bytes - 1) == -6
+    assert call([[0, 2, 1]], ws=ctypes.c_void_p(4096 + 16)) == -1
+    f32 = pk.CacheDesc(64, 2, 128, "f32")
+    st = pk.lib.pa_decode_shared_prefix(ctypes.byref(f32.c), one, one, al, 0, al, one, mb, one,
+                                        128, B, Hq, 1.0, np.zeros(3, np.int32).ctypes.data, 1,
+                                        al, ws_bytes, None)
+    assert st == -2
+    assert pk.shared_prefix_workspace_bytes(f32, B, Hq, mb, 128) == 0
+    # the layout: pa_decode's scratch, suffix tables and lengths, prefix
+    # lengths, then one record of D + 4 floats per (sequence, query head)
+    assert ws_bytes >= pk.decode_workspace_bytes(d, B, Hq, 128) + 4 * B * mb + 8 * B + \
+        4 * B * Hq * (128 + 4)

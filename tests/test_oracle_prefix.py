@@ -163,3 +163,71 @@ def test_invariants_hold_under_random_prompt_scripts(seed):
         except oracle.NoBlocks:
             pass
         bm.check_invariants()
+
+
+def test_shared_prefix_groups_hand_worked():
+    """Requests 0..2 share a 40-token prompt (2 full blocks), request 3 has
+    its own prompt, requests 4..5 share a 20-token prompt (1 full block),
+    request 6 repeats the first prompt after them: runs are of adjacent
+    sequences only, and a shared block must leave each member a token."""
+    bm = oracle.RefBlockManager(64)
+    bm.enable_prefix_caching()
+    a = list(range(100, 140))
+    b = list(range(200, 220))
+    prompts = [a + [1, 2], a + [3], a + [4, 5, 6, 7], [9] * 30, b + [1], b + [2, 3], a + [8]]
+    for s, p in enumerate(prompts):
+        bm.add_seq_prompt(s, p)
+    assert bm.shared_prefix_groups(range(7)) == [(0, 3, 2), (4, 2, 1)]
+    # the same sequences in another order: runs follow the order given
+    assert bm.shared_prefix_groups([6, 0, 3, 1, 2]) == [(0, 2, 2), (3, 2, 2)]
+    # a member whose whole length is the shared blocks caps the run one block
+    # lower (32 tokens: blocks 0, 1 full, nothing after them)
+    bm.add_seq_prompt(7, a[:32])
+    assert bm.table(7) == bm.table(0)[:2]
+    assert bm.shared_prefix_groups([0, 7, 1]) == [(0, 3, 1)]
+    # forks share every block, the partial last one included, but the
+    # shared run stops at the full blocks below each length
+    bm.fork(3, 8)
+    assert bm.shared_prefix_groups([3, 8]) == [(0, 2, 1)]
+    assert bm.shared_prefix_groups([3]) == [] and bm.shared_prefix_groups([]) == []
+
+
+def _groups_brute(bm, ids):
+    """Every split of ids into runs, scored: a run of two or more whose members
+    agree on their first k table entries and have more than k*bs tokens, for
+    the largest such k >= 1."""
+    out, i = [], 0
+    tabs = [bm.table(s) for s in ids]
+    lens = [bm.length(s) for s in ids]
+    while i < len(ids):
+        j = i + 1
+        while j < len(ids) and tabs[j][:1] and tabs[j][:1] == tabs[i][:1]:
+            j += 1
+        best = 0
+        for k in range(1, 1 + max(len(t) for t in tabs[i:j])):
+            if all(len(tabs[r]) >= k and tabs[r][:k] == tabs[i][:k] and lens[r] > k * bm.bs
+                   for r in range(i, j)):
+                best = k
+        if j - i >= 2 and best >= 1:
+            out.append((i, j - i, best))
+        i = j
+    return out
+
+
+@pytest.mark.parametrize("seed,bs", [(11, 16), (12, 8), (13, 32)])
+def test_shared_prefix_groups_against_brute_force(seed, bs):
+    rng = np.random.default_rng(seed)
+    bm = oracle.RefBlockManager(400, block_size=bs)
+    bm.enable_prefix_caching()
+    prompts = [[int(x) for x in rng.integers(0, 50, int(rng.integers(0, 100)))] for _ in range(4)]
+    live = []
+    for s in range(60):
+        if live and rng.random() < 0.2:
+            bm.fork(int(rng.choice(live)), s)
+        else:
+            bm.add_seq_prompt(s, prompts[int(rng.integers(0, 4))] +
+                              [int(x) for x in rng.integers(0, 50, int(rng.integers(0, 20)))])
+        live.append(s)
+    for _ in range(20):
+        ids = sorted(live, key=lambda s: (bm.table(s)[:1], rng.random()))
+        assert bm.shared_prefix_groups(ids) == _groups_brute(bm, ids)
