@@ -148,6 +148,14 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Transposing LDS read of 16-bit data (gfx950): each lane addresses 8
+// bytes; within every 16 lanes, lane i receives in element k element i mod 4
+// of the bytes lane 4k + i/4 addressed.  p must point into LDS.
+__device__ __forceinline__ u32x2_t lds_read_tr16(const char* p) {
+  typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p)));
+}
+
 // Maximum over the 64 lanes of a wave, as a wave-uniform value.
 __device__ __forceinline__ int wave_max_int(int x) {
 #pragma unroll
@@ -221,7 +229,10 @@ decode_stream_kernel(StreamArgs a) {
   constexpr int kLanesPerRow = kD / 8;             // V: lanes covering one token row
   constexpr int kRowsPerLoad = 64 / kLanesPerRow;  // V: token rows per load
   constexpr int kVLoads = kTile / kRowsPerLoad;   // V: loads per lane
-  constexpr int kVStride = kRowBytes + 16;         // LDS row pitch of the V staging tile
+  // LDS row pitch of the V staging tile: bf16 rows are read 8 bytes per
+  // lane, 4 rows by each 16 lanes (pitch = 32 mod 256 puts them on
+  // distinct banks); fp8 rows byte by byte
+  constexpr int kVStride = kRowBytes + (kFp8 ? 16 : 32);
   constexpr int kRowOutBytes = kD * 2;             // one bf16 output row
   using Chunk = typename std::conditional<kFp8, u32x2_t, u32x4_t>::type;
 
@@ -810,7 +821,10 @@ decode_stream_kernel(StreamArgs a) {
         else
           *reinterpret_cast<u32x4_t*>(dst) = vt[slot][i];
       }
-      const char* vsrc = s_v + (4 * quad) * kVStride + row * kE;   // token 4*quad, dim `row`
+      const char* vsrc = s_v + (4 * quad) * kVStride + row * kE;   // fp8: token 4*quad, dim `row`
+      // bf16: one transposing read per MFMA; lane (row, quad) addresses
+      // token 4 quad + row/4, dims 16c + 4 (row mod 4) .. +3
+      const char* vtr = s_v + (4 * quad + (row >> 2)) * kVStride + 8 * (row & 3);
 #pragma unroll
       for (int c = 0; c < kVC; ++c) {
         u32x2_t vw;                                                // tokens 4*quad..+3 of dim 16c+row
@@ -822,10 +836,7 @@ decode_stream_kernel(StreamArgs a) {
           vw[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w4, 1.0f, false));
           vw[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w4, 1.0f, true));
         } else {
-          const uint16_t* p = reinterpret_cast<const uint16_t*>(vsrc + 32 * c);
-          constexpr int kPitch = kVStride / 2;
-          vw[0] = static_cast<uint32_t>(p[0]) | (static_cast<uint32_t>(p[kPitch]) << 16);
-          vw[1] = static_cast<uint32_t>(p[2 * kPitch]) | (static_cast<uint32_t>(p[3 * kPitch]) << 16);
+          vw = lds_read_tr16(vtr + 32 * c);
         }
         oacc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, vw),
                                                            __builtin_bit_cast(s16x4_t, pb),
@@ -902,16 +913,26 @@ zero_fill_kernel(uint32_t* p, int64_t n_words) {
 // contraction per KV head -- every member's query rows against the same K
 // and V -- so it is computed once per group, on MFMA, with many query rows
 // per tile, and folded into each row's result by the log-sum-exp rule.
+//
+// What bounds it is moving the shared tiles from L2 into the CUs: a
+// workgroup reads each tile of its position range once, so the bytes moved
+// are the prefix's bytes times (rows / rows per workgroup).  A workgroup
+// therefore takes 128 rows (8 waves of 16) that all read each tile from
+// LDS, and the prefix's positions are split over several workgroups to
+// fill the chip; the last split of a row block to finish merges the
+// splits' records.
 constexpr int kMaxGroups = 32;
-constexpr int kPrefixWaves = 4;    // waves (16 query rows each) per workgroup
-constexpr int kMaxSplits = 8;      // position ranges of a prefix (one record each)
+constexpr int kPrefixWaves = 8;            // 16-row blocks per workgroup, one per wave
+constexpr int kPrefixRows = 16 * kPrefixWaves;
+constexpr int kPrefixTilesPerStep = 2;     // tiles loaded and run between barriers
+constexpr int kMaxSplits = 8;
 
 struct PrefixGroups {
   int num;
   int first[kMaxGroups];
   int count[kMaxGroups];
   int shared[kMaxGroups];          // blocks
-  int wg_begin[kMaxGroups + 1];    // prefix sum of row workgroups: ceil(count * G / 64)
+  int wg_begin[kMaxGroups + 1];    // prefix sum of row workgroups: ceil(count * G / 128)
 };
 
 __device__ __forceinline__ int group_of_seq(const PrefixGroups& gr, int s) {
@@ -920,63 +941,40 @@ __device__ __forceinline__ int group_of_seq(const PrefixGroups& gr, int s) {
   return -1;
 }
 
-// Suffix tables and lengths of every sequence (grouped ones drop their
-// shared blocks), and prefix_len[s] = shared positions it sees.  One thread
-// per table entry.
-__global__ void __launch_bounds__(256)
-shared_prefix_prep_kernel(const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
-                          int32_t* __restrict__ suf_tables, int32_t* __restrict__ suf_lens,
-                          int32_t* __restrict__ prefix_len, int num_seqs, int max_blocks, int bs,
-                          PrefixGroups gr) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= static_cast<int64_t>(num_seqs) * max_blocks) return;
-  const int s = static_cast<int>(idx / max_blocks);
-  const int j = static_cast<int>(idx - static_cast<int64_t>(s) * max_blocks);
-  const int gi = group_of_seq(gr, s);
-  const int m = gi >= 0 ? gr.shared[gi] : 0;
-  const int64_t row = static_cast<int64_t>(s) * max_blocks;
-  suf_tables[row + j] = (j + m < max_blocks) ? tables[row + j + m] : -1;
-  if (j == 0) {
-    const int L = lens[s];
-    const int p = min(m * bs, max(L, 0));     // a member no longer than the prefix is all prefix
-    suf_lens[s] = L - p;
-    prefix_len[s] = p;
-  }
-}
-
 struct PrefixArgs {
   const char* k_cache;
   const char* v_cache;
   const uint16_t* q;            // [B][Hq][D] bf16
   const int32_t* block_tables;
-  const int32_t* prefix_len;    // [B]: positions of the prefix each member sees
-  float* rec;                   // [splits][B*Hq][D+4]: o, m, l, padding
-  uint32_t* counters;           // [Hkv * workgroups]: split arrivals, zero between calls
-  int64_t split_stride;         // floats between the splits' records
+  const int32_t* context_lens;
+  int32_t* suf_tables;          // [B][max_blocks]: tables without the shared blocks
+  int32_t* suf_lens;            // [B]: lengths without them
+  int32_t* prefix_len;          // [B]: positions of the prefix each sequence sees
+  float* rec;                   // [splits][B*Hq][D+4]: o, m, l, padding; split 0 ends merged
+  uint32_t* counters;           // [workgroups * Hkv]: split arrivals, zero between calls
+  int64_t split_stride;         // floats between two splits' records
   int num_seqs;
   int hkv;
   int group;                    // G
   int max_blocks;
+  int bs;
   int sub_shift;
   int splits;
   float logit_scale;
   PrefixGroups gr;
 };
 
-// One workgroup of 4 waves per (KV head g, 64 query rows of a group, split
+// One workgroup of 8 waves per (KV head g, 128 query rows of a group, split
 // of the prefix's positions): rows are (member, head) pairs, member-major,
-// 16 per wave.  Each 16-token K and V tile is loaded once per workgroup,
-// 16 bytes per thread, into LDS (two stages; four tiles in flight in
-// registers) and read there by all four waves.  Workgroups are dispatched
+// 16 per wave.  A step loads 2 tiles' K and V once, 16 bytes per thread,
+// into LDS (two stages; eight steps in flight in registers); each wave then
+// runs both tiles against its 16 rows on MFMA.  Workgroups are dispatched
 // round-robin over the chip's 8 XCDs, so with g = block index mod Hkv all
-// workgroups of a head run on the same XCD(s) and share its tiles in L2.
-// A split writes one (o, m, l) record per row; with several splits, the
-// last of a row block's splits to finish merges them into split 0's record
-// (device-coherent stores, then an arrival counter, as in the decode
-// kernel), so the decode kernel folds one record per row.  Workgroups of
-// one group start their walk of the prefix at different tiles, so that the
-// first reads of a tile, which miss L2, are spread over the prefix instead
-// of all waiting on the same lines.
+// workgroups of a head run on the same XCD(s) and share its tiles in L2;
+// workgroups of one group start their walk at different steps, so that the
+// first reads of a tile, which miss L2, are spread over the prefix.  As a
+// side job the grid writes every sequence's suffix table and length, and
+// the positions of the prefix it sees, for the decode kernel that follows.
 template <int kD, bool kFp8>
 __global__ void __launch_bounds__(64 * kPrefixWaves)
 shared_prefix_kernel(PrefixArgs a) {
@@ -985,47 +983,81 @@ shared_prefix_kernel(PrefixArgs a) {
   constexpr int kTileBytes = kTile * kRowBytes;
   constexpr int kKK = kD / 32;
   constexpr int kVC = kD / 16;
-  constexpr int kPitch = kRowBytes + 16;            // LDS row pitch (K and V)
-  constexpr int kStage = 2 * kTile * kPitch;        // K rows, then V rows
+  // LDS row pitches: K rows are read 16 bytes per lane, 16 rows at once
+  // (pitch = 16 mod 256 bytes puts them on distinct banks); V rows are
+  // read 8 bytes per lane, 4 rows by each 16 lanes (pitch = 32 mod 256)
+  constexpr int kPitch = kRowBytes + 16;
+  constexpr int kVPitch = kRowBytes + 32;
+  constexpr int kTileLds = kTile * (kPitch + kVPitch);   // one tile's K rows, then V rows
+  constexpr int kStage = kPrefixTilesPerStep * kTileLds;
   constexpr int kThreads = 64 * kPrefixWaves;
-  constexpr int kKPieces = kTileBytes / 16;         // 16-byte pieces of a K (or V) tile
-  constexpr int kPer = (2 * kKPieces + kThreads - 1) / kThreads;
-  constexpr int kRing = 8;
-  constexpr int kIdCap = 1024;
-  static_assert(kKPieces % 64 == 0 && kIdCap % kRing == 0, "wave-uniform pieces, whole rings");
+  constexpr int kKPieces = kTileBytes / 16;              // 16-byte pieces of a K (or V) tile
+  constexpr int kStepPieces = kPrefixTilesPerStep * 2 * kKPieces;
+  constexpr int kPer = (kStepPieces + kThreads - 1) / kThreads;
+  constexpr int kRing = 8;                               // steps in flight
+  constexpr int kIdCap = 1024;                           // tile ids per round (LDS)
+  constexpr int kRec = kD + 4;                           // record floats
+  static_assert(kKPieces % 64 == 0 && kIdCap % (kPrefixTilesPerStep * kRing) == 0,
+                "wave-uniform pieces, whole rings");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6) & (kPrefixWaves - 1);   // < 4, known
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6) & (kPrefixWaves - 1);
   const int hkv = a.hkv, G = a.group, hq = hkv * G;
+
+  // side job: suffix tables and lengths, prefix lengths
+  {
+    const int64_t entries = static_cast<int64_t>(a.num_seqs) * a.max_blocks;
+    for (int64_t idx = static_cast<int64_t>(blockIdx.x) * kThreads + tid; idx < entries;
+         idx += static_cast<int64_t>(gridDim.x) * kThreads) {
+      const int s = static_cast<int>(idx / a.max_blocks);
+      const int j = static_cast<int>(idx - static_cast<int64_t>(s) * a.max_blocks);
+      const int gi = group_of_seq(a.gr, s);
+      const int m = gi >= 0 ? a.gr.shared[gi] : 0;
+      const int64_t row = static_cast<int64_t>(s) * a.max_blocks;
+      a.suf_tables[row + j] = (j + m < a.max_blocks) ? a.block_tables[row + j + m] : -1;
+      if (j == 0) {
+        const int L = a.context_lens[s];
+        const int p = min(m * a.bs, max(L, 0));          // a member no longer than the prefix is all prefix
+        a.suf_lens[s] = L - p;
+        a.prefix_len[s] = p;
+      }
+    }
+  }
+
   const int g = static_cast<int>(blockIdx.x) % hkv;
   const int rest = static_cast<int>(blockIdx.x) / hkv;
   const int sp = rest % a.splits;
   const int wg = rest / a.splits;
   int gi = 0;
   while (gi + 1 < a.gr.num && wg >= a.gr.wg_begin[gi + 1]) ++gi;
-  const int first = a.gr.first[gi], count = a.gr.count[gi];
+  // the group's values, made wave-uniform explicitly: read from the
+  // argument block at a computed index they would otherwise live in vector
+  // registers, and every buffer descriptor built from them would need a
+  // loop over lanes
+  const int first = __builtin_amdgcn_readfirstlane(a.gr.first[gi]);
+  const int count = __builtin_amdgcn_readfirstlane(a.gr.count[gi]);
+  const int shared_blocks = __builtin_amdgcn_readfirstlane(a.gr.shared[gi]);
+  const int wg_b = __builtin_amdgcn_readfirstlane(a.gr.wg_begin[gi]);
+  const int wg_e = __builtin_amdgcn_readfirstlane(a.gr.wg_begin[gi + 1]);
+  const int share = shared_blocks * a.bs;                // shared positions
+  const int ntiles = shared_blocks << a.sub_shift;
+  const int per_split = (ntiles + a.splits - 1) / a.splits;
+  const int tb = min(ntiles, sp * per_split), te = min(ntiles, tb + per_split);
+  const int wg_local = wg - wg_b;
+  const int wg_count = wg_e - wg_b;
   const int row = lane & 15, quad = lane >> 4;
-  const int ri = ((wg - a.gr.wg_begin[gi]) * kPrefixWaves + wv) * 16 + row;   // row in the group
+  const int ri = (wg_local * kPrefixWaves + wv) * 16 + row;   // row in the group
   const int member = ri / G;
   const bool row_ok = member < count;
   const int h = ri - member * G;
   const int s = first + (row_ok ? member : 0);
-  const int lim = row_ok ? a.prefix_len[s] : 0;               // positions this row sees
+  const int32_t* trow = a.block_tables + static_cast<int64_t>(first) * a.max_blocks;
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.context_lens, a.num_seqs * 4);
 
-  // positions up to the longest member's share; rows past a shorter
-  // member's share are masked, slots past the longest read as zero
-  int span = 0;
-  for (int i = lane; i < count; i += 64) span = max(span, a.prefix_len[first + i]);
-  span = wave_max_int(span);
-  const int ntiles = (span + kTile - 1) / kTile;
-  const int per = (ntiles + a.splits - 1) / a.splits;
-  const int tb = min(ntiles, sp * per), te = min(ntiles, tb + per);
-  const int hi = min(lim, kTile * te);                        // this row's end in this split
-  const int wg_local = wg - a.gr.wg_begin[gi];
-  const int wg_count = a.gr.wg_begin[gi + 1] - a.gr.wg_begin[gi];
-
-  // q rows in the B-operand layout of S^T = K q^T (rows past the group read 0)
+  // loads that need nothing else, issued together: q rows in the B-operand
+  // layout of S^T = K q^T (rows past the group read 0), this row's length,
+  // the members' lengths
   const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(a.q), 0, a.num_seqs * hq * kD * 2, kRsrcWord3);
   const int q_off = row_ok ? ((s * hq + g * G + h) * kD + 8 * quad) * 2 : kOutOfRange;
@@ -1033,10 +1065,24 @@ shared_prefix_kernel(PrefixArgs a) {
 #pragma unroll
   for (int kk = 0; kk < kKK; ++kk)
     qa[kk] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rq, q_off + 64 * kk, 0, 0));
+  const int my_len = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(rl, row_ok ? s * 4 : kOutOfRange, 0, 0));
+  // positions up to the longest member's share; rows past a shorter
+  // member's length are masked, slots past the longest read as zero
+  int span = 0;
+  for (int i0 = 0; i0 < count; i0 += 256) {
+    int v[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = i0 + 64 * r + lane;
+      v[r] = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(rl, i < count ? (first + i) * 4 : kOutOfRange, 0, 0));
+    }
+    span = max(span, max(max(v[0], v[1]), max(v[2], v[3])));
+  }
+  span = min(wave_max_int(span), share);
+  const int lim = min(max(my_len, 0), share);            // positions this row sees
 
   __shared__ uint32_t s_tile[kIdCap];
-  __shared__ __align__(16) char s_kv[2][kStage];
-  const int32_t* trow = a.block_tables + static_cast<int64_t>(first) * a.max_blocks;
+  __shared__ __align__(16) char s_lds[2 * kStage];
 
   float m_ref = kNoMax, l_part = 0.f;
   f32x4_t oacc[kVC];
@@ -1046,52 +1092,59 @@ shared_prefix_kernel(PrefixArgs a) {
 
   for (int c0 = tb; c0 < te; c0 += kIdCap) {
     const int n = min(kIdCap, te - c0);
-    const int rot = static_cast<int>(static_cast<int64_t>(wg_local) * n / wg_count);
-    // walk position t holds tile c0 + (t + rot) mod n
-    auto tile_at = [&](int t) -> int { return c0 + (t + rot < n ? t + rot : t + rot - n); };
+    const int nsteps = (n + kPrefixTilesPerStep - 1) / kPrefixTilesPerStep;
+    const int rot = static_cast<int>(static_cast<int64_t>(wg_local) * nsteps / wg_count);
+    // walk position i is step (i + rot) mod nsteps: tiles c0 + 2*step + 0, 1
+    auto step_at = [&](int i) -> int { return i + rot < nsteps ? i + rot : i + rot - nsteps; };
     __syncthreads();                                   // the previous round's ids are read
     for (int e = tid; e < n; e += kThreads) {
-      const int j = tile_at(e);
+      const int j = c0 + e;
       const uint32_t id = static_cast<uint32_t>(trow[j >> a.sub_shift]);
       s_tile[e] = ((id * static_cast<uint32_t>(hkv) + static_cast<uint32_t>(g)) << a.sub_shift) +
                   (static_cast<uint32_t>(j) & ((1u << a.sub_shift) - 1u));
     }
     __syncthreads();
-    // Load j of a thread is piece p = tid + 256j of the tile pair: K bytes
-    // 16p for p < kKPieces, V bytes 16(p - kKPieces) below 2 kKPieces, none
-    // past that.  Which one is the same for a whole wave, so every thread
-    // issues the same loads, unconditionally (past the end or the tile's
-    // rows the load reads 0), and the waits before the LDS writes count.
-    auto issue = [&](int slot, int t) {
-      const bool live = t < n;
-      const uint32_t tile = __builtin_amdgcn_readfirstlane(live ? s_tile[t] : 0u);
-      const int rows = live ? min(kTile, span - kTile * tile_at(t)) : 0;
-      const int64_t off = static_cast<int64_t>(tile) * kTileBytes;
+    // Load j of a thread is piece p = 64*wave + 512j + lane of the step:
+    // tile p / (2 kKPieces), K or V by (p / kKPieces) & 1, bytes
+    // 16 (p mod kKPieces); pieces past the step are none.  All of this is
+    // the same for a whole wave, so every thread issues the same loads,
+    // unconditionally (past the walk or the tile's rows the load reads 0),
+    // and the waits before the LDS writes count.
+    auto issue = [&](int slot, int i) {
+      const int stp = i < nsteps ? step_at(i) : 0;
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
-        const int pw = 64 * wv + kThreads * j;                    // the wave's first piece
-        const bool is_k = pw < kKPieces;
-        const int nrec = pw < 2 * kKPieces ? rows * kRowBytes : 0;
+        const int pw = 64 * wv + kThreads * j;                     // the wave's first piece
+        const int tx = pw / (2 * kKPieces);
+        const bool is_k = ((pw / kKPieces) & 1) == 0;
+        const int e = kPrefixTilesPerStep * stp + tx;              // tile in the round
+        const bool live = pw < kStepPieces && i < nsteps && e < n;
+        const uint32_t tile = __builtin_amdgcn_readfirstlane(live ? s_tile[e] : 0u);
+        // (clamped in a vector register: readfirstlane keeps the descriptor scalar)
+        const int nrec = __builtin_amdgcn_readfirstlane(
+            live ? max(0, min(kTile, span - kTile * (c0 + e))) * kRowBytes : 0);
+        const int64_t off = static_cast<int64_t>(tile) * kTileBytes;
         const __amdgpu_buffer_rsrc_t r = make_rsrc((is_k ? a.k_cache : a.v_cache) + off, nrec);
-        const int b = 16 * (pw + lane - (is_k ? 0 : kKPieces));
-        buf[slot][j] = __builtin_amdgcn_raw_buffer_load_b128(r, b, 0, 0);
+        buf[slot][j] = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * (pw % kKPieces + lane), 0, 0);
       }
     };
     auto stage = [&](int slot, char* dst) {
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
         const int pw = 64 * wv + kThreads * j;
-        if (pw < 2 * kKPieces) {
-          const int kv = pw < kKPieces ? 0 : 1;
-          const int b = 16 * (pw + lane - kv * kKPieces);          // byte in the tile
+        if (pw < kStepPieces) {
+          const int tx = pw / (2 * kKPieces);
+          const int kv = (pw / kKPieces) & 1;
+          const int b = 16 * (pw % kKPieces + lane);               // byte in the tile
           const int r = b / kRowBytes;
-          *reinterpret_cast<u32x4_t*>(dst + (kv * kTile + r) * kPitch + (b - r * kRowBytes)) =
-              buf[slot][j];
+          *reinterpret_cast<u32x4_t*>(dst + tx * kTileLds + (kv ? kTile * kPitch + r * kVPitch : r * kPitch) +
+                                      (b - r * kRowBytes)) = buf[slot][j];
         }
       }
     };
-    auto compute = [&](const char* st, int t) {
-      const char* sk = st + row * kPitch + 8 * quad * kE;
+    auto compute = [&](const char* tl, int e, bool live) {
+      const int hi = live ? lim : 0;                              // positions below hi count
+      const char* sk = tl + row * kPitch + 8 * quad * kE;
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < kKK; ++kk) {
@@ -1110,7 +1163,7 @@ shared_prefix_kernel(PrefixArgs a) {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qa[kk], acc, 0, 0, 0);
       }
       float x[4];
-      const int p0 = kTile * (t < n ? tile_at(t) : te) + 4 * quad;   // position of x[0]
+      const int p0 = kTile * (c0 + e) + 4 * quad;                  // position of x[0]
 #pragma unroll
       for (int r = 0; r < 4; ++r) x[r] = p0 + r < hi ? acc[r] * a.logit_scale : -INFINITY;
       const float xm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
@@ -1133,80 +1186,87 @@ shared_prefix_kernel(PrefixArgs a) {
         pb[r] = static_cast<__bf16>(__builtin_amdgcn_exp2f(x[r] - m_ref));
         l_part += static_cast<float>(pb[r]);
       }
-      const char* vsrc = st + (kTile + 4 * quad) * kPitch + row * kE;   // token 4*quad, dim `row`
+      const char* tv = tl + kTile * kPitch;                         // V rows
+      // bf16: one transposing LDS read per MFMA.  Within each 16 lanes it
+      // hands lane i, element k, element i mod 4 of the 8 bytes that lane
+      // 4k + i/4 addressed; lane (row, quad) addresses token 4 quad + row/4,
+      // dims 16c + 4 (row mod 4) .. +3, so it receives tokens 4 quad .. +3
+      // of dim 16c + row, the A operand of O^T += V^T P^T.
+      const char* vtr = tv + (4 * quad + (row >> 2)) * kVPitch + 8 * (row & 3);
+      const char* vsrc = tv + 4 * quad * kVPitch + row * kE;       // fp8: token 4*quad, dim `row`
 #pragma unroll
       for (int c = 0; c < kVC; ++c) {
         u32x2_t vw;
         if constexpr (kFp8) {
           const char* p = vsrc + 16 * c;
-          const uint32_t b0 = static_cast<uint8_t>(p[0]), b1 = static_cast<uint8_t>(p[kPitch]);
-          const uint32_t b2 = static_cast<uint8_t>(p[2 * kPitch]), b3 = static_cast<uint8_t>(p[3 * kPitch]);
+          const uint32_t b0 = static_cast<uint8_t>(p[0]), b1 = static_cast<uint8_t>(p[kVPitch]);
+          const uint32_t b2 = static_cast<uint8_t>(p[2 * kVPitch]), b3 = static_cast<uint8_t>(p[3 * kVPitch]);
           const int w4 = static_cast<int>(b0 | (b1 << 8) | (b2 << 16) | (b3 << 24));
           vw[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w4, 1.0f, false));
           vw[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w4, 1.0f, true));
         } else {
-          const uint16_t* p = reinterpret_cast<const uint16_t*>(vsrc + 32 * c);
-          constexpr int kP2 = kPitch / 2;
-          vw[0] = static_cast<uint32_t>(p[0]) | (static_cast<uint32_t>(p[kP2]) << 16);
-          vw[1] = static_cast<uint32_t>(p[2 * kP2]) | (static_cast<uint32_t>(p[3 * kP2]) << 16);
+          vw = lds_read_tr16(vtr + 32 * c);
         }
         oacc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, vw),
                                                            __builtin_bit_cast(s16x4_t, pb),
                                                            oacc[c], 0, 0, 0);
       }
     };
-    // tile t: registers (slot t mod kRing) -> LDS stage t mod 2 -> MFMA.
-    // One barrier per tile: a thread writing stage t mod 2 has passed
-    // tile t-1's barrier, so every wave is done with tile t-2 that used it.
-    // The barrier waits for the LDS writes only (lgkmcnt), not for the
-    // loads in flight.  Rounds run whole rings: tiles t >= n read zeros and
-    // their positions (at or past this split's end) are masked.
+    // step i: registers (slot i mod kRing) -> LDS stage i mod 2 -> MFMA.
+    // One barrier per step: a thread writing stage i mod 2 has passed step
+    // i-1's barrier, so every wave is done with step i-2 that used it.  The
+    // barrier waits for the LDS writes only (lgkmcnt), not for the loads in
+    // flight.  Rounds run whole rings: steps past the walk read zeros and
+    // are masked.
     // (issued in slot order, which the loop's waits count on)
 #pragma unroll
     for (int k = 0; k < kRing; ++k) {
       issue(k, k);
       __builtin_amdgcn_sched_barrier(0);
     }
-    for (int t0 = 0; t0 < n; t0 += kRing) {
+    for (int i0 = 0; i0 < nsteps; i0 += kRing) {
 #pragma unroll
       for (int k = 0; k < kRing; ++k) {
-        const int t = t0 + k;
-        char* st = s_kv[t & 1];
-        stage(k, st);
-        issue(k, t + kRing);
+        const int i = i0 + k;
+        char* stg = s_lds + (i & 1) * kStage;
+        stage(k, stg);
+        issue(k, i + kRing);
         lds_barrier();
-        compute(st, t);
+        const int e0 = kPrefixTilesPerStep * (i < nsteps ? step_at(i) : 0);
+#pragma unroll
+        for (int tx = 0; tx < kPrefixTilesPerStep; ++tx)
+          compute(stg + tx * kTileLds, e0 + tx, i < nsteps && e0 + tx < n);
       }
     }
   }
+
   float l_tot = l_part;
   l_tot += __shfl_xor(l_tot, 16);
   l_tot += __shfl_xor(l_tot, 32);
-  const int64_t row_off = (static_cast<int64_t>(s) * hq + g * G + h) * (kD + 4);
+  const int64_t row_off = (static_cast<int64_t>(s) * hq + g * G + h) * kRec;
   if (a.splits == 1) {
     if (row_ok) {
       float* rec = a.rec + row_off;
 #pragma unroll
       for (int c = 0; c < kVC; ++c) *reinterpret_cast<f32x4_t*>(rec + 16 * c + 4 * quad) = oacc[c];
-      if (quad == 0) {
-        rec[kD] = m_ref;
-        rec[kD + 1] = l_tot;
-      }
+      if (quad == 0) *reinterpret_cast<f32x2_t*>(rec + kD) = f32x2_t{m_ref, l_tot};
     }
     return;
   }
-  // publish this split's records (device-coherent), count the arrival
+  // several splits: publish this split's records (device-coherent), count
+  // the arrival; the last split of the row block merges them all into
+  // split 0's records, in split order whichever split arrives last (the
+  // result does not depend on timing), 4 splits' records in flight at once
   const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.rec, 0x7FFFFFFF);
-  const int64_t mine = (sp * a.split_stride + row_off) * 4;            // bytes
   if (row_ok) {
+    const int mine = static_cast<int>((sp * a.split_stride + row_off) * 4);
 #pragma unroll
     for (int c = 0; c < kVC; ++c)
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, oacc[c]), rr,
-                                             static_cast<int>(mine + (16 * c + 4 * quad) * 4), 0,
-                                             kAuxCoherent);
+                                             mine + (16 * c + 4 * quad) * 4, 0, kAuxCoherent);
     if (quad == 0)
       __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{__float_as_uint(m_ref), __float_as_uint(l_tot)},
-                                            rr, static_cast<int>(mine + kD * 4), 0, kAuxCoherent);
+                                            rr, mine + kD * 4, 0, kAuxCoherent);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __shared__ uint32_t s_prev;
@@ -1216,35 +1276,46 @@ shared_prefix_kernel(PrefixArgs a) {
     s_prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   if (s_prev != static_cast<uint32_t>(a.splits - 1)) return;
-  // the last split: merge every split's record of each row into split 0's
-  if (row_ok) {
-    float M = m_ref, Ls = l_tot;
-    for (int k = 0; k < a.splits; ++k) {
-      if (k == sp) continue;
-      const int off = static_cast<int>((k * a.split_stride + row_off) * 4);
-      const u32x2_t ml = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rr, off + kD * 4, 0, kAuxCoherent));
-      const float mk = __uint_as_float(ml[0]), lk = __uint_as_float(ml[1]);
+  if (tid == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (!row_ok) return;
+  float M = kNoMax, Ls = 0.f;
+#pragma unroll
+  for (int c = 0; c < kVC; ++c) oacc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const __amdgpu_buffer_rsrc_t rz = make_rsrc(a.rec, 0);          // reads 0
+  for (int k0 = 0; k0 < a.splits; k0 += 4) {
+    f32x4_t o[4][kVC];
+    u32x2_t ml[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int k = k0 + u;
+      const bool use = k < a.splits;
+      const __amdgpu_buffer_rsrc_t ru = use ? rr : rz;
+      const int off = use ? static_cast<int>((k * a.split_stride + row_off) * 4) : 0;
+      ml[u] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(ru, off + kD * 4, 0, kAuxCoherent));
+#pragma unroll
+      for (int c = 0; c < kVC; ++c)
+        o[u][c] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  ru, off + (16 * c + 4 * quad) * 4, 0, kAuxCoherent));
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int k = k0 + u;
+      if (k >= a.splits) continue;
+      const float mk = __uint_as_float(ml[u][0]), lk = __uint_as_float(ml[u][1]);
       const float mn = fmaxf(M, mk);
       const float fa = __builtin_amdgcn_exp2f(M - mn), fb = __builtin_amdgcn_exp2f(mk - mn);
 #pragma unroll
-      for (int c = 0; c < kVC; ++c) {
-        const f32x4_t o = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                           rr, off + (16 * c + 4 * quad) * 4, 0, kAuxCoherent));
+      for (int c = 0; c < kVC; ++c)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) oacc[c][r] = oacc[c][r] * fa + o[r] * fb;
-      }
+        for (int r = 0; r < 4; ++r) oacc[c][r] = oacc[c][r] * fa + o[u][c][r] * fb;
       Ls = Ls * fa + lk * fb;
       M = mn;
     }
-    float* rec = a.rec + row_off;
-#pragma unroll
-    for (int c = 0; c < kVC; ++c) *reinterpret_cast<f32x4_t*>(rec + 16 * c + 4 * quad) = oacc[c];
-    if (quad == 0) {
-      rec[kD] = M;
-      rec[kD + 1] = Ls;
-    }
   }
-  if (tid == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  float* rec = a.rec + row_off;
+#pragma unroll
+  for (int c = 0; c < kVC; ++c) *reinterpret_cast<f32x4_t*>(rec + 16 * c + 4 * quad) = oacc[c];
+  if (quad == 0) *reinterpret_cast<f32x2_t*>(rec + kD) = f32x2_t{M, Ls};
 }
 
 
@@ -1659,7 +1730,7 @@ namespace {
 // Row workgroups of a launch: each group rounds its count * G rows up to
 // whole workgroups, at most one partial one per group.
 int64_t max_prefix_wgs(int32_t B, int G) {
-  return (static_cast<int64_t>(B) * G + 16 * kPrefixWaves - 1) / (16 * kPrefixWaves) + kMaxGroups;
+  return (static_cast<int64_t>(B) * G + kPrefixRows - 1) / kPrefixRows + kMaxGroups;
 }
 
 struct SharedPrefixLayout {
@@ -1727,7 +1798,7 @@ extern "C" pa_status pa_decode_shared_prefix(
   PrefixGroups gr{};
   gr.num = num_groups;
   std::vector<std::pair<int, int>> spans;
-  int rb = 0, max_tiles = 0;
+  int wgs = 0, max_tiles = 0;
   for (int i = 0; i < num_groups; ++i) {
     const int f = groups[3 * i], n = groups[3 * i + 1], m = groups[3 * i + 2];
     if (f < 0 || n < 1 || m < 1 || static_cast<int64_t>(f) + n > num_seqs || m > max_blocks_per_seq)
@@ -1735,12 +1806,12 @@ extern "C" pa_status pa_decode_shared_prefix(
     gr.first[i] = f;
     gr.count[i] = n;
     gr.shared[i] = m;
-    gr.wg_begin[i] = rb;
-    rb += (n * G + 16 * kPrefixWaves - 1) / (16 * kPrefixWaves);
+    gr.wg_begin[i] = wgs;
+    wgs += (n * G + kPrefixRows - 1) / kPrefixRows;
     max_tiles = std::max(max_tiles, m * (bs / kTile));
     spans.emplace_back(f, f + n);
   }
-  gr.wg_begin[num_groups] = rb;
+  gr.wg_begin[num_groups] = wgs;
   std::sort(spans.begin(), spans.end());
   for (size_t i = 1; i < spans.size(); ++i)
     if (spans[i].first < spans[i - 1].second)
@@ -1759,35 +1830,34 @@ extern "C" pa_status pa_decode_shared_prefix(
   int32_t* plen = reinterpret_cast<int32_t*>(ws + L.plen);
   float* recs = reinterpret_cast<float*>(ws + L.recs);
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  const int64_t entries = static_cast<int64_t>(num_seqs) * max_blocks_per_seq;
-  shared_prefix_prep_kernel<<<static_cast<unsigned>((entries + 255) / 256), 256, 0, hs>>>(
-      block_tables, context_lens, suf_tables, suf_lens, plen, num_seqs, max_blocks_per_seq, bs, gr);
-  st = launch_status(fn);
-  if (st != PA_OK) return st;
   const float kscale = (c->cache_dtype == PA_FP8_E4M3) ? c->k_scale : 1.f;
   PrefixArgs pa;
   pa.k_cache = static_cast<const char*>(k_cache);
   pa.v_cache = static_cast<const char*>(v_cache);
   pa.q = static_cast<const uint16_t*>(q);
   pa.block_tables = block_tables;
+  pa.context_lens = context_lens;
+  pa.suf_tables = suf_tables;
+  pa.suf_lens = suf_lens;
   pa.prefix_len = plen;
   pa.rec = recs;
   pa.counters = reinterpret_cast<uint32_t*>(ws + L.counters);
-  // splits of the prefix: enough workgroups for two per CU, each split at
-  // least 8 tiles
-  const int64_t wgs = static_cast<int64_t>(rb) * hkv;
-  int splits = static_cast<int>(std::min<int64_t>(kMaxSplits, (2 * device_cus() + wgs - 1) / wgs));
-  splits = std::max(1, std::min(splits, max_tiles / 8));
-  pa.splits = splits;
   pa.split_stride = L.split_stride;
+  // splits of the prefix: about one workgroup per CU, each split at least
+  // 16 tiles
+  const int64_t row_wgs = static_cast<int64_t>(wgs) * hkv;
+  int splits = static_cast<int>(std::min<int64_t>(kMaxSplits, (device_cus() + row_wgs - 1) / row_wgs));
+  splits = std::max(1, std::min(splits, max_tiles / 16));
+  pa.splits = splits;
   pa.num_seqs = num_seqs;
   pa.hkv = hkv;
   pa.group = G;
   pa.max_blocks = max_blocks_per_seq;
+  pa.bs = bs;
   pa.sub_shift = bs == 64 ? 2 : bs == 32 ? 1 : 0;
   pa.logit_scale = static_cast<float>(static_cast<double>(scale) * kscale * 1.4426950408889634);
   pa.gr = gr;
-  const unsigned grid = static_cast<unsigned>(wgs * splits);
+  const unsigned grid = static_cast<unsigned>(row_wgs * splits);
   const bool fp8 = c->cache_dtype == PA_FP8_E4M3;
   if (D == 128) {
     if (fp8) shared_prefix_kernel<128, true><<<grid, 64 * kPrefixWaves, 0, hs>>>(pa);
