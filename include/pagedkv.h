@@ -74,8 +74,10 @@ typedef enum {
 typedef struct {
   int32_t num_blocks;    /* physical blocks in each of the K and V caches */
   int32_t block_size;    /* tokens per block: 8, 16 (PA_BLOCK_SIZE), 32 or 64;
-                            decode streams tiles of 16 tokens, so 8-token blocks
-                            take the partition path */
+                            decode streams tiles of 16 tokens: 2 or 4 per block
+                            of 32 or 64, and a tile of two 8-token blocks when
+                            each cache is under 2 GiB - 128 KiB (larger
+                            8-token-block caches take the partition path) */
   int32_t num_kv_heads;  /* Hkv >= 1 */
   int32_t head_dim;      /* D: 64 or 128 */
   int32_t cache_dtype;   /* pa_dtype of both caches */

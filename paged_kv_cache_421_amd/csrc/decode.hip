@@ -203,6 +203,7 @@ struct StreamArgs {
   int chunk;                  // T: new tokens per sequence
   int window;                 // W > 0: attend only the last W positions; 0: all
   int sub_shift;              // log2(block size / 16): tiles per block = 1 << sub_shift
+  int pair_nrec;              // 8-token blocks: bytes of one cache (< 2^31 - 2^16)
   // shared prefixes (null when unused): a sequence with prefix_len[s] > 0
   // has the attention over its first prefix_len[s] positions in
   // prefix_rec[(s*Hq + h)*(kD + 4)]: unnormalised o[kD], max m (log2 units),
@@ -218,7 +219,7 @@ struct StreamArgs {
 
 // kD: head_dim; kFp8: E4M3 cache (else bf16); kAux: cache policy bits of the
 // KV loads.
-template <int kD, bool kFp8, int kAux>
+template <int kD, bool kFp8, int kAux, bool kPair>
 __global__ void __launch_bounds__(64 * kWavesPerGroup)
 decode_stream_kernel(StreamArgs a) {
   constexpr int kE = kFp8 ? 1 : 2;                 // bytes per cache element
@@ -366,6 +367,10 @@ decode_stream_kernel(StreamArgs a) {
   // segment's ends or the ends of this wave's range.
   __shared__ u32x4_t s_desc_all[kWavesPerGroup][kCap];
   u32x4_t* s_desc = s_desc_all[wig];
+  // 8-token blocks: a tile is two blocks; word 0 holds the first block's
+  // 8-row tile index (block * Hkv + head), this the second's
+  __shared__ uint32_t s_pair_all[kWavesPerGroup][kPair ? kCap : 1];
+  uint32_t* s_pair = s_pair_all[wig];
   // V tile staging (token-major rows, padded pitch): it turns the V tile's
   // rows into the P.V MFMA's operand, 4 tokens of one dim per lane
   __shared__ __align__(16) char s_v_all[kWavesPerGroup][kTile * kVStride];
@@ -674,6 +679,37 @@ decode_stream_kernel(StreamArgs a) {
       }
     }
     // pass 2: block ids from the tables, independent loads per lane
+    if constexpr (kPair) {
+      // tile j is blocks 2j (rows 0-7) and 2j+1 (rows 8-15); the second is
+      // read only when the context reaches past the first
+      for (int e0 = 0; e0 < n; e0 += 64 * kGather) {
+        int ida[kGather], idb[kGather];
+#pragma unroll
+        for (int r = 0; r < kGather; ++r) {
+          const int e = e0 + 64 * r + lane;
+          ida[r] = idb[r] = 0;
+          if (e < n) {
+            const u32x4_t d = s_desc[e];
+            const int base = static_cast<int>(d[2] & kSeqMask) * a.max_blocks + 2 * static_cast<int>(d[0]);
+            ida[r] = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(tbl_rsrc, base * 4, 0, 0));
+            idb[r] = (d[1] & 31u) > 8u
+                         ? static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(tbl_rsrc, (base + 1) * 4, 0, 0))
+                         : 0;
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < kGather; ++r) {
+          const int e = e0 + 64 * r + lane;
+          if (e < n) {
+            const uint32_t g = (s_desc[e][1] >> 7) & 511u;
+            const uint32_t ua = static_cast<uint32_t>(ida[r]) * static_cast<uint32_t>(hkv) + g;
+            const bool two = (s_desc[e][1] & 31u) > 8u;
+            s_desc[e][0] = ua;
+            s_pair[e] = two ? static_cast<uint32_t>(idb[r]) * static_cast<uint32_t>(hkv) + g : ua;
+          }
+        }
+      }
+    } else
     for (int e0 = 0; e0 < n; e0 += 64 * kGather) {
       int ids[kGather];
 #pragma unroll
@@ -721,6 +757,44 @@ decode_stream_kernel(StreamArgs a) {
       const __amdgpu_buffer_rsrc_t rq = make_rsrc(reinterpret_cast<const char*>(a.q) + q_off, q_nrec);
 #pragma unroll
       for (int kk = 0; kk < kKK; ++kk) qs[slot][kk] = __builtin_amdgcn_raw_buffer_load_b128(rq, q_lane_off + 64 * kk, 0, 0);
+      if constexpr (kPair) {
+        // one descriptor over the whole cache, per-lane offsets: rows 0-7
+        // of the tile in the first block, rows 8-15 in the second; rows
+        // past the context (and an empty slot) get an offset past the
+        // cache, which reads 0
+        uint32_t ha = 0, hb = 0;
+        if (t < n) {
+          ha = __builtin_amdgcn_readfirstlane(s_desc[t][0]);
+          hb = __builtin_amdgcn_readfirstlane(s_pair[t]);
+        }
+        const int rows = k_nrec / kRowBytes;
+        auto row_at = [&](int r) -> int {                  // byte offset of tile row r
+          return r < rows ? static_cast<int>((r < 8 ? ha : hb) * static_cast<uint32_t>(8 * kRowBytes)) +
+                                (r & 7) * kRowBytes
+                          : kOutOfRange;
+        };
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k_cache, a.pair_nrec);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v_cache, a.pair_nrec);
+        const int ko = row_at(row) + 8 * quad * kE;
+#pragma unroll
+        for (int kk = 0; kk < kKK; ++kk) {
+          if constexpr (kFp8)
+            kt[slot][kk] = __builtin_bit_cast(Chunk, __builtin_amdgcn_raw_buffer_load_b64(rk, ko + 32 * kk * kE, 0, kAux));
+          else
+            kt[slot][kk] = __builtin_amdgcn_raw_buffer_load_b128(rk, ko + 32 * kk * kE, 0, kAux);
+        }
+#pragma unroll
+        for (int i = 0; i < kVLoads; ++i) {
+          const int vo = row_at(v_r + i * kRowsPerLoad) + 8 * v_c * kE;
+          if constexpr (kFp8)
+            vt[slot][i] = __builtin_bit_cast(Chunk, __builtin_amdgcn_raw_buffer_load_b64(rv, vo, 0, kAux));
+          else
+            vt[slot][i] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo, 0, kAux);
+        }
+        (void)tile_off;
+        (void)v_nrec;
+        return;
+      }
       const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k_cache + tile_off, k_nrec);
       const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v_cache + tile_off, v_nrec);
 #pragma unroll
@@ -1445,12 +1519,18 @@ void launch_simple(int fmt, dim3 grid, hipStream_t st, const char* kc, const cha
 
 
 template <int kD>
-void launch_stream(bool fp8, int nw, hipStream_t st, const StreamArgs& a) {
+void launch_stream(bool fp8, bool pair, int nw, hipStream_t st, const StreamArgs& a) {
   const dim3 grid(nw / kWavesPerGroup), block(64 * kWavesPerGroup);
-  if (fp8)
-    decode_stream_kernel<kD, true, kAuxNonTemporal><<<grid, block, kPadLds, st>>>(a);
-  else
-    decode_stream_kernel<kD, false, kAuxNonTemporal><<<grid, block, kPadLds, st>>>(a);
+  if (pair) {
+    if (fp8)
+      decode_stream_kernel<kD, true, kAuxNonTemporal, true><<<grid, block, kPadLds, st>>>(a);
+    else
+      decode_stream_kernel<kD, false, kAuxNonTemporal, true><<<grid, block, kPadLds, st>>>(a);
+  } else if (fp8) {
+    decode_stream_kernel<kD, true, kAuxNonTemporal, false><<<grid, block, kPadLds, st>>>(a);
+  } else {
+    decode_stream_kernel<kD, false, kAuxNonTemporal, false><<<grid, block, kPadLds, st>>>(a);
+  }
 }
 
 }  // namespace
@@ -1465,9 +1545,26 @@ int num_partitions(int32_t max_context_len) {
   return (max_context_len + kPartTokens - 1) / kPartTokens;
 }
 
+// Largest cache (bytes of K, or of V) the 8-token-block mode addresses:
+// one buffer descriptor with 32-bit offsets, and room past it for the
+// out-of-range offset of masked rows.
+constexpr int64_t kPairCacheMax = int64_t{0x7FFF0000} - (int64_t{1} << 16);
+
 bool fast_path(int fmt, int q_dtype, int G, int D, int bs) {
   return (fmt == PA_BF16 || fmt == PA_FP8_E4M3) && q_dtype == PA_BF16 && G >= 1 &&
-         G <= kMaxRows && (D == 64 || D == 128) && bs % kTile == 0;
+         G <= kMaxRows && (D == 64 || D == 128) && (bs % kTile == 0 || bs == 8);
+}
+
+int64_t cache_bytes(const pa_cache_desc* c) {
+  const int e = c->cache_dtype == PA_F32 ? 4 : c->cache_dtype == PA_BF16 ? 2 : 1;
+  return static_cast<int64_t>(c->num_blocks) * c->num_kv_heads * c->block_size * c->head_dim * e;
+}
+
+// The fast path for this cache: 8-token blocks only while one cache fits
+// the paired mode's descriptor.
+bool fast_path(const pa_cache_desc* c, int q_dtype, int G) {
+  return fast_path(c->cache_dtype, q_dtype, G, c->head_dim, c->block_size) &&
+         (c->block_size != 8 || cache_bytes(c) <= kPairCacheMax);
 }
 
 // Chunk tokens per fast-path pass: as many as fit G rows each in 16 columns.
@@ -1515,7 +1612,7 @@ size_t workspace_bytes_for(const pa_cache_desc* c, int32_t num_seqs, int32_t num
     return 0;
   const int G = num_q_heads / c->num_kv_heads;
   const int q_dtype = (c->cache_dtype == PA_F32) ? PA_F32 : PA_BF16;
-  if (fast_path(c->cache_dtype, q_dtype, G, c->head_dim, c->block_size))
+  if (fast_path(c, q_dtype, G))
     return stream_workspace_bytes(num_seqs, c->num_kv_heads, G * tokens_per_pass(G, T),
                                   c->head_dim);
   return general_workspace_bytes(num_seqs, num_q_heads, T, c->head_dim, max_context_len);
@@ -1556,7 +1653,7 @@ pa_status attend(const char* fn, const pa_cache_desc* c, const void* k_cache,
   if (!k_cache || !v_cache || !q || !out || !block_tables || !context_lens)
     return fail(PA_ERR_INVALID_ARG, "%s: null pointer", fn);
   const int G = num_q_heads / hkv;
-  const bool fast = fast_path(fmt, q_dtype, G, D, bs);
+  const bool fast = fast_path(c, q_dtype, G);
   const int tpp = tokens_per_pass(G, T);
   const int64_t max_tiles = static_cast<int64_t>(hkv) * num_seqs *
                             ((static_cast<int64_t>(max_context_len) + kTile - 1) / kTile);
@@ -1610,6 +1707,7 @@ pa_status attend(const char* fn, const pa_cache_desc* c, const void* k_cache,
     a.chunk = T;
     a.window = W;
     a.sub_shift = bs == 64 ? 2 : bs == 32 ? 1 : 0;
+    a.pair_nrec = bs == 8 ? static_cast<int>(cache_bytes(c)) : 0;
     a.prefix_len = prefix_len;
     a.prefix_rec = prefix_rec;
     a.logit_scale = logit_scale;
@@ -1618,8 +1716,8 @@ pa_status attend(const char* fn, const pa_cache_desc* c, const void* k_cache,
     for (int t0 = 0; t0 < T; t0 += tpp) {
       a.t_first = t0;
       a.rows = G * std::min(tpp, T - t0);
-      if (D == 128) launch_stream<128>(fmt == PA_FP8_E4M3, a.num_waves, s, a);
-      else launch_stream<64>(fmt == PA_FP8_E4M3, a.num_waves, s, a);
+      if (D == 128) launch_stream<128>(fmt == PA_FP8_E4M3, bs == 8, a.num_waves, s, a);
+      else launch_stream<64>(fmt == PA_FP8_E4M3, bs == 8, a.num_waves, s, a);
       st = launch_status(fn);
       if (st != PA_OK) return st;
     }
@@ -1765,7 +1863,7 @@ extern "C" size_t pa_decode_shared_prefix_workspace_bytes(const pa_cache_desc* c
     return 0;
   const int G = num_q_heads / c->num_kv_heads;
   const int q_dtype = (c->cache_dtype == PA_F32) ? PA_F32 : PA_BF16;
-  if (!fast_path(c->cache_dtype, q_dtype, G, c->head_dim, c->block_size)) return 0;
+  if (!fast_path(c, q_dtype, G) || c->block_size % kTile != 0) return 0;
   return shared_prefix_layout(c, num_seqs, num_q_heads, max_blocks_per_seq).total;
 }
 
@@ -1789,7 +1887,7 @@ extern "C" pa_status pa_decode_shared_prefix(
       num_q_heads % c->num_kv_heads != 0)
     return fail(PA_ERR_INVALID_ARG, "%s: bad batch shape", fn);
   const int hkv = c->num_kv_heads, D = c->head_dim, G = num_q_heads / hkv, bs = c->block_size;
-  if (!fast_path(c->cache_dtype, q_dtype, G, D, bs))
+  if (!fast_path(c, q_dtype, G) || bs % kTile != 0)
     return fail(PA_ERR_UNSUPPORTED, "%s: needs a bf16 or fp8 cache with bf16 q, head_dim 64 or "
                 "128, G <= 16 and a block size that is a multiple of 16", fn);
   if (static_cast<int64_t>(num_seqs) * num_q_heads * D * 2 >= (int64_t{1} << 31) ||

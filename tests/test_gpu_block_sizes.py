@@ -1,7 +1,8 @@
 """GPU parity at block sizes 8, 32 and 64 through the C ABI: the library's
 slots and cache bytes equal the oracle's bit for bit, copy-on-write copies
 are exact, and decode / chunks / windows match the oracle.  32- and 64-token
-blocks stream as 2 or 4 tiles of 16; 8-token blocks take the partition path."""
+blocks stream as 2 or 4 tiles of 16, 8-token blocks as tiles of two blocks;
+an fp32 cache takes the partition path at every block size."""
 import numpy as np
 import pytest
 import torch
@@ -72,7 +73,8 @@ LENS = [0, 1, 7, 8, 9, 31, 32, 33, 64, 65, 200, 513, 1100]
 
 @pytest.mark.parametrize("bs,fmt,G,D", [(8, "bf16", 4, 128), (32, "bf16", 4, 128),
                                         (64, "bf16", 8, 64), (32, "fp8", 4, 128),
-                                        (64, "f32", 2, 64), (8, "fp8", 2, 64)])
+                                        (64, "f32", 2, 64), (8, "fp8", 2, 64),
+                                        (8, "f32", 2, 128), (8, "bf16", 16, 64)])
 def test_decode_chunk_and_window_at_block_size(bs, fmt, G, D):
     w, desc, kc, vc, kc_o, vc_o, bt, cl = _build(1000 + bs + D, fmt, bs, G, D, LENS)
     _say(f"block size {bs} {fmt} G={G} D={D}")
