@@ -371,7 +371,7 @@ pa_status pa_bm_cache_stats(const pa_bm* bm, int64_t* queried_blocks, int64_t* h
  * (group, KV head) on MFMA with all members' query rows and folded into each
  * row by the log-sum-exp rule, then the suffixes are decoded as usual.
  * Needs the bf16 / fp8 fast path (head_dim 64 or 128, G <= 16, block size a
- * multiple of 16), single-token decode.  workspace: zero-filled before first
+ * multiple of 16), single-token decode, a positive scale (with groups).  workspace: zero-filled before first
  * use, 256-byte aligned, pa_decode_shared_prefix_workspace_bytes(...) bytes;
  * it holds suffix tables and lengths and per-row prefix records besides
  * pa_decode's scratch.  num_groups = 0 is pa_decode.

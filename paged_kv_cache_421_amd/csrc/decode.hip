@@ -1236,11 +1236,15 @@ shared_prefix_kernel(PrefixArgs a) {
         }
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qa[kk], acc, 0, 0, 0);
       }
-      float x[4];
-      const int p0 = kTile * (c0 + e) + 4 * quad;                  // position of x[0]
+      // positions at or past a row's end are masked, where any lane has one
+      const int p0 = kTile * (c0 + e) + 4 * quad;                  // position of acc[0]
+      if (__builtin_amdgcn_ballot_w64(p0 + 3 >= hi) != 0) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) x[r] = p0 + r < hi ? acc[r] * a.logit_scale : -INFINITY;
-      const float xm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        for (int r = 0; r < 4; ++r) acc[r] = p0 + r < hi ? acc[r] : -INFINITY;
+      }
+      // the scale is positive: the largest logit is the scale times the
+      // largest product, and each weight is exp2(fma(product, scale, -max))
+      const float xm = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])) * a.logit_scale;
       if (__builtin_amdgcn_ballot_w64(xm > m_ref + kRescaleSlack) != 0) {
         float mt = xm;
         mt = fmaxf(mt, __shfl_xor(mt, 16));
@@ -1257,7 +1261,7 @@ shared_prefix_kernel(PrefixArgs a) {
       bf16x4_t pb;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        pb[r] = static_cast<__bf16>(__builtin_amdgcn_exp2f(x[r] - m_ref));
+        pb[r] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(acc[r], a.logit_scale, -m_ref)));
         l_part += static_cast<float>(pb[r]);
       }
       const char* tv = tl + kTile * kPitch;                         // V rows
@@ -1883,6 +1887,8 @@ extern "C" pa_status pa_decode_shared_prefix(
   pa_status st = check_desc(c, fn);
   if (st != PA_OK) return st;
   if (!groups) return fail(PA_ERR_INVALID_ARG, "%s: null groups", fn);
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(PA_ERR_INVALID_ARG, "%s: scale must be positive and finite", fn);
   if (num_seqs <= 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0 ||
       num_q_heads % c->num_kv_heads != 0)
     return fail(PA_ERR_INVALID_ARG, "%s: bad batch shape", fn);

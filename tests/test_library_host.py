@@ -531,6 +531,11 @@ def test_shared_prefix_decode_validates_groups_on_the_host():
     assert call([[0, 1, 0]]) == -1                       # nothing shared
     assert call([[0, 2, 1]] * 33, ng=33) == -1           # too many groups
     assert call([[0, 2, 1]], nbytes=ws_bytes - 1) == -6
+    g1 = np.array([[0, 2, 1]], np.int32)
+    for bad in (0.0, -0.5, float("inf")):
+        assert pk.lib.pa_decode_shared_prefix(
+            ctypes.byref(d.c), one, one, al, 1, al, one, mb, one, 128, B, Hq, bad,
+            g1.ctypes.data, 1, al, ws_bytes, None) == -1
     assert call([[0, 2, 1]], ws=ctypes.c_void_p(4096 + 16)) == -1
     f32 = pk.CacheDesc(64, 2, 128, "f32")
     st = pk.lib.pa_decode_shared_prefix(ctypes.byref(f32.c), one, one, al, 0, al, one, mb, one,
