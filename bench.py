@@ -68,6 +68,17 @@ bytes (every sequence's whole context) are reported beside them, with the
 other path's time on the final batch, the block manager's hit rate and that
 of a simulated multi-turn chat.
 
+With ``--config N`` (2, 4 or 5) the step is pa_decode alone on another of
+the seeded decode configurations, once per layer, lengths fixed: 2 is a
+13B-shaped MHA layer (batch 64, 40 heads, lengths U[128, 2048]), 4 a
+70B-shaped long-context GQA layer (batch 8, 64 query / 8 KV heads, 32768
+tokens each: 64 pieces of 512 tokens per sequence), 5 parallel sampling on
+an fp8-e4m3 cache (64 prompts of 1024 + r tokens, each forked into 4
+samples with copy-on-write of the shared partial block, suffixes U[1, 256]).
+The roofline takes the distinct KV bytes a call reads; for config 5 the
+logical bytes (each sample's whole context, the shared prompt blocks once per
+sample) are reported beside them.
+
 With ``--window W`` the decode (or chunk) step attends only the last W
 positions of each context (pa_decode_window); the roofline's algorithmic
 bytes are then the positions the window keeps, min(L, W + T - 1) per
@@ -431,6 +442,138 @@ def chat_hit_rate(seed=11, conversations=64, turns=8, block_size=16):
     return h / q, q, t_lookup / n_lookup * 1e6
 
 
+def run_config(args):
+    """pa_decode on decode configuration 2, 4 or 5 (lengths fixed)."""
+    import torch
+    import paged_kv_cache_421_amd as pk
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    steps = args.steps or 50
+    warm = args.warmup if args.warmup is not None else 5
+    NL = args.layers
+    n = args.config
+    w = workloads.CONFIGS[n](rows=False)
+    B, Hq, Hkv, D = w.B, w.Hq, w.Hkv, w.D
+    fmt = "fp8" if n == 5 else "bf16"
+    elem = 1 if fmt == "fp8" else 2
+    g = torch.Generator(device=dev)
+    g.manual_seed(n)
+    bm = pk.BlockManager(w.num_blocks, free_order=w.free_order)
+    pairs = []
+    if n == 5:                       # prompt, 3 forks, then each sample's suffix
+        for grp in w.groups:
+            s0 = grp["seqs"][0]
+            bm.add_seq(s0)
+            bm.append_tokens(s0, grp["prompt"])
+            for sid in grp["seqs"][1:]:
+                bm.fork(s0, sid)
+            for sid, sl in zip(grp["seqs"], grp["suffix"]):
+                _, pr = bm.append_tokens(sid, sl)
+                if pr is not None:
+                    pairs.append(pr)
+    else:
+        for s in range(B):
+            bm.add_seq(s)
+            bm.append_tokens(s, int(w.lens[s]))
+    cap = int(-(-int(w.lens.max()) // 16))
+    bt, cl = bm.pack(np.arange(B), cap)
+    used = np.unique(bt[bt >= 0])
+    # caches: random rows in every slot of every block a table names (the
+    # contents do not change the work); fp8 codes from N(0, 1) rows at scale
+    # max|x| / 448
+    rows = int(len(used)) * 16
+    slots = torch.from_numpy((used.astype(np.int64)[:, None] * 16 + np.arange(16)).reshape(-1)).to(dev)
+    k_rows = torch.randn((rows, Hkv, D), device=dev, generator=g).to(torch.bfloat16)
+    v_rows = torch.randn((rows, Hkv, D), device=dev, generator=g).to(torch.bfloat16)
+    ks = float(k_rows.float().abs().max()) / 448.0 if fmt == "fp8" else 1.0
+    vs = float(v_rows.float().abs().max()) / 448.0 if fmt == "fp8" else 1.0
+    desc = pk.CacheDesc(w.num_blocks, Hkv, D, fmt, ks, vs)
+    tdt = torch.uint8 if fmt == "fp8" else torch.bfloat16
+    kc = [torch.zeros(desc.shape, dtype=tdt, device=dev) for _ in range(NL)]
+    vc = [torch.zeros(desc.shape, dtype=tdt, device=dev) for _ in range(NL)]
+    pk.write_kv(desc, kc[0], vc[0], k_rows, v_rows, slots, stream=stream)
+    for l in range(1, NL):
+        kc[l].view(torch.uint8).copy_(kc[0].view(torch.uint8))
+        vc[l].view(torch.uint8).copy_(vc[0].view(torch.uint8))
+    del k_rows, v_rows, slots
+    q = [torch.randn((B, Hq, D), device=dev, generator=g).to(torch.bfloat16) for _ in range(NL)]
+    out = [torch.empty_like(q[0]) for _ in range(NL)]
+    btd = torch.from_numpy(bt).to(dev)
+    cld = torch.from_numpy(cl).to(dev)
+    max_len = int(cl.max())
+    workspace = pk.new_decode_workspace(desc, B, Hq, max_len, dev)
+    logical = _kv_bytes(cl, Hkv, D, elem)
+    # distinct bytes: every position of every sequence once, shared positions once
+    seen = {}
+    for s in range(B):
+        L = int(cl[s])
+        for j in range(-(-L // 16)):
+            b = int(bt[s, j])
+            seen[b] = max(seen.get(b, 0), min(16, L - 16 * j))
+    unique = sum(seen.values()) * Hkv * D * elem * 2
+    torch.cuda.synchronize()
+
+    def call(l):
+        pk.decode(desc, kc[l], vc[l], q[l], out[l], btd, cld, max_len, float(w.scale),
+                  workspace, stream=stream)
+
+    for i in range(warm * NL):
+        call(i % NL)
+    torch.cuda.synchronize()
+    evs = [(HipEvent(), HipEvent()) for _ in range(steps * NL)]
+    t0 = time.perf_counter()
+    for i in range(steps * NL):
+        evs[i][0].record(stream)
+        call(i % NL)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec_us = [a.elapsed_ms(b) * 1e3 for a, b in evs]
+    for a, b in evs:
+        a.destroy()
+        b.destroy()
+    mean_s = statistics.mean(dec_us) / 1e6
+    ach = unique / mean_s / 1e9
+    names = {2: "mha13b-bf16-b64: 13B-shaped MHA decode layer, batch 64, 40 heads, head_dim 128, "
+                "bf16 KV in 16-token shuffled blocks, lengths U[128, 2048]",
+             4: "gqa70b-bf16-32k: 70B-shaped long-context GQA decode layer, batch 8, 64 query / 8 KV "
+                "heads, head_dim 128, bf16 KV, 32768 tokens per sequence in shuffled 16-token blocks",
+             5: "cow-fp8-4x64: parallel sampling, 64 prompts of 1024 + U[1, 15] tokens forked into 4 "
+                "samples each (copy-on-write of the shared partial block), suffixes U[1, 256]; "
+                "32 query / 8 KV heads, head_dim 128, fp8-e4m3 KV with per-tensor scales"}
+    _log(f"bench: config {n}: pa_decode mean {mean_s * 1e6:.1f} us (p10 "
+         f"{np.percentile(dec_us, 10):.1f}, p90 {np.percentile(dec_us, 90):.1f}); distinct "
+         f"{unique / 1e9:.4f} GB at {ach:.0f} GB/s, logical {logical / 1e9:.4f} GB")
+    res = {
+        "metric": METRIC,
+        "value": round(B * steps * NL / wall, 1),
+        "unit": "seqs/s",
+        "n_gpus": 1, "steps": steps, "warmup": warm,
+        "ms_per_step": round(wall / steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": fmt, "data": "synthetic",
+        "config": {"workload": names[n], "global_batch": B, "layers_per_step": NL,
+                   "step": "per layer pa_decode (lengths fixed)",
+                   "value_is": "sequences decoded per second per attention layer",
+                   "parallelism": "single GPU"},
+        "decode_us_mean": round(mean_s * 1e6, 2),
+        "decode_us_p10": round(float(np.percentile(dec_us, 10)), 2),
+        "decode_us_p90": round(float(np.percentile(dec_us, 90)), 2),
+        "distinct_kv_gb": round(unique / 1e9, 4), "logical_kv_gb": round(logical / 1e9, 4),
+        "logical_kv_gbps": round(logical / mean_s / 1e9, 1),
+        "copy_on_write_pairs": len(pairs),
+        "roofline": {"kernel": ("decode_stream_kernel (pa_decode)" if n != 4 else
+                                "decode_stream_kernel (pa_decode: long contexts split over waves)"),
+                     "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def run_prefix(args):
     """256 requests sharing a 2048-token prompt, decoded step by step."""
     import torch
@@ -616,6 +759,8 @@ def main():
                     help="decode a batch that shares a system prompt through prefix caching")
     ap.add_argument("--prefix-path", choices=("cascade", "plain"), default="cascade",
                     help="with --prefix: pa_decode_shared_prefix (default) or pa_decode")
+    ap.add_argument("--config", type=int, default=0, choices=(0, 2, 4, 5),
+                    help="pa_decode alone on decode configuration 2, 4 or 5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     args = ap.parse_args()
@@ -627,6 +772,8 @@ def main():
         return run_swap(args)
     if args.prefix:
         return run_prefix(args)
+    if args.config:
+        return run_config(args)
     T = args.chunk
     if not 1 <= T <= 16:
         sys.exit("--chunk must be in 1..16")

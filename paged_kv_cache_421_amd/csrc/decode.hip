@@ -353,7 +353,13 @@ decode_stream_kernel(StreamArgs a) {
   const int h_row = row_ok ? row - (row / G) * G : 0;
   const int mshift = nchunk - 1 - t_row;
   const int q_bytes = ((nchunk - 1) * hq + G) * kD * 2;            // one segment's q rows
-  const int q_lane_off = row_ok ? ((t_row * hq + h_row) * kD + 8 * quad) * 2 : kOutOfRange;  // + 64*kk
+  // q in the B-operand layout, dims matching K's: bf16 step kk, quad q
+  // holds dims 32kk + 8q .. +7; fp8 K is loaded 16 dims per lane (one
+  // 16-byte load for two steps: half the cache-line requests of 8-byte
+  // loads), so there step kk, quad q holds dims 64 (kk/2) + 16q + 8 (kk%2)
+  // .. +7 -- a permutation of the contraction's dims, applied to both sides
+  const int q_lane_off = row_ok ? ((t_row * hq + h_row) * kD + (kFp8 ? 16 : 8) * quad) * 2 : kOutOfRange;
+  auto q_step_off = [](int kk) -> int { return kFp8 ? 128 * (kk >> 1) + 16 * (kk & 1) : 64 * kk; };
 
   // ---- 3. tile descriptors, built in LDS in rounds of up to kCap tiles
   // word 0: tile index block * Hkv + g (the block's position in the table
@@ -418,7 +424,8 @@ decode_stream_kernel(StreamArgs a) {
   //    dims 32*kk + 8*quad .. +7.
   //  V: plain rows, lane l holds token l / kLanesPerRow (+ kRowsPerLoad per
   //    load), dims 8 * (l % kLanesPerRow) .. +7; they pass through LDS.
-  const int k_off = (row * kD + 8 * quad) * kE;               // + 32*kk*kE
+  const int k_off = kFp8 ? row * kRowBytes + 16 * quad           // fp8: + 64*j, j < kKK/2
+                         : (row * kD + 8 * quad) * kE;            // bf16: + 32*kk*kE
   const int v_c = lane % kLanesPerRow;
   const int v_r = lane / kLanesPerRow;
   const int v_off = (v_r * kD + 8 * v_c) * kE;                // + i*kRowsPerLoad*kRowBytes
@@ -640,7 +647,8 @@ decode_stream_kernel(StreamArgs a) {
   };
 
   // ring slots: tile data and the segment's q
-  Chunk kt[kNT][kKK];
+  constexpr int kKLoads = kFp8 ? kKK / 2 : kKK;    // 16-byte K loads per lane
+  u32x4_t kt[kNT][kKLoads];
   Chunk vt[kNT][kVLoads];
   u32x4_t qs[kNT][kKK];
 
@@ -756,7 +764,7 @@ decode_stream_kernel(StreamArgs a) {
       }
       const __amdgpu_buffer_rsrc_t rq = make_rsrc(reinterpret_cast<const char*>(a.q) + q_off, q_nrec);
 #pragma unroll
-      for (int kk = 0; kk < kKK; ++kk) qs[slot][kk] = __builtin_amdgcn_raw_buffer_load_b128(rq, q_lane_off + 64 * kk, 0, 0);
+      for (int kk = 0; kk < kKK; ++kk) qs[slot][kk] = __builtin_amdgcn_raw_buffer_load_b128(rq, q_lane_off + q_step_off(kk), 0, 0);
       if constexpr (kPair) {
         // one descriptor over the whole cache, per-lane offsets: rows 0-7
         // of the tile in the first block, rows 8-15 in the second; rows
@@ -775,14 +783,10 @@ decode_stream_kernel(StreamArgs a) {
         };
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k_cache, a.pair_nrec);
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v_cache, a.pair_nrec);
-        const int ko = row_at(row) + 8 * quad * kE;
+        const int ko = row_at(row) + (kFp8 ? 16 : 8 * kE) * quad;
 #pragma unroll
-        for (int kk = 0; kk < kKK; ++kk) {
-          if constexpr (kFp8)
-            kt[slot][kk] = __builtin_bit_cast(Chunk, __builtin_amdgcn_raw_buffer_load_b64(rk, ko + 32 * kk * kE, 0, kAux));
-          else
-            kt[slot][kk] = __builtin_amdgcn_raw_buffer_load_b128(rk, ko + 32 * kk * kE, 0, kAux);
-        }
+        for (int j = 0; j < kKLoads; ++j)
+          kt[slot][j] = __builtin_amdgcn_raw_buffer_load_b128(rk, ko + (kFp8 ? 64 : 32 * kE) * j, 0, kAux);
 #pragma unroll
         for (int i = 0; i < kVLoads; ++i) {
           const int vo = row_at(v_r + i * kRowsPerLoad) + 8 * v_c * kE;
@@ -798,12 +802,8 @@ decode_stream_kernel(StreamArgs a) {
       const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k_cache + tile_off, k_nrec);
       const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v_cache + tile_off, v_nrec);
 #pragma unroll
-      for (int kk = 0; kk < kKK; ++kk) {
-        if constexpr (kFp8)
-          kt[slot][kk] = __builtin_bit_cast(Chunk, __builtin_amdgcn_raw_buffer_load_b64(rk, k_off + 32 * kk * kE, 0, kAux));
-        else
-          kt[slot][kk] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_off + 32 * kk * kE, 0, kAux);
-      }
+      for (int j = 0; j < kKLoads; ++j)
+        kt[slot][j] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_off + (kFp8 ? 64 : 32 * kE) * j, 0, kAux);
 #pragma unroll
       for (int i = 0; i < kVLoads; ++i) {
         if constexpr (kFp8)
@@ -833,8 +833,8 @@ decode_stream_kernel(StreamArgs a) {
       for (int kk = 0; kk < kKK; ++kk) {
         bf16x8_t kb;
         if constexpr (kFp8) {
-          const u32x2_t wv = kt[slot][kk];
-          const int w0 = static_cast<int>(wv[0]), w1 = static_cast<int>(wv[1]);
+          const u32x4_t wv = kt[slot][kk >> 1];
+          const int w0 = static_cast<int>(wv[2 * (kk & 1)]), w1 = static_cast<int>(wv[2 * (kk & 1) + 1]);
           const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
           const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
           const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
