@@ -143,6 +143,18 @@ def test_decode_empty_sequences_between_others():
     _small_case(311, "bf16", len(lens), 8, 2, 128, 0, lens=lens)
 
 
+def test_decode_batch_past_256_with_short_and_empty_sequences():
+    """700 sequences, a third empty, most a few tokens long, some long: the
+    lengths past the first 256 are read in later rounds, and the work split
+    weighs segment starts, so waves over many short sequences take fewer
+    tiles."""
+    rng = np.random.default_rng(315)
+    lens = rng.integers(1, 40, 700).astype(np.int32)
+    lens[rng.random(700) < 0.33] = 0
+    lens[rng.choice(700, 12, replace=False)] = rng.integers(1000, 3000, 12)
+    _small_case(315, "bf16", len(lens), 8, 2, 128, 0, lens=lens)
+
+
 @pytest.mark.parametrize("L", [1, 16, 17, 130])
 def test_decode_one_sequence(L):
     """Fewer tiles than a wave's minimum share: most waves get nothing."""
