@@ -443,7 +443,8 @@ def chat_hit_rate(seed=11, conversations=64, turns=8, block_size=16):
 
 
 def run_config(args):
-    """pa_decode on decode configuration 2, 4 or 5 (lengths fixed)."""
+    """pa_decode on decode configuration 2, 4 or 5 (lengths fixed); configuration 5
+    through pa_decode_shared_prefix with --prefix-path cascade."""
     import torch
     import paged_kv_cache_421_amd as pk
 
@@ -514,28 +515,54 @@ def run_config(args):
             b = int(bt[s, j])
             seen[b] = max(seen.get(b, 0), min(16, L - 16 * j))
     unique = sum(seen.values()) * Hkv * D * elem * 2
+    # configuration 5 also times pa_decode_shared_prefix, which attends each
+    # prompt's full blocks (shared by its 4 samples) once; with --prefix-path
+    # cascade that is the timed path, else pa_decode is
+    groups = bm.shared_prefix_groups(np.arange(B)) if n == 5 else np.zeros((0, 3), np.int32)
+    cascade = len(groups) > 0 and args.prefix_path == "cascade"
+    sp_ws = (pk.new_shared_prefix_workspace(desc, B, Hq, bt.shape[1], max_len, dev)
+             if len(groups) else None)
     torch.cuda.synchronize()
 
-    def call(l):
-        pk.decode(desc, kc[l], vc[l], q[l], out[l], btd, cld, max_len, float(w.scale),
-                  workspace, stream=stream)
+    def call(l, shared):
+        if shared:
+            pk.decode_shared_prefix(desc, kc[l], vc[l], q[l], out[l], btd, cld, max_len,
+                                    float(w.scale), groups, sp_ws, stream=stream)
+        else:
+            pk.decode(desc, kc[l], vc[l], q[l], out[l], btd, cld, max_len, float(w.scale),
+                      workspace, stream=stream)
 
-    for i in range(warm * NL):
-        call(i % NL)
-    torch.cuda.synchronize()
-    evs = [(HipEvent(), HipEvent()) for _ in range(steps * NL)]
-    t0 = time.perf_counter()
-    for i in range(steps * NL):
-        evs[i][0].record(stream)
-        call(i % NL)
-        evs[i][1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    dec_us = [a.elapsed_ms(b) * 1e3 for a, b in evs]
-    for a, b in evs:
-        a.destroy()
-        b.destroy()
+    def timed(shared, nsteps):
+        for i in range(warm * NL):
+            call(i % NL, shared)
+        torch.cuda.synchronize()
+        evs = [(HipEvent(), HipEvent()) for _ in range(nsteps * NL)]
+        t0 = time.perf_counter()
+        for i in range(nsteps * NL):
+            evs[i][0].record(stream)
+            call(i % NL, shared)
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        us = [a.elapsed_ms(b) * 1e3 for a, b in evs]
+        for a, b in evs:
+            a.destroy()
+            b.destroy()
+        return wall, us
+
+    wall, dec_us = timed(cascade, steps)
     mean_s = statistics.mean(dec_us) / 1e6
+    other = None
+    if len(groups):
+        # the other path on the same batch, and how far its output lies from this one's
+        res_this = [o.float().clone() for o in out]
+        _, other_us = timed(not cascade, max(steps // 2, 1))
+        diff = max(float((o.float() - r).abs().max()) for o, r in zip(out, res_this))
+        other = {"path": "pa_decode" if cascade else "pa_decode_shared_prefix",
+                 "decode_us_mean": round(statistics.mean(other_us), 2),
+                 "max_abs_diff_vs_this_path": round(diff, 5)}
+        _log(f"bench: config {n}: {other['path']} mean {other['decode_us_mean']:.1f} us; "
+             f"outputs differ by at most {diff:.4g}")
     ach = unique / mean_s / 1e9
     names = {2: "mha13b-bf16-b64: 13B-shaped MHA decode layer, batch 64, 40 heads, head_dim 128, "
                 "bf16 KV in 16-token shuffled blocks, lengths U[128, 2048]",
@@ -556,7 +583,8 @@ def run_config(args):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": fmt, "data": "synthetic",
         "config": {"workload": names[n], "global_batch": B, "layers_per_step": NL,
-                   "step": "per layer pa_decode (lengths fixed)",
+                   "step": ("per layer pa_decode_shared_prefix (lengths fixed)" if cascade
+                            else "per layer pa_decode (lengths fixed)"),
                    "value_is": "sequences decoded per second per attention layer",
                    "parallelism": "single GPU"},
         "decode_us_mean": round(mean_s * 1e6, 2),
@@ -565,7 +593,10 @@ def run_config(args):
         "distinct_kv_gb": round(unique / 1e9, 4), "logical_kv_gb": round(logical / 1e9, 4),
         "logical_kv_gbps": round(logical / mean_s / 1e9, 1),
         "copy_on_write_pairs": len(pairs),
-        "roofline": {"kernel": ("decode_stream_kernel (pa_decode)" if n != 4 else
+        "shared_prefix_groups": len(groups),
+        "other_path": other,
+        "roofline": {"kernel": ("shared_prefix_kernel + decode_stream_kernel (pa_decode_shared_prefix)"
+                                if cascade else "decode_stream_kernel (pa_decode)" if n != 4 else
                                 "decode_stream_kernel (pa_decode: long contexts split over waves)"),
                      "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None},
@@ -621,7 +652,7 @@ def run_prefix(args):
     out = [torch.empty_like(q[0]) for _ in range(NL)]
     max_len_final = int(lens.max()) + steps + warm
     cap = -(-max_len_final // 16)
-    cascade = args.prefix_path == "cascade"
+    cascade = args.prefix_path != "plain"
     workspace = pk.new_decode_workspace(desc, B, Hq, max_len_final, dev)
     sp_workspace = pk.new_shared_prefix_workspace(desc, B, Hq, cap, max_len_final, dev)
     h_slots = torch.empty(B, dtype=torch.int64, pin_memory=True)
@@ -757,8 +788,9 @@ def main():
                     help="sliding window of W positions (0: none)")
     ap.add_argument("--prefix", action="store_true",
                     help="decode a batch that shares a system prompt through prefix caching")
-    ap.add_argument("--prefix-path", choices=("cascade", "plain"), default="cascade",
-                    help="with --prefix: pa_decode_shared_prefix (default) or pa_decode")
+    ap.add_argument("--prefix-path", choices=("cascade", "plain"), default=None,
+                    help="pa_decode_shared_prefix or pa_decode: with --prefix the default is "
+                         "cascade, with --config 5 plain")
     ap.add_argument("--config", type=int, default=0, choices=(0, 2, 4, 5),
                     help="pa_decode alone on decode configuration 2, 4 or 5")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -70,6 +70,8 @@ typedef enum {
 #define PA_PARTITION_TOKENS 512
 /* Largest chunk of new tokens per sequence pa_decode_chunk takes. */
 #define PA_MAX_CHUNK 16
+/* Most shared-prefix groups one pa_decode_shared_prefix call takes. */
+#define PA_MAX_PREFIX_GROUPS 128
 
 typedef struct {
   int32_t num_blocks;    /* physical blocks in each of the K and V caches */
@@ -365,7 +367,7 @@ pa_status pa_bm_cache_stats(const pa_bm* bm, int64_t* queried_blocks, int64_t* h
  * pa_decode_shared_prefix -- pa_decode for a batch in which groups[k] =
  * (first, count, shared) says sequences first .. first+count-1 hold the
  * same valid block ids in their first `shared` table entries (host array,
- * at most 32 disjoint groups; a member no longer than shared * block_size
+ * at most PA_MAX_PREFIX_GROUPS disjoint groups; a member no longer than shared * block_size
  * sees only its own length of them).  The result is pa_decode's (up to
  * rounding order); the prefix is attended once per
  * (group, KV head) on MFMA with all members' query rows and folded into each

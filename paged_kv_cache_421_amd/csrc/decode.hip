@@ -995,7 +995,7 @@ zero_fill_kernel(uint32_t* p, int64_t n_words) {
 // LDS, and the prefix's positions are split over several workgroups to
 // fill the chip; the last split of a row block to finish merges the
 // splits' records.
-constexpr int kMaxGroups = 32;
+constexpr int kMaxGroups = PA_MAX_PREFIX_GROUPS;   // groups travel in the kernel arguments
 constexpr int kPrefixWaves = 8;            // 16-row blocks per workgroup, one per wave
 constexpr int kPrefixRows = 16 * kPrefixWaves;
 constexpr int kPrefixTilesPerStep = 2;     // tiles loaded and run between barriers

@@ -15,7 +15,7 @@ import torch
 import oracle
 import workloads
 from tests import _oracle_setup as osu
-from tests._gpu_setup import GpuView, cache_to_numpy, fill_sequential, out_to_f64
+from tests._gpu_setup import GpuView, cache_to_numpy, fill_sequential, out_to_f64, to_device_rows
 
 pk = pytest.importorskip("paged_kv_cache_421_amd")
 
@@ -145,9 +145,9 @@ def test_decode_empty_sequences_between_others():
 
 def test_decode_batch_past_256_with_short_and_empty_sequences():
     """700 sequences, a third empty, most a few tokens long, some long: the
-    lengths past the first 256 are read in later rounds, and the work split
-    weighs segment starts, so waves over many short sequences take fewer
-    tiles."""
+    lengths past the first 256 are read in later rounds, waves start inside
+    every kind of segment, and empty sequences' zero rows are written by
+    waves past the first 256."""
     rng = np.random.default_rng(315)
     lens = rng.integers(1, 40, 700).astype(np.int32)
     lens[rng.random(700) < 0.33] = 0
@@ -311,3 +311,17 @@ def test_full_parallel_sampling_fp8_with_copy_on_write():
     err = _check_out(out, ref, "fp8", rows)
     assert torch.isfinite(out.float()).all()
     _say(f"workload 5: max abs err {err:.3e}")
+    # the same batch with each prompt's shared full blocks attended once
+    groups = view.bm.shared_prefix_groups(np.arange(w.B))
+    assert len(groups) == 64 and set(groups[:, 1].tolist()) == {4}
+    assert np.all(groups[:, 2] == 64)            # 1024 + r tokens: 64 full blocks shared
+    qd = to_device_rows(w.q, w.q_fmt)
+    out_sp = torch.empty_like(qd)
+    pk.decode_shared_prefix(view.desc, view.kc, view.vc, qd, out_sp, view.bt, view.cl,
+                            int(cl.max()), float(w.scale), groups)
+    torch.cuda.synchronize()
+    err_sp = _check_out(out_sp, ref, "fp8", rows)
+    diff = float((out_sp.float() - out.float()).abs().max())
+    _say(f"workload 5 through pa_decode_shared_prefix: max abs err {err_sp:.3e}, "
+         f"vs pa_decode {diff:.3e}")
+    assert diff <= TOL["fp8"]

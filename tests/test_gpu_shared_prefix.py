@@ -169,15 +169,17 @@ def test_members_no_longer_than_the_shared_blocks():
 
 
 def test_many_groups_and_row_blocks():
-    """32 groups (the most one call takes), G = 16 so every member fills a
-    16-row block, and groups of 2 to 5 members."""
+    """128 groups (PA_MAX_PREFIX_GROUPS, the most one call takes), G = 16 so
+    every member fills a 16-row block, and groups of 2 to 5 members."""
+    n_groups = 128
     rng = np.random.default_rng(4)
-    counts = [int(x) for x in rng.integers(2, 6, 32)]
-    ws = _workloads(1000, 32, 2, 128, [int(x) for x in rng.integers(16, 200, 32)], counts, qmax=40)
+    counts = [int(x) for x in rng.integers(2, 6, n_groups)]
+    ws = _workloads(1000, 32, 2, 128, [int(x) for x in rng.integers(16, 200, n_groups)], counts,
+                    qmax=40)
     order = [(i, r) for i, n in enumerate(counts) for r in range(n)]
     b = Batch(ws, order, "bf16", 16, 9)
-    assert len(b.groups) == 32            # every prompt has a full block
-    _say(f"32 prompts: {len(b.groups)} groups over {b.B} requests")
+    assert len(b.groups) == n_groups      # every prompt has a full block
+    _say(f"{n_groups} prompts: {len(b.groups)} groups over {b.B} requests")
     out = b.shared(b.groups)
     torch.cuda.synchronize()
     err = np.abs(out_to_f64(out) - b.oracle()).max()

@@ -529,7 +529,7 @@ def test_shared_prefix_decode_validates_groups_on_the_host():
     assert call([[0, 2, 9]]) == -1                       # more shared blocks than the table
     assert call([[0, 3, 1], [2, 2, 1]]) == -1 and b"overlap" in pk.lib.pa_last_error()
     assert call([[0, 1, 0]]) == -1                       # nothing shared
-    assert call([[0, 2, 1]] * 33, ng=33) == -1           # too many groups
+    assert call([[0, 2, 1]] * 129, ng=129) == -1         # too many groups (PA_MAX_PREFIX_GROUPS)
     assert call([[0, 2, 1]], nbytes=ws_bytes - 1) == -6
     g1 = np.array([[0, 2, 1]], np.int32)
     for bad in (0.0, -0.5, float("inf")):
