@@ -88,6 +88,11 @@ def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} not found: build it with `python paged_kv_cache_421_amd/build.py`")
+    # torch first: it carries its own HIP runtime, and the library must bind to
+    # that same runtime (it launches on torch's streams and reads its memory).
+    # Loaded before torch, the library would pull in the system runtime and
+    # the process would hold two, each seeing no device the other set up.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)
