@@ -36,6 +36,11 @@ The JSON line also carries
     counter summary, when that was taken on the current kernel source;
   * ``cpu_baseline``: the CPU float64 oracle's decode of the same batch on the
     host, single-threaded;
+  * ``path_steps``: the other steps of the path, each timed on its own -- the
+    host block manager's time per step (append + pack), pa_write_kv of the
+    whole cache's rows (the bulk fill of one layer) and of one step's rows,
+    and pa_copy_blocks of 1024 whole-block pairs, with their rates (bytes
+    read plus written) against the HBM peak;
   * ``stream_read_probe``: context for the roofline fraction -- the rate
     pa_read_probe streams a 4 GiB buffer at with the decode kernel's load
     form, in address order and in 4 KiB chunks visited in a seeded random
@@ -852,7 +857,17 @@ def main():
     k_rows = torch.from_numpy(w.k_rows.view(np.int16)).to(dev).view(torch.bfloat16)
     v_rows = torch.from_numpy(w.v_rows.view(np.int16)).to(dev).view(torch.bfloat16)
     pk.write_kv(desc, kc[0], vc[0], k_rows, v_rows, slots)
-    for l in range(1, NL):
+    # the same rows into layer 1 again, timed: the bulk rate of pa_write_kv
+    bulk_ev = (HipEvent(), HipEvent())
+    torch.cuda.synchronize()
+    bulk_ev[0].record(stream)
+    pk.write_kv(desc, kc[1 % NL], vc[1 % NL], k_rows, v_rows, slots, stream=stream)
+    bulk_ev[1].record(stream)
+    bulk_us = bulk_ev[0].elapsed_ms(bulk_ev[1]) * 1e3
+    bulk_ev[0].destroy()
+    bulk_ev[1].destroy()
+    bulk_rows = int(slots.numel())
+    for l in range(2, NL):
         kc[l].copy_(kc[0])
         vc[l].copy_(vc[0])
     del k_rows, v_rows, slots
@@ -890,10 +905,13 @@ def main():
     ids = np.arange(B, dtype=np.int64)
     lens = w.lens.astype(np.int64).copy()
 
+    host_bm_s = []                           # block manager + table packing, per step
+
     def step(i, ev_pairs):
         b = i % NBUF
         if buf_ev[b] is not None:
             buf_ev[b].synchronize()          # the upload that last read buffer b is done
+        th = time.perf_counter()
         if T == 1:
             sl, pairs = bm.append_batch(ids, slots=h_slots[b].numpy())
             assert len(pairs) == 0
@@ -903,6 +921,7 @@ def main():
                 assert len(pairs) == 0
             h_slots[b].numpy().reshape(B, T)[:] = slots_tb.T
         bm.pack(ids, cap, block_tables=h_bt[b].numpy(), context_lens=h_cl[b].numpy())
+        host_bm_s.append(time.perf_counter() - th)
         lens[:] += T
         d_slots.copy_(h_slots[b], non_blocking=True)
         d_bt.copy_(h_bt[b], non_blocking=True)
@@ -944,6 +963,57 @@ def main():
     t1 = time.perf_counter()
     wall = t1 - t0
     assert torch.isfinite(out[0].float()).all(), "non-finite decode output"
+    host_bm_us = statistics.mean(host_bm_s[args.warmup:]) * 1e6
+
+    # ---- the other device steps of the path, each timed on its own after the
+    # timed steps (back to back, one event pair around n calls): pa_write_kv of
+    # one step's B*T rows, and pa_copy_blocks of 1024 pairs from blocks in use
+    # into free ones (whole blocks of both caches) on the last layer's cache
+    def timed_calls(fn, n=50):
+        e0, e1 = HipEvent(), HipEvent()
+        fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        us = e0.elapsed_ms(e1) * 1e3 / n
+        e0.destroy()
+        e1.destroy()
+        return us
+
+    step_us = timed_calls(lambda: pk.write_kv(desc, kc[0], vc[0], k_new[0], v_new[0], d_slots,
+                                              stream=stream))
+    bt_now, _ = bm.pack(ids, cap)
+    used_blocks = np.unique(bt_now[bt_now >= 0])
+    free_blocks = np.setdiff1d(np.arange(n_blocks), used_blocks)
+    prng = np.random.default_rng(77)
+    n_pairs = int(min(1024, len(free_blocks), len(used_blocks)))
+    cp_pairs = torch.from_numpy(np.stack([prng.choice(used_blocks, n_pairs, replace=False),
+                                          prng.choice(free_blocks, n_pairs, replace=False)],
+                                         axis=1).astype(np.int32)).to(dev)
+    copy_us = timed_calls(lambda: pk.copy_blocks(desc, kc[NL - 1], vc[NL - 1], cp_pairs,
+                                                 stream=stream))
+    blk_bytes = bs * Hkv * D * 2                       # one block of one cache
+    row_bytes = Hkv * D * 2                            # one token row of K (or V)
+    bulk_b = 2 * 2 * bulk_rows * row_bytes             # K and V rows read, then written
+    step_b = 2 * 2 * B * T * row_bytes
+    copy_b = 2 * 2 * n_pairs * blk_bytes               # both caches, read and written
+    path_steps = {
+        "block_manager_host_us_per_step": round(host_bm_us, 1),
+        "pa_write_kv_bulk": {"rows": bulk_rows, "us": round(bulk_us, 1),
+                             "gbps": round(bulk_b / bulk_us / 1e3, 1),
+                             "frac": round(bulk_b / bulk_us / 1e3 / HBM_PEAK_GBPS, 4)},
+        "pa_write_kv_step": {"rows": B * T, "us": round(step_us, 2),
+                             "gbps": round(step_b / step_us / 1e3, 1)},
+        "pa_copy_blocks": {"pairs": n_pairs, "us": round(copy_us, 2),
+                           "gbps": round(copy_b / copy_us / 1e3, 1),
+                           "frac": round(copy_b / copy_us / 1e3 / HBM_PEAK_GBPS, 4)},
+    }
+    _log(f"bench: block manager {host_bm_us:.0f} us/step (host); pa_write_kv bulk "
+         f"{bulk_rows} rows {bulk_us:.1f} us ({bulk_b / bulk_us / 1e3:.0f} GB/s), "
+         f"{B * T} rows {step_us:.2f} us; pa_copy_blocks {n_pairs} pairs {copy_us:.2f} us "
+         f"({copy_b / copy_us / 1e3:.0f} GB/s)")
 
     dec_ms = [a.elapsed_ms(b) for row in evs for (a, b) in row]
     for row in evs:
@@ -994,6 +1064,7 @@ def main():
             "parallelism": "single GPU",
         },
         "kv_gbps_step": round(mean_kv * NL / steps_s / 1e9, 1),
+        "path_steps": path_steps,
         "block_size": bs,
         "paged_utilisation": round(float(lens.sum()) / (bs * float(np.sum(-(-lens // bs)))), 4),
         "decode_us_mean": round(mean_dec_s * 1e6, 2),
