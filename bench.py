@@ -449,7 +449,7 @@ def chat_hit_rate(seed=11, conversations=64, turns=8, block_size=16):
 
 def run_config(args):
     """pa_decode on decode configuration 2, 4 or 5 (lengths fixed); configuration 5
-    through pa_decode_shared_prefix with --prefix-path cascade."""
+    through pa_decode_shared_prefix unless --prefix-path plain."""
     import torch
     import paged_kv_cache_421_amd as pk
 
@@ -520,11 +520,11 @@ def run_config(args):
             b = int(bt[s, j])
             seen[b] = max(seen.get(b, 0), min(16, L - 16 * j))
     unique = sum(seen.values()) * Hkv * D * elem * 2
-    # configuration 5 also times pa_decode_shared_prefix, which attends each
-    # prompt's full blocks (shared by its 4 samples) once; with --prefix-path
-    # cascade that is the timed path, else pa_decode is
+    # configuration 5 goes through pa_decode_shared_prefix, which attends each
+    # prompt's full blocks (shared by its 4 samples) once, and times pa_decode
+    # beside it; --prefix-path plain swaps the two
     groups = bm.shared_prefix_groups(np.arange(B)) if n == 5 else np.zeros((0, 3), np.int32)
-    cascade = len(groups) > 0 and args.prefix_path == "cascade"
+    cascade = len(groups) > 0 and args.prefix_path != "plain"
     sp_ws = (pk.new_shared_prefix_workspace(desc, B, Hq, bt.shape[1], max_len, dev)
              if len(groups) else None)
     torch.cuda.synchronize()
@@ -600,8 +600,8 @@ def run_config(args):
         "copy_on_write_pairs": len(pairs),
         "shared_prefix_groups": len(groups),
         "other_path": other,
-        "roofline": {"kernel": ("shared_prefix_kernel + decode_stream_kernel (pa_decode_shared_prefix)"
-                                if cascade else "decode_stream_kernel (pa_decode)" if n != 4 else
+        "roofline": {"kernel": ("decode_stream_kernel group pass + suffix pass "
+                                "(pa_decode_shared_prefix)" if cascade else "decode_stream_kernel (pa_decode)" if n != 4 else
                                 "decode_stream_kernel (pa_decode: long contexts split over waves)"),
                      "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None},
@@ -794,8 +794,8 @@ def main():
     ap.add_argument("--prefix", action="store_true",
                     help="decode a batch that shares a system prompt through prefix caching")
     ap.add_argument("--prefix-path", choices=("cascade", "plain"), default=None,
-                    help="pa_decode_shared_prefix or pa_decode: with --prefix the default is "
-                         "cascade, with --config 5 plain")
+                    help="with --prefix or --config 5: pa_decode_shared_prefix (cascade, the "
+                         "default) or pa_decode (plain)")
     ap.add_argument("--config", type=int, default=0, choices=(0, 2, 4, 5),
                     help="pa_decode alone on decode configuration 2, 4 or 5")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -372,6 +372,11 @@ pa_status pa_bm_cache_stats(const pa_bm* bm, int64_t* queried_blocks, int64_t* h
  * rounding order); the prefix is attended once per
  * (group, KV head) on MFMA with all members' query rows and folded into each
  * row by the log-sum-exp rule, then the suffixes are decoded as usual.
+ * When every group's rows of a KV head (members x G) fit 16, the prefix
+ * runs through pa_decode's own tile stream with the members as query rows;
+ * a group with a member no longer than shared * block_size is then decoded
+ * whole by the suffix pass (same result).  Larger groups use a kernel that
+ * shares each prefix tile among up to 128 rows in LDS.
  * Needs the bf16 / fp8 fast path (head_dim 64 or 128, G <= 16, block size a
  * multiple of 16), single-token decode, a positive scale (with groups).  workspace: zero-filled before first
  * use, 256-byte aligned, pa_decode_shared_prefix_workspace_bytes(...) bytes;

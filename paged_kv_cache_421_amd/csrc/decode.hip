@@ -215,6 +215,19 @@ struct StreamArgs {
   int rows;                   // query rows of this pass (<= kMaxRows)
   float logit_scale;          // scale * k_scale * log2(e)
   float v_scale;
+  // q rows (of Hq heads each) from one sequence's to the next (the chunk
+  // length T; 1 in a group pass) and in all of q: loads past them read 0
+  int q_seq_rows;
+  int q_total_rows;
+  int causal;                 // 1: chunk token t sees positions < L - T + 1 + t; 0: all < L
+  // group pass (null otherwise): "sequence" s leads a group of rec_count[s]
+  // consecutive sequences whose rows are the chunk tokens (T = the most
+  // members of any group); its length and table are the group's shared
+  // prefix.  Each member row's attention over it is written as a record
+  // rec_out[((s + t)*Hq + h)*(kD + 4)]: unnormalised o[kD], max m (log2
+  // units), sum l -- the prefix records a later pass folds in.
+  float* rec_out;
+  const int32_t* rec_count;
 };
 
 // kD: head_dim; kFp8: E4M3 cache (else bf16); kAux: cache policy bits of the
@@ -269,7 +282,8 @@ decode_stream_kernel(StreamArgs a) {
     for (int r = 0; r < 4; ++r) {
       const int s = s0 + 64 * r + lane;
       c += tiles_of(L[r]);
-      const uint64_t empty = __builtin_amdgcn_ballot_w64(s < B && L[r] == 0 && s % a.num_waves == w);
+      const uint64_t empty = __builtin_amdgcn_ballot_w64(s < B && L[r] == 0 && s % a.num_waves == w &&
+                                                         a.rec_out == nullptr);
       for (uint64_t m = empty; m != 0; m &= m - 1) {
         const int se = s0 + 64 * r + __builtin_ctzll(m);
         uint16_t* orow = a.out + (static_cast<int64_t>(se) * nchunk + a.t_first) * hq * kD;
@@ -351,8 +365,9 @@ decode_stream_kernel(StreamArgs a) {
   const bool row_ok = row < R;
   const int t_row = a.t_first + (row_ok ? row / G : 0);
   const int h_row = row_ok ? row - (row / G) * G : 0;
-  const int mshift = nchunk - 1 - t_row;
+  const int mshift = a.causal ? nchunk - 1 - t_row : 0;
   const int q_bytes = ((nchunk - 1) * hq + G) * kD * 2;            // one segment's q rows
+  const int64_t q_all_bytes = static_cast<int64_t>(a.q_total_rows) * hq * kD * 2;
   // q in the B-operand layout, dims matching K's: bf16 step kk, quad q
   // holds dims 32kk + 8q .. +7; fp8 K is loaded 16 dims per lane (one
   // 16-byte load for two steps: half the cache-line requests of 8-byte
@@ -474,21 +489,38 @@ decode_stream_kernel(StreamArgs a) {
     l_tot += __shfl_xor(l_tot, 32);
     const int wf = seg / per;
     const int wl = (seg + nb - 1) / per;
+    if (wf == wl && a.rec_out != nullptr) {   // group pass: the member rows' records
+      const int cnt = a.rec_count[s];
+      if (row_ok && t_row < cnt) {
+        float* rec = a.rec_out + ((static_cast<int64_t>(s) + t_row) * hq + g * G + h_row) * (kD + 4);
+#pragma unroll
+        for (int c = 0; c < kVC; ++c) *reinterpret_cast<f32x4_t*>(rec + 16 * c + 4 * quad) = oacc[c];
+        if (quad == 0) *reinterpret_cast<f32x2_t*>(rec + kD) = f32x2_t{m_ref, l_tot};
+      }
+      return;
+    }
     if (wf == wl) {   // the whole segment was in this wave: write the output
-      const bool has_prefix = a.prefix_len != nullptr && a.prefix_len[s] > 0;
       if (row_ok) {
-        if (has_prefix) {                                    // fold in the shared prefix
+        if (a.prefix_len != nullptr) {                       // fold in the shared prefix
+          // the record is read together with the prefix length (one round
+          // trip in the middle of the ring, not two); a sequence without a
+          // prefix ignores what it read and keeps its values exactly
           const float* rec = a.prefix_rec + (static_cast<int64_t>(s) * hq + g * G + h_row) * (kD + 4);
-          const float mp = rec[kD], lp = rec[kD + 1];
+          const int plen = a.prefix_len[s];
+          const f32x2_t ml = *reinterpret_cast<const f32x2_t*>(rec + kD);
+          f32x4_t po[kVC];
+#pragma unroll
+          for (int c = 0; c < kVC; ++c) po[c] = *reinterpret_cast<const f32x4_t*>(rec + 16 * c + 4 * quad);
+          const bool has = plen > 0;
+          const float mp = has ? ml[0] : kNoMax, lp = has ? ml[1] : 0.f;
           const float mn = fmaxf(m_ref, mp);
-          const float fa = __builtin_amdgcn_exp2f(m_ref - mn), fb = __builtin_amdgcn_exp2f(mp - mn);
+          const float fa = __builtin_amdgcn_exp2f(m_ref - mn);
+          const float fb = has ? __builtin_amdgcn_exp2f(mp - mn) : 0.f;
           l_tot = l_tot * fa + lp * fb;
 #pragma unroll
-          for (int c = 0; c < kVC; ++c) {
-            const f32x4_t po = *reinterpret_cast<const f32x4_t*>(rec + 16 * c + 4 * quad);
+          for (int c = 0; c < kVC; ++c)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) oacc[c][r] = oacc[c][r] * fa + po[r] * fb;
-          }
+            for (int r = 0; r < 4; ++r) oacc[c][r] = oacc[c][r] * fa + (has ? po[c][r] : 0.f) * fb;
         }
         // a row that saw no position has l = 0 and o = 0: a zero row
         const float inv = (l_tot > 0.f) ? a.v_scale * __builtin_amdgcn_rcpf(l_tot) : 0.f;
@@ -630,6 +662,22 @@ decode_stream_kernel(StreamArgs a) {
         }
       }
     }
+    if (a.rec_out != nullptr) {                           // group pass: member records
+      const int cnt = a.rec_count[s];
+#pragma unroll
+      for (int i = 0; i < kE4; ++i) {
+        const int q = lane + 64 * i;
+        const int r = q % R;
+        const int t = a.t_first + r / G;
+        if (q < n_grp && t < cnt) {
+          float* rec = a.rec_out + ((static_cast<int64_t>(s) + t) * hq + g * G + (r - (r / G) * G)) * (kD + 4);
+          *reinterpret_cast<f32x4_t*>(rec + 4 * (q / R)) = num[i];
+          if (q < R) *reinterpret_cast<f32x2_t*>(rec + kD) = f32x2_t{M[i], den[i]};
+        }
+      }
+      if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < kE4; ++i) {
       const int q = lane + 64 * i;
@@ -758,8 +806,8 @@ decode_stream_kernel(StreamArgs a) {
         v_nrec = k_nrec;
         tile_off = static_cast<int64_t>(tile) * kTileBytes;
         if (info & 32u) {
-          q_off = (static_cast<int64_t>(s) * nchunk * hq + static_cast<int>((info >> 7) & 511u) * G) * kD * 2;
-          q_nrec = q_bytes;
+          q_off = (static_cast<int64_t>(s) * a.q_seq_rows * hq + static_cast<int>((info >> 7) & 511u) * G) * kD * 2;
+          q_nrec = static_cast<int>(min(static_cast<int64_t>(q_bytes), q_all_bytes - q_off));
         }
       }
       const __amdgpu_buffer_rsrc_t rq = make_rsrc(reinterpret_cast<const char*>(a.q) + q_off, q_nrec);
@@ -1009,11 +1057,6 @@ struct PrefixGroups {
   int wg_begin[kMaxGroups + 1];    // prefix sum of row workgroups: ceil(count * G / 128)
 };
 
-__device__ __forceinline__ int group_of_seq(const PrefixGroups& gr, int s) {
-  for (int i = 0; i < gr.num; ++i)
-    if (s >= gr.first[i] && s < gr.first[i] + gr.count[i]) return i;
-  return -1;
-}
 
 struct PrefixArgs {
   const char* k_cache;
@@ -1035,6 +1078,11 @@ struct PrefixArgs {
   int sub_shift;
   int splits;
   float logit_scale;
+  // group pass (null otherwise): each group leader's prefix length and
+  // member count, 0 for every other sequence; the grid then does only the
+  // side job
+  int32_t* grp_lens;
+  int32_t* grp_count;
   PrefixGroups gr;
 };
 
@@ -1079,6 +1127,17 @@ shared_prefix_kernel(PrefixArgs a) {
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6) & (kPrefixWaves - 1);
   const int hkv = a.hkv, G = a.group, hq = hkv * G;
 
+  // the groups' (first, count, shared) in LDS: looked up per lane at varying
+  // indices, they would otherwise be read from the argument block one
+  // scalar-cache line at a time
+  __shared__ int s_grp[3][kMaxGroups];
+  for (int i = tid; i < a.gr.num; i += kThreads) {
+    s_grp[0][i] = a.gr.first[i];
+    s_grp[1][i] = a.gr.count[i];
+    s_grp[2][i] = a.gr.shared[i];
+  }
+  __syncthreads();
+
   // side job: suffix tables and lengths, prefix lengths
   {
     const int64_t entries = static_cast<int64_t>(a.num_seqs) * a.max_blocks;
@@ -1086,19 +1145,44 @@ shared_prefix_kernel(PrefixArgs a) {
          idx += static_cast<int64_t>(gridDim.x) * kThreads) {
       const int s = static_cast<int>(idx / a.max_blocks);
       const int j = static_cast<int>(idx - static_cast<int64_t>(s) * a.max_blocks);
-      const int gi = group_of_seq(a.gr, s);
-      const int m = gi >= 0 ? a.gr.shared[gi] : 0;
+      int gi = -1;
+      for (int i = 0; i < a.gr.num; ++i)
+        if (s >= s_grp[0][i] && s < s_grp[0][i] + s_grp[1][i]) gi = i;
+      int m = gi >= 0 ? s_grp[2][gi] : 0;
       const int64_t row = static_cast<int64_t>(s) * a.max_blocks;
-      a.suf_tables[row + j] = (j + m < a.max_blocks) ? a.block_tables[row + j + m] : -1;
+      const int L = a.context_lens[s];
+      const int e_shift = (j + m < a.max_blocks) ? a.block_tables[row + j + m] : -1;
+      if (a.grp_lens != nullptr && m > 0) {
+        // the group pass gives every member all m blocks: a group with a
+        // member no longer than them is left whole to the suffix pass (its
+        // members' lengths and both table entries are read at once)
+        const int f = s_grp[0][gi], n = s_grp[1][gi];
+        const int e_own = a.block_tables[row + j];
+        int Lm[kMaxRows];
+#pragma unroll
+        for (int i = 0; i < kMaxRows; ++i) Lm[i] = (i < n) ? a.context_lens[f + i] : 0x7FFFFFFF;
+        bool short_member = false;
+#pragma unroll
+        for (int i = 0; i < kMaxRows; ++i) short_member |= Lm[i] <= m * a.bs;
+        if (short_member) m = 0;
+        a.suf_tables[row + j] = short_member ? e_own : e_shift;
+      } else {
+        a.suf_tables[row + j] = e_shift;
+      }
       if (j == 0) {
-        const int L = a.context_lens[s];
         const int p = min(m * a.bs, max(L, 0));          // a member no longer than the prefix is all prefix
         a.suf_lens[s] = L - p;
         a.prefix_len[s] = p;
+        if (a.grp_lens != nullptr) {
+          const bool lead = m > 0 && s == s_grp[0][gi];
+          a.grp_lens[s] = lead ? m * a.bs : 0;
+          a.grp_count[s] = lead ? s_grp[1][gi] : 0;
+        }
       }
     }
   }
 
+  if (a.grp_lens != nullptr) return;                     // group pass: the side job only
   const int g = static_cast<int>(blockIdx.x) % hkv;
   const int rest = static_cast<int>(blockIdx.x) / hkv;
   const int sp = rest % a.splits;
@@ -1716,6 +1800,11 @@ pa_status attend(const char* fn, const pa_cache_desc* c, const void* k_cache,
     a.prefix_rec = prefix_rec;
     a.logit_scale = logit_scale;
     a.v_scale = vscale;
+    a.q_seq_rows = T;
+    a.q_total_rows = num_seqs * T;
+    a.causal = 1;
+    a.rec_out = nullptr;
+    a.rec_count = nullptr;
     // one pass per tpp chunk tokens; each pass leaves the counters zeroed
     for (int t0 = 0; t0 < T; t0 += tpp) {
       a.t_first = t0;
@@ -1836,7 +1925,7 @@ int64_t max_prefix_wgs(int32_t B, int G) {
 }
 
 struct SharedPrefixLayout {
-  size_t stream, tables, lens, plen, counters, recs, total;
+  size_t stream, tables, lens, plen, counters, grp_lens, grp_count, recs, total;
   int64_t split_stride;         // floats
 };
 
@@ -1844,12 +1933,15 @@ SharedPrefixLayout shared_prefix_layout(const pa_cache_desc* c, int32_t B, int32
                                         int32_t max_blocks) {
   SharedPrefixLayout L{};
   const int G = Hq / c->num_kv_heads;
-  L.stream = align256(stream_workspace_bytes(B, c->num_kv_heads, G, c->head_dim));
+  // decode scratch for up to 16 query rows: the group pass's chunk rows
+  L.stream = align256(stream_workspace_bytes(B, c->num_kv_heads, std::max(G, kMaxRows), c->head_dim));
   L.tables = L.stream;
   L.lens = L.tables + align256(static_cast<size_t>(B) * max_blocks * 4);
   L.plen = L.lens + align256(static_cast<size_t>(B) * 4);
   L.counters = L.plen + align256(static_cast<size_t>(B) * 4);
-  L.recs = L.counters + align256(static_cast<size_t>(c->num_kv_heads) * max_prefix_wgs(B, G) * 4);
+  L.grp_lens = L.counters + align256(static_cast<size_t>(c->num_kv_heads) * max_prefix_wgs(B, G) * 4);
+  L.grp_count = L.grp_lens + align256(static_cast<size_t>(B) * 4);
+  L.recs = L.grp_count + align256(static_cast<size_t>(B) * 4);
   L.split_stride = static_cast<int64_t>(B) * Hq * (c->head_dim + 4);
   L.total = L.recs + static_cast<size_t>(L.split_stride) * kMaxSplits * 4;
   return L;
@@ -1902,9 +1994,10 @@ extern "C" pa_status pa_decode_shared_prefix(
   PrefixGroups gr{};
   gr.num = num_groups;
   std::vector<std::pair<int, int>> spans;
-  int wgs = 0, max_tiles = 0;
+  int wgs = 0, max_tiles = 0, max_count = 0;
   for (int i = 0; i < num_groups; ++i) {
     const int f = groups[3 * i], n = groups[3 * i + 1], m = groups[3 * i + 2];
+    max_count = std::max(max_count, n);
     if (f < 0 || n < 1 || m < 1 || static_cast<int64_t>(f) + n > num_seqs || m > max_blocks_per_seq)
       return fail(PA_ERR_INVALID_ARG, "%s: group %d = (%d, %d, %d) out of range", fn, i, f, n, m);
     gr.first[i] = f;
@@ -1961,8 +2054,72 @@ extern "C" pa_status pa_decode_shared_prefix(
   pa.sub_shift = bs == 64 ? 2 : bs == 32 ? 1 : 0;
   pa.logit_scale = static_cast<float>(static_cast<double>(scale) * kscale * 1.4426950408889634);
   pa.gr = gr;
-  const unsigned grid = static_cast<unsigned>(row_wgs * splits);
+  pa.grp_lens = nullptr;
+  pa.grp_count = nullptr;
   const bool fp8 = c->cache_dtype == PA_FP8_E4M3;
+  if (max_count * G <= kMaxRows) {
+    // Small groups (all members' rows of a KV head fit one 16-row MFMA
+    // block): the prefix goes through the decode kernel's tile stream, each
+    // group leader standing for its group, with the members' rows as chunk
+    // tokens that all see the whole prefix.  The prefix kernel's grid only
+    // prepares the tables, lengths and group lengths.
+    pa.grp_lens = reinterpret_cast<int32_t*>(ws + L.grp_lens);
+    pa.grp_count = reinterpret_cast<int32_t*>(ws + L.grp_count);
+    const int64_t entries = static_cast<int64_t>(num_seqs) * max_blocks_per_seq;
+    const unsigned side_grid = static_cast<unsigned>(
+        std::max<int64_t>(1, std::min<int64_t>(4 * device_cus(), (entries + 64 * kPrefixWaves - 1) /
+                                                                     (64 * kPrefixWaves))));
+    if (D == 128) {
+      if (fp8) shared_prefix_kernel<128, true><<<side_grid, 64 * kPrefixWaves, 0, hs>>>(pa);
+      else shared_prefix_kernel<128, false><<<side_grid, 64 * kPrefixWaves, 0, hs>>>(pa);
+    } else {
+      if (fp8) shared_prefix_kernel<64, true><<<side_grid, 64 * kPrefixWaves, 0, hs>>>(pa);
+      else shared_prefix_kernel<64, false><<<side_grid, 64 * kPrefixWaves, 0, hs>>>(pa);
+    }
+    st = launch_status(fn);
+    if (st != PA_OK) return st;
+    const int64_t prefix_tiles = static_cast<int64_t>(hkv) * num_groups * max_tiles;
+    const int64_t waves_max = static_cast<int64_t>(device_cus()) * kWavesPerCU;
+    const int64_t nw = std::max<int64_t>(
+        1, std::min(waves_max, (prefix_tiles + kMinTilesPerWave - 1) / kMinTilesPerWave));
+    StreamArgs a;
+    a.k_cache = pa.k_cache;
+    a.v_cache = pa.v_cache;
+    a.q = pa.q;
+    a.out = static_cast<uint16_t*>(out);                 // not written by a group pass
+    a.block_tables = block_tables;
+    a.context_lens = pa.grp_lens;
+    a.counters = reinterpret_cast<uint32_t*>(ws);        // decode scratch comes first
+    a.partials = reinterpret_cast<float*>(ws + align256(static_cast<size_t>(num_seqs) * hkv * 4));
+    a.num_seqs = num_seqs;
+    a.hkv = hkv;
+    a.max_blocks = max_blocks_per_seq;
+    a.num_waves = static_cast<int>(nw);
+    a.group = G;
+    a.chunk = max_count;
+    a.window = 0;
+    a.sub_shift = pa.sub_shift;
+    a.pair_nrec = 0;
+    a.prefix_len = nullptr;
+    a.prefix_rec = nullptr;
+    a.t_first = 0;
+    a.rows = G * max_count;
+    a.logit_scale = pa.logit_scale;
+    a.v_scale = (c->cache_dtype == PA_FP8_E4M3) ? c->v_scale : 1.f;
+    a.q_seq_rows = 1;
+    a.q_total_rows = num_seqs;
+    a.causal = 0;
+    a.rec_out = recs;
+    a.rec_count = pa.grp_count;
+    if (D == 128) launch_stream<128>(fp8, false, a.num_waves, hs, a);
+    else launch_stream<64>(fp8, false, a.num_waves, hs, a);
+    st = launch_status(fn);
+    if (st != PA_OK) return st;
+    return attend(fn, c, k_cache, v_cache, q, q_dtype, out, 1, 0, pa.suf_tables, max_blocks_per_seq,
+                  pa.suf_lens, max_context_len, num_seqs, num_q_heads, scale, workspace, L.stream,
+                  stream, pa.prefix_len, recs);
+  }
+  const unsigned grid = static_cast<unsigned>(row_wgs * splits);
   if (D == 128) {
     if (fp8) shared_prefix_kernel<128, true><<<grid, 64 * kPrefixWaves, 0, hs>>>(pa);
     else shared_prefix_kernel<128, false><<<grid, 64 * kPrefixWaves, 0, hs>>>(pa);

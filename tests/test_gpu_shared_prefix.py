@@ -168,13 +168,16 @@ def test_members_no_longer_than_the_shared_blocks():
     assert np.all(got[4] == 0)
 
 
-def test_many_groups_and_row_blocks():
-    """128 groups (PA_MAX_PREFIX_GROUPS, the most one call takes), G = 16 so
-    every member fills a 16-row block, and groups of 2 to 5 members."""
+@pytest.mark.parametrize("Hq,cmax", [(32, 5), (8, 4)])
+def test_many_groups_and_row_blocks(Hq, cmax):
+    """128 groups (PA_MAX_PREFIX_GROUPS, the most one call takes): G = 16, so
+    every member fills a 16-row block (the prefix kernel), or G = 4 with at
+    most 4 members, so a group's rows of a KV head fit one 16-row block (the
+    group pass through the decode kernel)."""
     n_groups = 128
-    rng = np.random.default_rng(4)
-    counts = [int(x) for x in rng.integers(2, 6, n_groups)]
-    ws = _workloads(1000, 32, 2, 128, [int(x) for x in rng.integers(16, 200, n_groups)], counts,
+    rng = np.random.default_rng(4 + Hq)
+    counts = [int(x) for x in rng.integers(2, cmax + 1, n_groups)]
+    ws = _workloads(1000, Hq, 2, 128, [int(x) for x in rng.integers(16, 200, n_groups)], counts,
                     qmax=40)
     order = [(i, r) for i, n in enumerate(counts) for r in range(n)]
     b = Batch(ws, order, "bf16", 16, 9)
@@ -185,6 +188,34 @@ def test_many_groups_and_row_blocks():
     err = np.abs(out_to_f64(out) - b.oracle()).max()
     _say(f"  max abs err {err:.3e}")
     assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("fmt,D,Hq", [("bf16", 128, 8), ("fp8", 64, 4)])
+def test_small_groups_with_short_members_fall_back(fmt, D, Hq):
+    """Groups whose members' rows fit one 16-row block go through the decode
+    kernel's group pass, which gives every member the whole shared run; a
+    group with a member no longer than that run is decoded whole by the
+    suffix pass instead.  Both kinds in one call, against the oracle and
+    pa_decode."""
+    G = Hq // 2
+    ws = _workloads(960 + D, Hq, 2, D, (300, 200, 120), (4, 3, 2))
+    order = [(0, r) for r in range(4)] + [(1, r) for r in range(3)] + [(2, r) for r in range(2)]
+    b = Batch(ws, order, fmt, 16, 7)
+    assert len(b.groups) == 3 and max(b.groups[:, 1]) * G <= 16
+    cl = b.cl.copy()
+    m1 = int(b.groups[1, 2])
+    cl[5] = m1 * 16            # a member of the second group exactly as long as its shared run
+    _say(f"small groups {fmt} D={D} G={G}: groups {b.groups.tolist()}, lens {cl.tolist()}")
+    out = b.shared(b.groups, cl=cl)
+    again = b.shared(b.groups, cl=cl)
+    plain = b.plain(cl=cl)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), again.view(torch.int16))
+    got = out_to_f64(out)
+    err = np.abs(got - b.oracle(cl=cl)).max()
+    diff = np.abs(got - out_to_f64(plain)).max()
+    _say(f"  max abs err vs oracle {err:.3e}, vs pa_decode {diff:.3e}")
+    assert err <= TOL[fmt] and diff <= TOL[fmt]
 
 
 def test_bench_sized_batch_sampled():
