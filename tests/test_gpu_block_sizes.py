@@ -74,7 +74,7 @@ LENS = [0, 1, 7, 8, 9, 31, 32, 33, 64, 65, 200, 513, 1100]
 @pytest.mark.parametrize("bs,fmt,G,D", [(8, "bf16", 4, 128), (32, "bf16", 4, 128),
                                         (64, "bf16", 8, 64), (32, "fp8", 4, 128),
                                         (64, "f32", 2, 64), (8, "fp8", 2, 64),
-                                        (8, "f32", 2, 128), (8, "bf16", 16, 64)])
+                                        (8, "f32", 2, 128), (8, "bf16", 16, 64), (8, "fp8", 4, 128)])
 def test_decode_chunk_and_window_at_block_size(bs, fmt, G, D):
     w, desc, kc, vc, kc_o, vc_o, bt, cl = _build(1000 + bs + D, fmt, bs, G, D, LENS)
     _say(f"block size {bs} {fmt} G={G} D={D}")
