@@ -114,8 +114,12 @@ def _workloads(seed, Hq, Hkv, D, prefixes, counts, qmax=90):
 
 
 @pytest.mark.parametrize("fmt,bs,D,Hq,Hkv", [("bf16", 16, 128, 8, 2), ("fp8", 32, 128, 16, 2),
-                                             ("bf16", 64, 64, 32, 2), ("bf16", 16, 64, 4, 4)])
+                                             ("bf16", 64, 64, 32, 2), ("bf16", 16, 64, 4, 4),
+                                             ("bf16", 32, 128, 8, 2), ("fp8", 64, 64, 4, 2)])
 def test_shared_prefix_decode_matches_oracle_and_decode(fmt, bs, D, Hq, Hkv):
+    """Groups of 3 and 4 members: with G <= 4 their rows of a KV head fit one
+    16-row block and the prefix takes the group pass through the decode
+    kernel; with G = 8 or 16 it takes the prefix kernel."""
     ws = _workloads(900 + bs + D, Hq, Hkv, D, (300, 100, 40), (5, 4, 1))
     # two runs that share a prompt, then requests left alone: one that
     # shares the first prompt but is not adjacent to its run, one with a
