@@ -243,10 +243,11 @@ decode_stream_kernel(StreamArgs a) {
   constexpr int kLanesPerRow = kD / 8;             // V: lanes covering one token row
   constexpr int kRowsPerLoad = 64 / kLanesPerRow;  // V: token rows per load
   constexpr int kVLoads = kTile / kRowsPerLoad;   // V: loads per lane
-  // LDS row pitch of the V staging tile: bf16 rows are read 8 bytes per
+  // LDS row pitch of the V staging tile, which holds bf16 rows (an fp8
+  // cache's V is widened on its way in, exactly): rows are read 8 bytes per
   // lane, 4 rows by each 16 lanes (pitch = 32 mod 256 puts them on
-  // distinct banks); fp8 rows byte by byte
-  constexpr int kVStride = kRowBytes + (kFp8 ? 16 : 32);
+  // distinct banks)
+  constexpr int kVStride = kD * 2 + 32;
   constexpr int kRowOutBytes = kD * 2;             // one bf16 output row
   using Chunk = typename std::conditional<kFp8, u32x2_t, u32x4_t>::type;
 
@@ -937,29 +938,26 @@ decode_stream_kernel(StreamArgs a) {
       // V rows through LDS: rows past the context were read as zeros
 #pragma unroll
       for (int i = 0; i < kVLoads; ++i) {
-        char* dst = s_v + (v_r + i * kRowsPerLoad) * kVStride + 8 * v_c * kE;
-        if constexpr (kFp8)
-          *reinterpret_cast<u32x2_t*>(dst) = vt[slot][i];
-        else
+        char* dst = s_v + (v_r + i * kRowsPerLoad) * kVStride + 16 * v_c;   // 8 dims, bf16
+        if constexpr (kFp8) {
+          // 8 E4M3 codes (dims 8 v_c .. +7) to bf16, exactly: 2 per instruction
+          const int w0 = static_cast<int>(vt[slot][i][0]), w1 = static_cast<int>(vt[slot][i][1]);
+          const u32x4_t wide = {
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false)),
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true)),
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false)),
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true))};
+          *reinterpret_cast<u32x4_t*>(dst) = wide;
+        } else {
           *reinterpret_cast<u32x4_t*>(dst) = vt[slot][i];
+        }
       }
-      const char* vsrc = s_v + (4 * quad) * kVStride + row * kE;   // fp8: token 4*quad, dim `row`
-      // bf16: one transposing read per MFMA; lane (row, quad) addresses
-      // token 4 quad + row/4, dims 16c + 4 (row mod 4) .. +3
+      // one transposing read per MFMA; lane (row, quad) addresses token
+      // 4 quad + row/4, dims 16c + 4 (row mod 4) .. +3
       const char* vtr = s_v + (4 * quad + (row >> 2)) * kVStride + 8 * (row & 3);
 #pragma unroll
       for (int c = 0; c < kVC; ++c) {
-        u32x2_t vw;                                                // tokens 4*quad..+3 of dim 16c+row
-        if constexpr (kFp8) {
-          const char* p = vsrc + 16 * c;
-          const uint32_t b0 = static_cast<uint8_t>(p[0]), b1 = static_cast<uint8_t>(p[kVStride]);
-          const uint32_t b2 = static_cast<uint8_t>(p[2 * kVStride]), b3 = static_cast<uint8_t>(p[3 * kVStride]);
-          const int w4 = static_cast<int>(b0 | (b1 << 8) | (b2 << 16) | (b3 << 24));
-          vw[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w4, 1.0f, false));
-          vw[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w4, 1.0f, true));
-        } else {
-          vw = lds_read_tr16(vtr + 32 * c);
-        }
+        const u32x2_t vw = lds_read_tr16(vtr + 32 * c);           // tokens 4*quad..+3 of dim 16c+row
         oacc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, vw),
                                                            __builtin_bit_cast(s16x4_t, pb),
                                                            oacc[c], 0, 0, 0);
