@@ -1,0 +1,91 @@
+"""The path on a stream other than the default one, and captured in a HIP
+graph.  The library launches only kernels on the stream it is given (no
+allocation, no memset, no synchronisation) and leaves the decode workspace's
+arrival counters at zero after every call, so a captured pa_write_kv +
+pa_decode replays correctly.  Each replay is checked against the eager result
+on the same inputs, with eager work (new queries written into the captured
+buffer) between the replays."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from tests._gpu_setup import GpuView, fill_sequential, to_device_rows
+
+pk = pytest.importorskip("paged_kv_cache_421_amd")
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _view(seed):
+    lens = np.array([1, 17, 300, 640, 33, 2100, 900, 5], dtype=np.int32)
+    w = workloads.small_random(seed, len(lens), 16, 4, 128, "bf16", 0, lens=lens)
+    view = GpuView(w)
+    fill_sequential(view)
+    view.tables(cap=int(lens.max()) // 16 + 2)
+    return w, view
+
+
+def test_decode_on_a_side_stream_matches_default_stream():
+    w, view = _view(1200)
+    _say("side stream: decode on the default stream, then on a new stream")
+    a = view.decode().clone()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        b = view.decode()
+    side.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_write_and_decode_replay_from_a_captured_graph():
+    w, view = _view(1201)
+    B, Hq, Hkv, D = w.B, w.Hq, w.Hkv, w.D
+    rng = np.random.default_rng(1202)
+    max_len = int(view.cl_host.max()) + 1
+    # one new token per sequence: its slot from the manager, its rows drawn here
+    slots = np.array([view.bm.append_slot(s)[0] for s in range(B)], dtype=np.int64)
+    view.tables(cap=view.bt_host.shape[1])
+    k_new = to_device_rows(workloads.f32_to_bf16_bits(
+        rng.standard_normal((B, Hkv, D)).astype(np.float32)), "bf16")
+    v_new = to_device_rows(workloads.f32_to_bf16_bits(
+        rng.standard_normal((B, Hkv, D)).astype(np.float32)), "bf16")
+    d_slots = torch.from_numpy(slots).cuda()
+    q = to_device_rows(w.q, w.q_fmt)
+    out = torch.empty_like(q)
+    ws = pk.new_decode_workspace(view.desc, B, Hq, max_len)
+
+    def step(stream=None):
+        pk.write_kv(view.desc, view.kc, view.vc, k_new, v_new, d_slots, stream=stream)
+        pk.decode(view.desc, view.kc, view.vc, q, out, view.bt, view.cl, max_len,
+                  float(w.scale), ws, stream=stream)
+
+    _say("graph: warm-up on a side stream, capture, then 3 replays against eager")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for i in range(3):
+        q.copy_(to_device_rows(workloads.f32_to_bf16_bits(
+            rng.standard_normal((B, Hq, D)).astype(np.float32)), "bf16"))
+        step()                                   # eager, on the current stream
+        torch.cuda.synchronize()
+        eager = out.clone()
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {i}"
+        assert int(ws[:B * Hkv * 4].count_nonzero()) == 0, "arrival counters not reset"
+        _say(f"  replay {i}: bit-identical to eager")
