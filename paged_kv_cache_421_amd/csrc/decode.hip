@@ -1077,12 +1077,78 @@ struct PrefixArgs {
   int splits;
   float logit_scale;
   // group pass (null otherwise): each group leader's prefix length and
-  // member count, 0 for every other sequence; the grid then does only the
-  // side job
+  // member count, 0 for every other sequence (written by prefix_prep_kernel)
   int32_t* grp_lens;
   int32_t* grp_count;
   PrefixGroups gr;
 };
+
+// Side job of a shared-prefix call: every sequence's suffix table (its
+// table without the group's shared blocks) and suffix length, the prefix
+// length it sees, and for a group pass each leader's prefix length and
+// member count.  s_grp: LDS for the group table; threads nthreads per
+// workgroup, grid-strided over (sequence, table entry).
+__device__ __forceinline__ void prefix_side_job(const PrefixArgs& a, int (*s_grp)[kMaxGroups],
+                                                int tid, int nthreads) {
+  // the groups' (first, count, shared) in LDS: looked up per lane at varying
+  // indices, they would otherwise be read from the argument block one
+  // scalar-cache line at a time
+  for (int i = tid; i < a.gr.num; i += nthreads) {
+    s_grp[0][i] = a.gr.first[i];
+    s_grp[1][i] = a.gr.count[i];
+    s_grp[2][i] = a.gr.shared[i];
+  }
+  __syncthreads();
+
+  const int64_t entries = static_cast<int64_t>(a.num_seqs) * a.max_blocks;
+  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * nthreads + tid; idx < entries;
+       idx += static_cast<int64_t>(gridDim.x) * nthreads) {
+    const int s = static_cast<int>(idx / a.max_blocks);
+    const int j = static_cast<int>(idx - static_cast<int64_t>(s) * a.max_blocks);
+    int gi = -1;
+    for (int i = 0; i < a.gr.num; ++i)
+      if (s >= s_grp[0][i] && s < s_grp[0][i] + s_grp[1][i]) gi = i;
+    int m = gi >= 0 ? s_grp[2][gi] : 0;
+    const int64_t row = static_cast<int64_t>(s) * a.max_blocks;
+    const int L = a.context_lens[s];
+    const int e_shift = (j + m < a.max_blocks) ? a.block_tables[row + j + m] : -1;
+    if (a.grp_lens != nullptr && m > 0) {
+      // the group pass gives every member all m blocks: a group with a
+      // member no longer than them is left whole to the suffix pass (its
+      // members' lengths and both table entries are read at once)
+      const int f = s_grp[0][gi], n = s_grp[1][gi];
+      const int e_own = a.block_tables[row + j];
+      int Lm[kMaxRows];
+#pragma unroll
+      for (int i = 0; i < kMaxRows; ++i) Lm[i] = (i < n) ? a.context_lens[f + i] : 0x7FFFFFFF;
+      bool short_member = false;
+#pragma unroll
+      for (int i = 0; i < kMaxRows; ++i) short_member |= Lm[i] <= m * a.bs;
+      if (short_member) m = 0;
+      a.suf_tables[row + j] = short_member ? e_own : e_shift;
+    } else {
+      a.suf_tables[row + j] = e_shift;
+    }
+    if (j == 0) {
+      const int p = min(m * a.bs, max(L, 0));          // a member no longer than the prefix is all prefix
+      a.suf_lens[s] = L - p;
+      a.prefix_len[s] = p;
+      if (a.grp_lens != nullptr) {
+        const bool lead = m > 0 && s == s_grp[0][gi];
+        a.grp_lens[s] = lead ? m * a.bs : 0;
+        a.grp_count[s] = lead ? s_grp[1][gi] : 0;
+      }
+    }
+  }
+}
+
+// The side job alone, for a group pass (the prefix itself runs through
+// the decode kernel): a light grid without the prefix kernel's registers
+// and LDS.
+__global__ void __launch_bounds__(256) prefix_prep_kernel(PrefixArgs a) {
+  __shared__ int s_grp[3][kMaxGroups];
+  prefix_side_job(a, s_grp, threadIdx.x, 256);
+}
 
 // One workgroup of 8 waves per (KV head g, 128 query rows of a group, split
 // of the prefix's positions): rows are (member, head) pairs, member-major,
@@ -1125,62 +1191,10 @@ shared_prefix_kernel(PrefixArgs a) {
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6) & (kPrefixWaves - 1);
   const int hkv = a.hkv, G = a.group, hq = hkv * G;
 
-  // the groups' (first, count, shared) in LDS: looked up per lane at varying
-  // indices, they would otherwise be read from the argument block one
-  // scalar-cache line at a time
-  __shared__ int s_grp[3][kMaxGroups];
-  for (int i = tid; i < a.gr.num; i += kThreads) {
-    s_grp[0][i] = a.gr.first[i];
-    s_grp[1][i] = a.gr.count[i];
-    s_grp[2][i] = a.gr.shared[i];
-  }
-  __syncthreads();
-
   // side job: suffix tables and lengths, prefix lengths
-  {
-    const int64_t entries = static_cast<int64_t>(a.num_seqs) * a.max_blocks;
-    for (int64_t idx = static_cast<int64_t>(blockIdx.x) * kThreads + tid; idx < entries;
-         idx += static_cast<int64_t>(gridDim.x) * kThreads) {
-      const int s = static_cast<int>(idx / a.max_blocks);
-      const int j = static_cast<int>(idx - static_cast<int64_t>(s) * a.max_blocks);
-      int gi = -1;
-      for (int i = 0; i < a.gr.num; ++i)
-        if (s >= s_grp[0][i] && s < s_grp[0][i] + s_grp[1][i]) gi = i;
-      int m = gi >= 0 ? s_grp[2][gi] : 0;
-      const int64_t row = static_cast<int64_t>(s) * a.max_blocks;
-      const int L = a.context_lens[s];
-      const int e_shift = (j + m < a.max_blocks) ? a.block_tables[row + j + m] : -1;
-      if (a.grp_lens != nullptr && m > 0) {
-        // the group pass gives every member all m blocks: a group with a
-        // member no longer than them is left whole to the suffix pass (its
-        // members' lengths and both table entries are read at once)
-        const int f = s_grp[0][gi], n = s_grp[1][gi];
-        const int e_own = a.block_tables[row + j];
-        int Lm[kMaxRows];
-#pragma unroll
-        for (int i = 0; i < kMaxRows; ++i) Lm[i] = (i < n) ? a.context_lens[f + i] : 0x7FFFFFFF;
-        bool short_member = false;
-#pragma unroll
-        for (int i = 0; i < kMaxRows; ++i) short_member |= Lm[i] <= m * a.bs;
-        if (short_member) m = 0;
-        a.suf_tables[row + j] = short_member ? e_own : e_shift;
-      } else {
-        a.suf_tables[row + j] = e_shift;
-      }
-      if (j == 0) {
-        const int p = min(m * a.bs, max(L, 0));          // a member no longer than the prefix is all prefix
-        a.suf_lens[s] = L - p;
-        a.prefix_len[s] = p;
-        if (a.grp_lens != nullptr) {
-          const bool lead = m > 0 && s == s_grp[0][gi];
-          a.grp_lens[s] = lead ? m * a.bs : 0;
-          a.grp_count[s] = lead ? s_grp[1][gi] : 0;
-        }
-      }
-    }
-  }
+  __shared__ int s_grp[3][kMaxGroups];
+  prefix_side_job(a, s_grp, tid, kThreads);
 
-  if (a.grp_lens != nullptr) return;                     // group pass: the side job only
   const int g = static_cast<int>(blockIdx.x) % hkv;
   const int rest = static_cast<int>(blockIdx.x) / hkv;
   const int sp = rest % a.splits;
@@ -2065,15 +2079,8 @@ extern "C" pa_status pa_decode_shared_prefix(
     pa.grp_count = reinterpret_cast<int32_t*>(ws + L.grp_count);
     const int64_t entries = static_cast<int64_t>(num_seqs) * max_blocks_per_seq;
     const unsigned side_grid = static_cast<unsigned>(
-        std::max<int64_t>(1, std::min<int64_t>(4 * device_cus(), (entries + 64 * kPrefixWaves - 1) /
-                                                                     (64 * kPrefixWaves))));
-    if (D == 128) {
-      if (fp8) shared_prefix_kernel<128, true><<<side_grid, 64 * kPrefixWaves, 0, hs>>>(pa);
-      else shared_prefix_kernel<128, false><<<side_grid, 64 * kPrefixWaves, 0, hs>>>(pa);
-    } else {
-      if (fp8) shared_prefix_kernel<64, true><<<side_grid, 64 * kPrefixWaves, 0, hs>>>(pa);
-      else shared_prefix_kernel<64, false><<<side_grid, 64 * kPrefixWaves, 0, hs>>>(pa);
-    }
+        std::max<int64_t>(1, std::min<int64_t>(8 * device_cus(), (entries + 255) / 256)));
+    prefix_prep_kernel<<<side_grid, 256, 0, hs>>>(pa);
     st = launch_status(fn);
     if (st != PA_OK) return st;
     const int64_t prefix_tiles = static_cast<int64_t>(hkv) * num_groups * max_tiles;
