@@ -26,12 +26,14 @@ timed region starts.
 The JSON line also carries
   * ``roofline``: pa_decode's algorithmic KV bytes per call (sum over
     sequences of L * Hkv * D * 2 bytes * 2 for K and V) over its mean
-    duration, taken with HIP events recorded around every pa_decode of the
-    timed steps on the stream it runs on, against the 8 TB/s HBM peak.  The
-    events are created without the system-scope fence (the path exchanges
-    nothing with the host); each one still delays the next dispatch by a few
-    microseconds, which the event interval includes, so the figure is a
-    slight underestimate of the kernel's own rate;
+    duration, taken with HIP events recorded around one pa_decode of every
+    timed step (layer step mod layers, so each layer in turn) on the stream it
+    runs on, against the 8 TB/s HBM peak.  The events are created without the
+    system-scope fence (the path exchanges nothing with the host); each one
+    still delays the next dispatch by a few microseconds, which the event
+    interval includes, so the figure is a slight underestimate of the
+    kernel's own rate, and timing one call per step keeps that delay out of
+    the other three;
     ``traffic`` is the HBM bytes per call from the committed rocprofv3
     counter summary, when that was taken on the current kernel source;
   * ``cpu_baseline``: the CPU float64 oracle's decode of the same batch on the
@@ -909,7 +911,11 @@ def main():
 
     host_bm_s = []                           # block manager + table packing, per step
 
-    def step(i, ev_pairs):
+    def step(i, ev_pair):
+        """One step; with ev_pair, HIP events around the decode of layer i mod
+        layers (one timed decode per step, the layers in turn: each event
+        delays the next dispatch by a few microseconds, so timing every call
+        would slow the step it measures)."""
         b = i % NBUF
         if buf_ev[b] is not None:
             buf_ev[b].synchronize()          # the upload that last read buffer b is done
@@ -934,8 +940,9 @@ def main():
         max_len = int(lens.max())
         for l in range(NL):
             pk.write_kv(desc, kc[l], vc[l], k_new[l], v_new[l], d_slots, stream=stream)
-            if ev_pairs is not None:
-                ev_pairs[l][0].record(stream)
+            timed_here = ev_pair is not None and l == i % NL
+            if timed_here:
+                ev_pair[0].record(stream)
             if T == 1 and not args.window:
                 pk.decode(desc, kc[l], vc[l], q[l], out[l], d_bt, d_cl, max_len,
                           float(w.scale), workspace, stream=stream)
@@ -944,8 +951,8 @@ def main():
                 oo = out[l] if T > 1 else out[l].view(B, 1, Hq, D)
                 pk.decode_chunk(desc, kc[l], vc[l], qq, oo, d_bt, d_cl, max_len,
                                 float(w.scale), workspace, stream=stream, window=args.window)
-            if ev_pairs is not None:
-                ev_pairs[l][1].record(stream)
+            if timed_here:
+                ev_pair[1].record(stream)
         if args.window:
             return _kv_bytes(np.minimum(lens, args.window + T - 1), Hkv, D, 2)
         return _kv_bytes(lens, Hkv, D, 2)
@@ -955,7 +962,7 @@ def main():
         step(i, None)
     torch.cuda.synchronize()
 
-    evs = [[(HipEvent(), HipEvent()) for _ in range(NL)] for _ in range(args.steps)]
+    evs = [(HipEvent(), HipEvent()) for _ in range(args.steps)]
     kv_per_call = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -1017,11 +1024,10 @@ def main():
          f"{B * T} rows {step_us:.2f} us; pa_copy_blocks {n_pairs} pairs {copy_us:.2f} us "
          f"({copy_b / copy_us / 1e3:.0f} GB/s)")
 
-    dec_ms = [a.elapsed_ms(b) for row in evs for (a, b) in row]
-    for row in evs:
-        for a, b in row:
-            a.destroy()
-            b.destroy()
+    dec_ms = [a.elapsed_ms(b) for (a, b) in evs]
+    for a, b in evs:
+        a.destroy()
+        b.destroy()
     mean_dec_s = statistics.mean(dec_ms) / 1e3
     mean_kv = statistics.mean(kv_per_call)
     achieved = mean_kv / mean_dec_s / 1e9
