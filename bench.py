@@ -13,7 +13,8 @@ layers, as in a decoder:
   1. host block manager: append one token to each of the 256 sequences
      (slot mapping, new blocks) and pack the tables -- pa_bm_append_batch,
      pa_bm_pack, into pinned buffers;
-  2. one async upload of slot mapping, block tables and context lengths;
+  2. one async upload of the slot mapping, the context lengths and the block-table
+     entries of blocks opened this step, scattered into the device-resident tables;
   3. per layer: pa_write_kv of the new token's K/V rows, then pa_decode.
 
 With 4 layers of 0.75 GB each, a layer's KV has been pushed out of the
@@ -897,17 +898,25 @@ def main():
     workspace = pk.new_chunk_workspace(desc, B, Hq, T, max_len_final, dev)
 
     # ---- pinned host staging, triple-buffered against the running GPU
+    # The block tables stay on the device; a step uploads the slot mapping,
+    # the lengths and only the table entries of blocks it opened (a block
+    # opens where a new token's position is a multiple of the block size),
+    # as (row, column, block) triples that one scatter writes in place.
     NBUF = 3
-    h_slots = [torch.empty(B * T, dtype=torch.int64, pin_memory=True) for _ in range(NBUF)]
-    h_bt = [torch.empty((B, cap), dtype=torch.int32, pin_memory=True) for _ in range(NBUF)]
-    h_cl = [torch.empty(B, dtype=torch.int32, pin_memory=True) for _ in range(NBUF)]
+    nmax = B * T
+    h_i64 = [torch.empty(3 * nmax, dtype=torch.int64, pin_memory=True)      # slots | rows | cols
+             for _ in range(NBUF)]
+    h_i32 = [torch.empty(B + nmax, dtype=torch.int32, pin_memory=True)      # lens | blocks
+             for _ in range(NBUF)]
     buf_ev = [None] * NBUF
-    d_slots = torch.empty(B * T, dtype=torch.int64, device=dev)
+    d_i64 = torch.empty(3 * nmax, dtype=torch.int64, device=dev)
+    d_i32 = torch.empty(B + nmax, dtype=torch.int32, device=dev)
+    d_slots = d_i64[:nmax]
+    d_cl = d_i32[:B]
     slots_tb = np.empty((T, B), dtype=np.int64)
-    d_bt = torch.empty((B, cap), dtype=torch.int32, device=dev)
-    d_cl = torch.empty(B, dtype=torch.int32, device=dev)
     ids = np.arange(B, dtype=np.int64)
     lens = w.lens.astype(np.int64).copy()
+    d_bt = torch.from_numpy(bm.pack(ids, cap)[0]).to(dev)
 
     host_bm_s = []                           # block manager + table packing, per step
 
@@ -920,20 +929,28 @@ def main():
         if buf_ev[b] is not None:
             buf_ev[b].synchronize()          # the upload that last read buffer b is done
         th = time.perf_counter()
+        hi, hj = h_i64[b].numpy(), h_i32[b].numpy()
         if T == 1:
-            sl, pairs = bm.append_batch(ids, slots=h_slots[b].numpy())
+            sl, pairs = bm.append_batch(ids, slots=hi[:nmax])
             assert len(pairs) == 0
         else:
             for t in range(T):                   # token t of every sequence
                 sl, pairs = bm.append_batch(ids, slots=slots_tb[t])
                 assert len(pairs) == 0
-            h_slots[b].numpy().reshape(B, T)[:] = slots_tb.T
-        bm.pack(ids, cap, block_tables=h_bt[b].numpy(), context_lens=h_cl[b].numpy())
-        host_bm_s.append(time.perf_counter() - th)
+            hi[:nmax].reshape(B, T)[:] = slots_tb.T
+        pos = lens[:, None] + np.arange(T)       # positions of the new tokens
+        opened = pos % bs == 0
+        n = int(opened.sum())
+        hi[nmax:nmax + n] = np.nonzero(opened)[0]
+        hi[2 * nmax:2 * nmax + n] = pos[opened] // bs
+        hj[B:B + n] = hi[:nmax].reshape(B, T)[opened] // bs
         lens[:] += T
-        d_slots.copy_(h_slots[b], non_blocking=True)
-        d_bt.copy_(h_bt[b], non_blocking=True)
-        d_cl.copy_(h_cl[b], non_blocking=True)
+        hj[:B] = lens
+        host_bm_s.append(time.perf_counter() - th)
+        d_i64.copy_(h_i64[b], non_blocking=True)
+        d_i32.copy_(h_i32[b], non_blocking=True)
+        if n:
+            d_bt[d_i64[nmax:nmax + n], d_i64[2 * nmax:2 * nmax + n]] = d_i32[B:B + n]
         ev = torch.cuda.Event()
         ev.record()
         buf_ev[b] = ev
@@ -972,6 +989,10 @@ def main():
     t1 = time.perf_counter()
     wall = t1 - t0
     assert torch.isfinite(out[0].float()).all(), "non-finite decode output"
+    # the patched device tables and lengths are the manager's, entry for entry
+    bt_ref, cl_ref = bm.pack(ids, cap)
+    assert np.array_equal(d_bt.cpu().numpy(), bt_ref), "device block tables drifted"
+    assert np.array_equal(d_cl.cpu().numpy(), cl_ref), "device lengths drifted"
     host_bm_us = statistics.mean(host_bm_s[args.warmup:]) * 1e6
 
     # ---- the other device steps of the path, each timed on its own after the
@@ -1064,7 +1085,8 @@ def main():
             "global_batch": B,
             "chunk_tokens": T,
             "layers_per_step": NL,
-            "step": ("block-manager append + table upload + per layer pa_write_kv and " +
+            "step": ("block-manager append + upload of slots, lengths and opened table entries + "
+                     "per layer pa_write_kv and " +
                      ("pa_decode" if T == 1 else "pa_decode_chunk")),
             "value_is": ("sequences decoded per second per attention layer" if T == 1 else
                          "query tokens per second per attention layer"),
