@@ -663,13 +663,19 @@ def run_prefix(args):
     cascade = args.prefix_path != "plain"
     workspace = pk.new_decode_workspace(desc, B, Hq, max_len_final, dev)
     sp_workspace = pk.new_shared_prefix_workspace(desc, B, Hq, cap, max_len_final, dev)
-    h_slots = torch.empty(B, dtype=torch.int64, pin_memory=True)
-    h_bt = torch.empty((B, cap), dtype=torch.int32, pin_memory=True)
-    h_cl = torch.empty(B, dtype=torch.int32, pin_memory=True)
-    d_slots = torch.empty(B, dtype=torch.int64, device=dev)
-    d_bt = torch.empty((B, cap), dtype=torch.int32, device=dev)
-    d_cl = torch.empty(B, dtype=torch.int32, device=dev)
+    # as in the decode step: device-resident tables patched with the entries
+    # of opened blocks; slots, lengths and those entries staged in pinned
+    # buffers, triple-buffered against the running GPU
+    NBUF = 3
+    h_i64 = [torch.empty(3 * B, dtype=torch.int64, pin_memory=True) for _ in range(NBUF)]
+    h_i32 = [torch.empty(2 * B, dtype=torch.int32, pin_memory=True) for _ in range(NBUF)]
+    buf_ev = [None] * NBUF
+    d_i64 = torch.empty(3 * B, dtype=torch.int64, device=dev)
+    d_i32 = torch.empty(2 * B, dtype=torch.int32, device=dev)
+    d_slots = d_i64[:B]
+    d_cl = d_i32[:B]
     ids = np.arange(B, dtype=np.int64)
+    d_bt = torch.from_numpy(bm.pack(ids, cap)[0]).to(dev)
     nfull = P // 16
 
     def attend(l, groups, max_len):
@@ -680,43 +686,59 @@ def run_prefix(args):
             pk.decode(desc, kc[l], vc[l], q[l], out[l], d_bt, d_cl, max_len, float(w.scale),
                       workspace, stream=stream)
 
-    def step(ev_pairs):
-        torch.cuda.current_stream().synchronize()        # host buffers are reused
-        sl, pairs = bm.append_batch(ids, slots=h_slots.numpy())
+    def step(i, ev_pair):
+        """One step; with ev_pair, HIP events around layer i mod layers."""
+        b = i % NBUF
+        if buf_ev[b] is not None:
+            buf_ev[b].synchronize()          # the upload that last read buffer b is done
+        hi, hj = h_i64[b].numpy(), h_i32[b].numpy()
+        sl, pairs = bm.append_batch(ids, slots=hi[:B])
         assert len(pairs) == 0
-        bm.pack(ids, cap, block_tables=h_bt.numpy(), context_lens=h_cl.numpy())
+        opened = lens % 16 == 0              # the new token opens a block
+        n = int(opened.sum())
+        hi[B:B + n] = np.nonzero(opened)[0]
+        hi[2 * B:2 * B + n] = lens[opened] // 16
+        hj[B:B + n] = hi[:B][opened] // 16
         lens[:] += 1
-        d_slots.copy_(h_slots, non_blocking=True)
-        d_bt.copy_(h_bt, non_blocking=True)
-        d_cl.copy_(h_cl, non_blocking=True)
+        hj[:B] = lens
+        d_i64.copy_(h_i64[b], non_blocking=True)
+        d_i32.copy_(h_i32[b], non_blocking=True)
+        if n:
+            d_bt[d_i64[B:B + n], d_i64[2 * B:2 * B + n]] = d_i32[B:B + n]
+        ev = torch.cuda.Event()
+        ev.record()
+        buf_ev[b] = ev
         max_len = int(lens.max())
         groups = bm.shared_prefix_groups(ids) if cascade else None
         for l in range(NL):
             pk.write_kv(desc, kc[l], vc[l], k_new[l], v_new[l], d_slots, stream=stream)
-            if ev_pairs is not None:
-                ev_pairs[l][0].record(stream)
+            timed_here = ev_pair is not None and l == i % NL
+            if timed_here:
+                ev_pair[0].record(stream)
             attend(l, groups, max_len)
-            if ev_pairs is not None:
-                ev_pairs[l][1].record(stream)
+            if timed_here:
+                ev_pair[1].record(stream)
         logical = int(lens.sum()) * Hkv * D * 4
         unique = (16 * nfull + int((lens - 16 * nfull).sum())) * Hkv * D * 4
         return logical, unique
 
-    for _ in range(warm):
-        step(None)
+    for i in range(warm):
+        step(i, None)
     torch.cuda.synchronize()
-    evs = [[(HipEvent(), HipEvent()) for _ in range(NL)] for _ in range(steps)]
+    evs = [(HipEvent(), HipEvent()) for _ in range(steps)]
     per = []
     t0 = time.perf_counter()
     for i in range(steps):
-        per.append(step(evs[i]))
+        per.append(step(warm + i, evs[i]))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    dec_ms = [a.elapsed_ms(b) for row in evs for (a, b) in row]
-    for row in evs:
-        for a, b in row:
-            a.destroy()
-            b.destroy()
+    bt_ref, cl_ref = bm.pack(ids, cap)
+    assert np.array_equal(d_bt.cpu().numpy(), bt_ref), "device block tables drifted"
+    assert np.array_equal(d_cl.cpu().numpy(), cl_ref), "device lengths drifted"
+    dec_ms = [a.elapsed_ms(b) for (a, b) in evs]
+    for a, b in evs:
+        a.destroy()
+        b.destroy()
     mean_s = statistics.mean(dec_ms) / 1e3
     logical = statistics.mean(p[0] for p in per)
     unique = statistics.mean(p[1] for p in per)
