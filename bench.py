@@ -541,6 +541,10 @@ def run_config(args):
                       workspace, stream=stream)
 
     def timed(shared, nsteps):
+        """nsteps steps of NL calls, HIP events around every call.  (With an
+        event pair around one call per step only, nothing paces the host
+        between back-to-back launches; a run then showed one stall of about
+        35 ms inside an event pair, so every call keeps its pair here.)"""
         for i in range(warm * NL):
             call(i % NL, shared)
         torch.cuda.synchronize()
