@@ -426,6 +426,18 @@ pa_status pa_swap_blocks(const pa_cache_desc* c, const void* src_k, const void* 
  * bytes (its contents are meaningless).
  * ------------------------------------------------------------------------- */
 size_t pa_read_probe_sink_bytes(int32_t num_cus);
+
+/*
+ * pa_time_next_call -- the next pa_decode, pa_decode_chunk or pa_decode_window
+ * made on the calling thread launches its kernels through hipExtLaunchKernel
+ * with these events (hipEvent_t, created by the caller; either may be null):
+ * start_event is recorded as its first kernel starts, stop_event as its last
+ * kernel ends, by the dispatches themselves, so no marker packet sits in the
+ * stream between the previous work and the kernel.  The request is consumed
+ * by that call whatever its outcome (a call that launches nothing records
+ * nothing); other entry points leave it pending.  Always PA_OK.
+ */
+pa_status pa_time_next_call(void* start_event, void* stop_event);
 pa_status pa_read_probe(const void* buf, size_t bytes, const int32_t* chunk_order,
                         void* sink, int32_t num_cus, void* stream);
 

@@ -12,11 +12,11 @@ from .api import (BLOCK_SIZE, MAX_CHUNK, PARTITION_TOKENS, BlockManager, CacheDe
                   decode_workspace_bytes, decode_workspace_init, dtype_code,
                   new_chunk_workspace, new_decode_workspace, read_probe, swap_blocks, write_kv,
                   decode_shared_prefix, new_shared_prefix_workspace,
-                  shared_prefix_workspace_bytes)
+                  shared_prefix_workspace_bytes, time_next_call)
 
 __all__ = ["LIB_PATH", "PagedKVError", "lib", "BLOCK_SIZE", "MAX_CHUNK", "PARTITION_TOKENS",
            "BlockManager", "CacheDesc", "chunk_workspace_bytes", "copy_blocks", "decode",
            "decode_chunk", "decode_workspace_bytes", "decode_workspace_init", "dtype_code",
            "new_chunk_workspace", "new_decode_workspace", "read_probe", "swap_blocks", "write_kv",
            "decode_shared_prefix", "new_shared_prefix_workspace",
-           "shared_prefix_workspace_bytes"]
+           "shared_prefix_workspace_bytes", "time_next_call"]

@@ -49,6 +49,7 @@ SIGNATURES = {
     "pa_swap_blocks": (c_i32, [P_desc, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp]),
     "pa_read_probe_sink_bytes": (c_sz, [c_i32]),
     "pa_read_probe": (c_i32, [c_vp, c_sz, c_vp, c_vp, c_i32, c_vp]),
+    "pa_time_next_call": (c_i32, [c_vp, c_vp]),
     "pa_bm_shared_prefix_groups": (c_i32, [c_vp, c_vp, c_i32, c_vp, c_i32, c_vp]),
     "pa_decode_shared_prefix_workspace_bytes": (c_sz, [P_desc, c_i32, c_i32, c_i32, c_i32]),
     "pa_decode_shared_prefix": (c_i32, [P_desc, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_vp,

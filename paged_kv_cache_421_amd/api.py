@@ -248,6 +248,13 @@ def decode_shared_prefix(desc: CacheDesc, k_cache: torch.Tensor, v_cache: torch.
     return out
 
 
+def time_next_call(start_event, stop_event) -> None:
+    """pa_time_next_call: the next decode call on this thread records these
+    HIP events (raw hipEvent_t handles, or None) from its own kernel
+    dispatches."""
+    check(lib.pa_time_next_call(start_event, stop_event))
+
+
 def read_probe(buf: torch.Tensor, chunk_order: Optional[torch.Tensor] = None,
                sink: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """pa_read_probe: stream ``buf`` (device) in 4 KiB chunks, in order or in

@@ -49,6 +49,7 @@
 // General path (fp32 cache, or shapes the fast path does not cover): one
 // wave per (512-token partition, query head, sequence), one token at a time,
 // plus a separate log-sum-exp reduce kernel.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -1605,31 +1606,59 @@ reduce_kernel(const int32_t* __restrict__ context_lens, int hq, int chunk, PartO
   store_out<kOutF32>(po.out, (static_cast<int64_t>(s) * gridDim.x + y) * kD + d, num / den);
 }
 
-template <int kD>
-void launch_simple(int fmt, dim3 grid, hipStream_t st, const char* kc, const char* vc,
-                   const void* q, const int32_t* bt, const int32_t* cl, int maxb, int hkv, int bs,
-                   int G, int hq, int T, int W, float ls, float vs, PartOut po) {
-  if (fmt == PA_F32)
-    decode_simple_kernel<kD, PA_F32, true><<<grid, 64, 0, st>>>(kc, vc, q, bt, cl, maxb, hkv, bs, G, hq, T, W, ls, vs, po);
-  else if (fmt == PA_BF16)
-    decode_simple_kernel<kD, PA_BF16, false><<<grid, 64, 0, st>>>(kc, vc, q, bt, cl, maxb, hkv, bs, G, hq, T, W, ls, vs, po);
+// Events a caller asked the next decode call on this thread to record
+// (pa_time_next_call): the first kernel's start and the last kernel's end.
+struct CallTiming {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+thread_local CallTiming t_next_call;
+
+CallTiming take_call_timing() {
+  const CallTiming t = t_next_call;
+  t_next_call = CallTiming{};
+  return t;
+}
+
+// Launches `kernel`; with events, through hipExtLaunchKernelGGL, which has
+// the dispatch itself record them as the kernel starts and ends (no marker
+// packets in the stream).
+template <typename... KArgs, typename... Args>
+void launch_k(void (*kernel)(KArgs...), dim3 grid, dim3 block, unsigned shmem, hipStream_t st,
+              hipEvent_t e0, hipEvent_t e1, Args... args) {
+  if (e0 != nullptr || e1 != nullptr)
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, e0, e1, 0, args...);
   else
-    decode_simple_kernel<kD, PA_FP8_E4M3, false><<<grid, 64, 0, st>>>(kc, vc, q, bt, cl, maxb, hkv, bs, G, hq, T, W, ls, vs, po);
+    kernel<<<grid, block, shmem, st>>>(args...);
+}
+
+template <int kD>
+void launch_simple(int fmt, dim3 grid, hipStream_t st, hipEvent_t e0, hipEvent_t e1,
+                   const char* kc, const char* vc, const void* q, const int32_t* bt,
+                   const int32_t* cl, int maxb, int hkv, int bs, int G, int hq, int T, int W,
+                   float ls, float vs, PartOut po) {
+  if (fmt == PA_F32)
+    launch_k(decode_simple_kernel<kD, PA_F32, true>, grid, dim3(64), 0, st, e0, e1, kc, vc, q, bt, cl, maxb, hkv, bs, G, hq, T, W, ls, vs, po);
+  else if (fmt == PA_BF16)
+    launch_k(decode_simple_kernel<kD, PA_BF16, false>, grid, dim3(64), 0, st, e0, e1, kc, vc, q, bt, cl, maxb, hkv, bs, G, hq, T, W, ls, vs, po);
+  else
+    launch_k(decode_simple_kernel<kD, PA_FP8_E4M3, false>, grid, dim3(64), 0, st, e0, e1, kc, vc, q, bt, cl, maxb, hkv, bs, G, hq, T, W, ls, vs, po);
 }
 
 
 template <int kD>
-void launch_stream(bool fp8, bool pair, int nw, hipStream_t st, const StreamArgs& a) {
+void launch_stream(bool fp8, bool pair, int nw, hipStream_t st, const StreamArgs& a,
+                   hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
   const dim3 grid(nw / kWavesPerGroup), block(64 * kWavesPerGroup);
   if (pair) {
     if (fp8)
-      decode_stream_kernel<kD, true, kAuxNonTemporal, true><<<grid, block, kPadLds, st>>>(a);
+      launch_k(decode_stream_kernel<kD, true, kAuxNonTemporal, true>, grid, block, kPadLds, st, e0, e1, a);
     else
-      decode_stream_kernel<kD, false, kAuxNonTemporal, true><<<grid, block, kPadLds, st>>>(a);
+      launch_k(decode_stream_kernel<kD, false, kAuxNonTemporal, true>, grid, block, kPadLds, st, e0, e1, a);
   } else if (fp8) {
-    decode_stream_kernel<kD, true, kAuxNonTemporal, false><<<grid, block, kPadLds, st>>>(a);
+    launch_k(decode_stream_kernel<kD, true, kAuxNonTemporal, false>, grid, block, kPadLds, st, e0, e1, a);
   } else {
-    decode_stream_kernel<kD, false, kAuxNonTemporal, false><<<grid, block, kPadLds, st>>>(a);
+    launch_k(decode_stream_kernel<kD, false, kAuxNonTemporal, false>, grid, block, kPadLds, st, e0, e1, a);
   }
 }
 
@@ -1727,7 +1756,7 @@ pa_status attend(const char* fn, const pa_cache_desc* c, const void* k_cache,
                  const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs,
                  int32_t num_q_heads, float scale, void* workspace, size_t workspace_bytes,
                  void* stream, const int32_t* prefix_len = nullptr,
-                 const float* prefix_rec = nullptr) {
+                 const float* prefix_rec = nullptr, CallTiming tm = CallTiming{}) {
   pa_status st = check_desc(c, fn);
   if (st != PA_OK) return st;
   const int hkv = c->num_kv_heads, D = c->head_dim, fmt = c->cache_dtype;
@@ -1821,8 +1850,10 @@ pa_status attend(const char* fn, const pa_cache_desc* c, const void* k_cache,
     for (int t0 = 0; t0 < T; t0 += tpp) {
       a.t_first = t0;
       a.rows = G * std::min(tpp, T - t0);
-      if (D == 128) launch_stream<128>(fmt == PA_FP8_E4M3, bs == 8, a.num_waves, s, a);
-      else launch_stream<64>(fmt == PA_FP8_E4M3, bs == 8, a.num_waves, s, a);
+      hipEvent_t e0 = t0 == 0 ? tm.start : nullptr;
+      hipEvent_t e1 = t0 + tpp >= T ? tm.stop : nullptr;
+      if (D == 128) launch_stream<128>(fmt == PA_FP8_E4M3, bs == 8, a.num_waves, s, a, e0, e1);
+      else launch_stream<64>(fmt == PA_FP8_E4M3, bs == 8, a.num_waves, s, a, e0, e1);
       st = launch_status(fn);
       if (st != PA_OK) return st;
     }
@@ -1838,11 +1869,12 @@ pa_status attend(const char* fn, const pa_cache_desc* c, const void* k_cache,
   const int rows = T * num_q_heads;
   {
     dim3 grid(P, rows, num_seqs);
+    hipEvent_t e1 = P > 1 ? nullptr : tm.stop;
     if (D == 128)
-      launch_simple<128>(fmt, grid, s, kc, vc, q, block_tables, context_lens,
+      launch_simple<128>(fmt, grid, s, tm.start, e1, kc, vc, q, block_tables, context_lens,
                          max_blocks_per_seq, hkv, bs, G, num_q_heads, T, W, logit_scale, vscale, po);
     else
-      launch_simple<64>(fmt, grid, s, kc, vc, q, block_tables, context_lens,
+      launch_simple<64>(fmt, grid, s, tm.start, e1, kc, vc, q, block_tables, context_lens,
                         max_blocks_per_seq, hkv, bs, G, num_q_heads, T, W, logit_scale, vscale, po);
   }
   st = launch_status(fn);
@@ -1850,12 +1882,13 @@ pa_status attend(const char* fn, const pa_cache_desc* c, const void* k_cache,
   if (P > 1) {
     dim3 grid(rows, num_seqs);
     const bool of32 = (q_dtype == PA_F32);
+    hipEvent_t e1 = tm.stop;
     if (D == 128) {
-      if (of32) reduce_kernel<128, true><<<grid, 128, 0, s>>>(context_lens, num_q_heads, T, po);
-      else reduce_kernel<128, false><<<grid, 128, 0, s>>>(context_lens, num_q_heads, T, po);
+      if (of32) launch_k(reduce_kernel<128, true>, grid, dim3(128), 0, s, nullptr, e1, context_lens, num_q_heads, T, po);
+      else launch_k(reduce_kernel<128, false>, grid, dim3(128), 0, s, nullptr, e1, context_lens, num_q_heads, T, po);
     } else {
-      if (of32) reduce_kernel<64, true><<<grid, 64, 0, s>>>(context_lens, num_q_heads, T, po);
-      else reduce_kernel<64, false><<<grid, 64, 0, s>>>(context_lens, num_q_heads, T, po);
+      if (of32) launch_k(reduce_kernel<64, true>, grid, dim3(64), 0, s, nullptr, e1, context_lens, num_q_heads, T, po);
+      else launch_k(reduce_kernel<64, false>, grid, dim3(64), 0, s, nullptr, e1, context_lens, num_q_heads, T, po);
     }
     st = launch_status(fn);
   }
@@ -1901,7 +1934,7 @@ extern "C" pa_status pa_decode(const pa_cache_desc* c, const void* k_cache, cons
                                void* workspace, size_t workspace_bytes, void* stream) {
   return attend("pa_decode", c, k_cache, v_cache, q, q_dtype, out, 1, 0, block_tables,
                 max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads, scale,
-                workspace, workspace_bytes, stream);
+                workspace, workspace_bytes, stream, nullptr, nullptr, take_call_timing());
 }
 
 extern "C" pa_status pa_decode_chunk(const pa_cache_desc* c, const void* k_cache,
@@ -1913,7 +1946,8 @@ extern "C" pa_status pa_decode_chunk(const pa_cache_desc* c, const void* k_cache
                                      size_t workspace_bytes, void* stream) {
   return attend("pa_decode_chunk", c, k_cache, v_cache, q, q_dtype, out, chunk_len, 0,
                 block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs,
-                num_q_heads, scale, workspace, workspace_bytes, stream);
+                num_q_heads, scale, workspace, workspace_bytes, stream, nullptr, nullptr,
+                take_call_timing());
 }
 
 extern "C" pa_status pa_decode_window(const pa_cache_desc* c, const void* k_cache,
@@ -1925,7 +1959,8 @@ extern "C" pa_status pa_decode_window(const pa_cache_desc* c, const void* k_cach
                                       void* workspace, size_t workspace_bytes, void* stream) {
   return attend("pa_decode_window", c, k_cache, v_cache, q, q_dtype, out, chunk_len, window,
                 block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs,
-                num_q_heads, scale, workspace, workspace_bytes, stream);
+                num_q_heads, scale, workspace, workspace_bytes, stream, nullptr, nullptr,
+                take_call_timing());
 }
 
 namespace {
@@ -2137,4 +2172,10 @@ extern "C" pa_status pa_decode_shared_prefix(
   return attend(fn, c, k_cache, v_cache, q, q_dtype, out, 1, 0, suf_tables, max_blocks_per_seq,
                 suf_lens, max_context_len, num_seqs, num_q_heads, scale, workspace, L.stream,
                 stream, plen, recs);
+}
+
+extern "C" pa_status pa_time_next_call(void* start_event, void* stop_event) {
+  t_next_call.start = static_cast<hipEvent_t>(start_event);
+  t_next_call.stop = static_cast<hipEvent_t>(stop_event);
+  return PA_OK;
 }

@@ -89,3 +89,48 @@ def test_write_and_decode_replay_from_a_captured_graph():
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {i}"
         assert int(ws[:B * Hkv * 4].count_nonzero()) == 0, "arrival counters not reset"
         _say(f"  replay {i}: bit-identical to eager")
+
+
+class _Ev:
+    """A raw HIP event on the runtime torch loaded (ctypes)."""
+    _hip = None
+
+    def __init__(self):
+        import ctypes
+        if _Ev._hip is None:
+            _Ev._hip = ctypes.CDLL("libamdhip64.so.7")
+        self._c = ctypes
+        self.h = ctypes.c_void_p()
+        assert _Ev._hip.hipEventCreate(ctypes.byref(self.h)) == 0
+
+    def ms_to(self, other):
+        ms = self._c.c_float()
+        assert _Ev._hip.hipEventSynchronize(other.h) == 0
+        assert _Ev._hip.hipEventElapsedTime(self._c.byref(ms), self.h, other.h) == 0
+        return ms.value
+
+    def destroy(self):
+        assert _Ev._hip.hipEventDestroy(self.h) == 0
+
+
+@pytest.mark.parametrize("T,window", [(1, 0), (4, 0), (1, 200)])
+def test_time_next_call_records_the_decode_kernels(T, window):
+    """pa_time_next_call: the next decode call's own dispatches record the
+    events; the output is the untimed call's, bit for bit; the request is
+    used once (a later call leaves the events as they were)."""
+    w, view = _view(1203 + T)
+    q = workloads.chunk_queries(np.random.default_rng(7), w.B, T, w.Hq, w.D, "bf16")
+    untimed = view.decode_chunk(q, window=window).clone()
+    e0, e1 = _Ev(), _Ev()
+    pk.time_next_call(e0.h, e1.h)
+    timed = view.decode_chunk(q, window=window).clone()
+    ms = e0.ms_to(e1)
+    again = view.decode_chunk(q, window=window)
+    torch.cuda.synchronize()
+    _say(f"time_next_call T={T} W={window}: {ms * 1e3:.1f} us")
+    assert 0.0 < ms < 1000.0
+    assert e0.ms_to(e1) == ms                      # the later call did not touch them
+    assert torch.equal(timed.view(torch.int16), untimed.view(torch.int16))
+    assert torch.equal(again.view(torch.int16), untimed.view(torch.int16))
+    e0.destroy()
+    e1.destroy()
