@@ -29,10 +29,11 @@ The JSON line also carries
     sequences of L * Hkv * D * 2 bytes * 2 for K and V) over its mean
     duration, taken with HIP events on one pa_decode of every timed step
     (layer step mod layers, so each layer in turn), against the 8 TB/s HBM
-    peak.  The events are recorded by the decode's own kernel dispatch on its
-    stream (pa_time_next_call: hipExtLaunchKernel with start and stop
-    events), so no marker packet sits between pa_write_kv and the decode;
-    they are created without the system-scope fence (the path exchanges
+    peak.  For single-token steps the events are recorded by the decode's own
+    kernel dispatch on its stream (pa_time_next_call: hipExtLaunchKernel with
+    start and stop events), so no marker packet sits between pa_write_kv and
+    the decode; chunks (--chunk) record them as markers around the call.
+    They are created without the system-scope fence (the path exchanges
     nothing with the host);
     ``traffic`` is the HBM bytes per call from the committed rocprofv3
     counter summary, when that was taken on the current kernel source;
@@ -982,10 +983,15 @@ def main():
         max_len = int(lens.max())
         for l in range(NL):
             pk.write_kv(desc, kc[l], vc[l], k_new[l], v_new[l], d_slots, stream=stream)
-            if ev_pair is not None and l == i % NL:
-                # the decode's own dispatches record the pair (no marker
-                # packet between pa_write_kv and the decode)
+            timed_here = ev_pair is not None and l == i % NL
+            if timed_here and T == 1:
+                # the decode's own dispatch records the pair (no marker packet
+                # between pa_write_kv and the decode)
                 pk.time_next_call(ev_pair[0].h, ev_pair[1].h)
+            elif timed_here:
+                # chunks: markers around the call (launching them with
+                # dispatch-recorded events slowed the whole chunk step)
+                ev_pair[0].record(stream)
             if T == 1 and not args.window:
                 pk.decode(desc, kc[l], vc[l], q[l], out[l], d_bt, d_cl, max_len,
                           float(w.scale), workspace, stream=stream)
@@ -994,6 +1000,8 @@ def main():
                 oo = out[l] if T > 1 else out[l].view(B, 1, Hq, D)
                 pk.decode_chunk(desc, kc[l], vc[l], qq, oo, d_bt, d_cl, max_len,
                                 float(w.scale), workspace, stream=stream, window=args.window)
+            if timed_here and T > 1:
+                ev_pair[1].record(stream)
         if args.window:
             return _kv_bytes(np.minimum(lens, args.window + T - 1), Hkv, D, 2)
         return _kv_bytes(lens, Hkv, D, 2)
