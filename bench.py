@@ -210,6 +210,18 @@ def _traffic_per_call(kv_bytes, T=1):
     return float(m_r.group(1)) * kv_bytes + float(m_w.group(1))
 
 
+def opened_table_entries(lens, slots, block_size):
+    """Table entries of the blocks a step opened.  lens: context lengths
+    before the step [B]; slots: the slots the manager gave the step's new
+    tokens [B, T] (token t of sequence s at position lens[s] + t).  A token
+    whose position is a multiple of the block size opens a block, whose id
+    is its slot // block_size.  Returns (rows, cols, blocks)."""
+    T = slots.shape[1]
+    pos = lens[:, None] + np.arange(T)
+    opened = pos % block_size == 0
+    return np.nonzero(opened)[0], pos[opened] // block_size, slots[opened] // block_size
+
+
 def stream_read_probe(dev, stream, gib=4, reps=3):
     """GB/s of pa_read_probe over a ``gib`` GiB buffer: (in order, random 4 KiB)."""
     import torch
@@ -698,11 +710,11 @@ def run_prefix(args):
         hi, hj = h_i64[b].numpy(), h_i32[b].numpy()
         sl, pairs = bm.append_batch(ids, slots=hi[:B])
         assert len(pairs) == 0
-        opened = lens % 16 == 0              # the new token opens a block
-        n = int(opened.sum())
-        hi[B:B + n] = np.nonzero(opened)[0]
-        hi[2 * B:2 * B + n] = lens[opened] // 16
-        hj[B:B + n] = hi[:B][opened] // 16
+        rows, cols, blocks = opened_table_entries(lens, hi[:B].reshape(B, 1), 16)
+        n = len(rows)
+        hi[B:B + n] = rows
+        hi[2 * B:2 * B + n] = cols
+        hj[B:B + n] = blocks
         lens[:] += 1
         hj[:B] = lens
         d_i64.copy_(h_i64[b], non_blocking=True)
@@ -964,12 +976,11 @@ def main():
                 sl, pairs = bm.append_batch(ids, slots=slots_tb[t])
                 assert len(pairs) == 0
             hi[:nmax].reshape(B, T)[:] = slots_tb.T
-        pos = lens[:, None] + np.arange(T)       # positions of the new tokens
-        opened = pos % bs == 0
-        n = int(opened.sum())
-        hi[nmax:nmax + n] = np.nonzero(opened)[0]
-        hi[2 * nmax:2 * nmax + n] = pos[opened] // bs
-        hj[B:B + n] = hi[:nmax].reshape(B, T)[opened] // bs
+        rows, cols, blocks = opened_table_entries(lens, hi[:nmax].reshape(B, T), bs)
+        n = len(rows)
+        hi[nmax:nmax + n] = rows
+        hi[2 * nmax:2 * nmax + n] = cols
+        hj[B:B + n] = blocks
         lens[:] += T
         hj[:B] = lens
         host_bm_s.append(time.perf_counter() - th)
