@@ -136,6 +136,7 @@ METRIC_PREFIX = ("paged decode with prefix caching: unique KV GB/s vs HBM peak; 
 METRIC_SWAP = "paged KV swap: device<->pinned host block copy GB/s vs host link peak"
 DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_421_amd", "csrc", "decode.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic_gqa8b_b256.txt")
+TRAFFIC_FILE_FP8 = os.path.join(ROOT, "profiles", "decode_traffic_gqa8b_fp8_b256.txt")
 TRAFFIC_FILE_CHUNK = os.path.join(ROOT, "profiles", "chunk_traffic_gqa8b_b256_t{T}.txt")
 
 
@@ -193,12 +194,17 @@ def kernel_source_sha256():
     return hashlib.sha256(text[a:b].encode()).hexdigest()
 
 
-def _traffic_per_call(kv_bytes, T=1):
+def _traffic_per_call(kv_bytes, T=1, kv_dtype="bf16"):
     """HBM bytes of one pa_decode (pa_decode_chunk for T > 1) call reading
     ``kv_bytes`` algorithmic KV bytes, from the committed rocprofv3 counter
     summary (bytes read per algorithmic byte, bytes written per call), if that
     summary was taken on the current kernel source; else None."""
-    path = TRAFFIC_FILE if T == 1 else TRAFFIC_FILE_CHUNK.format(T=T)
+    if kv_dtype == "fp8":
+        path = TRAFFIC_FILE_FP8 if T == 1 else None
+    else:
+        path = TRAFFIC_FILE if T == 1 else TRAFFIC_FILE_CHUNK.format(T=T)
+    if path is None:
+        return None
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -248,12 +254,15 @@ def stream_read_probe(dev, stream, gib=4, reps=3):
     return out[0], out[1]
 
 
-def cpu_baseline(w, budget_s=10.0, T=1):
+def cpu_baseline(w, budget_s=10.0, T=1, fmt="bf16", k_scale=1.0, v_scale=1.0):
     """The oracle's decode (gather blocks, textbook fp64 softmax attention) of
     the whole batch at its initial lengths, repeated until ``budget_s``
     seconds have passed (at least 3 runs); median run time.  With T > 1, the
     oracle's chunk attention, the last T positions of each context being the
-    chunk."""
+    chunk.  ``fmt`` is the cache format (fp8: the bf16 rows quantised with
+    the given scales, as pa_write_kv stores them).  The BLAS library may use
+    one thread per host core the process may run on; the same batch on one
+    thread is reported beside it."""
     import oracle
     from threadpoolctl import threadpool_limits
 
@@ -267,32 +276,43 @@ def cpu_baseline(w, budget_s=10.0, T=1):
     assert len(slots) == len(w.row_seq) and np.all(w.row_pos == np.arange(len(slots)) -
                                                   np.repeat(starts, w.lens))
     shape = (w.num_blocks, w.Hkv, 16, w.D)
-    kc, vc = oracle.write_kv(np.zeros(shape, np.uint16), np.zeros(shape, np.uint16),
-                             w.k_rows, w.v_rows, slots, "bf16", "bf16")
+    store = np.uint8 if fmt == "fp8" else np.uint16
+    kc, vc = oracle.write_kv(np.zeros(shape, store), np.zeros(shape, store),
+                             w.k_rows, w.v_rows, slots, "bf16", fmt, k_scale, v_scale)
     cap = max(-(-int(L) // 16) for L in w.lens)
     bt, cl = bm.pack(list(range(w.B)), cap)
-    times = []
     qc = None
     if T > 1:
         qc = workloads.chunk_queries(np.random.default_rng(1004), w.B, T, w.Hq, w.D, "bf16")
-    with threadpool_limits(limits=1):
-        t_all = time.perf_counter()
-        while len(times) < 3 or time.perf_counter() - t_all < budget_s:
-            t0 = time.perf_counter()
-            if T == 1:
-                oracle.decode(w.q, "bf16", kc, vc, "bf16", bt, cl, w.scale)
-            else:
-                oracle.decode_chunk(qc, "bf16", kc, vc, "bf16", bt, cl, w.scale)
-            times.append(time.perf_counter() - t0)
-    t = statistics.median(times)
+
+    def median_run(threads, budget):
+        times = []
+        with threadpool_limits(limits=threads):
+            t_all = time.perf_counter()
+            while len(times) < 3 or time.perf_counter() - t_all < budget:
+                t0 = time.perf_counter()
+                if T == 1:
+                    oracle.decode(w.q, "bf16", kc, vc, fmt, bt, cl, w.scale, k_scale, v_scale)
+                else:
+                    oracle.decode_chunk(qc, "bf16", kc, vc, fmt, bt, cl, w.scale, k_scale,
+                                        v_scale)
+                times.append(time.perf_counter() - t0)
+        return statistics.median(times), len(times)
+
+    cores = len(os.sched_getaffinity(0))
+    t, runs = median_run(cores, budget_s)
+    t1, runs1 = median_run(1, budget_s / 2)
+    e = 1 if fmt == "fp8" else 2
     what = "256 seqs x 32 heads" if T == 1 else f"256 seqs x {T} chunk tokens x 32 heads"
     return {"value": round(w.B * T / t, 2), "unit": "seqs/s" if T == 1 else "tokens/s",
-            "cores": 1, "kind": "oracle",
-            "kv_gbps": round(_kv_bytes(cl, w.Hkv, w.D, 2) / t / 1e9, 4),
-            "host_cores_visible": len(os.sched_getaffinity(0)),
-            "sample": (f"whole batch ({what}, sum L {int(cl.sum())}, initial "
-                       f"lengths), {len(times)} runs, median {t:.3f} s; numpy float64, "
-                       f"BLAS limited to 1 thread")}
+            "cores": cores, "kind": "oracle",
+            "kv_gbps": round(_kv_bytes(cl, w.Hkv, w.D, e) / t / 1e9, 4),
+            "host_cores_visible": cores,
+            "value_1_thread": round(w.B * T / t1, 2),
+            "sample": (f"whole batch ({what}, {fmt} cache, sum L {int(cl.sum())}, initial "
+                       f"lengths), {runs} runs, median {t:.3f} s; numpy float64 with BLAS "
+                       f"limited to {cores} threads (the host cores visible); on 1 thread "
+                       f"{runs1} runs, median {t1:.3f} s")}
 
 
 def swap_cpu_baseline(kc, vc, pairs, budget_s=10.0):
@@ -839,6 +859,9 @@ def main():
                          "default) or pa_decode (plain)")
     ap.add_argument("--config", type=int, default=0, choices=(0, 2, 4, 5),
                     help="pa_decode alone on decode configuration 2, 4 or 5")
+    ap.add_argument("--kv-dtype", choices=("bf16", "fp8"), default="bf16",
+                    help="cache format of the decode step (fp8: E4M3 with one scale per "
+                         "cache, written from the same bf16 rows by pa_write_kv)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     args = ap.parse_args()
@@ -881,7 +904,14 @@ def main():
     else:        # the same token capacity in bs-token blocks, one more per sequence
         n_blocks = -(-w.num_blocks * 16 // bs) + B
         order = np.random.default_rng(3000 + bs).permutation(n_blocks).astype(np.int32)
-    desc = pk.CacheDesc(n_blocks, Hkv, D, "bf16", block_size=bs)
+    kvd = args.kv_dtype
+    ks = vs = 1.0
+    if kvd == "fp8":
+        # one scale per cache: the largest magnitude of the rows written, / 448
+        ks = float(np.float32(np.abs(workloads.bf16_bits_to_f32(w.k_rows)).max() / np.float32(448)))
+        vs = float(np.float32(np.abs(workloads.bf16_bits_to_f32(w.v_rows)).max() / np.float32(448)))
+    elem = 1 if kvd == "fp8" else 2
+    desc = pk.CacheDesc(n_blocks, Hkv, D, kvd, ks, vs, block_size=bs)
 
     # ---- caches of layer 0 through the library's own write path; the other
     # layers get copies (distinct HBM, same contents)
@@ -893,8 +923,8 @@ def main():
         assert pair is None
         per.append(sl)
     slots = torch.from_numpy(np.concatenate(per)).to(dev)
-    kc = [torch.zeros(desc.shape, dtype=torch.bfloat16, device=dev) for _ in range(NL)]
-    vc = [torch.zeros(desc.shape, dtype=torch.bfloat16, device=dev) for _ in range(NL)]
+    kc = [torch.zeros(desc.shape, dtype=desc.torch_dtype, device=dev) for _ in range(NL)]
+    vc = [torch.zeros(desc.shape, dtype=desc.torch_dtype, device=dev) for _ in range(NL)]
     k_rows = torch.from_numpy(w.k_rows.view(np.int16)).to(dev).view(torch.bfloat16)
     v_rows = torch.from_numpy(w.v_rows.view(np.int16)).to(dev).view(torch.bfloat16)
     pk.write_kv(desc, kc[0], vc[0], k_rows, v_rows, slots)
@@ -1014,8 +1044,8 @@ def main():
             if timed_here and T > 1:
                 ev_pair[1].record(stream)
         if args.window:
-            return _kv_bytes(np.minimum(lens, args.window + T - 1), Hkv, D, 2)
-        return _kv_bytes(lens, Hkv, D, 2)
+            return _kv_bytes(np.minimum(lens, args.window + T - 1), Hkv, D, elem)
+        return _kv_bytes(lens, Hkv, D, elem)
 
     _log(f"bench: {NL} layers x {n_blocks} blocks of {bs}, warmup {args.warmup}, steps {args.steps}")
     for i in range(args.warmup):
@@ -1067,10 +1097,11 @@ def main():
                                          axis=1).astype(np.int32)).to(dev)
     copy_us = timed_calls(lambda: pk.copy_blocks(desc, kc[NL - 1], vc[NL - 1], cp_pairs,
                                                  stream=stream))
-    blk_bytes = bs * Hkv * D * 2                       # one block of one cache
-    row_bytes = Hkv * D * 2                            # one token row of K (or V)
-    bulk_b = 2 * 2 * bulk_rows * row_bytes             # K and V rows read, then written
-    step_b = 2 * 2 * B * T * row_bytes
+    blk_bytes = bs * Hkv * D * elem                    # one block of one cache
+    row_bytes = Hkv * D * 2                            # one bf16 source row of K (or V)
+    row_out = Hkv * D * elem                           # the same row in the cache
+    bulk_b = 2 * bulk_rows * (row_bytes + row_out)     # K and V rows read, then written
+    step_b = 2 * B * T * (row_bytes + row_out)
     copy_b = 2 * 2 * n_pairs * blk_bytes               # both caches, read and written
     path_steps = {
         "block_manager_host_us_per_step": round(host_bm_us, 1),
@@ -1096,8 +1127,9 @@ def main():
     mean_kv = statistics.mean(kv_per_call)
     achieved = mean_kv / mean_dec_s / 1e9
     steps_s = wall / args.steps
-    traffic = None if (args.window or bs != 16) else _traffic_per_call(mean_kv, T)
-    _log(f"bench: {'pa_decode' if T == 1 else 'pa_decode_chunk'} mean {mean_dec_s * 1e6:.1f} us (p10 "
+    traffic = None if (args.window or bs != 16) else _traffic_per_call(mean_kv, T, kvd)
+    _log(f"bench: {'pa_decode' if T == 1 else 'pa_decode_chunk'} mean {mean_dec_s * 1e6:.1f} us "
+         f"(median {np.median(dec_ms) * 1e3:.1f}, p10 "
          f"{np.percentile(dec_ms, 10) * 1e3:.1f}, p90 {np.percentile(dec_ms, 90) * 1e3:.1f}), "
          f"{achieved:.0f} GB/s; step {steps_s * 1e3:.3f} ms")
 
@@ -1110,6 +1142,9 @@ def main():
         workload += f", sliding window of {args.window} positions"
     if bs != 16:
         workload = workload.replace("16-token shuffled blocks", f"{bs}-token shuffled blocks")
+    if kvd == "fp8":
+        workload = workload.replace("gqa8b-bf16-b256", "gqa8b-fp8-b256").replace(
+            "bf16 KV", "fp8-e4m3 KV (one scale per cache; bf16 q and output)")
     res = {
         "metric": METRIC if T == 1 else METRIC_CHUNK,
         "value": round(B * T * NL * args.steps / wall, 1),
@@ -1121,7 +1156,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if kvd == "bf16" else "fp8-e4m3 KV, bf16 q/out, fp32 accumulation",
         "data": "synthetic",
         "config": {
             "workload": workload,
@@ -1141,6 +1176,7 @@ def main():
         "block_size": bs,
         "paged_utilisation": round(float(lens.sum()) / (bs * float(np.sum(-(-lens // bs)))), 4),
         "decode_us_mean": round(mean_dec_s * 1e6, 2),
+        "decode_us_median": round(float(np.median(dec_ms)) * 1e3, 2),
         "decode_us_p10": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
         "decode_us_p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),
         "roofline": {
@@ -1156,7 +1192,7 @@ def main():
             "traffic": None if traffic is None else round(traffic / mean_dec_s / 1e9, 1),
         },
     }
-    if T == 1 and not args.window and bs == 16:
+    if T == 1 and not args.window and bs == 16 and kvd == "bf16":
         seq_gbps, rnd_gbps = stream_read_probe(dev, stream)
         res["stream_read_probe"] = {"in_order_gbps": seq_gbps, "random_4k_gbps": rnd_gbps,
                                     "decode_frac_of_random_4k": round(achieved / rnd_gbps, 4)}
@@ -1174,7 +1210,7 @@ def main():
         res["chat_sim_hit_rate"] = round(rate, 4)
     if not args.no_cpu_baseline and not args.window and bs == 16:
         _log("bench: timing the CPU oracle")
-        res["cpu_baseline"] = cpu_baseline(w, T=T)
+        res["cpu_baseline"] = cpu_baseline(w, T=T, fmt=kvd, k_scale=ks, v_scale=vs)
     print(json.dumps(res), flush=True)
 
 

@@ -31,8 +31,6 @@ Readings where the pages are silent:
 """
 from __future__ import annotations
 
-from typing import Tuple
-
 import numpy as np
 
 from .formats import bf16_to_f64, widen_cache
@@ -156,27 +154,3 @@ def decode_partitioned(q: np.ndarray, q_fmt: str, k_cache: np.ndarray,
                     os_.append((e @ V[start:start + partition]) / li)
                 out[s, h] = merge_partitions(np.array(ms), np.array(ls), np.array(os_))
     return out
-
-
-def reference_rows(q: np.ndarray, q_fmt: str, k_cache, v_cache, fmt,
-                   block_tables, context_lens, scale, k_scale=1.0, v_scale=1.0,
-                   pairs=()) -> Tuple[np.ndarray, list]:
-    """Oracle outputs for a sample of (sequence, query head) pairs only."""
-    q64 = _q64(q, q_fmt)
-    B, Hq, D = q64.shape
-    Hkv = k_cache.shape[1]
-    G = Hq // Hkv
-    sc = np.float64(np.float32(scale))
-    rows = []
-    for (s, h) in pairs:
-        L = int(context_lens[s])
-        if L == 0:
-            rows.append(np.zeros(D))
-            continue
-        g = h // G
-        K = widen_cache(gather_kv(k_cache, block_tables[s], L, g), fmt, k_scale)
-        V = widen_cache(gather_kv(v_cache, block_tables[s], L, g), fmt, v_scale)
-        z = sc * (K @ q64[s, h])
-        e = np.exp(z - z.max())
-        rows.append((e / e.sum()) @ V)
-    return np.array(rows), list(pairs)

@@ -72,6 +72,59 @@ def _dev(t: torch.Tensor, name: str) -> ctypes.c_void_p:
     return ctypes.c_void_p(t.data_ptr())
 
 
+_CACHE_DTYPES = {PA_F32: (torch.float32, torch.int32), PA_BF16: (torch.bfloat16, torch.int16),
+                 PA_FP8_E4M3: (torch.uint8, torch.float8_e4m3fn)}
+
+
+def _caches(desc: CacheDesc, k_cache: torch.Tensor, v_cache: torch.Tensor):
+    """Pointers of a K and a V cache that have the dtype and byte size
+    ``desc`` describes, so the kernels' addresses stay inside them.  Both are
+    checked before the device test, so a mismatch is reported without
+    touching the GPU."""
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.dtype not in _CACHE_DTYPES[desc.c.cache_dtype]:
+            raise ValueError(f"{name}: dtype {t.dtype} does not match the descriptor's cache "
+                             f"format {desc.torch_dtype}")
+        nbytes = t.numel() * t.element_size()
+        if nbytes != desc.cache_bytes():
+            raise ValueError(f"{name}: {nbytes} bytes, the descriptor describes "
+                             f"{desc.cache_bytes()} ({desc.shape})")
+    return _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache")
+
+
+def _queries(desc: CacheDesc, q: torch.Tensor, out: torch.Tensor, ndim: int) -> None:
+    """q and out: [B, Hq, D] (decode) or [B, T, Hq, D] (chunks), D = the
+    cache's head_dim, Hq a multiple of its KV heads."""
+    if q.dim() != ndim:
+        raise ValueError(f"q must have {ndim} dimensions, got {tuple(q.shape)}")
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must have q's shape and dtype")
+    if q.shape[-1] != desc.c.head_dim:
+        raise ValueError(f"q head_dim {q.shape[-1]} != the cache's {desc.c.head_dim}")
+    if q.shape[-2] % desc.c.num_kv_heads != 0:
+        raise ValueError(f"{q.shape[-2]} query heads are not a multiple of "
+                         f"{desc.c.num_kv_heads} KV heads")
+
+
+def _tables(block_tables: torch.Tensor, context_lens: torch.Tensor, B: int) -> None:
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
+        raise ValueError("block_tables must be [B, max_blocks] and context_lens [B]")
+
+
+def _call_workspace(nbytes: int, device, stream) -> torch.Tensor:
+    """A zero-filled workspace for one call on ``stream``: allocated from
+    that stream's pool of the caching allocator and filled on that stream, so
+    the fill is ordered before the call, and the memory, released when the
+    tensor dies, is handed out again only to work ordered after the call."""
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    with torch.cuda.stream(s):
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    decode_workspace_init(ws, stream=s)
+    return ws
+
+
 def write_kv(desc: CacheDesc, k_cache: torch.Tensor, v_cache: torch.Tensor,
              k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
              stream=None) -> None:
@@ -83,8 +136,8 @@ def write_kv(desc: CacheDesc, k_cache: torch.Tensor, v_cache: torch.Tensor,
     T = k.shape[0]
     if tuple(k.shape[1:]) != (desc.c.num_kv_heads, desc.c.head_dim) or slot_mapping.numel() != T:
         raise ValueError("k/v must be [T, Hkv, D] and slot_mapping [T]")
-    check(lib.pa_write_kv(ctypes.byref(desc.c), _dev(k_cache, "k_cache"),
-                          _dev(v_cache, "v_cache"), _dev(k, "k"), _dev(v, "v"),
+    kc, vc = _caches(desc, k_cache, v_cache)
+    check(lib.pa_write_kv(ctypes.byref(desc.c), kc, vc, _dev(k, "k"), _dev(v, "v"),
                           dtype_code(k.dtype), _dev(slot_mapping, "slot_mapping"), T,
                           _stream(stream)))
 
@@ -94,11 +147,11 @@ def copy_blocks(desc: CacheDesc, k_cache: torch.Tensor, v_cache: torch.Tensor,
     """pa_copy_blocks: pairs int32 [n, 2] of (src, dst) blocks."""
     if pairs.dtype != torch.int32:
         raise ValueError("pairs must be int32")
+    kc, vc = _caches(desc, k_cache, v_cache)
     n = pairs.numel() // 2
     if n == 0:
         return
-    check(lib.pa_copy_blocks(ctypes.byref(desc.c), _dev(k_cache, "k_cache"),
-                             _dev(v_cache, "v_cache"), _dev(pairs, "pairs"), n,
+    check(lib.pa_copy_blocks(ctypes.byref(desc.c), kc, vc, _dev(pairs, "pairs"), n,
                              _stream(stream)))
 
 
@@ -117,12 +170,13 @@ def decode_workspace_init(workspace: torch.Tensor, stream=None) -> None:
 
 
 def new_decode_workspace(desc: CacheDesc, num_seqs: int, num_q_heads: int,
-                         max_context_len: int, device=None) -> torch.Tensor:
-    """A zero-filled uint8 device tensor of pa_decode_workspace_bytes bytes
-    (at least one byte), ready for pa_decode."""
+                         max_context_len: int, device=None, stream=None) -> torch.Tensor:
+    """A uint8 device tensor of pa_decode_workspace_bytes bytes (at least one
+    byte), zero-filled on ``stream`` (default: the current stream), ready for
+    pa_decode on that stream."""
     n = decode_workspace_bytes(desc, num_seqs, num_q_heads, max_context_len)
     ws = torch.empty(max(n, 1), dtype=torch.uint8, device=device or "cuda")
-    decode_workspace_init(ws)
+    decode_workspace_init(ws, stream=stream)
     return ws
 
 
@@ -134,20 +188,18 @@ def decode(desc: CacheDesc, k_cache: torch.Tensor, v_cache: torch.Tensor, q: tor
 
     ``workspace`` is a zero-filled device buffer of at least
     ``decode_workspace_bytes`` bytes (``new_decode_workspace``), reusable by
-    later calls on the same stream; if None, a fresh one is allocated for
-    this call."""
+    later calls on the same stream; if None, one is made for this call on
+    ``stream``."""
+    _queries(desc, q, out, 3)
     B, Hq, D = q.shape
-    if out.shape != q.shape or out.dtype != q.dtype:
-        raise ValueError("out must have q's shape and dtype")
-    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
-        raise ValueError("block_tables and context_lens must be int32")
-    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
-        raise ValueError("block_tables must be [B, max_blocks] and context_lens [B]")
+    _tables(block_tables, context_lens, B)
+    kc, vc = _caches(desc, k_cache, v_cache)
     if workspace is None:
-        workspace = new_decode_workspace(desc, B, Hq, max_context_len, q.device)
+        workspace = _call_workspace(decode_workspace_bytes(desc, B, Hq, max_context_len),
+                                    q.device, stream)
     ws_ptr = _dev(workspace, "workspace")
     ws_bytes = workspace.numel() * workspace.element_size()
-    check(lib.pa_decode(ctypes.byref(desc.c), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+    check(lib.pa_decode(ctypes.byref(desc.c), kc, vc,
                         _dev(q, "q"), dtype_code(q.dtype), _dev(out, "out"),
                         _dev(block_tables, "block_tables"), block_tables.shape[1],
                         _dev(context_lens, "context_lens"), int(max_context_len), B, Hq,
@@ -164,11 +216,12 @@ def chunk_workspace_bytes(desc: CacheDesc, num_seqs: int, num_q_heads: int, chun
 
 
 def new_chunk_workspace(desc: CacheDesc, num_seqs: int, num_q_heads: int, chunk_len: int,
-                        max_context_len: int, device=None) -> torch.Tensor:
-    """A zero-filled uint8 device tensor sized for pa_decode_chunk."""
+                        max_context_len: int, device=None, stream=None) -> torch.Tensor:
+    """A uint8 device tensor sized for pa_decode_chunk, zero-filled on
+    ``stream`` (default: the current stream)."""
     n = chunk_workspace_bytes(desc, num_seqs, num_q_heads, chunk_len, max_context_len)
     ws = torch.empty(max(n, 1), dtype=torch.uint8, device=device or "cuda")
-    decode_workspace_init(ws)
+    decode_workspace_init(ws, stream=stream)
     return ws
 
 
@@ -180,26 +233,22 @@ def decode_chunk(desc: CacheDesc, k_cache: torch.Tensor, v_cache: torch.Tensor,
     """pa_decode_chunk (pa_decode_window when ``window`` > 0): attention of
     T = q.shape[1] new tokens per sequence, causal inside the chunk; q and
     out are [B, T, Hq, D]."""
+    _queries(desc, q, out, 4)
     B, T, Hq, D = q.shape
-    if out.shape != q.shape or out.dtype != q.dtype:
-        raise ValueError("out must have q's shape and dtype")
-    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
-        raise ValueError("block_tables and context_lens must be int32")
-    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
-        raise ValueError("block_tables must be [B, max_blocks] and context_lens [B]")
+    _tables(block_tables, context_lens, B)
+    kc, vc = _caches(desc, k_cache, v_cache)
     if workspace is None:
-        workspace = new_chunk_workspace(desc, B, Hq, T, max_context_len, q.device)
+        workspace = _call_workspace(chunk_workspace_bytes(desc, B, Hq, T, max_context_len),
+                                    q.device, stream)
     if window:
-        check(lib.pa_decode_window(ctypes.byref(desc.c), _dev(k_cache, "k_cache"),
-                                   _dev(v_cache, "v_cache"), _dev(q, "q"), dtype_code(q.dtype),
+        check(lib.pa_decode_window(ctypes.byref(desc.c), kc, vc, _dev(q, "q"), dtype_code(q.dtype),
                                    _dev(out, "out"), T, int(window),
                                    _dev(block_tables, "block_tables"), block_tables.shape[1],
                                    _dev(context_lens, "context_lens"), int(max_context_len), B,
                                    Hq, float(scale), _dev(workspace, "workspace"),
                                    workspace.numel() * workspace.element_size(), _stream(stream)))
         return out
-    check(lib.pa_decode_chunk(ctypes.byref(desc.c), _dev(k_cache, "k_cache"),
-                              _dev(v_cache, "v_cache"), _dev(q, "q"), dtype_code(q.dtype),
+    check(lib.pa_decode_chunk(ctypes.byref(desc.c), kc, vc, _dev(q, "q"), dtype_code(q.dtype),
                               _dev(out, "out"), T, _dev(block_tables, "block_tables"),
                               block_tables.shape[1], _dev(context_lens, "context_lens"),
                               int(max_context_len), B, Hq, float(scale),
@@ -217,11 +266,13 @@ def shared_prefix_workspace_bytes(desc: CacheDesc, num_seqs: int, num_q_heads: i
 
 def new_shared_prefix_workspace(desc: CacheDesc, num_seqs: int, num_q_heads: int,
                                 max_blocks_per_seq: int, max_context_len: int,
-                                device=None) -> torch.Tensor:
+                                device=None, stream=None) -> torch.Tensor:
+    """A uint8 device tensor sized for pa_decode_shared_prefix, zero-filled on
+    ``stream`` (default: the current stream)."""
     n = shared_prefix_workspace_bytes(desc, num_seqs, num_q_heads, max_blocks_per_seq,
                                       max_context_len)
     ws = torch.empty(max(n, 1), dtype=torch.uint8, device=device or "cuda")
-    decode_workspace_init(ws)
+    decode_workspace_init(ws, stream=stream)
     return ws
 
 
@@ -232,15 +283,17 @@ def decode_shared_prefix(desc: CacheDesc, k_cache: torch.Tensor, v_cache: torch.
                          stream=None) -> torch.Tensor:
     """pa_decode_shared_prefix: pa_decode, with the shared prefix of each
     group (host int32 [k, 3] of (first, count, shared blocks)) attended once."""
+    _queries(desc, q, out, 3)
     B, Hq, D = q.shape
-    if out.shape != q.shape or out.dtype != q.dtype:
-        raise ValueError("out must have q's shape and dtype")
+    _tables(block_tables, context_lens, B)
+    kc, vc = _caches(desc, k_cache, v_cache)
     grp = np.ascontiguousarray(groups, dtype=np.int32).reshape(-1, 3)
     if workspace is None:
-        workspace = new_shared_prefix_workspace(desc, B, Hq, block_tables.shape[1],
-                                                max_context_len, q.device)
+        workspace = _call_workspace(
+            shared_prefix_workspace_bytes(desc, B, Hq, block_tables.shape[1], max_context_len),
+            q.device, stream)
     check(lib.pa_decode_shared_prefix(
-        ctypes.byref(desc.c), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(q, "q"),
+        ctypes.byref(desc.c), kc, vc, _dev(q, "q"),
         dtype_code(q.dtype), _dev(out, "out"), _dev(block_tables, "block_tables"),
         block_tables.shape[1], _dev(context_lens, "context_lens"), int(max_context_len), B, Hq,
         float(scale), _ptr(grp), len(grp), _dev(workspace, "workspace"),
@@ -290,6 +343,13 @@ def swap_blocks(desc: CacheDesc, src_k: torch.Tensor, src_v: torch.Tensor,
     if pairs.dtype != torch.int32:
         raise ValueError("pairs must be int32")
     n = pairs.numel() // 2
+    if src_k.shape != src_v.shape or dst_k.shape != dst_v.shape:
+        raise ValueError("K and V pools must have the same shape")
+    for name, t in (("src", src_k), ("dst", dst_k)):
+        if t.dtype not in _CACHE_DTYPES[desc.c.cache_dtype] or t.dim() != 4 or \
+                tuple(t.shape[1:]) != desc.shape[1:]:
+            raise ValueError(f"{name} pools must be [blocks, {desc.shape[1]}, {desc.shape[2]}, "
+                             f"{desc.shape[3]}] of the descriptor's cache format")
     check(lib.pa_swap_blocks(ctypes.byref(desc.c), _pool(src_k, "src_k"), _pool(src_v, "src_v"),
                              _pool(dst_k, "dst_k"), _pool(dst_v, "dst_v"),
                              _pool(pairs, "pairs"), n, _stream(stream)))

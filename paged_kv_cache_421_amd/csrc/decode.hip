@@ -998,7 +998,7 @@ decode_stream_kernel(StreamArgs a) {
                                                part_rsrc, static_cast<int>(mine + off), 0,
                                                kAuxCoherent);
     }
-    __builtin_amdgcn_s_waitcnt(0);
+    wait_memory_done();
     uint32_t prev[2] = {0u, 0u};
     if (lane == 0) {
 #pragma unroll
@@ -1007,6 +1007,7 @@ decode_stream_kernel(StreamArgs a) {
           prev[i] = __hip_atomic_fetch_add(a.counters + static_cast<int64_t>(pend_s[i]) * hkv + pend_g[i],
                                            1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    compiler_fence();
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       if (pend_s[i] < 0) continue;
@@ -1443,13 +1444,14 @@ shared_prefix_kernel(PrefixArgs a) {
       __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{__float_as_uint(m_ref), __float_as_uint(l_tot)},
                                             rr, mine + kD * 4, 0, kAuxCoherent);
   }
-  __builtin_amdgcn_s_waitcnt(0);
+  wait_memory_done();
   __shared__ uint32_t s_prev;
   __syncthreads();
   uint32_t* ctr = a.counters + static_cast<int64_t>(wg) * hkv + g;
   if (tid == 0)
     s_prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
+  compiler_fence();
   if (s_prev != static_cast<uint32_t>(a.splits - 1)) return;
   if (tid == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (!row_ok) return;

@@ -59,4 +59,18 @@ __device__ __forceinline__ uint32_t e4m3_encode(float y) {
   return sign | mag;
 }
 
+// Publishing partial results to other waves: the stores are issued, then
+// this waits until every memory access of the wave has completed, before the
+// arrival counter is bumped.  The memory clobber keeps the compiler from
+// moving any memory access across the wait (a relaxed atomic alone would let
+// it schedule the counter update ahead of the stores).
+__device__ __forceinline__ void wait_memory_done() {
+  asm volatile("s_waitcnt vmcnt(0) expcnt(0) lgkmcnt(0)" ::: "memory");
+}
+
+// Compiler-only barrier: memory accesses are not moved across it.  Placed
+// after an arrival-counter update whose result decides whether the wave
+// reads the other waves' results, so those loads stay after the update.
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
 }  // namespace pagedkv

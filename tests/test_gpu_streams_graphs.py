@@ -43,6 +43,36 @@ def test_decode_on_a_side_stream_matches_default_stream():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+def test_decode_on_an_explicit_stream_without_a_workspace():
+    """stream= given, no workspace, and that stream not current: the call's
+    workspace is made and zero-filled on that stream, so the fill precedes the
+    kernel there and the memory is not reused by the current stream while the
+    kernel may still run.  The current stream is kept busy with unrelated work
+    meanwhile; the output equals the default-stream result bit for bit."""
+    w, view = _view(1203)
+    a = view.decode().clone()
+    torch.cuda.synchronize()
+    qd = to_device_rows(w.q, w.q_fmt)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(3):
+        out = torch.empty_like(qd)
+        # memory freed on the current stream, so a workspace allocated there
+        # would likely be this block, still being written below
+        junk = torch.full((1 << 22,), 0x7F7F7F7F, dtype=torch.int32, device="cuda")
+        del junk
+        busy = torch.full((1 << 22,), 0x01010101, dtype=torch.int32, device="cuda")
+        pk.decode(view.desc, view.kc, view.vc, qd, out, view.bt, view.cl,
+                  int(view.cl_host.max()), float(w.scale), stream=side)
+        busy.add_(1)
+        outs.append(out)
+    side.synchronize()
+    torch.cuda.synchronize()
+    for b in outs:
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
 def test_write_and_decode_replay_from_a_captured_graph():
     w, view = _view(1201)
     B, Hq, Hkv, D = w.B, w.Hq, w.Hkv, w.D

@@ -547,3 +547,44 @@ def test_shared_prefix_decode_validates_groups_on_the_host():
     # lengths, then one record of D + 4 floats per (sequence, query head)
     assert ws_bytes >= pk.decode_workspace_bytes(d, B, Hq, 128) + 4 * B * mb + 8 * B + \
         4 * B * Hq * (128 + 4)
+
+
+def test_binding_rejects_mismatched_tensors_before_any_gpu_call():
+    """The C ABI cannot see tensor extents, so the binding compares them with
+    the descriptor: a cache one block short, a cache of another format, a
+    query of another head_dim, or query heads not a multiple of the KV heads
+    raise ValueError (host tensors here: the checks run before the device
+    test, so nothing reaches the GPU)."""
+    import torch
+    d = pk.CacheDesc(10, 2, 128, "bf16")
+    good = torch.zeros(d.shape, dtype=torch.bfloat16)
+    short = torch.zeros((9, 2, 16, 128), dtype=torch.bfloat16)
+    wrong = torch.zeros(d.shape, dtype=torch.float32)
+    rows = torch.zeros((1, 2, 128), dtype=torch.bfloat16)
+    slots = torch.zeros(1, dtype=torch.int64)
+    with pytest.raises(ValueError, match="bytes"):
+        pk.write_kv(d, short, good, rows, rows, slots)
+    with pytest.raises(ValueError, match="dtype"):
+        pk.write_kv(d, good, wrong, rows, rows, slots)
+    with pytest.raises(ValueError, match="bytes"):
+        pk.copy_blocks(d, good, short, torch.zeros((1, 2), dtype=torch.int32))
+    bt = torch.zeros((1, 4), dtype=torch.int32)
+    cl = torch.ones(1, dtype=torch.int32)
+    q = torch.zeros((1, 4, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="bytes"):
+        pk.decode(d, good, short, q, torch.empty_like(q), bt, cl, 16, 1.0)
+    q64 = torch.zeros((1, 4, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="head_dim"):
+        pk.decode(d, good, good, q64, torch.empty_like(q64), bt, cl, 16, 1.0)
+    q3 = torch.zeros((1, 3, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="multiple"):
+        pk.decode(d, good, good, q3, torch.empty_like(q3), bt, cl, 16, 1.0)
+    qc = torch.zeros((1, 2, 4, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="bytes"):
+        pk.decode_chunk(d, short, good, qc, torch.empty_like(qc), bt, cl, 16, 1.0)
+    with pytest.raises(ValueError, match="bytes"):
+        pk.decode_shared_prefix(d, good, short, q, torch.empty_like(q), bt, cl, 16, 1.0,
+                                np.zeros((0, 3), np.int32))
+    # right extents, host memory: the device test is what fails
+    with pytest.raises(ValueError, match="device tensor"):
+        pk.decode(d, good, good, q, torch.empty_like(q), bt, cl, 16, 1.0)
