@@ -187,6 +187,34 @@ pa_status pa_decode(const pa_cache_desc* c, const void* k_cache,
                     size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_noalloc -- pa_decode without a workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, serving
+ * loops and harnesses that forbid allocation.  Same arguments (minus the
+ * workspace), results (bit for bit: same kernels, same work split) and
+ * errors as pa_decode.
+ *   Scratch: a static device array inside the library, one per GPU, held
+ *   until the process ends: 256 KiB of arrival counters (at most 65536
+ *   sequences x KV heads per call) and 24 MiB of partial results.  A batch
+ *   that needs more returns PA_ERR_WORKSPACE_TOO_SMALL and launches nothing
+ *   (the bf16 / fp8 path needs about 2 * 4 * CUs * G * (head_dim + 2) * 4
+ *   bytes: 17 MiB at G = 16, head_dim 128 on 256 CUs; the fp32 path needs
+ *   num_seqs * num_q_heads * ceil(max_context_len / 512) * (head_dim + 2) * 4
+ *   bytes once a context spans more than one partition).
+ *   The first call on a device looks the array up and clears its counters
+ *   with a fill kernel on `stream`; every completed call leaves them zero.
+ *   The call itself allocates nothing and uses no memset.  All calls on one
+ *   GPU share the array: calls that may overlap on one GPU (different
+ *   streams, or graphs replayed concurrently) race and must be serialised by
+ *   the caller.  Like pa_decode it consumes a pa_time_next_call request.
+ */
+pa_status pa_decode_noalloc(const pa_cache_desc* c, const void* k_cache,
+                            const void* v_cache, const void* q, int32_t q_dtype,
+                            void* out, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t max_context_len, int32_t num_seqs,
+                            int32_t num_q_heads, float scale, void* stream);
+
+/*
  * pa_decode_chunk -- attention of a chunk of chunk_len = T new tokens per
  * sequence (1 <= T <= PA_MAX_CHUNK), as in chunked prefill (ybb.press §7.1,
  * §7.2) and draft-token verification in speculative decoding (ybb.press §9
@@ -428,8 +456,8 @@ pa_status pa_swap_blocks(const pa_cache_desc* c, const void* src_k, const void* 
 size_t pa_read_probe_sink_bytes(int32_t num_cus);
 
 /*
- * pa_time_next_call -- the next pa_decode, pa_decode_chunk or pa_decode_window
- * made on the calling thread launches its kernels through hipExtLaunchKernel
+ * pa_time_next_call -- the next pa_decode, pa_decode_noalloc, pa_decode_chunk
+ * or pa_decode_window made on the calling thread launches its kernels through hipExtLaunchKernel
  * with these events (hipEvent_t, created by the caller; either may be null):
  * start_event is recorded as its first kernel starts, stop_event as its last
  * kernel ends, by the dispatches themselves, so no marker packet sits in the

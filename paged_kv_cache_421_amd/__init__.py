@@ -8,7 +8,7 @@ from __future__ import annotations
 
 from ._lib import LIB_PATH, PagedKVError, lib
 from .api import (BLOCK_SIZE, MAX_CHUNK, PARTITION_TOKENS, BlockManager, CacheDesc,
-                  chunk_workspace_bytes, copy_blocks, decode, decode_chunk,
+                  chunk_workspace_bytes, copy_blocks, decode, decode_chunk, decode_noalloc,
                   decode_workspace_bytes, decode_workspace_init, dtype_code,
                   new_chunk_workspace, new_decode_workspace, read_probe, swap_blocks, write_kv,
                   decode_shared_prefix, new_shared_prefix_workspace,
@@ -16,7 +16,7 @@ from .api import (BLOCK_SIZE, MAX_CHUNK, PARTITION_TOKENS, BlockManager, CacheDe
 
 __all__ = ["LIB_PATH", "PagedKVError", "lib", "BLOCK_SIZE", "MAX_CHUNK", "PARTITION_TOKENS",
            "BlockManager", "CacheDesc", "chunk_workspace_bytes", "copy_blocks", "decode",
-           "decode_chunk", "decode_workspace_bytes", "decode_workspace_init", "dtype_code",
+           "decode_chunk", "decode_noalloc", "decode_workspace_bytes", "decode_workspace_init", "dtype_code",
            "new_chunk_workspace", "new_decode_workspace", "read_probe", "swap_blocks", "write_kv",
            "decode_shared_prefix", "new_shared_prefix_workspace",
            "shared_prefix_workspace_bytes", "time_next_call"]

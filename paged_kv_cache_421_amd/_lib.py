@@ -39,6 +39,8 @@ SIGNATURES = {
                                 c_i32, c_i32, c_i32, c_f32, c_vp, c_sz, c_vp]),
     "pa_decode": (c_i32, [P_desc, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_vp, c_i32,
                           c_i32, c_i32, c_f32, c_vp, c_sz, c_vp]),
+    "pa_decode_noalloc": (c_i32, [P_desc, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_vp,
+                                  c_i32, c_i32, c_i32, c_f32, c_vp]),
     "pa_bm_create": (c_vp, [c_i32, c_i32, c_vp]),
     "pa_bm_create_ex": (c_vp, [c_i32, c_i32, c_vp, c_i32, c_vp]),
     "pa_bm_swap_out": (c_i32, [c_vp, c_vp, c_i32, c_vp, c_i32, c_vp]),

@@ -207,6 +207,24 @@ def decode(desc: CacheDesc, k_cache: torch.Tensor, v_cache: torch.Tensor, q: tor
     return out
 
 
+def decode_noalloc(desc: CacheDesc, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   q: torch.Tensor, out: torch.Tensor, block_tables: torch.Tensor,
+                   context_lens: torch.Tensor, max_context_len: int, scale: float,
+                   stream=None) -> torch.Tensor:
+    """pa_decode_noalloc: pa_decode with the library's static per-GPU scratch
+    instead of a workspace (nothing is allocated; calls that may overlap on
+    one GPU race)."""
+    _queries(desc, q, out, 3)
+    B, Hq, D = q.shape
+    _tables(block_tables, context_lens, B)
+    kc, vc = _caches(desc, k_cache, v_cache)
+    check(lib.pa_decode_noalloc(ctypes.byref(desc.c), kc, vc, _dev(q, "q"), dtype_code(q.dtype),
+                                _dev(out, "out"), _dev(block_tables, "block_tables"),
+                                block_tables.shape[1], _dev(context_lens, "context_lens"),
+                                int(max_context_len), B, Hq, float(scale), _stream(stream)))
+    return out
+
+
 def chunk_workspace_bytes(desc: CacheDesc, num_seqs: int, num_q_heads: int, chunk_len: int,
                           max_context_len: int) -> int:
     """pa_decode_chunk_workspace_bytes: scratch bytes pa_decode_chunk needs."""

@@ -1720,13 +1720,17 @@ int device_cus() {
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-// Fast path workspace: arrival counters, then two partial slots per wave of
-// `rows` query rows each.
-size_t stream_workspace_bytes(int num_seqs, int hkv, int rows, int D) {
+// Fast path scratch: two partial slots per wave of `rows` query rows each.
+size_t stream_partials_bytes(int rows, int D) {
   const size_t waves = static_cast<size_t>(device_cus()) * kWavesPerCU;
   const size_t slot_floats = (static_cast<size_t>(rows) * (D + 2) + 3) & ~static_cast<size_t>(3);
+  return waves * 2 * slot_floats * sizeof(float);
+}
+
+// Fast path workspace: arrival counters, then the partial slots.
+size_t stream_workspace_bytes(int num_seqs, int hkv, int rows, int D) {
   return align256(static_cast<size_t>(num_seqs) * hkv * sizeof(uint32_t)) +
-         waves * 2 * slot_floats * sizeof(float);
+         stream_partials_bytes(rows, D);
 }
 
 size_t general_workspace_bytes(int num_seqs, int num_q_heads, int T, int D, int max_context_len) {
@@ -1758,7 +1762,10 @@ pa_status attend(const char* fn, const pa_cache_desc* c, const void* k_cache,
                  const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs,
                  int32_t num_q_heads, float scale, void* workspace, size_t workspace_bytes,
                  void* stream, const int32_t* prefix_len = nullptr,
-                 const float* prefix_rec = nullptr, CallTiming tm = CallTiming{}) {
+                 const float* prefix_rec = nullptr, CallTiming tm = CallTiming{},
+                 uint32_t* fixed_counters = nullptr) {
+  // fixed_counters: the fast path's arrival counters live there (zero
+  // between calls) and `workspace` holds only the partial results
   pa_status st = check_desc(c, fn);
   if (st != PA_OK) return st;
   const int hkv = c->num_kv_heads, D = c->head_dim, fmt = c->cache_dtype;
@@ -1798,8 +1805,9 @@ pa_status attend(const char* fn, const pa_cache_desc* c, const void* k_cache,
     return fail(PA_ERR_UNSUPPORTED, "%s: num_seqs / chunk_len * num_q_heads above 65535", fn);
   if (fast && (reinterpret_cast<uintptr_t>(out) % 16 != 0 || reinterpret_cast<uintptr_t>(q) % 16 != 0))
     return fail(PA_ERR_INVALID_ARG, "%s: q and out must be 16-byte aligned", fn);
-  const size_t need = fast ? stream_workspace_bytes(num_seqs, hkv, G * tpp, D)
-                           : general_workspace_bytes(num_seqs, num_q_heads, T, D, max_context_len);
+  const size_t need = !fast ? general_workspace_bytes(num_seqs, num_q_heads, T, D, max_context_len)
+                     : fixed_counters ? stream_partials_bytes(G * tpp, D)
+                                      : stream_workspace_bytes(num_seqs, hkv, G * tpp, D);
   if (workspace_bytes < need || (need > 0 && !workspace))
     return fail(PA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes, need %zu", fn,
                 workspace_bytes, need);
@@ -1827,9 +1835,10 @@ pa_status attend(const char* fn, const pa_cache_desc* c, const void* k_cache,
     a.out = static_cast<uint16_t*>(out);
     a.block_tables = block_tables;
     a.context_lens = context_lens;
-    a.counters = static_cast<uint32_t*>(workspace);
-    a.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                          align256(static_cast<size_t>(num_seqs) * hkv * 4));
+    a.counters = fixed_counters ? fixed_counters : static_cast<uint32_t*>(workspace);
+    a.partials = fixed_counters ? static_cast<float*>(workspace)
+                                : reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                           align256(static_cast<size_t>(num_seqs) * hkv * 4));
     a.num_seqs = num_seqs;
     a.hkv = hkv;
     a.max_blocks = max_blocks_per_seq;
@@ -1963,6 +1972,92 @@ extern "C" pa_status pa_decode_window(const pa_cache_desc* c, const void* k_cach
                 block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs,
                 num_q_heads, scale, workspace, workspace_bytes, stream, nullptr, nullptr,
                 take_call_timing());
+}
+
+// ---------------------------------------------------------------------------
+// pa_decode_noalloc: pa_decode with its scratch in a static device array
+// instead of a caller workspace.  Layout: arrival counters of up to
+// kStaticCounters (sequence, KV head) segments, which every completed call
+// leaves at zero, then the partial results (written before they are read).
+namespace {
+constexpr size_t kStaticCounters = size_t{1} << 16;
+constexpr size_t kStaticCounterBytes = kStaticCounters * sizeof(uint32_t);
+constexpr size_t kStaticPartialBytes = size_t{24} << 20;
+}  // namespace
+
+static __device__ __align__(256) char scratch[kStaticCounterBytes + kStaticPartialBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch[kMaxDevices] = {};    // device address of `scratch`, per device
+
+// The current device's address of `scratch`; on the first call for a device
+// it is looked up and its counters are cleared on `st` (a fill kernel, so it
+// precedes the caller's decode on that stream).
+pa_status device_scratch(hipStream_t st, char** base, const char* fn) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess)
+    return fail(PA_ERR_HIP, "%s: hipGetDevice failed", fn);
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PA_ERR_UNSUPPORTED, "%s: device %d (at most %d devices)", fn, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(PA_ERR_HIP, "%s: hipGetSymbolAddress of the static scratch: %s", fn,
+                  hipGetErrorString(e));
+    const int64_t words = static_cast<int64_t>(kStaticCounterBytes / 4);
+    zero_fill_kernel<<<static_cast<unsigned>((words + 255) / 256), 256, 0, st>>>(
+        static_cast<uint32_t*>(p), words);
+    const pa_status ls = launch_status(fn);
+    if (ls != PA_OK) return ls;
+    g_scratch[dev] = static_cast<char*>(p);
+  }
+  *base = g_scratch[dev];
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" pa_status pa_decode_noalloc(const pa_cache_desc* c, const void* k_cache,
+                                       const void* v_cache, const void* q, int32_t q_dtype,
+                                       void* out, const int32_t* block_tables,
+                                       int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                       int32_t max_context_len, int32_t num_seqs,
+                                       int32_t num_q_heads, float scale, void* stream) {
+  const char* fn = "pa_decode_noalloc";
+  pa_status st = check_desc(c, fn);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (num_q_heads % c->num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: %d query heads not a multiple of %d KV heads", fn,
+                num_q_heads, c->num_kv_heads);
+  if (num_seqs == 0) return PA_OK;
+  const int G = num_q_heads / c->num_kv_heads;
+  const bool fast = fast_path(c, q_dtype, G);
+  if (fast && static_cast<size_t>(num_seqs) * c->num_kv_heads > kStaticCounters)
+    return fail(PA_ERR_WORKSPACE_TOO_SMALL,
+                "%s: %d sequences x %d KV heads exceed the static scratch's %zu counters", fn,
+                num_seqs, c->num_kv_heads, kStaticCounters);
+  const size_t need = fast ? stream_partials_bytes(G, c->head_dim)
+                           : general_workspace_bytes(num_seqs, num_q_heads, 1, c->head_dim,
+                                                     max_context_len);
+  if (need > kStaticPartialBytes)
+    return fail(PA_ERR_WORKSPACE_TOO_SMALL,
+                "%s: this batch needs %zu bytes of scratch, the static scratch holds %zu", fn,
+                need, kStaticPartialBytes);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  char* base = nullptr;
+  st = device_scratch(hs, &base, fn);
+  if (st != PA_OK) return st;
+  return attend(fn, c, k_cache, v_cache, q, q_dtype, out, 1, 0, block_tables, max_blocks_per_seq,
+                context_lens, max_context_len, num_seqs, num_q_heads, scale,
+                base + kStaticCounterBytes, kStaticPartialBytes, stream, nullptr, nullptr,
+                take_call_timing(), reinterpret_cast<uint32_t*>(base));
 }
 
 namespace {
