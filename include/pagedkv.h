@@ -272,7 +272,10 @@ pa_status pa_decode_window(const pa_cache_desc* c, const void* k_cache,
  * ------------------------------------------------------------------------- */
 typedef struct pa_bm pa_bm;
 
-/* NULL on invalid arguments (see pa_last_error). */
+/* A pool of num_blocks device blocks of block_size tokens, all free: the
+ * block pool that logical blocks are mapped onto (explore.n1n.ai,
+ * "vLLM 深度解析", 映射机制详解; ybb.press §2.2, block division and
+ * allocation on demand).  NULL on invalid arguments (see pa_last_error). */
 pa_bm* pa_bm_create(int32_t num_blocks, int32_t block_size,
                     const int32_t* free_order);
 /* The same with a pool of num_host_blocks host blocks for swapping
@@ -282,34 +285,49 @@ pa_bm* pa_bm_create_ex(int32_t num_blocks, int32_t block_size,
                        const int32_t* host_free_order);
 void pa_bm_destroy(pa_bm* bm);
 
+/* A new sequence with an empty block table (ybb.press §6: the block manager
+ * allocates a new prompt's blocks; they are taken as tokens are appended). */
 pa_status pa_bm_add_seq(pa_bm* bm, int64_t seq_id);
-/* child shares all of parent's blocks (each gains one reference). */
+/* child shares all of parent's blocks (each gains one reference): samples of
+ * one prompt start from the same block table, with reference counts on the
+ * shared blocks (ybb.press §2.3, copy-on-write and parallel sampling). */
 pa_status pa_bm_fork(pa_bm* bm, int64_t parent_id, int64_t child_id);
 /* Append one token: *slot receives its cache slot; *cow_src / *cow_dst
- * receive the copy pair, or -1 / -1 when no copy is needed. */
+ * receive the copy pair, or -1 / -1 when no copy is needed.  Each decode
+ * iteration writes the new token's KV into its block, then checks whether a
+ * new block is needed (ybb.press §6); a block is taken only when the
+ * sequence needs it (§2.2, allocation on demand); a shared block is copied
+ * before it is modified (§2.3). */
 pa_status pa_bm_append_slot(pa_bm* bm, int64_t seq_id, int64_t* slot,
                             int32_t* cow_src, int32_t* cow_dst);
-/* Append n >= 0 tokens: slots[n]; at most one copy pair (the first token). */
+/* Append n >= 0 tokens (a prompt, or several decode steps; ybb.press §6):
+ * slots[n]; at most one copy pair (the first token, ybb.press §2.3). */
 pa_status pa_bm_append_tokens(pa_bm* bm, int64_t seq_id, int32_t n,
                               int64_t* slots, int32_t* cow_src,
                               int32_t* cow_dst);
-/* One decode step for a batch: append one token to each of seq_ids[0..n-1],
- * in order.  slots[n] receive the slots; cow_pairs[2*k], cow_pairs[2*k+1]
+/* One decode step for a batch (ybb.press §6, the decode loop of the running
+ * batch): append one token to each of seq_ids[0..n-1], in order.  slots[n] receive the slots; cow_pairs[2*k], cow_pairs[2*k+1]
  * the k-th copy pair (room for n pairs); *num_pairs their count.  All or
  * nothing across the whole batch. */
 pa_status pa_bm_append_batch(pa_bm* bm, const int64_t* seq_ids, int32_t n,
                              int64_t* slots, int32_t* cow_pairs,
                              int32_t* num_pairs);
+/* A finished sequence gives back its references; blocks whose count reaches
+ * zero return to the pool at once (ybb.press §2.2, blocks are reclaimed as
+ * soon as a sequence ends). */
 pa_status pa_bm_free_seq(pa_bm* bm, int64_t seq_id);
 
 /* Blocks an allocation can take (free, plus evictable with prefix caching). */
 int32_t pa_bm_num_free(const pa_bm* bm);
-/* Reference count of `block`, or -1 if out of range. */
+/* Reference count of `block`, or -1 if out of range (the counts copy-on-write
+ * tests, ybb.press §2.3). */
 int32_t pa_bm_refcount(const pa_bm* bm, int32_t block);
 /* Context length of a sequence in *len. */
 pa_status pa_bm_length(const pa_bm* bm, int64_t seq_id, int32_t* len);
 /* Pack tables of seq_ids[0..n-1]: block_tables[n][cap] padded with -1,
- * context_lens[n].  Host memory. */
+ * context_lens[n].  Host memory.  These are the per-sequence block tables
+ * (logical block -> physical block, explore.n1n.ai, "vLLM 深度解析",
+ * 映射机制详解) and lengths that pa_decode reads. */
 pa_status pa_bm_pack(const pa_bm* bm, const int64_t* seq_ids, int32_t n,
                      int32_t* block_tables, int32_t cap, int32_t* context_lens);
 

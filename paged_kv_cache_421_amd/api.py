@@ -11,6 +11,7 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 import torch
 
+from . import _lib as _libmod
 from ._lib import CacheDescC, PagedKVError, check, lib
 
 BLOCK_SIZE = 16
@@ -380,7 +381,7 @@ class BlockManager:
     def __init__(self, num_blocks: int, free_order: Optional[Sequence[int]] = None,
                  num_host_blocks: int = 0, host_free_order: Optional[Sequence[int]] = None,
                  block_size: int = BLOCK_SIZE):
-        self._lib = lib                      # kept alive for __del__ at interpreter exit
+        self._lib = _libmod.host_lib   # kept alive for __del__ at interpreter exit
         self._order = self._horder = None
         ptr = hptr = ctypes.c_void_p(0)
         if free_order is not None:
@@ -389,13 +390,16 @@ class BlockManager:
         if host_free_order is not None:
             self._horder = np.ascontiguousarray(host_free_order, dtype=np.int32)
             hptr = _ptr(self._horder)
-        h = lib.pa_bm_create_ex(int(num_blocks), int(block_size), ptr, int(num_host_blocks), hptr)
+        h = self._lib.pa_bm_create_ex(int(num_blocks), int(block_size), ptr, int(num_host_blocks), hptr)
         if not h:
-            raise PagedKVError(-1, lib.pa_last_error().decode())
+            raise PagedKVError(-1, self._lib.pa_last_error().decode())
         self._h = ctypes.c_void_p(h)
         self.num_blocks = int(num_blocks)
         self.num_host_blocks = int(num_host_blocks)
         self.block_size = int(block_size)
+
+    def _check(self, status: int) -> None:
+        check(status, self._lib)
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -407,26 +411,26 @@ class BlockManager:
         ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
         pairs = np.empty((max(cap, 1), 2), dtype=np.int32)
         n = ctypes.c_int32()
-        check(fn(self._h, _ptr(ids), len(ids), _ptr(pairs), cap, ctypes.byref(n)))
+        self._check(fn(self._h, _ptr(ids), len(ids), _ptr(pairs), cap, ctypes.byref(n)))
         return pairs[:n.value].copy()
 
     def swap_out(self, seq_ids) -> np.ndarray:
         """pa_bm_swap_out: (device block, host block) pairs, int32 [k, 2]."""
-        return self._move(lib.pa_bm_swap_out, seq_ids, self.num_host_blocks)
+        return self._move(self._lib.pa_bm_swap_out, seq_ids, self.num_host_blocks)
 
     def swap_in(self, seq_ids) -> np.ndarray:
         """pa_bm_swap_in: (host block, device block) pairs, int32 [k, 2]."""
-        return self._move(lib.pa_bm_swap_in, seq_ids, self.num_blocks)
+        return self._move(self._lib.pa_bm_swap_in, seq_ids, self.num_blocks)
 
     def enable_prefix_caching(self) -> None:
-        check(lib.pa_bm_enable_prefix_caching(self._h))
+        self._check(self._lib.pa_bm_enable_prefix_caching(self._h))
 
     def add_seq_prompt(self, seq: int, tokens):
         """pa_bm_add_seq_prompt: (slots int64 [n], num_cached)."""
         toks = np.ascontiguousarray(tokens, dtype=np.int32)
         slots = np.empty(max(len(toks), 1), dtype=np.int64)
         nc = ctypes.c_int32()
-        check(lib.pa_bm_add_seq_prompt(self._h, int(seq), _ptr(toks), len(toks), _ptr(slots),
+        self._check(self._lib.pa_bm_add_seq_prompt(self._h, int(seq), _ptr(toks), len(toks), _ptr(slots),
                                        ctypes.byref(nc)))
         return slots[:len(toks)], nc.value
 
@@ -435,7 +439,7 @@ class BlockManager:
         toks = np.ascontiguousarray(tokens, dtype=np.int32)
         slots = np.empty(max(len(toks), 1), dtype=np.int64)
         src, dst = ctypes.c_int32(), ctypes.c_int32()
-        check(lib.pa_bm_append_token_ids(self._h, int(seq), _ptr(toks), len(toks), _ptr(slots),
+        self._check(self._lib.pa_bm_append_token_ids(self._h, int(seq), _ptr(toks), len(toks), _ptr(slots),
                                          ctypes.byref(src), ctypes.byref(dst)))
         return slots[:len(toks)], (None if src.value < 0 else (src.value, dst.value))
 
@@ -443,7 +447,7 @@ class BlockManager:
         """(queried blocks, hit blocks, registered blocks, evictable blocks)."""
         q, h = ctypes.c_int64(), ctypes.c_int64()
         r, e = ctypes.c_int32(), ctypes.c_int32()
-        check(lib.pa_bm_cache_stats(self._h, ctypes.byref(q), ctypes.byref(h), ctypes.byref(r),
+        self._check(self._lib.pa_bm_cache_stats(self._h, ctypes.byref(q), ctypes.byref(h), ctypes.byref(r),
                                     ctypes.byref(e)))
         return q.value, h.value, r.value, e.value
 
@@ -453,38 +457,38 @@ class BlockManager:
         cap = max(len(ids) // 2, 1)
         out = np.empty((cap, 3), dtype=np.int32)
         n = ctypes.c_int32()
-        check(lib.pa_bm_shared_prefix_groups(self._h, _ptr(ids), len(ids), _ptr(out), cap,
+        self._check(self._lib.pa_bm_shared_prefix_groups(self._h, _ptr(ids), len(ids), _ptr(out), cap,
                                              ctypes.byref(n)))
         return out[:n.value].copy()
 
     def num_free_host(self) -> int:
-        return int(lib.pa_bm_num_free_host(self._h))
+        return int(self._lib.pa_bm_num_free_host(self._h))
 
     def host_refcount(self, block: int) -> int:
-        return int(lib.pa_bm_host_refcount(self._h, int(block)))
+        return int(self._lib.pa_bm_host_refcount(self._h, int(block)))
 
     def is_swapped(self, seq: int) -> bool:
         v = ctypes.c_int32()
-        check(lib.pa_bm_is_swapped(self._h, int(seq), ctypes.byref(v)))
+        self._check(self._lib.pa_bm_is_swapped(self._h, int(seq), ctypes.byref(v)))
         return bool(v.value)
 
     def add_seq(self, seq: int) -> None:
-        check(lib.pa_bm_add_seq(self._h, int(seq)))
+        self._check(self._lib.pa_bm_add_seq(self._h, int(seq)))
 
     def fork(self, parent: int, child: int) -> None:
-        check(lib.pa_bm_fork(self._h, int(parent), int(child)))
+        self._check(self._lib.pa_bm_fork(self._h, int(parent), int(child)))
 
     def append_slot(self, seq: int):
         slot = ctypes.c_int64()
         src, dst = ctypes.c_int32(), ctypes.c_int32()
-        check(lib.pa_bm_append_slot(self._h, int(seq), ctypes.byref(slot), ctypes.byref(src),
+        self._check(self._lib.pa_bm_append_slot(self._h, int(seq), ctypes.byref(slot), ctypes.byref(src),
                                     ctypes.byref(dst)))
         return slot.value, (None if src.value < 0 else (src.value, dst.value))
 
     def append_tokens(self, seq: int, n: int):
         slots = np.empty(max(int(n), 1), dtype=np.int64)
         src, dst = ctypes.c_int32(), ctypes.c_int32()
-        check(lib.pa_bm_append_tokens(self._h, int(seq), int(n), _ptr(slots), ctypes.byref(src),
+        self._check(self._lib.pa_bm_append_tokens(self._h, int(seq), int(n), _ptr(slots), ctypes.byref(src),
                                       ctypes.byref(dst)))
         return slots[:int(n)], (None if src.value < 0 else (src.value, dst.value))
 
@@ -499,22 +503,22 @@ class BlockManager:
         if pairs is None:
             pairs = np.empty((max(n, 1), 2), dtype=np.int32)
         npairs = ctypes.c_int32()
-        check(lib.pa_bm_append_batch(self._h, _ptr(ids), n, _ptr(slots), _ptr(pairs),
+        self._check(self._lib.pa_bm_append_batch(self._h, _ptr(ids), n, _ptr(slots), _ptr(pairs),
                                      ctypes.byref(npairs)))
         return slots[:n], pairs[:npairs.value]
 
     def free_seq(self, seq: int) -> None:
-        check(lib.pa_bm_free_seq(self._h, int(seq)))
+        self._check(self._lib.pa_bm_free_seq(self._h, int(seq)))
 
     def num_free(self) -> int:
-        return int(lib.pa_bm_num_free(self._h))
+        return int(self._lib.pa_bm_num_free(self._h))
 
     def refcount(self, block: int) -> int:
-        return int(lib.pa_bm_refcount(self._h, int(block)))
+        return int(self._lib.pa_bm_refcount(self._h, int(block)))
 
     def length(self, seq: int) -> int:
         n = ctypes.c_int32()
-        check(lib.pa_bm_length(self._h, int(seq), ctypes.byref(n)))
+        self._check(self._lib.pa_bm_length(self._h, int(seq), ctypes.byref(n)))
         return n.value
 
     def pack(self, seq_ids, cap: int, block_tables: Optional[np.ndarray] = None,
@@ -526,6 +530,6 @@ class BlockManager:
             block_tables = np.empty((n, cap), dtype=np.int32)
         if context_lens is None:
             context_lens = np.empty(n, dtype=np.int32)
-        check(lib.pa_bm_pack(self._h, _ptr(ids), n, _ptr(block_tables), int(cap),
+        self._check(self._lib.pa_bm_pack(self._h, _ptr(ids), n, _ptr(block_tables), int(cap),
                              _ptr(context_lens)))
         return block_tables, context_lens

@@ -15,6 +15,7 @@
 
 #include <cmath>
 
+#include "debug_checks.h"
 #include "device_common.h"
 #include "status.h"
 
@@ -138,6 +139,7 @@ extern "C" pa_status pa_write_kv(const pa_cache_desc* c, void* k_cache, void* v_
   if (num_tokens == 0) return PA_OK;
   if (!k_cache || !v_cache || !k || !v || !slot_mapping)
     return fail(PA_ERR_INVALID_ARG, "pa_write_kv: null pointer");
+  PA_DEBUG_CHECK(debug::check_slots(c, slot_mapping, num_tokens, stream, "pa_write_kv"));
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int hkv = c->num_kv_heads, d = c->head_dim;
   const int elems = (src_dtype == PA_F32) ? 4 : 8;
@@ -179,6 +181,7 @@ extern "C" pa_status pa_copy_blocks(const pa_cache_desc* c, void* k_cache, void*
     return fail(PA_ERR_UNSUPPORTED, "pa_copy_blocks: %d pairs (at most 65535 per call)",
                 num_pairs);
   if (!k_cache || !v_cache || !pairs) return fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: null pointer");
+  PA_DEBUG_CHECK(debug::check_pairs(pairs, num_pairs, c->num_blocks, stream, "pa_copy_blocks"));
   const int64_t block_bytes = static_cast<int64_t>(c->num_kv_heads) * c->block_size *
                               c->head_dim * dtype_bytes(c->cache_dtype);
   const int64_t chunks = block_bytes / 16;
@@ -231,6 +234,8 @@ extern "C" pa_status pa_swap_blocks(const pa_cache_desc* c, const void* src_k,
     if (!gpu_addressable(ptrs[i]))
       return fail(PA_ERR_INVALID_ARG,
                   "pa_swap_blocks: %s is not device or pinned host memory", names[i]);
+  // the pools' sizes are not passed, so only signs and distinct destinations
+  PA_DEBUG_CHECK(debug::check_pairs(pairs, num_pairs, -1, stream, "pa_swap_blocks"));
   const int64_t block_bytes = static_cast<int64_t>(c->num_kv_heads) * c->block_size *
                               c->head_dim * dtype_bytes(c->cache_dtype);
   const int64_t chunks = block_bytes / 16;

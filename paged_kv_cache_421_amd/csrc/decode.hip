@@ -11,9 +11,10 @@
 // KV tile is read once.
 //
 // Decode reads every KV byte once and does 2*G flops per KV element, so it
-// is bound by HBM bandwidth (ybb.press §7: decode is memory-bound).
+// is bound by HBM bandwidth (ybb.press §9, 九、前沿进展与未来展望, item 4: decode
+// is the memory-bound phase).
 //
-// Fast path (bf16 or fp8 cache, bf16 q, head_dim 64/128, G <= 8):
+// Fast path (bf16 or fp8 cache, bf16 q, head_dim 64/128, G <= 16):
 //  * Work unit: a tile = one 16-token block of one KV head (16 x D elements
 //    of K and of V, contiguous in the cache).  The tiles of all sequences
 //    form one ordered list, (sequence, KV head, block) with the block index
@@ -59,6 +60,7 @@
 #include <utility>
 #include <vector>
 
+#include "debug_checks.h"
 #include "device_common.h"
 #include "status.h"
 
@@ -1813,6 +1815,8 @@ pa_status attend(const char* fn, const pa_cache_desc* c, const void* k_cache,
                 workspace_bytes, need);
   if (need > 0 && reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
     return fail(PA_ERR_INVALID_ARG, "%s: workspace not 16-byte aligned", fn);
+  PA_DEBUG_CHECK(debug::check_tables(c, block_tables, max_blocks_per_seq, context_lens,
+                                     max_context_len, num_seqs, stream, fn));
 
   const float kscale = (fmt == PA_FP8_E4M3) ? c->k_scale : 1.f;
   const float vscale = (fmt == PA_FP8_E4M3) ? c->v_scale : 1.f;
@@ -2165,6 +2169,10 @@ extern "C" pa_status pa_decode_shared_prefix(
     return fail(PA_ERR_INVALID_ARG, "%s: workspace not 256-byte aligned", fn);
   if (!k_cache || !v_cache || !q || !out || !block_tables || !context_lens)
     return fail(PA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  PA_DEBUG_CHECK(debug::check_tables(c, block_tables, max_blocks_per_seq, context_lens,
+                                     max_context_len, num_seqs, stream, fn));
+  PA_DEBUG_CHECK(debug::check_groups(block_tables, max_blocks_per_seq, num_seqs, groups,
+                                     num_groups, stream, fn));
   char* ws = static_cast<char*>(workspace);
   int32_t* suf_tables = reinterpret_cast<int32_t*>(ws + L.tables);
   int32_t* suf_lens = reinterpret_cast<int32_t*>(ws + L.lens);

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
+#include "debug_checks.h"
 #include "status.h"
 
 namespace pagedkv {
@@ -68,6 +69,7 @@ extern "C" pa_status pa_read_probe(const void* buf, size_t bytes, const int32_t*
   if (chunks == 0) return PA_OK;
   if (chunks >= (int64_t{1} << 31))
     return fail(PA_ERR_UNSUPPORTED, "pa_read_probe: buffer too large");
+  if (chunk_order) PA_DEBUG_CHECK(debug::check_order(chunk_order, chunks, stream, "pa_read_probe"));
   // 8 waves per compute unit: two 4-wave blocks per CU
   const unsigned blocks = static_cast<unsigned>(num_cus) * 2;
   read_probe_kernel<<<blocks, 256, 0, static_cast<hipStream_t>(stream)>>>(

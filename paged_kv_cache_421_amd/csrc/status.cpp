@@ -19,4 +19,8 @@ pa_status fail(pa_status s, const char* fmt, ...) {
 
 extern "C" const char* pa_last_error(void) { return pagedkv::g_last_error; }
 
+#ifdef PA_DEBUG
+extern "C" const char* pa_version(void) { return "pagedkv 0.1 (gfx950, PA_DEBUG)"; }
+#else
 extern "C" const char* pa_version(void) { return "pagedkv 0.1 (gfx950)"; }
+#endif

@@ -15,6 +15,9 @@ from tests._oracle_setup import cow_flow_slots
 pk = pytest.importorskip("paged_kv_cache_421_amd")
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "pagedkv.h")
+# the random-script tests run SCRIPT_SCALE times as many operations (the
+# sanitizer run of tests/test_block_manager_sanitized.py raises it)
+SCRIPT_SCALE = int(os.environ.get("PAGEDKV_SCRIPT_SCALE", "1"))
 
 
 def _declared():
@@ -192,7 +195,7 @@ def test_cpp_manager_matches_oracle_under_random_scripts(seed):
     ref = oracle.RefBlockManager(N, free_order=order)
     cpp = pk.BlockManager(N, free_order=order)
     live, nxt = [], 0
-    for step in range(4000):
+    for step in range(4000 * SCRIPT_SCALE):
         r = int(rng.integers(0, 12))
         pick = live[int(rng.integers(len(live)))] if live else 0
         if r == 0 or not live:
@@ -346,7 +349,7 @@ def test_cpp_manager_matches_oracle_with_swapping(seed):
     ref = oracle.RefBlockManager(N, free_order=order, num_host_blocks=H, host_free_order=horder)
     cpp = pk.BlockManager(N, free_order=order, num_host_blocks=H, host_free_order=horder)
     live, nxt = [], 0
-    for step in range(3000):
+    for step in range(3000 * SCRIPT_SCALE):
         r = int(rng.integers(0, 12))
         pick = live[int(rng.integers(len(live)))] if live else 0
         if r == 0 or not live:
@@ -437,7 +440,7 @@ def test_cpp_prefix_cache_matches_oracle_under_random_scripts(seed, bs):
     cpp.enable_prefix_caching()
     prefixes = [[int(x) for x in rng.integers(-5, 40, int(rng.integers(0, 90)))] for _ in range(5)]
     live, nxt = [], 0
-    for step in range(2500):
+    for step in range(2500 * SCRIPT_SCALE):
         r = int(rng.integers(0, 12))
         pick = live[int(rng.integers(len(live)))] if live else 0
         if r <= 3 or not live:
@@ -588,3 +591,14 @@ def test_binding_rejects_mismatched_tensors_before_any_gpu_call():
     # right extents, host memory: the device test is what fails
     with pytest.raises(ValueError, match="device tensor"):
         pk.decode(d, good, good, q, torch.empty_like(q), bt, cl, 16, 1.0)
+
+
+def test_debug_build_loads_and_exports_every_declared_function():
+    """libpagedkv_debug.so is the same library built with PA_DEBUG (host-side
+    checks of the values inside device arrays); it loads without a GPU and
+    exports the same C ABI."""
+    from paged_kv_cache_421_amd import _lib
+    dbg = _lib.load_library(_lib.DEBUG_LIB_PATH)
+    for n in _declared():
+        assert hasattr(dbg, n), n
+    assert b"PA_DEBUG" in dbg.pa_version() and b"PA_DEBUG" not in pk.lib.pa_version()
