@@ -100,11 +100,13 @@ take the partition path.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers N]
                       [--chunk T | --swap | --prefix] [--window W]
-                      [--block-size BS] [--no-cpu-baseline]
-                      [--copy-calibration MIB]
+                      [--block-size BS] [--kv-dtype bf16|fp8] [--no-cpu-baseline]
+                      [--copy-calibration MIB] [--probe-calibration MIB]
 
---copy-calibration MIB ends the run with plain device copies of MIB MiB, the
-reference a hardware-counter run scales FETCH_SIZE / WRITE_SIZE by.
+--copy-calibration MIB ends the run with plain device copies of MIB MiB (the
+reference a hardware-counter run scales WRITE_SIZE by); --probe-calibration
+MIB with pa_read_probe passes over MIB MiB, read with the decode kernel's own
+load form (the reference FETCH_SIZE is scaled by).
 """
 from __future__ import annotations
 
@@ -864,6 +866,10 @@ def main():
                          "cache, written from the same bf16 rows by pa_write_kv)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
+    ap.add_argument("--probe-calibration", type=int, default=0, metavar="MIB",
+                    help="end with 3 pa_read_probe passes over MIB MiB in address order: a "
+                         "known byte count read with the decode kernel's load form, the "
+                         "reference FETCH_SIZE is scaled by")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); the decode path "
@@ -1197,6 +1203,15 @@ def main():
         res["stream_read_probe"] = {"in_order_gbps": seq_gbps, "random_4k_gbps": rnd_gbps,
                                     "decode_frac_of_random_4k": round(achieved / rnd_gbps, 4)}
         _log(f"bench: read probe {seq_gbps} GB/s in order, {rnd_gbps} GB/s random 4 KiB chunks")
+    if args.probe_calibration > 0:
+        n = args.probe_calibration << 20
+        buf = torch.ones(n, dtype=torch.uint8, device=dev)
+        sink = pk.read_probe(buf, stream=stream)
+        for _ in range(3):
+            pk.read_probe(buf, None, sink, stream=stream)
+        torch.cuda.synchronize()
+        del buf, sink
+        _log(f"bench: probe calibration {n} bytes x 3 (+1 warm)")
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)

@@ -370,6 +370,9 @@ decode_stream_kernel(StreamArgs a) {
   const int t_row = a.t_first + (row_ok ? row / G : 0);
   const int h_row = row_ok ? row - (row / G) * G : 0;
   const int mshift = a.causal ? nchunk - 1 - t_row : 0;
+  // the largest shift of the pass (its first chunk token): a tile with at
+  // least 16 + mshift_max rows to the context's end masks nothing
+  const int mshift_max = a.causal ? nchunk - 1 - a.t_first : 0;
   const int q_bytes = ((nchunk - 1) * hq + G) * kD * 2;            // one segment's q rows
   const int64_t q_all_bytes = static_cast<int64_t>(a.q_total_rows) * hq * kD * 2;
   // q in the B-operand layout, dims matching K's: bf16 step kk, quad q
@@ -455,11 +458,16 @@ decode_stream_kernel(StreamArgs a) {
   // of the B operand of the 16x16x16 MFMA that forms P.V.  m_ref is the
   // reference max of the row, the same in its four lanes (kNoMax while the
   // row has seen no position: masked logits then still weigh exactly 0);
-  // l_part is this lane's share of the exponent sum; oacc[c][r] =
+  // lacc holds the row's exponent sum (every element: it is formed by an
+  // MFMA of the rounded weights with an all-ones operand); oacc[c][r] =
   // O[query row][16*c + 4*quad + r].
   bf16x8_t qa[kKK];
-  float m_ref = kNoMax, l_part = 0.f;
+  float m_ref = kNoMax;
+  f32x4_t lacc = {0.f, 0.f, 0.f, 0.f};
   f32x4_t oacc[kVC];
+  // A operand of the exponent-sum MFMA: bf16 1.0 in every element, so
+  // D[i][row] = sum over the tile's tokens of the row's rounded weights
+  const s16x4_t ones = {0x3F80, 0x3F80, 0x3F80, 0x3F80};
   int pend_s[2] = {-1, -1}, pend_g[2] = {0, 0}, pend_seg[2] = {0, 0}, pend_nb[2] = {0, 0};
 
   auto slot_ptr = [&](int wave, int seg) -> int64_t {       // byte offset of a partial slot
@@ -488,9 +496,7 @@ decode_stream_kernel(StreamArgs a) {
   };
 
   auto finalize = [&](int s, int g, int seg, int nb) {
-    float l_tot = l_part;
-    l_tot += __shfl_xor(l_tot, 16);
-    l_tot += __shfl_xor(l_tot, 32);
+    float l_tot = lacc[0];
     const int wf = seg / per;
     const int wl = (seg + nb - 1) / per;
     if (wf == wl && a.rec_out != nullptr) {   // group pass: the member rows' records
@@ -872,7 +878,7 @@ decode_stream_kernel(StreamArgs a) {
       const int rows_left = static_cast<int>(info & 31u);   // min(31, L - 16j)
       if (info & 32u) {                                      // a piece starts here
         m_ref = kNoMax;
-        l_part = 0.f;
+        lacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < kVC; ++c) oacc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -898,19 +904,24 @@ decode_stream_kernel(StreamArgs a) {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qa[kk], acc, 0, 0, 0);
       }
       float x[4];
-      const int lim = rows_left - mshift;                    // tile rows this query row may see
-      // window start: tile rows below `lo` are cut (never, without a window)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[r] = acc[r] * a.logit_scale;
+      // Masks.  Only a tile that reaches the context's end (less the causal
+      // shift), or one a window start cuts, has rows a query row may not
+      // see; a wave-uniform test skips the masking for every other tile.
       const uint32_t wcode =
           static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(d[2]))) >> kSeqBits;
-      int lo = -kTile;
-      if (wcode != 0u) {
-        const int j_local = t_begin + done + t - __builtin_amdgcn_readfirstlane(static_cast<int>(d[3]));
-        lo = static_cast<int>(wcode) - (kTile + 1) + t_row - kTile * j_local;
-      }
+      if (wcode != 0u || rows_left - mshift_max < kTile) {
+        const int lim = rows_left - mshift;                  // tile rows this query row may see
+        // window start: tile rows below `lo` are cut (never, without a window)
+        int lo = -kTile;
+        if (wcode != 0u) {
+          const int j_local = t_begin + done + t - __builtin_amdgcn_readfirstlane(static_cast<int>(d[3]));
+          lo = static_cast<int>(wcode) - (kTile + 1) + t_row - kTile * j_local;
+        }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        x[r] = acc[r] * a.logit_scale;
-        if (4 * quad + r >= lim || 4 * quad + r < lo) x[r] = -INFINITY;
+        for (int r = 0; r < 4; ++r)
+          if (4 * quad + r >= lim || 4 * quad + r < lo) x[r] = -INFINITY;
       }
 
       // ---- lazy running max: moved only when a logit exceeds it by more
@@ -922,7 +933,7 @@ decode_stream_kernel(StreamArgs a) {
         mt = fmaxf(mt, __shfl_xor(mt, 32));                   // max over the head's 16 tokens
         const float mn = (mt > m_ref + kRescaleSlack) ? mt : m_ref;
         const float alpha = __builtin_amdgcn_exp2f(m_ref - mn);
-        l_part *= alpha;
+        lacc[0] *= alpha;
 #pragma unroll
         for (int c = 0; c < kVC; ++c)
 #pragma unroll
@@ -930,14 +941,17 @@ decode_stream_kernel(StreamArgs a) {
         m_ref = mn;
       }
 
-      // ---- P in bf16 (the sum takes the rounded values, so the weights the
-      // MFMA applies are exactly normalised), then O^T += V^T P^T
-      bf16x4_t pb;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pb[r] = static_cast<__bf16>(__builtin_amdgcn_exp2f(x[r] - m_ref));
-        l_part += static_cast<float>(pb[r]);
-      }
+      // ---- P in bf16, two weights per conversion; the exponent sum takes the
+      // rounded values (one MFMA against the all-ones operand), so the
+      // weights the P.V MFMA applies are exactly normalised
+      const bf16x2_t p01 = __builtin_convertvector(
+          (f32x2_t{__builtin_amdgcn_exp2f(x[0] - m_ref), __builtin_amdgcn_exp2f(x[1] - m_ref)}),
+          bf16x2_t);
+      const bf16x2_t p23 = __builtin_convertvector(
+          (f32x2_t{__builtin_amdgcn_exp2f(x[2] - m_ref), __builtin_amdgcn_exp2f(x[3] - m_ref)}),
+          bf16x2_t);
+      const bf16x4_t pb = {p01[0], p01[1], p23[0], p23[1]};
+      lacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, __builtin_bit_cast(s16x4_t, pb), lacc, 0, 0, 0);
       // V rows through LDS: rows past the context were read as zeros
 #pragma unroll
       for (int i = 0; i < kVLoads; ++i) {
