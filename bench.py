@@ -191,7 +191,7 @@ def kernel_source_sha256():
     """Hash of the decode kernel's device code: the text from the kernel's
     signature line to the end of its body in decode.hip."""
     text = open(DECODE_SRC).read()
-    a = text.index("decode_stream_kernel(StreamArgs a) {")
+    a = text.index("decode_stream_kernel(StreamArgs a")
     b = text.index("// Zero-fill of a decode workspace.")
     return hashlib.sha256(text[a:b].encode()).hexdigest()
 

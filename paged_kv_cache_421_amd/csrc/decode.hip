@@ -128,20 +128,24 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int b
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, kRsrcWord3);
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
+// Inclusive prefix sum over the 64 lanes of a wave, by DPP operand moves
+// (register-to-register, no LDS round trips): shifts right by 1, 2, 4 and 8
+// lanes inside each 16-lane row (lanes shifted in from outside the row add
+// 0), then lane 15's total is added to rows 1 and 3 and lane 31's to rows 2
+// and 3.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  constexpr int kRowShr = 0x110, kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+  x += __builtin_amdgcn_update_dpp(0, x, kRowShr + 1, 0xf, 0xf, true);
+  x += __builtin_amdgcn_update_dpp(0, x, kRowShr + 2, 0xf, 0xf, true);
+  x += __builtin_amdgcn_update_dpp(0, x, kRowShr + 4, 0xf, 0xf, true);
+  x += __builtin_amdgcn_update_dpp(0, x, kRowShr + 8, 0xf, 0xf, true);
+  x += __builtin_amdgcn_update_dpp(0, x, kRowBcast15, 0xa, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, kRowBcast31, 0xc, 0xf, false);
   return x;
 }
 // Sum over the 64 lanes of a wave, as a wave-uniform value.
 __device__ __forceinline__ int wave_sum(int x) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d);
-  return __builtin_amdgcn_readfirstlane(x);
+  return __builtin_amdgcn_readlane(wave_incl_scan(x), 63);
 }
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS
 // operations, then for the other waves; global loads stay in flight (a
@@ -233,11 +237,35 @@ struct StreamArgs {
   const int32_t* rec_count;
 };
 
+// Groups of a shared-prefix batch decoded in one launch (kGrp): group k is
+// sequences first[k] .. first[k] + count[k] - 1, whose first shared[k]
+// table entries name the same blocks.  Entries k >= num are all zero.
+struct GroupTable {
+  int num;
+  int first[PA_MAX_PREFIX_GROUPS];
+  int count[PA_MAX_PREFIX_GROUPS];
+  int shared[PA_MAX_PREFIX_GROUPS];
+};
+struct NoGroupTable {
+  int num;
+};
+
 // kD: head_dim; kFp8: E4M3 cache (else bf16); kAux: cache policy bits of the
-// KV loads.
-template <int kD, bool kFp8, int kAux, bool kPair>
+// KV loads; kPair: 8-token blocks; kGrp: shared-prefix groups in one launch.
+//
+// kGrp (at most 256 sequences, single-token decode, block size a multiple
+// of 16): a group is one segment per KV head -- the tiles of the shared
+// prefix, then each member's own tiles past it -- with the members' query
+// rows (member t, head h: row t * G + h, q rows one sequence apart) as the
+// pass's rows.  Every member row sees the prefix tiles (up to its own
+// length), a member's own tiles are seen by its rows only, so each row's
+// result is its sequence's attention over its whole context; the segment is
+// split between waves and merged like any other.  Sequences outside groups
+// are segments of their own, written for one sequence's rows.
+template <int kD, bool kFp8, int kAux, bool kPair, bool kGrp = false>
 __global__ void __launch_bounds__(64 * kWavesPerGroup)
-decode_stream_kernel(StreamArgs a) {
+decode_stream_kernel(StreamArgs a,
+                     typename std::conditional<kGrp, GroupTable, NoGroupTable>::type gt) {
   constexpr int kE = kFp8 ? 1 : 2;                 // bytes per cache element
   constexpr int kRowBytes = kD * kE;
   constexpr int kTileBytes = kTile * kRowBytes;
@@ -280,14 +308,89 @@ decode_stream_kernel(StreamArgs a) {
 #pragma unroll
   for (int r = 0; r < 4; ++r)
     Lr[r] = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(lens_rsrc, (64 * r + lane) * 4, 0, 0));
+
+  // kGrp: the group table in LDS, each sequence's group (Gid, -1 for none)
+  // and the tiles per KV head of the segment it starts (Ur: a group's
+  // leader counts the prefix and every member's own tiles, the other
+  // members 0, a sequence outside groups its own tiles)
+  __shared__ int s_gt_all[kWavesPerGroup][3][kGrp ? PA_MAX_PREFIX_GROUPS : 1];
+  __shared__ short s_gid_all[kWavesPerGroup][kGrp ? 256 : 1];
+  int (&s_gt)[3][kGrp ? PA_MAX_PREFIX_GROUPS : 1] = s_gt_all[wig];
+  short* s_gid = s_gid_all[wig];
+  int Gid[4] = {-1, -1, -1, -1}, Ur[4] = {0, 0, 0, 0};
+  const int tile_shift = a.sub_shift;                      // block tiles = 1 << tile_shift
+  if constexpr (kGrp) {
+    // all PA_MAX_PREFIX_GROUPS entries, two per lane, read without waiting
+    // for gt.num (entries past it are zero: count 0 marks nothing), so the
+    // reads overlap the length loads
+    static_assert(PA_MAX_PREFIX_GROUPS == 128, "two group-table entries per lane");
+    int gf[2], gc[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int i = 64 * e + lane;
+      gf[e] = gt.first[i];
+      gc[e] = gt.count[i];
+      s_gt[0][i] = gf[e];
+      s_gt[1][i] = gc[e];
+      s_gt[2][i] = gt.shared[i];
+    }
+    for (int i = lane; i < 256; i += 64) s_gid[i] = -1;
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      for (int m = 0; m < gc[e]; ++m) s_gid[gf[e] + m] = static_cast<short>(64 * e + lane);
+    int suf[4], S[4], carry = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int sq = 64 * r + lane;
+      Gid[r] = sq < B ? s_gid[sq] : -1;
+      const int P = Gid[r] >= 0 ? (s_gt[2][Gid[r]] << tile_shift) * kTile : 0;
+      suf[r] = Gid[r] >= 0 ? (max(Lr[r] - P, 0) + kTile - 1) / kTile : 0;
+      S[r] = wave_incl_scan(suf[r]) + carry;
+      carry = readlane_i(S[r], 63);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int sq = 64 * r + lane;
+      const int k = Gid[r];
+      const bool lead = k >= 0 && s_gt[0][k] == sq;
+      const int end = lead ? sq + s_gt[1][k] - 1 : sq;     // the group's last member
+      const int e_same = __shfl(S[r], end & 63);
+      const int e_next = __shfl(S[r < 3 ? r + 1 : 3], end & 63);
+      const int s_end = (end >> 6) == r ? e_same : e_next;
+      Ur[r] = k < 0 ? (sq < B ? (Lr[r] + kTile - 1) / kTile : 0)
+                    : lead ? (s_gt[2][k] << tile_shift) + s_end - S[r] + suf[r] : 0;
+    }
+  }
+  (void)gt;
+  // group of sequence sq (< 256), wave-uniform; its rows written per segment
+  auto gid_of = [&](int sq) -> int {
+    const int r = sq >> 6;
+    const int v = (r == 0) ? Gid[0] : (r == 1) ? Gid[1] : (r == 2) ? Gid[2] : Gid[3];
+    return readlane_i(v, sq & 63);
+  };
+  auto ut_of = [&](int sq) -> int {
+    const int r = sq >> 6;
+    const int v = (r == 0) ? Ur[0] : (r == 1) ? Ur[1] : (r == 2) ? Ur[2] : Ur[3];
+    return readlane_i(v, sq & 63);
+  };
+  // sequences whose rows a segment started by sq writes: its group's
+  // members for a group leader, else sq alone
+  auto seg_count = [&](int sq) -> int {
+    if constexpr (kGrp) {
+      const int k = gid_of(sq);
+      return (k >= 0 && s_gt[0][k] == sq) ? s_gt[1][k] : 1;
+    } else {
+      return R / G;
+    }
+  };
   auto round_blocks = [&](int s0, const int (&L)[4]) -> int {   // blocks of s0..s0+255
     int c = 0;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int s = s0 + 64 * r + lane;
-      c += tiles_of(L[r]);
+      c += kGrp ? Ur[r] : tiles_of(L[r]);
       const uint64_t empty = __builtin_amdgcn_ballot_w64(s < B && L[r] == 0 && s % a.num_waves == w &&
-                                                         a.rec_out == nullptr);
+                                                         a.rec_out == nullptr && Gid[r] < 0);
       for (uint64_t m = empty; m != 0; m &= m - 1) {
         const int se = s0 + 64 * r + __builtin_ctzll(m);
         uint16_t* orow = a.out + (static_cast<int64_t>(se) * nchunk + a.t_first) * hq * kD;
@@ -307,7 +410,7 @@ decode_stream_kernel(StreamArgs a) {
             reinterpret_cast<u32x4_t*>(orow)[i] = __builtin_bit_cast(u32x4_t, v);
           }
         } else {
-          for (int i = lane; i < (R / G) * hq * kD / 8; i += 64)
+          for (int i = lane; i < (kGrp ? 1 : R / G) * hq * kD / 8; i += 64)
             reinterpret_cast<u32x4_t*>(orow)[i] = u32x4_t{0u, 0u, 0u, 0u};
         }
       }
@@ -329,12 +432,12 @@ decode_stream_kernel(StreamArgs a) {
 
   // ---- 2. the segment and block of tile t_begin: the first sequence whose
   // inclusive tile prefix passes t_begin
-  int s_cur = -1, off = 0, L_cur = 0, seg0 = 0;
+  int s_cur = -1, off = 0, L_cur = 0, U_cur = 0, seg0 = 0;
   {
     int base = 0;
-    auto scan64 = [&](int s0, int L) {
-      const int c = hkv * tiles_of(L);
-      const int incl = wave_incl_scan(c, lane);
+    auto scan64 = [&](int s0, int L, int U) {
+      const int c = hkv * (kGrp ? U : tiles_of(L));
+      const int incl = wave_incl_scan(c);
       const uint64_t m = __builtin_amdgcn_ballot_w64(base + incl > t_begin);
       if (m != 0) {
         const int l0 = __builtin_ctzll(m);
@@ -342,19 +445,23 @@ decode_stream_kernel(StreamArgs a) {
         const int excl = base + readlane_i(incl, l0) - readlane_i(c, l0);
         off = t_begin - excl;
         L_cur = readlane_i(L, l0);
+        U_cur = readlane_i(U, l0);
         seg0 = excl;
       }
       base += readlane_i(incl, 63);
     };
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      if (s_cur < 0) scan64(64 * r, Lr[r]);
+      if (s_cur < 0) scan64(64 * r, Lr[r], Ur[r]);
     for (int s0 = 256; s0 < B && s_cur < 0; s0 += 64)
-      scan64(s0, static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(lens_rsrc, (s0 + lane) * 4, 0, 0)));
+      scan64(s0, static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(lens_rsrc, (s0 + lane) * 4, 0, 0)),
+             0);
   }
-  if (s_cur < 0 || L_cur <= 0) return;   // lengths changed under us: nothing safe to do
-  // tile t_begin is block j0 of KV head g0 of sequence s_cur
-  const int nb0 = tiles_of(L_cur);
+  // lengths changed under us: nothing safe to do
+  if (s_cur < 0 || (kGrp ? U_cur <= 0 : L_cur <= 0)) return;
+  // tile t_begin is block j0 of KV head g0 of sequence s_cur (kGrp: tile j0
+  // of the segment s_cur starts)
+  const int nb0 = kGrp ? U_cur : tiles_of(L_cur);
   const int g0 = off / nb0;
   const int j0 = first_blk(L_cur) + (off - g0 * nb0);
   const int n_total = min(per, T - t_begin);
@@ -373,7 +480,8 @@ decode_stream_kernel(StreamArgs a) {
   // the largest shift of the pass (its first chunk token): a tile with at
   // least 16 + mshift_max rows to the context's end masks nothing
   const int mshift_max = a.causal ? nchunk - 1 - a.t_first : 0;
-  const int q_bytes = ((nchunk - 1) * hq + G) * kD * 2;            // one segment's q rows
+  // one segment's q rows (kGrp: up to R / G member sequences, one apart)
+  const int q_bytes = (((kGrp ? R / G : nchunk) - 1) * hq + G) * kD * 2;
   const int64_t q_all_bytes = static_cast<int64_t>(a.q_total_rows) * hq * kD * 2;
   // q in the B-operand layout, dims matching K's: bf16 step kk, quad q
   // holds dims 32kk + 8q .. +7; fp8 K is loaded 16 dims per lane (one
@@ -414,7 +522,7 @@ decode_stream_kernel(StreamArgs a) {
   constexpr int kSlotBytesMax = kMaxRows * (kD + 2) * 4;
   __shared__ __align__(16) char s_p_all[kWavesPerGroup][2 * kSlotBytesMax];
   char* s_p = s_p_all[wig];
-  int w_s = s_cur, w_g = g0, w_j = j0, w_L = L_cur, w_nb = (L_cur + kTile - 1) / kTile;
+  int w_s = s_cur, w_g = g0, w_j = j0, w_L = L_cur, w_nb = kGrp ? U_cur : (L_cur + kTile - 1) / kTile;
   int w_jf = first_blk(L_cur), w_seg = seg0 + g0 * nb0;
   // The first chunk token's window starts at L - T + 1 - W; a row of chunk
   // token t starts t later.  Code = that start relative to the segment's
@@ -463,6 +571,11 @@ decode_stream_kernel(StreamArgs a) {
   // O[query row][16*c + 4*quad + r].
   bf16x8_t qa[kKK];
   float m_ref = kNoMax;
+  // kGrp: this lane's row may see the prefix below g_plim (its member's
+  // length, capped at the prefix); g_short: some row of the segment stops
+  // inside the prefix
+  int g_plim = 1 << 30;
+  bool g_short = false;
   f32x4_t lacc = {0.f, 0.f, 0.f, 0.f};
   f32x4_t oacc[kVC];
   // A operand of the exponent-sum MFMA: bf16 1.0 in every element, so
@@ -483,9 +596,10 @@ decode_stream_kernel(StreamArgs a) {
     constexpr int kRPP = 64 / kLPR;                        // rows per pass
     const int rr = lane / kLPR;
     const int ch = lane - rr * kLPR;
-    for (int r0 = 0; r0 < R; r0 += kRPP) {
+    const int nrows = kGrp ? seg_count(s) * G : R;         // kGrp: the segment's members only
+    for (int r0 = 0; r0 < nrows; r0 += kRPP) {
       const int n = r0 + rr;
-      if (n < R) {
+      if (n < nrows) {
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(s_o + n * kOPitch + ch * 16);
         const int nt = n / G;
         uint16_t* dst = a.out + ((static_cast<int64_t>(s) * nchunk + a.t_first + nt) * hq +
@@ -713,6 +827,68 @@ decode_stream_kernel(StreamArgs a) {
   for (int done = 0; done < n_total;) {
     const int n = min(kCap, n_total - done);
     // pass 1: walk the pieces of this round, one lane per tile
+    if constexpr (kGrp) {
+      // a group's segment: the prefix tiles (table of the leader, rows to
+      // the prefix end), then each member's own tiles (its table from the
+      // prefix on, rows to its end), the member in word 2's top bits (1 +
+      // its index; 0 for the prefix and for segments outside groups)
+      for (int pos = 0; pos < n;) {
+        const int k = gid_of(w_s);
+        int sub_start = 0, sub_end = w_nb, tbase = 0, sublen = w_L, tseq = w_s, code = 0;
+        if (k >= 0) {
+          const int Pt = s_gt[2][k] << tile_shift, P = Pt * kTile;
+          if (w_j < Pt) {
+            sub_end = Pt;
+            sublen = P;
+          } else {
+            int cum = Pt;
+            const int cnt = s_gt[1][k];
+            for (int m = 0; m < cnt; ++m) {
+              const int Lm = len_of(w_s + m);
+              const int sm = (max(Lm - P, 0) + kTile - 1) / kTile;
+              if (w_j < cum + sm) {
+                sub_start = cum;
+                sub_end = cum + sm;
+                tbase = Pt;
+                sublen = Lm - P;
+                tseq = w_s + m;
+                code = m + 1;
+                break;
+              }
+              cum += sm;
+            }
+          }
+        }
+        const int span = min(sub_end - w_j, n - pos);
+        const uint32_t word2 = static_cast<uint32_t>(tseq) | (static_cast<uint32_t>(code) << kSeqBits);
+        for (int c = lane; c < span; c += 64) {
+          const int j = w_j + c;
+          const int gpos = done + pos + c;                   // position in the range
+          const uint32_t valid = static_cast<uint32_t>(min(31, sublen - kTile * (j - sub_start)));
+          const uint32_t first = (j == 0 || gpos == 0) ? 1u : 0u;
+          const uint32_t last = (j == w_nb - 1 || gpos == n_total - 1) ? 1u : 0u;
+          s_desc[pos + c] = u32x4_t{static_cast<uint32_t>(tbase + j - sub_start),
+                                    valid | (first << 5) | (last << 6) |
+                                        (static_cast<uint32_t>(w_g) << 7) |
+                                        (static_cast<uint32_t>(w_nb) << 16),
+                                    word2, static_cast<uint32_t>(w_seg)};
+        }
+        pos += span;
+        w_j += span;
+        if (w_j == w_nb) {                                   // next segment
+          w_seg += w_nb;
+          if (++w_g == hkv) {                                // next segment-starting sequence
+            w_g = 0;
+            do {
+              w_s += seg_count(w_s);
+              w_nb = (w_s < B) ? ut_of(w_s) : 0;
+            } while (w_nb == 0 && w_s < B);
+            w_L = (w_s < B) ? len_of(w_s) : 0;
+          }
+          w_j = 0;
+        }
+      }
+    } else
     for (int pos = 0; pos < n;) {
       const int span = min(w_nb - w_j, n - pos);
       const uint32_t word2 = static_cast<uint32_t>(w_s) | (lo_code(w_L, w_jf) << kSeqBits);
@@ -811,7 +987,11 @@ decode_stream_kernel(StreamArgs a) {
         const u32x4_t d = s_desc[t];
         const uint32_t tile = __builtin_amdgcn_readfirstlane(d[0]);
         const uint32_t info = __builtin_amdgcn_readfirstlane(d[1]);
-        const int s = __builtin_amdgcn_readfirstlane(static_cast<int>(d[2] & kSeqMask));
+        int s = __builtin_amdgcn_readfirstlane(static_cast<int>(d[2] & kSeqMask));
+        if constexpr (kGrp) {                              // a member's tile: the group's leader
+          const int code = __builtin_amdgcn_readfirstlane(static_cast<int>(d[2])) >> kSeqBits;
+          s -= code > 0 ? code - 1 : 0;
+        }
         k_nrec = min(static_cast<int>(info & 31u), kTile) * kRowBytes;   // rows past the context read 0
         v_nrec = k_nrec;
         tile_off = static_cast<int64_t>(tile) * kTileBytes;
@@ -876,7 +1056,30 @@ decode_stream_kernel(StreamArgs a) {
       const u32x4_t d = s_desc[t];
       const uint32_t info = __builtin_amdgcn_readfirstlane(d[1]);
       const int rows_left = static_cast<int>(info & 31u);   // min(31, L - 16j)
+      // kGrp: the member code of the tile and the segment's first sequence
+      int code = 0, lead = 0;
+      if constexpr (kGrp) {
+        code = __builtin_amdgcn_readfirstlane(static_cast<int>(d[2])) >> kSeqBits;
+        lead = __builtin_amdgcn_readfirstlane(static_cast<int>(d[2] & kSeqMask)) - (code > 0 ? code - 1 : 0);
+      }
       if (info & 32u) {                                      // a piece starts here
+        if constexpr (kGrp) {
+          // a group's rows see the prefix up to their own member's length
+          const int k = gid_of(lead);
+          if (k >= 0 && s_gt[0][k] == lead) {
+            const int P = (s_gt[2][k] << tile_shift) * kTile, cnt = s_gt[1][k];
+            const int sq = lead + min(t_row, cnt - 1);        // < 256
+            const int li = sq & 63, rb = sq >> 6;
+            const int l0 = __shfl(Lr[0], li), l1 = __shfl(Lr[1], li);
+            const int l2 = __shfl(Lr[2], li), l3 = __shfl(Lr[3], li);
+            const int Lt = rb == 0 ? l0 : rb == 1 ? l1 : rb == 2 ? l2 : l3;
+            g_plim = t_row < cnt ? min(Lt, P) : P;
+            g_short = __builtin_amdgcn_ballot_w64(g_plim < P) != 0;
+          } else {
+            g_plim = 1 << 30;
+            g_short = false;
+          }
+        }
         m_ref = kNoMax;
         lacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -909,9 +1112,23 @@ decode_stream_kernel(StreamArgs a) {
       // Masks.  Only a tile that reaches the context's end (less the causal
       // shift), or one a window start cuts, has rows a query row may not
       // see; a wave-uniform test skips the masking for every other tile.
+      if constexpr (kGrp) {
+        if (code != 0) {                                     // a member's tile: its rows only
+          const int lim = (t_row == code - 1) ? rows_left : 0;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (4 * quad + r >= lim) x[r] = -INFINITY;
+        } else if (g_short || rows_left < kTile) {          // prefix (or a lone sequence's) tile
+          const int jl = t_begin + done + t - __builtin_amdgcn_readfirstlane(static_cast<int>(d[3]));
+          const int lim = min(rows_left, g_plim - kTile * jl);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (4 * quad + r >= lim) x[r] = -INFINITY;
+        }
+      }
       const uint32_t wcode =
-          static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(d[2]))) >> kSeqBits;
-      if (wcode != 0u || rows_left - mshift_max < kTile) {
+          kGrp ? 0u : static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(d[2]))) >> kSeqBits;
+      if (!kGrp && (wcode != 0u || rows_left - mshift_max < kTile)) {
         const int lim = rows_left - mshift;                  // tile rows this query row may see
         // window start: tile rows below `lo` are cut (never, without a window)
         int lo = -kTile;
@@ -981,7 +1198,7 @@ decode_stream_kernel(StreamArgs a) {
       }
 
       if (info & 64u)                                        // a piece ends here
-        finalize(__builtin_amdgcn_readfirstlane(static_cast<int>(d[2] & kSeqMask)),
+        finalize(kGrp ? lead : __builtin_amdgcn_readfirstlane(static_cast<int>(d[2] & kSeqMask)),
                  static_cast<int>((info >> 7) & 511u),
                  __builtin_amdgcn_readfirstlane(static_cast<int>(d[3])),
                  static_cast<int>(info >> 16));
@@ -1668,16 +1885,28 @@ template <int kD>
 void launch_stream(bool fp8, bool pair, int nw, hipStream_t st, const StreamArgs& a,
                    hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
   const dim3 grid(nw / kWavesPerGroup), block(64 * kWavesPerGroup);
+  const NoGroupTable ng{0};
   if (pair) {
     if (fp8)
-      launch_k(decode_stream_kernel<kD, true, kAuxNonTemporal, true>, grid, block, kPadLds, st, e0, e1, a);
+      launch_k(decode_stream_kernel<kD, true, kAuxNonTemporal, true>, grid, block, kPadLds, st, e0, e1, a, ng);
     else
-      launch_k(decode_stream_kernel<kD, false, kAuxNonTemporal, true>, grid, block, kPadLds, st, e0, e1, a);
+      launch_k(decode_stream_kernel<kD, false, kAuxNonTemporal, true>, grid, block, kPadLds, st, e0, e1, a, ng);
   } else if (fp8) {
-    launch_k(decode_stream_kernel<kD, true, kAuxNonTemporal, false>, grid, block, kPadLds, st, e0, e1, a);
+    launch_k(decode_stream_kernel<kD, true, kAuxNonTemporal, false>, grid, block, kPadLds, st, e0, e1, a, ng);
   } else {
-    launch_k(decode_stream_kernel<kD, false, kAuxNonTemporal, false>, grid, block, kPadLds, st, e0, e1, a);
+    launch_k(decode_stream_kernel<kD, false, kAuxNonTemporal, false>, grid, block, kPadLds, st, e0, e1, a, ng);
   }
+}
+
+// The same with shared-prefix groups decoded in the one launch.
+template <int kD>
+void launch_stream_groups(bool fp8, int nw, hipStream_t st, const StreamArgs& a,
+                          const GroupTable& gt, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
+  const dim3 grid(nw / kWavesPerGroup), block(64 * kWavesPerGroup);
+  if (fp8)
+    launch_k(decode_stream_kernel<kD, true, kAuxNonTemporal, false, true>, grid, block, kPadLds, st, e0, e1, a, gt);
+  else
+    launch_k(decode_stream_kernel<kD, false, kAuxNonTemporal, false, true>, grid, block, kPadLds, st, e0, e1, a, gt);
 }
 
 }  // namespace
@@ -2223,6 +2452,54 @@ extern "C" pa_status pa_decode_shared_prefix(
   pa.grp_lens = nullptr;
   pa.grp_count = nullptr;
   const bool fp8 = c->cache_dtype == PA_FP8_E4M3;
+  if (max_count * G <= kMaxRows && num_seqs <= 256) {
+    // Small groups, at most 256 sequences: one launch of the decode kernel
+    // in which each (group, KV head) is one segment -- the prefix tiles,
+    // then every member's own tiles -- with all members' rows (kGrp).
+    GroupTable gtab{};
+    gtab.num = num_groups;
+    int64_t tiles = 0;
+    for (int i = 0; i < num_groups; ++i) {
+      gtab.first[i] = groups[3 * i];
+      gtab.count[i] = groups[3 * i + 1];
+      gtab.shared[i] = groups[3 * i + 2];
+    }
+    tiles = static_cast<int64_t>(hkv) * num_seqs * ((static_cast<int64_t>(max_context_len) + kTile - 1) / kTile);
+    const int64_t waves_max = static_cast<int64_t>(device_cus()) * kWavesPerCU;
+    const int64_t nw = std::max<int64_t>(1, std::min(waves_max, (tiles + kMinTilesPerWave - 1) / kMinTilesPerWave));
+    StreamArgs a;
+    a.k_cache = pa.k_cache;
+    a.v_cache = pa.v_cache;
+    a.q = pa.q;
+    a.out = static_cast<uint16_t*>(out);
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.counters = reinterpret_cast<uint32_t*>(ws);        // decode scratch comes first
+    a.partials = reinterpret_cast<float*>(ws + align256(static_cast<size_t>(num_seqs) * hkv * 4));
+    a.num_seqs = num_seqs;
+    a.hkv = hkv;
+    a.max_blocks = max_blocks_per_seq;
+    a.num_waves = static_cast<int>(nw);
+    a.group = G;
+    a.chunk = 1;
+    a.window = 0;
+    a.sub_shift = pa.sub_shift;
+    a.pair_nrec = 0;
+    a.prefix_len = nullptr;
+    a.prefix_rec = nullptr;
+    a.t_first = 0;
+    a.rows = G * max_count;
+    a.logit_scale = pa.logit_scale;
+    a.v_scale = (c->cache_dtype == PA_FP8_E4M3) ? c->v_scale : 1.f;
+    a.q_seq_rows = 1;
+    a.q_total_rows = num_seqs;
+    a.causal = 0;
+    a.rec_out = nullptr;
+    a.rec_count = nullptr;
+    if (D == 128) launch_stream_groups<128>(fp8, a.num_waves, hs, a, gtab);
+    else launch_stream_groups<64>(fp8, a.num_waves, hs, a, gtab);
+    return launch_status(fn);
+  }
   if (max_count * G <= kMaxRows) {
     // Small groups (all members' rows of a KV head fit one 16-row MFMA
     // block): the prefix goes through the decode kernel's tile stream, each

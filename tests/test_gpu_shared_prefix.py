@@ -241,3 +241,35 @@ def test_bench_sized_batch_every_row():
     par.check(out_to_f64(plain), ref, "bf16", "prefix bench batch pa_decode", stats=stats)
     _say(f"bench batch: max abs diff vs pa_decode {diff:.3e}")
     assert diff <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("fmt,pad", [("bf16", 0), ("fp8", 0), ("bf16", 260)])
+def test_small_groups_members_inside_the_prefix(fmt, pad):
+    """Small groups (members x G <= 16) with a member whose length ends
+    inside the shared blocks, one of length 0 and one exactly as long as
+    them.  Up to 256 requests the batch runs in one launch, each group's
+    prefix and members' own blocks one segment with all members' rows (a
+    member's rows see the prefix only up to its length); with `pad` requests
+    more it takes the two-pass path.  Every row against the oracle."""
+    ws = _workloads(970, 8, 2, 128, (300, 200), (4, 3))
+    order = [(0, r) for r in range(4)] + [(1, r) for r in range(3)]
+    if pad:
+        ws.append(workloads.prefix_batch(975, pad, 8, 1, 20, Hq=8, Hkv=2, D=128))
+        order += [(2, r) for r in range(pad)]
+    b = Batch(ws, order, fmt, 16, 13)
+    assert len(b.groups) == 2 and list(b.groups[:, 1]) == [4, 3]
+    cl = b.cl.copy()
+    sh0 = int(b.groups[0, 2]) * 16
+    cl[1] = sh0 - 37           # ends inside the shared blocks
+    cl[2] = 0
+    cl[5] = int(b.groups[1, 2]) * 16
+    _say(f"members inside the prefix {fmt} B={b.B}: groups {b.groups.tolist()}, lens {cl[:7].tolist()}")
+    out = b.shared(b.groups, cl=cl)
+    again = b.shared(b.groups, cl=cl)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), again.view(torch.int16))
+    got = out_to_f64(out)
+    ref = b.oracle(cl=cl)
+    par.check(got, ref, fmt, f"small groups, members inside the prefix, B={b.B}",
+              stats=par.value_stats(b.q, "bf16", b.kc_o, b.vc_o, fmt, b.bt, cl, ref, b.ks, b.vs))
+    assert np.all(got[2] == 0)
