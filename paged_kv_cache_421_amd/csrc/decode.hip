@@ -123,6 +123,14 @@ __device__ __forceinline__ float readlane_f(float x, int lane) {
 __device__ __forceinline__ int readlane_i(int x, int lane) {
   return __builtin_amdgcn_readlane(x, lane);
 }
+// floor(x / d) for 0 <= x < 2^12 and 1 <= d <= 32, given rcp = 1/d to within
+// 2 ulp: (x + 1/2) / d is at least 1/(2d) >= 2^-6 away from an integer,
+// while the float error of the product is below 2^12 * 2^-22 = 2^-10.  A
+// handful of instructions instead of the ~25 of an integer division by a
+// runtime value.
+__device__ __forceinline__ int div_small(int x, float rcp) {
+  return static_cast<int>((static_cast<float>(x) + 0.5f) * rcp);
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, kRsrcWord3);
@@ -294,6 +302,8 @@ decode_stream_kernel(StreamArgs a,
   const int R = a.rows;
   const int hq = hkv * G;
   const int slot_floats = (R * (kD + 2) + 3) & ~3; // floats per partial slot (16-byte multiple)
+  const float rcp_R = __builtin_amdgcn_rcpf(static_cast<float>(R));   // for div_small (R, G <= 16)
+  const float rcp_G = __builtin_amdgcn_rcpf(static_cast<float>(G));
   // With a window, a (sequence, KV head) segment covers the blocks from the
   // one holding the first chunk token's window start to the last.
   const int win = a.window;
@@ -601,7 +611,7 @@ decode_stream_kernel(StreamArgs a,
       const int n = r0 + rr;
       if (n < nrows) {
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(s_o + n * kOPitch + ch * 16);
-        const int nt = n / G;
+        const int nt = div_small(n, rcp_G);
         uint16_t* dst = a.out + ((static_cast<int64_t>(s) * nchunk + a.t_first + nt) * hq +
                                  g * G + (n - nt * G)) * kD + ch * 8;
         *reinterpret_cast<u32x4_t*>(dst) = v;
@@ -611,9 +621,9 @@ decode_stream_kernel(StreamArgs a,
 
   auto finalize = [&](int s, int g, int seg, int nb) {
     float l_tot = lacc[0];
-    const int wf = seg / per;
-    const int wl = (seg + nb - 1) / per;
-    if (wf == wl && a.rec_out != nullptr) {   // group pass: the member rows' records
+    // the whole segment lies in this wave's range [t_begin, t_begin + per)
+    const bool whole = seg >= t_begin && seg + nb <= t_begin + per;
+    if (whole && a.rec_out != nullptr) {   // group pass: the member rows' records
       const int cnt = a.rec_count[s];
       if (row_ok && t_row < cnt) {
         float* rec = a.rec_out + ((static_cast<int64_t>(s) + t_row) * hq + g * G + h_row) * (kD + 4);
@@ -623,7 +633,7 @@ decode_stream_kernel(StreamArgs a,
       }
       return;
     }
-    if (wf == wl) {   // the whole segment was in this wave: write the output
+    if (whole) {   // the whole segment was in this wave: write the output
       if (row_ok) {
         if (a.prefix_len != nullptr) {                       // fold in the shared prefix
           // the record is read together with the prefix length (one round
@@ -731,7 +741,7 @@ decode_stream_kernel(StreamArgs a,
         if (64 * i >= n_grp) break;
         const int q = min(lane + 64 * i, n_grp - 1);
         op[i] = *reinterpret_cast<const f32x4_t*>(own_slot + q * 16);
-        const f32x2_t ml = *reinterpret_cast<const f32x2_t*>(own_slot + (n_el + 2 * (q % R)) * 4);
+        const f32x2_t ml = *reinterpret_cast<const f32x2_t*>(own_slot + (n_el + 2 * (q - div_small(q, rcp_R) * R)) * 4);
         mp[i] = ml[0];
         lp[i] = ml[1];
       }
@@ -750,7 +760,7 @@ decode_stream_kernel(StreamArgs a,
       for (int i = 0; i < kE4; ++i) {
         if (64 * i >= n_grp) break;
         const int q = min(lane + 64 * i, n_grp - 1);
-        const int mo = (n_el + 2 * (q % R)) * 4;
+        const int mo = (n_el + 2 * (q - div_small(q, rcp_R) * R)) * 4;
         oa[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, q * 16, 0, kAuxCoherent));
         ob[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rb, q * 16, 0, kAuxCoherent));
         const u32x2_t mla = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(ra, mo, 0, kAuxCoherent));
@@ -770,9 +780,9 @@ decode_stream_kernel(StreamArgs a,
       for (int i = 0; i < kE4; ++i) {
         const int q = lane + 64 * i;
         if (q < n_grp) {
-          const int r = q % R;
-          const int cq = q / R;
-          const int nt = r / G;
+          const int cq = div_small(q, rcp_R);
+          const int r = q - cq * R;
+          const int nt = div_small(r, rcp_G);
           const float* rec = a.prefix_rec + ((static_cast<int64_t>(s) * nchunk + a.t_first + nt) * hq +
                                              g * G + (r - nt * G)) * (kD + 4);
           const float mp = rec[kD], lp = rec[kD + 1];
@@ -791,11 +801,13 @@ decode_stream_kernel(StreamArgs a,
 #pragma unroll
       for (int i = 0; i < kE4; ++i) {
         const int q = lane + 64 * i;
-        const int r = q % R;
-        const int t = a.t_first + r / G;
+        const int cq = div_small(q, rcp_R);
+        const int r = q - cq * R;
+        const int rt = div_small(r, rcp_G);
+        const int t = a.t_first + rt;
         if (q < n_grp && t < cnt) {
-          float* rec = a.rec_out + ((static_cast<int64_t>(s) + t) * hq + g * G + (r - (r / G) * G)) * (kD + 4);
-          *reinterpret_cast<f32x4_t*>(rec + 4 * (q / R)) = num[i];
+          float* rec = a.rec_out + ((static_cast<int64_t>(s) + t) * hq + g * G + (r - rt * G)) * (kD + 4);
+          *reinterpret_cast<f32x4_t*>(rec + 4 * cq) = num[i];
           if (q < R) *reinterpret_cast<f32x2_t*>(rec + kD) = f32x2_t{M[i], den[i]};
         }
       }
@@ -806,8 +818,8 @@ decode_stream_kernel(StreamArgs a,
     for (int i = 0; i < kE4; ++i) {
       const int q = lane + 64 * i;
       if (q < n_grp) {
-        const int r = q % R;
-        const int cq = q / R;                              // c * 4 + quad
+        const int cq = div_small(q, rcp_R);                // c * 4 + quad
+        const int r = q - cq * R;
         const float inv = (den[i] > 0.f) ? a.v_scale * __builtin_amdgcn_rcpf(den[i]) : 0.f;
         const bf16x4_t pk = {static_cast<__bf16>(num[i][0] * inv), static_cast<__bf16>(num[i][1] * inv),
                              static_cast<__bf16>(num[i][2] * inv), static_cast<__bf16>(num[i][3] * inv)};
