@@ -731,9 +731,10 @@ decode_stream_kernel(StreamArgs a,
       }
     };
     // Pieces are combined in wave order whoever merges, so the result does
-    // not depend on which piece arrived last.  Two are loaded at a time;
-    // this wave's own piece comes from its LDS slot (its workspace load has
-    // an empty range, as has a second piece past the last).
+    // not depend on which piece arrived last.  The other waves' pieces are
+    // loaded two at a time (a segment of up to three pieces takes one round
+    // trip); this wave's own piece comes from its LDS slot and is combined
+    // at its place in the order.
     const char* own_slot = s_p + own * kSlotBytesMax;
     auto from_lds = [&](f32x4_t (&op)[kE4], float (&mp)[kE4], float (&lp)[kE4]) {
 #pragma unroll
@@ -746,16 +747,24 @@ decode_stream_kernel(StreamArgs a,
         lp[i] = ml[1];
       }
     };
-    for (int p0 = wf; p0 <= wl; p0 += 2) {
+    auto own_piece = [&]() {
+      f32x4_t oo[kE4];
+      float mo_[kE4], lo_[kE4];
+      from_lds(oo, mo_, lo_);
+      combine(oo, mo_, lo_);
+    };
+    bool own_done = false;
+    int pa = (wf == w) ? wf + 1 : wf;                      // first remote piece
+    while (pa <= wl) {
+      int pb = pa + 1;                                     // the next remote piece, if any
+      if (pb == w) ++pb;
+      const bool has_b = pb <= wl;
       f32x4_t oa[kE4], ob[kE4];
       float ma[kE4], la[kE4], mb[kE4], lb[kE4];
-      const bool has_b = p0 + 1 <= wl;
-      const bool ga = p0 != w;
-      const bool gb = has_b && p0 + 1 != w;
       const char* base = reinterpret_cast<const char*>(a.partials);
-      const __amdgpu_buffer_rsrc_t ra = make_rsrc(base + slot_ptr(p0, seg), ga ? slot_floats * 4 : 0);
-      const __amdgpu_buffer_rsrc_t rb = make_rsrc(base + (has_b ? slot_ptr(p0 + 1, seg) : 0),
-                                                  gb ? slot_floats * 4 : 0);
+      const __amdgpu_buffer_rsrc_t ra = make_rsrc(base + slot_ptr(pa, seg), slot_floats * 4);
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(base + (has_b ? slot_ptr(pb, seg) : 0),
+                                                  has_b ? slot_floats * 4 : 0);
 #pragma unroll
       for (int i = 0; i < kE4; ++i) {
         if (64 * i >= n_grp) break;
@@ -770,11 +779,22 @@ decode_stream_kernel(StreamArgs a,
         mb[i] = __uint_as_float(mlb[0]);
         lb[i] = __uint_as_float(mlb[1]);
       }
-      if (!ga) from_lds(oa, ma, la);
-      if (has_b && !gb) from_lds(ob, mb, lb);
+      if (!own_done && w < pa) {
+        own_piece();
+        own_done = true;
+      }
       combine(oa, ma, la);
-      if (has_b) combine(ob, mb, lb);
+      if (has_b) {
+        if (!own_done && w < pb) {
+          own_piece();
+          own_done = true;
+        }
+        combine(ob, mb, lb);
+      }
+      pa = pb + 1;
+      if (pa == w) ++pa;
     }
+    if (!own_done) own_piece();
     if (a.prefix_len != nullptr && a.prefix_len[s] > 0) {     // fold in the shared prefix
 #pragma unroll
       for (int i = 0; i < kE4; ++i) {
