@@ -201,6 +201,12 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
 // A pass covers `rows` = G * (chunk tokens of the pass) <= 16 query rows per
 // KV head: row n is chunk token t_first + n / G of query head g*G + n % G.
 // Single-token decode is chunk = 1, one pass with rows = G.
+// A KV head with more than 16 query heads is decoded as kv_split row blocks
+// of G = (query heads per KV head) / kv_split heads each: the kernel's
+// "heads" (hkv of them, hkv = cache heads * kv_split) are those blocks, and
+// block g reads cache head g / kv_split.  Query head gG + h of the kernel's
+// numbering is the same query head as in the caller's, so q, out and the
+// arrival counters need no other change.
 struct StreamArgs {
   const char* k_cache;
   const char* v_cache;
@@ -211,10 +217,11 @@ struct StreamArgs {
   uint32_t* counters;         // [B * Hkv], zero between calls
   float* partials;            // [num_waves][2][rows][kD + 2]
   int num_seqs;
-  int hkv;
+  int hkv;                    // kernel heads: cache KV heads * kv_split
+  int kv_split;               // row blocks per cache KV head (1 unless G > 16)
   int max_blocks;
   int num_waves;
-  int group;                  // G: query heads per KV head
+  int group;                  // G: query heads per kernel head
   int chunk;                  // T: new tokens per sequence
   int window;                 // W > 0: attend only the last W positions; 0: all
   int sub_shift;              // log2(block size / 16): tiles per block = 1 << sub_shift
@@ -558,6 +565,12 @@ decode_stream_kernel(StreamArgs a,
   };
   const int tbl_bytes = B * a.max_blocks * 4;
   const __amdgpu_buffer_rsrc_t tbl_rsrc = make_rsrc(a.block_tables, tbl_bytes);
+  // the cache head a kernel head reads (row blocks of one KV head share its tiles)
+  const int kv_split = a.kv_split;
+  const uint32_t hkv_cache = static_cast<uint32_t>(hkv / kv_split);
+  auto cache_head = [&](uint32_t g) -> uint32_t {
+    return kv_split == 1 ? g : g / static_cast<uint32_t>(kv_split);
+  };
 
   // Lane offsets inside a (block, KV head) tile [16][D], in bytes.
   //  K: MFMA A operand of S^T = K q^T, lane (row, quad) holds token `row`,
@@ -717,16 +730,22 @@ decode_stream_kernel(StreamArgs a,
       den[i] = 0.f;
       num[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
+    // The rounding is spelled out (a product, then one fused multiply-add;
+    // no contraction left to the compiler): the function is inlined at
+    // several places, and which place takes a given piece depends on which
+    // wave merges, so every place must round alike for the result not to
+    // depend on arrival order.
     auto combine = [&](const f32x4_t (&op)[kE4], const float (&mp)[kE4], const float (&lp)[kE4]) {
+#pragma clang fp contract(off)
 #pragma unroll
       for (int i = 0; i < kE4; ++i) {
         if (64 * i >= n_grp) break;                        // wave-uniform
         const float mn = fmaxf(M[i], mp[i]);
         const float f_old = __builtin_amdgcn_exp2f(M[i] - mn);
         const float f_new = __builtin_amdgcn_exp2f(mp[i] - mn);
-        den[i] = den[i] * f_old + lp[i] * f_new;
+        den[i] = __builtin_fmaf(lp[i], f_new, den[i] * f_old);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) num[i][e] = num[i][e] * f_old + op[i][e] * f_new;
+        for (int e = 0; e < 4; ++e) num[i][e] = __builtin_fmaf(op[i][e], f_new, num[i][e] * f_old);
         M[i] = mn;
       }
     };
@@ -976,10 +995,10 @@ decode_stream_kernel(StreamArgs a,
           const int e = e0 + 64 * r + lane;
           if (e < n) {
             const uint32_t g = (s_desc[e][1] >> 7) & 511u;
-            const uint32_t ua = static_cast<uint32_t>(ida[r]) * static_cast<uint32_t>(hkv) + g;
+            const uint32_t ua = static_cast<uint32_t>(ida[r]) * hkv_cache + cache_head(g);
             const bool two = (s_desc[e][1] & 31u) > 8u;
             s_desc[e][0] = ua;
-            s_pair[e] = two ? static_cast<uint32_t>(idb[r]) * static_cast<uint32_t>(hkv) + g : ua;
+            s_pair[e] = two ? static_cast<uint32_t>(idb[r]) * hkv_cache + cache_head(g) : ua;
           }
         }
       }
@@ -1004,7 +1023,7 @@ decode_stream_kernel(StreamArgs a,
           // tile j of the sequence is sub-tile j % (tiles per block) of its block
           const uint32_t g = (s_desc[e][1] >> 7) & 511u;
           const uint32_t u = s_desc[e][0] & ((1u << a.sub_shift) - 1u);
-          s_desc[e][0] = ((static_cast<uint32_t>(ids[r]) * static_cast<uint32_t>(hkv) + g) << a.sub_shift) + u;
+          s_desc[e][0] = ((static_cast<uint32_t>(ids[r]) * hkv_cache + cache_head(g)) << a.sub_shift) + u;
         }
       }
     }
@@ -1960,7 +1979,17 @@ constexpr int64_t kPairCacheMax = int64_t{0x7FFF0000} - (int64_t{1} << 16);
 
 bool fast_path(int fmt, int q_dtype, int G, int D, int bs) {
   return (fmt == PA_BF16 || fmt == PA_FP8_E4M3) && q_dtype == PA_BF16 && G >= 1 &&
-         G <= kMaxRows && (D == 64 || D == 128) && (bs % kTile == 0 || bs == 8);
+         (D == 64 || D == 128) && (bs % kTile == 0 || bs == 8);
+}
+
+// Row blocks per KV head on the fast path: a KV head with more than 16
+// query heads is decoded as the fewest equal blocks of at most 16 (the
+// smallest divisor of G that brings G / split to 16 or below).
+int head_split(int G) {
+  if (G <= kMaxRows) return 1;
+  for (int d = 2; d < G; ++d)
+    if (G % d == 0 && G / d <= kMaxRows) return d;
+  return G;
 }
 
 int64_t cache_bytes(const pa_cache_desc* c) {
@@ -1972,7 +2001,8 @@ int64_t cache_bytes(const pa_cache_desc* c) {
 // the paired mode's descriptor.
 bool fast_path(const pa_cache_desc* c, int q_dtype, int G) {
   return fast_path(c->cache_dtype, q_dtype, G, c->head_dim, c->block_size) &&
-         (c->block_size != 8 || cache_bytes(c) <= kPairCacheMax);
+         (c->block_size != 8 || cache_bytes(c) <= kPairCacheMax) &&
+         static_cast<int64_t>(c->num_kv_heads) * head_split(G) <= 511;   // 9-bit head field
 }
 
 // Chunk tokens per fast-path pass: as many as fit G rows each in 16 columns.
@@ -2024,9 +2054,11 @@ size_t workspace_bytes_for(const pa_cache_desc* c, int32_t num_seqs, int32_t num
     return 0;
   const int G = num_q_heads / c->num_kv_heads;
   const int q_dtype = (c->cache_dtype == PA_F32) ? PA_F32 : PA_BF16;
-  if (fast_path(c, q_dtype, G))
-    return stream_workspace_bytes(num_seqs, c->num_kv_heads, G * tokens_per_pass(G, T),
+  if (fast_path(c, q_dtype, G)) {
+    const int split = head_split(G), Gk = G / split;
+    return stream_workspace_bytes(num_seqs, c->num_kv_heads * split, Gk * tokens_per_pass(Gk, T),
                                   c->head_dim);
+  }
   return general_workspace_bytes(num_seqs, num_q_heads, T, c->head_dim, max_context_len);
 }
 
@@ -2069,13 +2101,15 @@ pa_status attend(const char* fn, const pa_cache_desc* c, const void* k_cache,
     return fail(PA_ERR_INVALID_ARG, "%s: null pointer", fn);
   const int G = num_q_heads / hkv;
   const bool fast = fast_path(c, q_dtype, G);
-  const int tpp = tokens_per_pass(G, T);
-  const int64_t max_tiles = static_cast<int64_t>(hkv) * num_seqs *
+  // the kernel's heads: row blocks of Gk query heads, split per KV head
+  const int split = fast ? head_split(G) : 1, Gk = G / split, hk = hkv * split;
+  const int tpp = tokens_per_pass(Gk, T);
+  const int64_t max_tiles = static_cast<int64_t>(hk) * num_seqs *
                             ((static_cast<int64_t>(max_context_len) + kTile - 1) / kTile);
   if (fast && (max_tiles >= (int64_t{1} << 30) || num_seqs > static_cast<int32_t>(kSeqMask) ||
                static_cast<int64_t>(c->num_blocks) * hkv * (bs / kTile) >= (int64_t{1} << 32) ||
                static_cast<int64_t>(max_blocks_per_seq) * 4 >= (int64_t{1} << 31) ||
-               (static_cast<int64_t>(T - 1) * num_q_heads + G) * D * 2 >= (int64_t{1} << 30)))
+               (static_cast<int64_t>(T - 1) * num_q_heads + Gk) * D * 2 >= (int64_t{1} << 30)))
     return fail(PA_ERR_UNSUPPORTED, "%s: %lld tiles in one call (limit 2^30)", fn,
                 static_cast<long long>(max_tiles));
   if (!fast && (num_seqs > 65535 || static_cast<int64_t>(T) * num_q_heads > 65535))
@@ -2083,8 +2117,8 @@ pa_status attend(const char* fn, const pa_cache_desc* c, const void* k_cache,
   if (fast && (reinterpret_cast<uintptr_t>(out) % 16 != 0 || reinterpret_cast<uintptr_t>(q) % 16 != 0))
     return fail(PA_ERR_INVALID_ARG, "%s: q and out must be 16-byte aligned", fn);
   const size_t need = !fast ? general_workspace_bytes(num_seqs, num_q_heads, T, D, max_context_len)
-                     : fixed_counters ? stream_partials_bytes(G * tpp, D)
-                                      : stream_workspace_bytes(num_seqs, hkv, G * tpp, D);
+                     : fixed_counters ? stream_partials_bytes(Gk * tpp, D)
+                                      : stream_workspace_bytes(num_seqs, hk, Gk * tpp, D);
   if (workspace_bytes < need || (need > 0 && !workspace))
     return fail(PA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes, need %zu", fn,
                 workspace_bytes, need);
@@ -2117,12 +2151,13 @@ pa_status attend(const char* fn, const pa_cache_desc* c, const void* k_cache,
     a.counters = fixed_counters ? fixed_counters : static_cast<uint32_t*>(workspace);
     a.partials = fixed_counters ? static_cast<float*>(workspace)
                                 : reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                                           align256(static_cast<size_t>(num_seqs) * hkv * 4));
+                                                           align256(static_cast<size_t>(num_seqs) * hk * 4));
     a.num_seqs = num_seqs;
-    a.hkv = hkv;
+    a.hkv = hk;
+    a.kv_split = split;
     a.max_blocks = max_blocks_per_seq;
     a.num_waves = static_cast<int>(nw);
-    a.group = G;
+    a.group = Gk;
     a.chunk = T;
     a.window = W;
     a.sub_shift = bs == 64 ? 2 : bs == 32 ? 1 : 0;
@@ -2139,7 +2174,7 @@ pa_status attend(const char* fn, const pa_cache_desc* c, const void* k_cache,
     // one pass per tpp chunk tokens; each pass leaves the counters zeroed
     for (int t0 = 0; t0 < T; t0 += tpp) {
       a.t_first = t0;
-      a.rows = G * std::min(tpp, T - t0);
+      a.rows = Gk * std::min(tpp, T - t0);
       hipEvent_t e0 = t0 == 0 ? tm.start : nullptr;
       hipEvent_t e1 = t0 + tpp >= T ? tm.stop : nullptr;
       if (D == 128) launch_stream<128>(fmt == PA_FP8_E4M3, bs == 8, a.num_waves, s, a, e0, e1);
@@ -2318,11 +2353,12 @@ extern "C" pa_status pa_decode_noalloc(const pa_cache_desc* c, const void* k_cac
   if (num_seqs == 0) return PA_OK;
   const int G = num_q_heads / c->num_kv_heads;
   const bool fast = fast_path(c, q_dtype, G);
-  if (fast && static_cast<size_t>(num_seqs) * c->num_kv_heads > kStaticCounters)
+  const int split = fast ? head_split(G) : 1;
+  if (fast && static_cast<size_t>(num_seqs) * c->num_kv_heads * split > kStaticCounters)
     return fail(PA_ERR_WORKSPACE_TOO_SMALL,
-                "%s: %d sequences x %d KV heads exceed the static scratch's %zu counters", fn,
-                num_seqs, c->num_kv_heads, kStaticCounters);
-  const size_t need = fast ? stream_partials_bytes(G, c->head_dim)
+                "%s: %d sequences x %d KV heads x %d row blocks exceed the static scratch's %zu "
+                "counters", fn, num_seqs, c->num_kv_heads, split, kStaticCounters);
+  const size_t need = fast ? stream_partials_bytes(G / split, c->head_dim)
                            : general_workspace_bytes(num_seqs, num_q_heads, 1, c->head_dim,
                                                      max_context_len);
   if (need > kStaticPartialBytes)
@@ -2382,7 +2418,7 @@ extern "C" size_t pa_decode_shared_prefix_workspace_bytes(const pa_cache_desc* c
     return 0;
   const int G = num_q_heads / c->num_kv_heads;
   const int q_dtype = (c->cache_dtype == PA_F32) ? PA_F32 : PA_BF16;
-  if (!fast_path(c, q_dtype, G) || c->block_size % kTile != 0) return 0;
+  if (!fast_path(c, q_dtype, G) || G > kMaxRows || c->block_size % kTile != 0) return 0;
   return shared_prefix_layout(c, num_seqs, num_q_heads, max_blocks_per_seq).total;
 }
 
@@ -2408,7 +2444,7 @@ extern "C" pa_status pa_decode_shared_prefix(
       num_q_heads % c->num_kv_heads != 0)
     return fail(PA_ERR_INVALID_ARG, "%s: bad batch shape", fn);
   const int hkv = c->num_kv_heads, D = c->head_dim, G = num_q_heads / hkv, bs = c->block_size;
-  if (!fast_path(c, q_dtype, G) || bs % kTile != 0)
+  if (!fast_path(c, q_dtype, G) || G > kMaxRows || bs % kTile != 0)
     return fail(PA_ERR_UNSUPPORTED, "%s: needs a bf16 or fp8 cache with bf16 q, head_dim 64 or "
                 "128, G <= 16 and a block size that is a multiple of 16", fn);
   if (static_cast<int64_t>(num_seqs) * num_q_heads * D * 2 >= (int64_t{1} << 31) ||
@@ -2510,6 +2546,7 @@ extern "C" pa_status pa_decode_shared_prefix(
     a.partials = reinterpret_cast<float*>(ws + align256(static_cast<size_t>(num_seqs) * hkv * 4));
     a.num_seqs = num_seqs;
     a.hkv = hkv;
+    a.kv_split = 1;
     a.max_blocks = max_blocks_per_seq;
     a.num_waves = static_cast<int>(nw);
     a.group = G;
@@ -2561,6 +2598,7 @@ extern "C" pa_status pa_decode_shared_prefix(
     a.partials = reinterpret_cast<float*>(ws + align256(static_cast<size_t>(num_seqs) * hkv * 4));
     a.num_seqs = num_seqs;
     a.hkv = hkv;
+    a.kv_split = 1;
     a.max_blocks = max_blocks_per_seq;
     a.num_waves = static_cast<int>(nw);
     a.group = G;

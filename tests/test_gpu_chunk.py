@@ -69,12 +69,13 @@ LENS = np.array([0, 1, 2, 3, 15, 16, 17, 33, 511, 513, 1024, 1400, 700], dtype=n
     ("fp8", 4, 128, 4),
     ("fp8", 8, 64, 3),        # two passes (2 + 1)
     ("f32", 2, 64, 5),        # partition path
-    ("bf16", 32, 64, 2),      # G = 32: partition path
+    ("bf16", 32, 64, 2),      # G = 32: two row blocks of 16, one token per pass
+    ("fp8", 24, 128, 3),      # G = 24: two row blocks of 12
 ])
 def test_chunk_small_ragged(fmt, G, D, T):
     """Lengths 0..1400 including L < T (tokens that see nothing get zero
     rows), sub-block and ragged last blocks."""
-    Hkv = 1 if G == 32 else 2
+    Hkv = 1 if G >= 24 else 2
     _small(500 + G + D + T, fmt, G, D, T, Hkv=Hkv, lens=LENS)
 
 
@@ -164,8 +165,8 @@ def _small_window(seed, fmt, G, D, T, W, Hkv=2, lens=None):
     ("fp8", 8, 64, 2, 40), ("f32", 2, 64, 3, 600), ("bf16", 32, 64, 2, 700)])
 def test_window_small_ragged(fmt, G, D, T, W):
     """Windows below, at and above a block, longer than every context, with
-    chunks (the window and the causal cut together), fp8, and the partition
-    path (fp32, G = 32) whose partitions may see nothing."""
+    chunks (the window and the causal cut together), fp8, the partition path
+    (fp32) whose partitions may see nothing, and G = 32 in two row blocks."""
     Hkv = 1 if G == 32 else 2
     _small_window(900 + W + T, fmt, G, D, T, W, Hkv=Hkv, lens=LENS)
 

@@ -87,11 +87,13 @@ def _small_case(seed, fmt, B, Hq, Hkv, D, max_len, min_len=0, lens=None):
 @pytest.mark.parametrize("fmt,G,D", [
     ("bf16", 1, 128), ("bf16", 4, 128), ("bf16", 8, 128), ("bf16", 3, 64), ("bf16", 5, 128),
     ("bf16", 2, 64), ("fp8", 4, 128), ("fp8", 8, 64), ("fp8", 1, 128),
-    ("f32", 1, 64), ("f32", 4, 128), ("bf16", 16, 128), ("fp8", 12, 64), ("bf16", 32, 64)])
+    ("f32", 1, 64), ("f32", 4, 128), ("bf16", 16, 128), ("fp8", 12, 64), ("bf16", 32, 64),
+    ("bf16", 32, 128), ("fp8", 24, 128), ("bf16", 20, 64), ("bf16", 17, 64), ("fp8", 64, 128)])
 def test_decode_small_ragged(fmt, G, D):
     """Lengths 0..1400: empty, sub-block, ragged last blocks, one to three
-    partitions; G up to 16 streams tiles, G = 32 and fp32 caches take the
-    partition kernel."""
+    partitions; bf16 and fp8 caches stream tiles (G above 16 in row blocks of
+    at most 16 query heads: 32 -> 2 x 16, 24 -> 2 x 12, 20 -> 2 x 10,
+    17 -> 17 x 1, 64 -> 4 x 16), fp32 caches take the partition kernel."""
     Hkv = 2
     lens = np.array([0, 1, 15, 16, 17, 33, 511, 512, 513, 1024, 1400, 700], dtype=np.int32)
     _small_case(100 + G + D, fmt, len(lens), G * Hkv, Hkv, D, 0, lens=lens)

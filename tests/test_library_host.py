@@ -87,6 +87,17 @@ def test_workspace_size_formula():
     fp8 = pk.CacheDesc(64, 2, 64, "fp8", 0.5, 0.5)
     # slots are padded to whole 16-byte chunks: 1 * 66 floats -> 68
     assert pk.decode_workspace_bytes(fp8, 5, 2, 100) == 256 + waves * 2 * 68 * 4
+    # more than 16 query heads per KV head: the fewest equal row blocks of at
+    # most 16 heads (G 32 -> 2 x 16, G 24 -> 2 x 12, G 17 -> 17 x 1), each a
+    # kernel head with its own counter per sequence
+    assert pk.decode_workspace_bytes(bf, 256, 256, 4096) == 256 * 16 * 4 + waves * 2 * 16 * 130 * 4
+    two = pk.CacheDesc(64, 2, 128, "bf16")
+    assert pk.decode_workspace_bytes(two, 10, 48, 100) == 256 + waves * 2 * 12 * 130 * 4
+    one = pk.CacheDesc(64, 1, 64, "bf16")
+    assert pk.decode_workspace_bytes(one, 100, 17, 100) == 6912 + waves * 2 * 68 * 4
+    # at most 511 kernel heads: beyond that the partition path and its workspace
+    many = pk.CacheDesc(64, 31, 64, "bf16")
+    assert pk.decode_workspace_bytes(many, 2, 31 * 17, 1000) == 2 * 31 * 17 * 2 * 66 * 4
     # invalid shapes report 0
     assert pk.decode_workspace_bytes(bf, 4, 12, 100) == 0
     assert pk.decode_workspace_bytes(bf, 0, 8, 100) == 0
@@ -113,9 +124,10 @@ def test_chunk_workspace_size_formula():
     # G = 16 still takes the streaming path, one token per pass
     assert pk.chunk_workspace_bytes(pk.CacheDesc(64, 2, 64, "bf16"), 3, 32, 2, 100) == \
         256 + waves * 2 * 16 * 66 * 4
-    # G = 32 and fp32 caches take the partition path: a record per query row and partition
+    # G = 32 streams as two row blocks of 16 query heads, one token per pass
     assert pk.chunk_workspace_bytes(pk.CacheDesc(64, 1, 64, "bf16"), 2, 32, 3, 1000) == \
-        2 * 3 * 32 * 2 * 66 * 4
+        256 + waves * 2 * 16 * 66 * 4
+    # fp32 caches take the partition path: a record per query row and partition
     f32 = pk.CacheDesc(64, 2, 64, "f32")
     assert pk.chunk_workspace_bytes(f32, 4, 4, 16, 513) == 4 * 16 * 4 * 2 * 66 * 4
     assert pk.chunk_workspace_bytes(f32, 4, 4, 16, 512) == 0
