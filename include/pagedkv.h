@@ -174,9 +174,14 @@ pa_status pa_decode_workspace_init(void* workspace, size_t workspace_bytes,
  *                  arrival counters of one call at a time: calls that may
  *                  overlap (different streams) need separate workspaces.
  *   A context is processed in pieces whose partial (max, sum, output) are
- *   merged by the log-sum-exp rule: with a bf16 or fp8 cache, head_dim 64
- *   or 128 and G <= 16, pieces are equal shares of the whole batch's KV
- *   tiles; otherwise pieces are PA_PARTITION_TOKENS-token partitions.
+ *   merged by the log-sum-exp rule: with a bf16 or fp8 cache and head_dim
+ *   64 or 128, pieces are equal shares of the whole batch's KV tiles (a KV
+ *   head with G > 16 query heads is streamed as the fewest equal blocks of
+ *   at most 16 of them, each reading the head's tiles; at most 511 such
+ *   blocks over all KV heads); otherwise (fp32 caches, and 8-token-block
+ *   caches of 2 GiB or more) pieces are PA_PARTITION_TOKENS-token
+ *   partitions.  Pieces are merged in a fixed order, so repeated calls give
+ *   bit-identical results.
  */
 pa_status pa_decode(const pa_cache_desc* c, const void* k_cache,
                     const void* v_cache, const void* q, int32_t q_dtype,
@@ -196,8 +201,9 @@ pa_status pa_decode(const pa_cache_desc* c, const void* k_cache,
  *   until the process ends: 256 KiB of arrival counters (at most 65536
  *   sequences x KV heads per call) and 24 MiB of partial results.  A batch
  *   that needs more returns PA_ERR_WORKSPACE_TOO_SMALL and launches nothing
- *   (the bf16 / fp8 path needs about 2 * 4 * CUs * G * (head_dim + 2) * 4
- *   bytes: 17 MiB at G = 16, head_dim 128 on 256 CUs; the fp32 path needs
+ *   (the bf16 / fp8 path needs about 2 * 4 * CUs * min(G, 16) * (head_dim +
+ *   2) * 4 bytes: 17 MiB at G = 16, head_dim 128 on 256 CUs, and one counter
+ *   per sequence and block of at most 16 query heads; the fp32 path needs
  *   num_seqs * num_q_heads * ceil(max_context_len / 512) * (head_dim + 2) * 4
  *   bytes once a context spans more than one partition).
  *   The first call on a device looks the array up and clears its counters
@@ -230,7 +236,8 @@ pa_status pa_decode_noalloc(const pa_cache_desc* c, const void* k_cache,
  *               as pa_decode's.
  *   With a bf16 or fp8 cache the KV tiles are streamed once per pass of
  *   floor(16 / G) chunk tokens (each pass's G * tokens query rows share the
- *   tile loads); other shapes take the partition path.
+ *   tile loads; G > 16 is split into blocks of at most 16 query heads as for
+ *   pa_decode, one token per pass); other caches take the partition path.
  *   pa_decode is pa_decode_chunk with chunk_len = 1.
  */
 pa_status pa_decode_chunk(const pa_cache_desc* c, const void* k_cache,

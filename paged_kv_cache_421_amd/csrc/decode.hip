@@ -14,7 +14,8 @@
 // is bound by HBM bandwidth (ybb.press §9, 九、前沿进展与未来展望, item 4: decode
 // is the memory-bound phase).
 //
-// Fast path (bf16 or fp8 cache, bf16 q, head_dim 64/128, G <= 16):
+// Fast path (bf16 or fp8 cache, bf16 q, head_dim 64/128; a KV head with G > 16
+// query heads runs as blocks of at most 16 of them, each a head of its own):
 //  * Work unit: a tile = one 16-token block of one KV head (16 x D elements
 //    of K and of V, contiguous in the cache).  The tiles of all sequences
 //    form one ordered list, (sequence, KV head, block) with the block index

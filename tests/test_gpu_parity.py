@@ -148,6 +148,25 @@ def test_decode_is_deterministic():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+def test_decode_full_batch_bit_identical_across_calls():
+    """The GQA batch-256 workload, eight calls: thousands of segments are cut
+    between waves and merged by whichever wave arrives last, so the merging
+    wave differs from call to call; the pieces are combined in wave order
+    with the same rounding wherever they are combined, so every call gives
+    the same bits (a regression test: once one element in a million could
+    come out one ulp apart)."""
+    w = workloads.config3()
+    view = GpuView(w)
+    fill_sequential(view)
+    view.tables()
+    first = view.decode().clone()
+    for i in range(7):
+        again = view.decode()
+        torch.cuda.synchronize()
+        diff = int((again.view(torch.int16) != first.view(torch.int16)).sum())
+        assert diff == 0, f"call {i + 2}: {diff} elements differ from the first call"
+
+
 def test_decode_long_contexts_split_across_many_waves():
     """Two long GQA contexts: each (sequence, KV head) run of tiles is cut
     between well over a hundred waves, whose pieces the last one merges."""
