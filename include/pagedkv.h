@@ -77,9 +77,9 @@ typedef struct {
   int32_t num_blocks;    /* physical blocks in each of the K and V caches */
   int32_t block_size;    /* tokens per block: 8, 16 (PA_BLOCK_SIZE), 32 or 64;
                             decode streams tiles of 16 tokens: 2 or 4 per block
-                            of 32 or 64, and a tile of two 8-token blocks when
-                            each cache is under 2 GiB - 128 KiB (larger
-                            8-token-block caches take the partition path) */
+                            of 32 or 64, and a tile of two 8-token blocks (one
+                            buffer descriptor over a cache under 2 GiB - 128
+                            KiB, 64-bit per-lane addresses beyond) */
   int32_t num_kv_heads;  /* Hkv >= 1 */
   int32_t head_dim;      /* D: 64 or 128 */
   int32_t cache_dtype;   /* pa_dtype of both caches */
@@ -178,9 +178,8 @@ pa_status pa_decode_workspace_init(void* workspace, size_t workspace_bytes,
  *   64 or 128, pieces are equal shares of the whole batch's KV tiles (a KV
  *   head with G > 16 query heads is streamed as the fewest equal blocks of
  *   at most 16 of them, each reading the head's tiles; at most 511 such
- *   blocks over all KV heads); otherwise (fp32 caches, and 8-token-block
- *   caches of 2 GiB or more) pieces are PA_PARTITION_TOKENS-token
- *   partitions.  Pieces are merged in a fixed order, so repeated calls give
+ *   blocks over all KV heads); otherwise (fp32 caches) pieces are
+ *   PA_PARTITION_TOKENS-token partitions.  Pieces are merged in a fixed order, so repeated calls give
  *   bit-identical results.
  */
 pa_status pa_decode(const pa_cache_desc* c, const void* k_cache,

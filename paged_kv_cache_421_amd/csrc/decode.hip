@@ -226,7 +226,8 @@ struct StreamArgs {
   int chunk;                  // T: new tokens per sequence
   int window;                 // W > 0: attend only the last W positions; 0: all
   int sub_shift;              // log2(block size / 16): tiles per block = 1 << sub_shift
-  int pair_nrec;              // 8-token blocks: bytes of one cache (< 2^31 - 2^16)
+  int pair_nrec;              // 8-token blocks: bytes of one cache (< 2^31 - 2^16), or 0
+                              // for a larger cache (a descriptor per block)
   // shared prefixes (null when unused): a sequence with prefix_len[s] > 0
   // has the attention over its first prefix_len[s] positions in
   // prefix_rec[(s*Hq + h)*(kD + 4)]: unnormalised o[kD], max m (log2 units),
@@ -1066,6 +1067,41 @@ decode_stream_kernel(StreamArgs a,
           hb = __builtin_amdgcn_readfirstlane(s_pair[t]);
         }
         const int rows = k_nrec / kRowBytes;
+        if (a.pair_nrec == 0) {
+          // a cache of 2 GiB or more, beyond one descriptor's 32-bit offsets.
+          // Each K load spans all 16 rows, so K is read with global loads
+          // from per-lane 64-bit addresses (rows 0-7 in the first block,
+          // 8-15 in the second), switched off for rows past the context,
+          // whose registers are zeroed first; a V load covers rows of one
+          // block only and keeps a buffer descriptor per block.
+          const int64_t blk_a = static_cast<int64_t>(ha) * (8 * kRowBytes);
+          const int64_t blk_b = static_cast<int64_t>(hb) * (8 * kRowBytes);
+          const char* kp = a.k_cache + (row < 8 ? blk_a : blk_b) + (row & 7) * kRowBytes +
+                           (kFp8 ? 16 : 8 * kE) * quad;
+#pragma unroll
+          for (int j = 0; j < kKLoads; ++j) kt[slot][j] = u32x4_t{0u, 0u, 0u, 0u};
+          if (row < rows) {
+#pragma unroll
+            for (int j = 0; j < kKLoads; ++j)
+              kt[slot][j] = __builtin_nontemporal_load(
+                  reinterpret_cast<const u32x4_t*>(kp + (kFp8 ? 64 : 32 * kE) * j));
+          }
+          const __amdgpu_buffer_rsrc_t rva = make_rsrc(a.v_cache + blk_a, min(rows, 8) * kRowBytes);
+          const __amdgpu_buffer_rsrc_t rvb = make_rsrc(a.v_cache + blk_b, max(rows - 8, 0) * kRowBytes);
+          static_assert(8 % kRowsPerLoad == 0, "a V load stays inside one 8-row block");
+#pragma unroll
+          for (int i = 0; i < kVLoads; ++i) {
+            const bool second = i * kRowsPerLoad >= 8;       // the block of this load's rows
+            const int vo = ((v_r + i * kRowsPerLoad) & 7) * kRowBytes + 8 * v_c * kE;
+            if constexpr (kFp8)
+              vt[slot][i] = __builtin_bit_cast(Chunk, __builtin_amdgcn_raw_buffer_load_b64(second ? rvb : rva, vo, 0, kAux));
+            else
+              vt[slot][i] = __builtin_amdgcn_raw_buffer_load_b128(second ? rvb : rva, vo, 0, kAux);
+          }
+          (void)tile_off;
+          (void)v_nrec;
+          return;
+        }
         auto row_at = [&](int r) -> int {                  // byte offset of tile row r
           return r < rows ? static_cast<int>((r < 8 ? ha : hb) * static_cast<uint32_t>(8 * kRowBytes)) +
                                 (r & 7) * kRowBytes
@@ -1973,9 +2009,10 @@ int num_partitions(int32_t max_context_len) {
   return (max_context_len + kPartTokens - 1) / kPartTokens;
 }
 
-// Largest cache (bytes of K, or of V) the 8-token-block mode addresses:
-// one buffer descriptor with 32-bit offsets, and room past it for the
-// out-of-range offset of masked rows.
+// Largest cache (bytes of K, or of V) the 8-token-block mode addresses
+// with one buffer descriptor (32-bit offsets, and room past it for the
+// out-of-range offset of masked rows); larger caches take a descriptor per
+// block, with K loaded once per block of the tile.
 constexpr int64_t kPairCacheMax = int64_t{0x7FFF0000} - (int64_t{1} << 16);
 
 bool fast_path(int fmt, int q_dtype, int G, int D, int bs) {
@@ -1998,11 +2035,9 @@ int64_t cache_bytes(const pa_cache_desc* c) {
   return static_cast<int64_t>(c->num_blocks) * c->num_kv_heads * c->block_size * c->head_dim * e;
 }
 
-// The fast path for this cache: 8-token blocks only while one cache fits
-// the paired mode's descriptor.
+// The fast path for this cache and head map.
 bool fast_path(const pa_cache_desc* c, int q_dtype, int G) {
   return fast_path(c->cache_dtype, q_dtype, G, c->head_dim, c->block_size) &&
-         (c->block_size != 8 || cache_bytes(c) <= kPairCacheMax) &&
          static_cast<int64_t>(c->num_kv_heads) * head_split(G) <= 511;   // 9-bit head field
 }
 
@@ -2108,7 +2143,7 @@ pa_status attend(const char* fn, const pa_cache_desc* c, const void* k_cache,
   const int64_t max_tiles = static_cast<int64_t>(hk) * num_seqs *
                             ((static_cast<int64_t>(max_context_len) + kTile - 1) / kTile);
   if (fast && (max_tiles >= (int64_t{1} << 30) || num_seqs > static_cast<int32_t>(kSeqMask) ||
-               static_cast<int64_t>(c->num_blocks) * hkv * (bs / kTile) >= (int64_t{1} << 32) ||
+               static_cast<int64_t>(c->num_blocks) * hkv * std::max(1, bs / kTile) >= (int64_t{1} << 32) ||
                static_cast<int64_t>(max_blocks_per_seq) * 4 >= (int64_t{1} << 31) ||
                (static_cast<int64_t>(T - 1) * num_q_heads + Gk) * D * 2 >= (int64_t{1} << 30)))
     return fail(PA_ERR_UNSUPPORTED, "%s: %lld tiles in one call (limit 2^30)", fn,
@@ -2162,7 +2197,8 @@ pa_status attend(const char* fn, const pa_cache_desc* c, const void* k_cache,
     a.chunk = T;
     a.window = W;
     a.sub_shift = bs == 64 ? 2 : bs == 32 ? 1 : 0;
-    a.pair_nrec = bs == 8 ? static_cast<int>(cache_bytes(c)) : 0;
+    // 8-token blocks: one descriptor over a cache below 2 GiB - 128 KiB, else one per block
+    a.pair_nrec = (bs == 8 && cache_bytes(c) <= kPairCacheMax) ? static_cast<int>(cache_bytes(c)) : 0;
     a.prefix_len = prefix_len;
     a.prefix_rec = prefix_rec;
     a.logit_scale = logit_scale;

@@ -2,7 +2,8 @@
 slots and cache bytes equal the oracle's bit for bit, copy-on-write copies
 are exact, and decode / chunks / windows match the oracle.  32- and 64-token
 blocks stream as 2 or 4 tiles of 16, 8-token blocks as tiles of two blocks;
-an fp32 cache takes the partition path at every block size."""
+an fp32 cache takes the partition path at every block size; 8-token blocks in a
+cache over 2 GiB give the small cache's results bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -115,3 +116,45 @@ def test_copy_on_write_at_block_size(bs):
     torch.cuda.synchronize()
     assert np.array_equal(cache_to_numpy(kc, "bf16").view(np.uint8), kc_o.view(np.uint8))
     assert np.array_equal(cache_to_numpy(vc, "bf16").view(np.uint8), vc_o.view(np.uint8))
+
+
+@pytest.mark.parametrize("fmt,G,D", [("bf16", 4, 128), ("fp8", 8, 64)])
+def test_8_token_blocks_in_caches_over_2gib(fmt, G, D):
+    """Caches of 2 GiB and more cannot be addressed by one buffer descriptor
+    with 32-bit offsets, so their 8-token tiles take a descriptor per block.
+    The small case's blocks are placed in a 2.5 GiB cache, every other one
+    past 2 GiB (so tiles straddle the boundary): decode, chunks and windows
+    give the small cache's results bit for bit (those match the oracle in
+    test_decode_chunk_and_window_at_block_size)."""
+    bs = 8
+    w, desc, kc, vc, kc_o, vc_o, bt, cl = _build(1200 + D, fmt, bs, G, D, LENS)
+    nb = desc.c.num_blocks
+    per_block = w.Hkv * bs * D * (1 if fmt == "fp8" else 2)
+    nb_big = (5 << 29) // per_block                       # 2.5 GiB per cache
+    high = (1 << 31) // per_block + 1000                  # first block id past 2 GiB
+    ids = np.arange(nb)
+    to_big = np.where(ids % 2 == 0, ids, high + ids).astype(np.int64)
+    assert to_big.max() < nb_big
+    desc_big = pk.CacheDesc(nb_big, w.Hkv, D, fmt, w.k_scale, w.v_scale, block_size=bs)
+    kb = torch.zeros((nb_big, w.Hkv, bs, D), dtype=kc.dtype, device="cuda")
+    vb = torch.zeros_like(kb)
+    idx = torch.from_numpy(to_big).cuda()
+    kb.index_copy_(0, idx, kc)
+    vb.index_copy_(0, idx, vc)
+    bt_big = to_big[bt].astype(np.int32)
+    _say(f"8-token blocks {fmt} G={G} D={D}: cache {nb_big} blocks, {nb_big * per_block / 2**30:.2f} GiB")
+    cld = torch.from_numpy(cl).cuda()
+    max_len = int(cl.max())
+    for T, W in ((1, 0), (4, 0), (3, 40)):
+        q = workloads.chunk_queries(np.random.default_rng(bs + T + W), w.B, T, w.Hq, D, w.q_fmt)
+        qd = to_device_rows(q, w.q_fmt)
+        small, big = torch.empty_like(qd), torch.empty_like(qd)
+        pk.decode_chunk(desc, kc, vc, qd, small, torch.from_numpy(bt).cuda(), cld, max_len,
+                        float(w.scale), window=W)
+        pk.decode_chunk(desc_big, kb, vb, qd, big, torch.from_numpy(bt_big).cuda(), cld, max_len,
+                        float(w.scale), window=W)
+        torch.cuda.synchronize()
+        assert torch.equal(small.view(torch.int16), big.view(torch.int16)), (T, W)
+        _say(f"  T={T} W={W}: bit-identical")
+    del kb, vb
+    torch.cuda.empty_cache()

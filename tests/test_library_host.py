@@ -101,14 +101,14 @@ def test_workspace_size_formula():
     # invalid shapes report 0
     assert pk.decode_workspace_bytes(bf, 4, 12, 100) == 0
     assert pk.decode_workspace_bytes(bf, 0, 8, 100) == 0
-    # 8-token blocks stream in pairs while one cache stays under 2 GiB -
-    # 128 KiB (one buffer descriptor over it); larger caches take the
-    # partition path and its workspace
+    # 8-token blocks stream in pairs with one buffer descriptor while a cache
+    # stays under 2 GiB - 128 KiB, with one per block beyond: the same
+    # workspace either way
     per_block = 8 * 8 * 128 * 2                      # Hkv 8, D 128, bf16
     small = pk.CacheDesc((0x7FFF0000 - (1 << 16)) // per_block, 8, 128, "bf16", block_size=8)
     big = pk.CacheDesc((0x7FFF0000 - (1 << 16)) // per_block + 1, 8, 128, "bf16", block_size=8)
     assert pk.decode_workspace_bytes(small, 256, 32, 4096) == 256 * 8 * 4 + waves * 2 * 4 * 130 * 4
-    assert pk.decode_workspace_bytes(big, 256, 32, 4096) == 256 * 32 * 8 * 130 * 4
+    assert pk.decode_workspace_bytes(big, 256, 32, 4096) == 256 * 8 * 4 + waves * 2 * 4 * 130 * 4
 
 
 def test_chunk_workspace_size_formula():
