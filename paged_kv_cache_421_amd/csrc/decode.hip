@@ -254,15 +254,19 @@ struct StreamArgs {
   const int32_t* rec_count;
 };
 
-// Groups of a shared-prefix batch decoded in one launch (kGrp): group k is
-// sequences first[k] .. first[k] + count[k] - 1, whose first shared[k]
-// table entries name the same blocks.  Entries k >= num are all zero.
+// Groups of a shared-prefix batch decoded in one launch (kGrp), one word per
+// sequence (at most 256): bit 0 -- the sequence is a member of a group
+// whose first `shared` table entries name the same blocks; bit 1 -- it is
+// the group's first member (its leader); bits 2..10 -- the group's member
+// count, in the leader's word only; bits 11..31 -- shared.  Sequences
+// outside groups (and past the batch) have word 0.
 struct GroupTable {
-  int num;
-  int first[PA_MAX_PREFIX_GROUPS];
-  int count[PA_MAX_PREFIX_GROUPS];
-  int shared[PA_MAX_PREFIX_GROUPS];
+  uint32_t info[256];
 };
+constexpr uint32_t kGrpMember = 1u, kGrpLeader = 2u;
+__host__ __device__ constexpr uint32_t grp_count(uint32_t w) { return (w >> 2) & 511u; }
+__host__ __device__ constexpr uint32_t grp_shared(uint32_t w) { return w >> 11; }
+constexpr uint32_t kGrpMaxShared = (1u << 21) - 1;
 struct NoGroupTable {
   int num;
 };
@@ -328,64 +332,43 @@ decode_stream_kernel(StreamArgs a,
   for (int r = 0; r < 4; ++r)
     Lr[r] = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(lens_rsrc, (64 * r + lane) * 4, 0, 0));
 
-  // kGrp: the group table in LDS, each sequence's group (Gid, -1 for none)
-  // and the tiles per KV head of the segment it starts (Ur: a group's
-  // leader counts the prefix and every member's own tiles, the other
-  // members 0, a sequence outside groups its own tiles)
-  __shared__ int s_gt_all[kWavesPerGroup][3][kGrp ? PA_MAX_PREFIX_GROUPS : 1];
-  __shared__ short s_gid_all[kWavesPerGroup][kGrp ? 256 : 1];
-  int (&s_gt)[3][kGrp ? PA_MAX_PREFIX_GROUPS : 1] = s_gt_all[wig];
-  short* s_gid = s_gid_all[wig];
-  int Gid[4] = {-1, -1, -1, -1}, Ur[4] = {0, 0, 0, 0};
+  // kGrp: each sequence's group word (Inf: lane l of register r holds
+  // sequence 64r + l), read from the kernel arguments beside the lengths,
+  // and the tiles per KV head of the segment the sequence starts (Ur: a
+  // group's leader counts the prefix and every member's own tiles, the
+  // other members 0, a sequence outside groups its own tiles)
+  uint32_t Inf[4] = {0u, 0u, 0u, 0u};
+  int Ur[4] = {0, 0, 0, 0};
   const int tile_shift = a.sub_shift;                      // block tiles = 1 << tile_shift
   if constexpr (kGrp) {
-    // all PA_MAX_PREFIX_GROUPS entries, two per lane, read without waiting
-    // for gt.num (entries past it are zero: count 0 marks nothing), so the
-    // reads overlap the length loads
-    static_assert(PA_MAX_PREFIX_GROUPS == 128, "two group-table entries per lane");
-    int gf[2], gc[2];
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int i = 64 * e + lane;
-      gf[e] = gt.first[i];
-      gc[e] = gt.count[i];
-      s_gt[0][i] = gf[e];
-      s_gt[1][i] = gc[e];
-      s_gt[2][i] = gt.shared[i];
-    }
-    for (int i = lane; i < 256; i += 64) s_gid[i] = -1;
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-      for (int m = 0; m < gc[e]; ++m) s_gid[gf[e] + m] = static_cast<short>(64 * e + lane);
+    for (int r = 0; r < 4; ++r) Inf[r] = gt.info[64 * r + lane];
     int suf[4], S[4], carry = 0;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int sq = 64 * r + lane;
-      Gid[r] = sq < B ? s_gid[sq] : -1;
-      const int P = Gid[r] >= 0 ? (s_gt[2][Gid[r]] << tile_shift) * kTile : 0;
-      suf[r] = Gid[r] >= 0 ? (max(Lr[r] - P, 0) + kTile - 1) / kTile : 0;
+      const int P = static_cast<int>(grp_shared(Inf[r]) << tile_shift) * kTile;
+      suf[r] = (Inf[r] & kGrpMember) ? (max(Lr[r] - P, 0) + kTile - 1) / kTile : 0;
       S[r] = wave_incl_scan(suf[r]) + carry;
       carry = readlane_i(S[r], 63);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int sq = 64 * r + lane;
-      const int k = Gid[r];
-      const bool lead = k >= 0 && s_gt[0][k] == sq;
-      const int end = lead ? sq + s_gt[1][k] - 1 : sq;     // the group's last member
+      const bool lead = (Inf[r] & kGrpLeader) != 0;
+      const int end = lead ? sq + static_cast<int>(grp_count(Inf[r])) - 1 : sq;   // the group's last member
       const int e_same = __shfl(S[r], end & 63);
       const int e_next = __shfl(S[r < 3 ? r + 1 : 3], end & 63);
       const int s_end = (end >> 6) == r ? e_same : e_next;
-      Ur[r] = k < 0 ? (sq < B ? (Lr[r] + kTile - 1) / kTile : 0)
-                    : lead ? (s_gt[2][k] << tile_shift) + s_end - S[r] + suf[r] : 0;
+      Ur[r] = !(Inf[r] & kGrpMember) ? (sq < B ? (Lr[r] + kTile - 1) / kTile : 0)
+              : lead ? static_cast<int>(grp_shared(Inf[r]) << tile_shift) + s_end - S[r] + suf[r] : 0;
     }
   }
   (void)gt;
-  // group of sequence sq (< 256), wave-uniform; its rows written per segment
-  auto gid_of = [&](int sq) -> int {
+  // group word of sequence sq (< 256), wave-uniform
+  auto info_of = [&](int sq) -> uint32_t {
     const int r = sq >> 6;
-    const int v = (r == 0) ? Gid[0] : (r == 1) ? Gid[1] : (r == 2) ? Gid[2] : Gid[3];
-    return readlane_i(v, sq & 63);
+    const uint32_t v = (r == 0) ? Inf[0] : (r == 1) ? Inf[1] : (r == 2) ? Inf[2] : Inf[3];
+    return static_cast<uint32_t>(readlane_i(static_cast<int>(v), sq & 63));
   };
   auto ut_of = [&](int sq) -> int {
     const int r = sq >> 6;
@@ -396,8 +379,8 @@ decode_stream_kernel(StreamArgs a,
   // members for a group leader, else sq alone
   auto seg_count = [&](int sq) -> int {
     if constexpr (kGrp) {
-      const int k = gid_of(sq);
-      return (k >= 0 && s_gt[0][k] == sq) ? s_gt[1][k] : 1;
+      const uint32_t inf = info_of(sq);
+      return (inf & kGrpLeader) ? static_cast<int>(grp_count(inf)) : 1;
     } else {
       return R / G;
     }
@@ -409,7 +392,7 @@ decode_stream_kernel(StreamArgs a,
       const int s = s0 + 64 * r + lane;
       c += kGrp ? Ur[r] : tiles_of(L[r]);
       const uint64_t empty = __builtin_amdgcn_ballot_w64(s < B && L[r] == 0 && s % a.num_waves == w &&
-                                                         a.rec_out == nullptr && Gid[r] < 0);
+                                                         a.rec_out == nullptr && !(Inf[r] & kGrpMember));
       for (uint64_t m = empty; m != 0; m &= m - 1) {
         const int se = s0 + 64 * r + __builtin_ctzll(m);
         uint16_t* orow = a.out + (static_cast<int64_t>(se) * nchunk + a.t_first) * hq * kD;
@@ -886,16 +869,16 @@ decode_stream_kernel(StreamArgs a,
       // prefix on, rows to its end), the member in word 2's top bits (1 +
       // its index; 0 for the prefix and for segments outside groups)
       for (int pos = 0; pos < n;) {
-        const int k = gid_of(w_s);
+        const uint32_t inf = info_of(w_s);                    // a leader, or a lone sequence
         int sub_start = 0, sub_end = w_nb, tbase = 0, sublen = w_L, tseq = w_s, code = 0;
-        if (k >= 0) {
-          const int Pt = s_gt[2][k] << tile_shift, P = Pt * kTile;
+        if (inf & kGrpLeader) {
+          const int Pt = static_cast<int>(grp_shared(inf) << tile_shift), P = Pt * kTile;
           if (w_j < Pt) {
             sub_end = Pt;
             sublen = P;
           } else {
             int cum = Pt;
-            const int cnt = s_gt[1][k];
+            const int cnt = static_cast<int>(grp_count(inf));
             for (int m = 0; m < cnt; ++m) {
               const int Lm = len_of(w_s + m);
               const int sm = (max(Lm - P, 0) + kTile - 1) / kTile;
@@ -1153,9 +1136,10 @@ decode_stream_kernel(StreamArgs a,
       if (info & 32u) {                                      // a piece starts here
         if constexpr (kGrp) {
           // a group's rows see the prefix up to their own member's length
-          const int k = gid_of(lead);
-          if (k >= 0 && s_gt[0][k] == lead) {
-            const int P = (s_gt[2][k] << tile_shift) * kTile, cnt = s_gt[1][k];
+          const uint32_t inf = info_of(lead);
+          if (inf & kGrpLeader) {
+            const int P = static_cast<int>(grp_shared(inf) << tile_shift) * kTile;
+            const int cnt = static_cast<int>(grp_count(inf));
             const int sq = lead + min(t_row, cnt - 1);        // < 256
             const int li = sq & 63, rb = sq >> 6;
             const int l0 = __shfl(Lr[0], li), l1 = __shfl(Lr[1], li);
@@ -2490,10 +2474,11 @@ extern "C" pa_status pa_decode_shared_prefix(
   PrefixGroups gr{};
   gr.num = num_groups;
   std::vector<std::pair<int, int>> spans;
-  int wgs = 0, max_tiles = 0, max_count = 0;
+  int wgs = 0, max_tiles = 0, max_count = 0, max_shared = 0;
   for (int i = 0; i < num_groups; ++i) {
     const int f = groups[3 * i], n = groups[3 * i + 1], m = groups[3 * i + 2];
     max_count = std::max(max_count, n);
+    max_shared = std::max(max_shared, m);
     if (f < 0 || n < 1 || m < 1 || static_cast<int64_t>(f) + n > num_seqs || m > max_blocks_per_seq)
       return fail(PA_ERR_INVALID_ARG, "%s: group %d = (%d, %d, %d) out of range", fn, i, f, n, m);
     gr.first[i] = f;
@@ -2557,17 +2542,18 @@ extern "C" pa_status pa_decode_shared_prefix(
   pa.grp_lens = nullptr;
   pa.grp_count = nullptr;
   const bool fp8 = c->cache_dtype == PA_FP8_E4M3;
-  if (max_count * G <= kMaxRows && num_seqs <= 256) {
+  if (max_count * G <= kMaxRows && num_seqs <= 256 &&
+      static_cast<uint32_t>(max_shared) <= kGrpMaxShared) {
     // Small groups, at most 256 sequences: one launch of the decode kernel
     // in which each (group, KV head) is one segment -- the prefix tiles,
     // then every member's own tiles -- with all members' rows (kGrp).
     GroupTable gtab{};
-    gtab.num = num_groups;
     int64_t tiles = 0;
     for (int i = 0; i < num_groups; ++i) {
-      gtab.first[i] = groups[3 * i];
-      gtab.count[i] = groups[3 * i + 1];
-      gtab.shared[i] = groups[3 * i + 2];
+      const int f = groups[3 * i], n = groups[3 * i + 1];
+      const uint32_t sh = static_cast<uint32_t>(groups[3 * i + 2]) << 11;
+      for (int m = 0; m < n; ++m)
+        gtab.info[f + m] = kGrpMember | sh | (m == 0 ? kGrpLeader | (static_cast<uint32_t>(n) << 2) : 0u);
     }
     tiles = static_cast<int64_t>(hkv) * num_seqs * ((static_cast<int64_t>(max_context_len) + kTile - 1) / kTile);
     const int64_t waves_max = static_cast<int64_t>(device_cus()) * kWavesPerCU;
