@@ -136,6 +136,18 @@ __device__ __forceinline__ int div_small(int x, float rcp) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, kRsrcWord3);
 }
+// The same for a base and size that are wave-uniform but that the compiler
+// may not prove so (values merged across branches): taken through
+// readfirstlane, the descriptor stays in scalar registers instead of a
+// loop over lanes around every load that uses it.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_uniform(const char* base, int64_t off,
+                                                                     int bytes) {
+  const uint64_t o = static_cast<uint64_t>(off);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(o & 0xFFFFFFFFu)));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(o >> 32)));
+  const int n = __builtin_amdgcn_readfirstlane(bytes);
+  return make_rsrc(base + static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo), n);
+}
 
 // Inclusive prefix sum over the 64 lanes of a wave, by DPP operand moves
 // (register-to-register, no LDS round trips): shifts right by 1, 2, 4 and 8
@@ -1036,7 +1048,7 @@ decode_stream_kernel(StreamArgs a,
           q_nrec = static_cast<int>(min(static_cast<int64_t>(q_bytes), q_all_bytes - q_off));
         }
       }
-      const __amdgpu_buffer_rsrc_t rq = make_rsrc(reinterpret_cast<const char*>(a.q) + q_off, q_nrec);
+      const __amdgpu_buffer_rsrc_t rq = make_rsrc_uniform(reinterpret_cast<const char*>(a.q), q_off, q_nrec);
 #pragma unroll
       for (int kk = 0; kk < kKK; ++kk) qs[slot][kk] = __builtin_amdgcn_raw_buffer_load_b128(rq, q_lane_off + q_step_off(kk), 0, 0);
       if constexpr (kPair) {
@@ -1108,8 +1120,8 @@ decode_stream_kernel(StreamArgs a,
         (void)v_nrec;
         return;
       }
-      const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k_cache + tile_off, k_nrec);
-      const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v_cache + tile_off, v_nrec);
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc_uniform(a.k_cache, tile_off, k_nrec);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc_uniform(a.v_cache, tile_off, v_nrec);
 #pragma unroll
       for (int j = 0; j < kKLoads; ++j)
         kt[slot][j] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_off + (kFp8 ? 64 : 32 * kE) * j, 0, kAux);
@@ -1185,14 +1197,17 @@ decode_stream_kernel(StreamArgs a,
       // shift), or one a window start cuts, has rows a query row may not
       // see; a wave-uniform test skips the masking for every other tile.
       if constexpr (kGrp) {
-        if (code != 0) {                                     // a member's tile: its rows only
-          const int lim = (t_row == code - 1) ? rows_left : 0;
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (4 * quad + r >= lim) x[r] = -INFINITY;
-        } else if (g_short || rows_left < kTile) {          // prefix (or a lone sequence's) tile
-          const int jl = t_begin + done + t - __builtin_amdgcn_readfirstlane(static_cast<int>(d[3]));
-          const int lim = min(rows_left, g_plim - kTile * jl);
+        // one masking step for every case (a member's tile: its rows only; a
+        // prefix tile: each row up to its member's length; a tile at a
+        // context's end), skipped by one wave-uniform test otherwise
+        if (code != 0 || g_short || rows_left < kTile) {
+          int lim = rows_left;
+          if (code != 0) {
+            lim = (t_row == code - 1) ? rows_left : 0;
+          } else if (g_short) {
+            const int jl = t_begin + done + t - __builtin_amdgcn_readfirstlane(static_cast<int>(d[3]));
+            lim = min(rows_left, g_plim - kTile * jl);
+          }
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             if (4 * quad + r >= lim) x[r] = -INFINITY;
