@@ -26,7 +26,10 @@ __global__ void __launch_bounds__(256)
 read_probe_kernel(const char* __restrict__ buf, int64_t num_chunks,
                   const int32_t* __restrict__ order, uint32_t* __restrict__ sink) {
   const int lane = threadIdx.x & 63;
-  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
+  // wave-uniform, taken through readfirstlane so that the chunk descriptors
+  // stay in scalar registers (no loop over lanes around each load)
+  const int64_t wave = __builtin_amdgcn_readfirstlane(
+      static_cast<int>((static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6));
   const int64_t waves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
   u32x4_t acc = {0u, 0u, 0u, 0u};
   for (int64_t c0 = wave; c0 < num_chunks; c0 += waves * kProbeUnroll) {
