@@ -617,14 +617,15 @@ decode_stream_kernel(StreamArgs a,
     const int rr = lane / kLPR;
     const int ch = lane - rr * kLPR;
     const int nrows = kGrp ? seg_count(s) * G : R;         // kGrp: the segment's members only
+    // the segment's first output row (wave-uniform); row n is chunk token (or
+    // member) n / G, one token or sequence = hq rows further
+    uint16_t* const obase = a.out + ((static_cast<int64_t>(s) * nchunk + a.t_first) * hq + g * G) * kD;
     for (int r0 = 0; r0 < nrows; r0 += kRPP) {
       const int n = r0 + rr;
       if (n < nrows) {
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(s_o + n * kOPitch + ch * 16);
         const int nt = div_small(n, rcp_G);
-        uint16_t* dst = a.out + ((static_cast<int64_t>(s) * nchunk + a.t_first + nt) * hq +
-                                 g * G + (n - nt * G)) * kD + ch * 8;
-        *reinterpret_cast<u32x4_t*>(dst) = v;
+        *reinterpret_cast<u32x4_t*>(obase + (nt * hq + (n - nt * G)) * kD + ch * 8) = v;
       }
     }
   };
