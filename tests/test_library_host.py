@@ -558,6 +558,12 @@ def test_shared_prefix_decode_validates_groups_on_the_host():
                                         al, ws_bytes, None)
     assert st == -2
     assert pk.shared_prefix_workspace_bytes(f32, B, Hq, mb, 128) == 0
+    # more than 16 query heads per KV head: pa_decode streams them in row
+    # blocks, the shared-prefix path does not take them
+    st = pk.lib.pa_decode_shared_prefix(ctypes.byref(d.c), one, one, al, 1, al, one, mb, one,
+                                        128, B, 64, 1.0, g1.ctypes.data, 1, al, ws_bytes, None)
+    assert st == -2 and b"G <= 16" in pk.lib.pa_last_error()
+    assert pk.shared_prefix_workspace_bytes(d, B, 64, mb, 128) == 0
     # the layout: pa_decode's scratch, suffix tables and lengths, prefix
     # lengths, then one record of D + 4 floats per (sequence, query head)
     assert ws_bytes >= pk.decode_workspace_bytes(d, B, Hq, 128) + 4 * B * mb + 8 * B + \

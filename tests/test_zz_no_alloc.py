@@ -51,7 +51,7 @@ def _both(w, view):
 
 
 @pytest.mark.parametrize("fmt,G,D", [("bf16", 4, 128), ("fp8", 8, 64), ("bf16", 16, 128),
-                                     ("f32", 2, 64)])
+                                     ("f32", 2, 64), ("bf16", 32, 64)])
 def test_noalloc_matches_decode_on_two_calls_second_smaller(fmt, G, D):
     Hkv = 4 if fmt != "f32" else 2
     big = [0, 1, 17, 300, 2100, 5000, 640, 33, 1200, 16, 9000, 700] * 3
