@@ -73,6 +73,10 @@ def test_decode_on_an_explicit_stream_without_a_workspace():
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+@pytest.mark.skipif(
+    pytest.importorskip("paged_kv_cache_421_amd._lib").LIB_PATH.endswith("_debug.so"),
+    reason="the PA_DEBUG library copies device arrays back before each launch (a synchronising "
+           "copy), which graph capture does not allow")
 def test_write_and_decode_replay_from_a_captured_graph():
     w, view = _view(1201)
     B, Hq, Hkv, D = w.B, w.Hq, w.Hkv, w.D
