@@ -181,7 +181,7 @@ extern "C" pa_status pa_copy_blocks(const pa_cache_desc* c, void* k_cache, void*
     return fail(PA_ERR_UNSUPPORTED, "pa_copy_blocks: %d pairs (at most 65535 per call)",
                 num_pairs);
   if (!k_cache || !v_cache || !pairs) return fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: null pointer");
-  PA_DEBUG_CHECK(debug::check_pairs(pairs, num_pairs, c->num_blocks, stream, "pa_copy_blocks"));
+  PA_DEBUG_CHECK(debug::check_pairs(pairs, num_pairs, c->num_blocks, true, stream, "pa_copy_blocks"));
   const int64_t block_bytes = static_cast<int64_t>(c->num_kv_heads) * c->block_size *
                               c->head_dim * dtype_bytes(c->cache_dtype);
   const int64_t chunks = block_bytes / 16;
@@ -235,7 +235,7 @@ extern "C" pa_status pa_swap_blocks(const pa_cache_desc* c, const void* src_k,
       return fail(PA_ERR_INVALID_ARG,
                   "pa_swap_blocks: %s is not device or pinned host memory", names[i]);
   // the pools' sizes are not passed, so only signs and distinct destinations
-  PA_DEBUG_CHECK(debug::check_pairs(pairs, num_pairs, -1, stream, "pa_swap_blocks"));
+  PA_DEBUG_CHECK(debug::check_pairs(pairs, num_pairs, -1, false, stream, "pa_swap_blocks"));
   const int64_t block_bytes = static_cast<int64_t>(c->num_kv_heads) * c->block_size *
                               c->head_dim * dtype_bytes(c->cache_dtype);
   const int64_t chunks = block_bytes / 16;

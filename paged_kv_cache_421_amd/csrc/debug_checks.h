@@ -16,10 +16,11 @@ namespace debug {
 pa_status check_slots(const pa_cache_desc* c, const int64_t* slots, int32_t n, void* stream,
                       const char* fn);
 
-// pairs[n][2] of (src, dst) blocks: destinations distinct and none of them a
-// source; with num_blocks >= 0 every id is below it (else only >= 0).
-pa_status check_pairs(const int32_t* pairs, int32_t n, int32_t num_blocks, void* stream,
-                      const char* fn);
+// pairs[n][2] of (src, dst) blocks: destinations distinct, and with
+// same_pool (a copy inside one pool) none of them a source; with
+// num_blocks >= 0 every id is below it (else only >= 0).
+pa_status check_pairs(const int32_t* pairs, int32_t n, int32_t num_blocks, bool same_pool,
+                      void* stream, const char* fn);
 
 // context_lens[B] within [0, max_len]; the first ceil(L / bs) entries of each
 // row of block_tables[B][max_blocks] are valid block ids.

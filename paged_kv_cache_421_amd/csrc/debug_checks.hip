@@ -55,8 +55,8 @@ pa_status check_slots(const pa_cache_desc* c, const int64_t* slots, int32_t n, v
   return PA_OK;
 }
 
-pa_status check_pairs(const int32_t* pairs, int32_t n, int32_t num_blocks, void* stream,
-                      const char* fn) {
+pa_status check_pairs(const int32_t* pairs, int32_t n, int32_t num_blocks, bool same_pool,
+                      void* stream, const char* fn) {
   std::vector<int32_t> h;
   pa_status st = fetch(pairs, 2 * static_cast<int64_t>(n), stream, &h, fn);
   if (st != PA_OK) return st;
@@ -73,8 +73,10 @@ pa_status check_pairs(const int32_t* pairs, int32_t n, int32_t num_blocks, void*
       return fail(PA_ERR_INVALID_ARG, "%s (PA_DEBUG): destination block %d appears twice", fn,
                   h[2 * i + 1]);
   }
+  // within one pool a block must not be both read and written by one call;
+  // between two pools (a swap) the ids name different blocks
   for (int32_t d : dst)
-    if (src.count(d))
+    if (same_pool && src.count(d))
       return fail(PA_ERR_INVALID_ARG, "%s (PA_DEBUG): block %d is both a source and a destination",
                   fn, d);
   return PA_OK;

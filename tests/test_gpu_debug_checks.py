@@ -136,3 +136,26 @@ def test_groups_whose_tables_differ_are_reported(debug_lib):
                                                     float(w.scale),
                                                     np.array([[2, 2, 2]], np.int32)),
                     "group 0")
+
+
+def test_swap_pairs_may_reuse_an_id_across_the_two_pools(debug_lib):
+    """A swap reads one pool and writes the other, so a device block and a
+    host block with the same id are different blocks: the debug build takes
+    such pairs (only a copy inside one pool rejects an id that is both read
+    and written), and the blocks arrive byte for byte.  A destination named
+    twice is still reported."""
+    w, view = _view()
+    nb = view.desc.c.num_blocks
+    host_k = torch.zeros(view.kc.shape, dtype=view.kc.dtype, pin_memory=True)
+    host_v = torch.zeros(view.kc.shape, dtype=view.kc.dtype, pin_memory=True)
+    pairs = torch.tensor([[2, 3], [3, 2], [5, 5]], dtype=torch.int32, device="cuda")
+    pk.swap_blocks(view.desc, view.kc, view.vc, host_k, host_v, pairs)
+    torch.cuda.synchronize()
+    for s, d in ((2, 3), (3, 2), (5, 5)):
+        assert torch.equal(host_k[d].view(torch.int16), view.kc[s].cpu().view(torch.int16))
+        assert torch.equal(host_v[d].view(torch.int16), view.vc[s].cpu().view(torch.int16))
+    _raises_invalid(lambda: pk.swap_blocks(view.desc, view.kc, view.vc, host_k, host_v,
+                                           torch.tensor([[1, 4], [2, 4]], dtype=torch.int32,
+                                                        device="cuda")),
+                    "destination block 4 appears twice")
+    assert nb > 5
