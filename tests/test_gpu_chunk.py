@@ -144,6 +144,11 @@ def test_chunk_gqa_batch256_every_row():
     torch.cuda.synchronize()
     ref = oracle.decode_chunk(q, "bf16", kc, vc, "bf16", bt, cl, w.scale)
     par.check(out_to_f64(out), ref, "bf16", "config 3 pa_decode_chunk T=4")
+    # 16-row segments merged by whichever wave arrives last: the same bits every call
+    for i in range(3):
+        again = view.decode_chunk(q)
+        torch.cuda.synchronize()
+        assert torch.equal(again.view(torch.int16), out.view(torch.int16)), f"repeat {i + 2}
 
 
 # ---------------------------------------------------------------- sliding window

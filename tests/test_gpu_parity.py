@@ -349,6 +349,11 @@ def _cow_case(w, n_pairs):
 
     out_sp = shared(w.q)
     torch.cuda.synchronize()
+    # group mode merges 16-row segments across waves too: every call the same bits
+    for i in range(3):
+        again = shared(w.q)
+        torch.cuda.synchronize()
+        assert torch.equal(again.view(torch.int16), out_sp.view(torch.int16)), f"repeat {i + 2}"
     err_sp = _check_out(out_sp, ref, w, kc_ref, vc_ref, bt_ref, cl_ref,
                         f"config 5 {tag}pa_decode_shared_prefix")
     diff = float((out_sp.float() - out.float()).abs().max())
