@@ -148,7 +148,7 @@ def test_chunk_gqa_batch256_every_row():
     for i in range(3):
         again = view.decode_chunk(q)
         torch.cuda.synchronize()
-        assert torch.equal(again.view(torch.int16), out.view(torch.int16)), f"repeat {i + 2}
+        assert torch.equal(again.view(torch.int16), out.view(torch.int16)), f"repeat {i + 2}"
 
 
 # ---------------------------------------------------------------- sliding window
