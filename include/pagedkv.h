@@ -423,16 +423,20 @@ pa_status pa_bm_cache_stats(const pa_bm* bm, int64_t* queried_blocks, int64_t* h
  * sees only its own length of them).  The result is pa_decode's (up to
  * rounding order); the prefix is attended once per
  * (group, KV head) on MFMA with all members' query rows and folded into each
- * row by the log-sum-exp rule.  With at most 256 sequences and every
- * group's rows of a KV head (members x G) within 16, this is one launch of
- * pa_decode's tile stream in which each (group, KV head) is one segment:
- * the prefix tiles, seen by every member's rows up to its own length, then
- * each member's own tiles, seen by that member's rows only.  With more
- * sequences the prefix runs through the same tile stream with the members
- * as query rows and the suffixes are decoded afterwards (a group with a
- * member no longer than shared * block_size is then decoded whole by the
- * suffix pass; same result).  Larger groups use a kernel that shares each
- * prefix tile among up to 128 rows in LDS, then the suffix pass.
+ * row by the log-sum-exp rule.  With at most 256 sequences this is one
+ * launch of pa_decode's tile stream in which each (group, KV head) is one
+ * segment: the prefix tiles, seen by every member's rows up to its own
+ * length, then each member's own tiles, seen by that member's rows only.  A
+ * group whose rows of a KV head (members x G) exceed 16 is cut into row
+ * groups of 16 / G members, each such a segment over the same prefix, and
+ * the tile stream then runs KV head by KV head so that the row groups of a
+ * head read its prefix tiles from one L2.  With more sequences, groups
+ * whose rows of a KV head fit 16 run the prefix through the same tile
+ * stream with the members as query rows and the suffixes are decoded
+ * afterwards (a group with a member no longer than shared * block_size is
+ * then decoded whole by the suffix pass; same result); larger groups use a
+ * kernel that shares each prefix tile among up to 128 rows in LDS, then the
+ * suffix pass.
  * Needs the bf16 / fp8 fast path (head_dim 64 or 128, G <= 16, block size a
  * multiple of 16), single-token decode, a positive scale (with groups).  workspace: zero-filled before first
  * use, 256-byte aligned, pa_decode_shared_prefix_workspace_bytes(...) bytes;

@@ -264,6 +264,14 @@ struct StreamArgs {
   // units), sum l -- the prefix records a later pass folds in.
   float* rec_out;
   const int32_t* rec_count;
+  // group mode only (kGrp), 1: the tile list is ordered by KV head first,
+  // then by segment-starting sequence, and wave w of the grid works on the
+  // range of index (w mod 8) * (waves / 8) + w / 8 (waves a multiple of 8):
+  // the dispatcher deals work-groups to the 8 XCDs in turn, so the waves of
+  // one XCD take one eighth of the list, i.e. the segments of 1/8 of the KV
+  // heads, and a prefix read by many row groups of a head stays in that
+  // XCD's L2.  0: (sequence, KV head) order, wave w takes range w.
+  int head_major;
 };
 
 // Groups of a shared-prefix batch decoded in one launch (kGrp), one word per
@@ -318,7 +326,10 @@ decode_stream_kernel(StreamArgs a,
   // waves of a work-group are independent (no barriers): a work-group only
   // places kWavesPerGroup waves on one CU together
   const int wig = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int w = blockIdx.x * kWavesPerGroup + wig;
+  const int w_grid = blockIdx.x * kWavesPerGroup + wig;
+  const bool hmaj = kGrp && a.head_major != 0;
+  // the wave's range index (head-major group mode: XCD-major, see StreamArgs)
+  const int w = hmaj ? (w_grid & 7) * (a.num_waves >> 3) + (w_grid >> 3) : w_grid;
   const int lane = threadIdx.x & 63;
   const int B = a.num_seqs;
   const int hkv = a.hkv;
@@ -376,6 +387,16 @@ decode_stream_kernel(StreamArgs a,
     }
   }
   (void)gt;
+  // the first sequence that starts a segment (head-major walk: where each
+  // head's block of the list begins)
+  int s_first = B;
+  if constexpr (kGrp) {
+#pragma unroll
+    for (int r = 3; r >= 0; --r) {
+      const uint64_t m = __builtin_amdgcn_ballot_w64(Ur[r] > 0);
+      if (m != 0) s_first = 64 * r + __builtin_ctzll(m);
+    }
+  }
   // group word of sequence sq (< 256), wave-uniform
   auto info_of = [&](int sq) -> uint32_t {
     const int r = sq >> 6;
@@ -439,6 +460,7 @@ decode_stream_kernel(StreamArgs a,
       L[r] = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(lens_rsrc, (s0 + 64 * r + lane) * 4, 0, 0));
     T += round_blocks(s0, L);
   }
+  const int Tg = T;                                       // tiles of one KV head
   T *= hkv;
   const int per = (T + a.num_waves - 1) / a.num_waves;
   const int t_begin = w * per;
@@ -446,18 +468,22 @@ decode_stream_kernel(StreamArgs a,
 
   // ---- 2. the segment and block of tile t_begin: the first sequence whose
   // inclusive tile prefix passes t_begin
+  // (head-major: the head of tile t_begin, then the segment inside its
+  // block of Tg tiles)
   int s_cur = -1, off = 0, L_cur = 0, U_cur = 0, seg0 = 0;
+  const int g_hm = hmaj ? t_begin / Tg : 0;
+  const int tgt = t_begin - g_hm * Tg;
   {
     int base = 0;
     auto scan64 = [&](int s0, int L, int U) {
-      const int c = hkv * (kGrp ? U : tiles_of(L));
+      const int c = hmaj ? U : hkv * (kGrp ? U : tiles_of(L));
       const int incl = wave_incl_scan(c);
-      const uint64_t m = __builtin_amdgcn_ballot_w64(base + incl > t_begin);
+      const uint64_t m = __builtin_amdgcn_ballot_w64(base + incl > tgt);
       if (m != 0) {
         const int l0 = __builtin_ctzll(m);
         s_cur = s0 + l0;
         const int excl = base + readlane_i(incl, l0) - readlane_i(c, l0);
-        off = t_begin - excl;
+        off = tgt - excl;
         L_cur = readlane_i(L, l0);
         U_cur = readlane_i(U, l0);
         seg0 = excl;
@@ -476,8 +502,8 @@ decode_stream_kernel(StreamArgs a,
   // tile t_begin is block j0 of KV head g0 of sequence s_cur (kGrp: tile j0
   // of the segment s_cur starts)
   const int nb0 = kGrp ? U_cur : tiles_of(L_cur);
-  const int g0 = off / nb0;
-  const int j0 = first_blk(L_cur) + (off - g0 * nb0);
+  const int g0 = hmaj ? g_hm : off / nb0;
+  const int j0 = first_blk(L_cur) + (off - (hmaj ? 0 : g0) * nb0);
   const int n_total = min(per, T - t_begin);
 
   // q of a segment travels with each ring slot, loaded straight into the
@@ -537,7 +563,7 @@ decode_stream_kernel(StreamArgs a,
   __shared__ __align__(16) char s_p_all[kWavesPerGroup][2 * kSlotBytesMax];
   char* s_p = s_p_all[wig];
   int w_s = s_cur, w_g = g0, w_j = j0, w_L = L_cur, w_nb = kGrp ? U_cur : (L_cur + kTile - 1) / kTile;
-  int w_jf = first_blk(L_cur), w_seg = seg0 + g0 * nb0;
+  int w_jf = first_blk(L_cur), w_seg = hmaj ? g_hm * Tg + seg0 : seg0 + g0 * nb0;
   // The first chunk token's window starts at L - T + 1 - W; a row of chunk
   // token t starts t later.  Code = that start relative to the segment's
   // first block, clamped at -16 (rows then cut nothing), plus 17: 1..32.
@@ -926,7 +952,17 @@ decode_stream_kernel(StreamArgs a,
         w_j += span;
         if (w_j == w_nb) {                                   // next segment
           w_seg += w_nb;
-          if (++w_g == hkv) {                                // next segment-starting sequence
+          if (hmaj) {                                        // the head's next sequence, then the next head
+            do {
+              w_s += seg_count(w_s);
+              w_nb = (w_s < B) ? ut_of(w_s) : 0;
+            } while (w_nb == 0 && w_s < B);
+            if (w_s >= B && ++w_g < hkv) {
+              w_s = s_first;
+              w_nb = ut_of(s_first);
+            }
+            w_L = (w_s < B) ? len_of(w_s) : 0;
+          } else if (++w_g == hkv) {                         // next segment-starting sequence
             w_g = 0;
             do {
               w_s += seg_count(w_s);
@@ -1368,6 +1404,7 @@ constexpr int kMaxGroups = PA_MAX_PREFIX_GROUPS;   // groups travel in the kerne
 constexpr int kPrefixWaves = 8;            // 16-row blocks per workgroup, one per wave
 constexpr int kPrefixRows = 16 * kPrefixWaves;
 constexpr int kPrefixTilesPerStep = 2;     // tiles loaded and run between barriers
+static_assert(kPrefixTilesPerStep % 2 == 0, "P.V takes the tiles of a step in pairs");
 constexpr int kMaxSplits = 8;
 
 struct PrefixGroups {
@@ -1577,7 +1614,9 @@ shared_prefix_kernel(PrefixArgs a) {
   __shared__ uint32_t s_tile[kIdCap];
   __shared__ __align__(16) char s_lds[2 * kStage];
 
-  float m_ref = kNoMax, l_part = 0.f;
+  float m_ref = kNoMax;
+  f32x4_t lacc = {0.f, 0.f, 0.f, 0.f};                   // the exponent sum, in every element
+  const bf16x8_t ones8 = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
   f32x4_t oacc[kVC];
 #pragma unroll
   for (int c = 0; c < kVC; ++c) oacc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -1635,78 +1674,112 @@ shared_prefix_kernel(PrefixArgs a) {
         }
       }
     };
-    auto compute = [&](const char* tl, int e, bool live) {
-      const int hi = live ? lim : 0;                              // positions below hi count
-      const char* sk = tl + row * kPitch + 8 * quad * kE;
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    // One step's tiles against the wave's 16 rows.  The logits of every
+    // tile are independent MFMA chains; the running max is checked once per
+    // step; then O^T += V^T P^T takes a pair of tiles (32 positions) per
+    // MFMA, K index 8 quad + e standing for position 4 quad + e of the
+    // pair's first tile (e < 4) or 4 quad + e - 4 of its second, which is
+    // how the logits' accumulator already holds them (lane (row, quad):
+    // positions 4 quad .. +3 of row `row`).  The exponent sum runs on the
+    // same pipe, against an all-ones operand, over the rounded weights.
+    // live: tiles of the step inside the walk (the rest are masked).
+    auto compute_step = [&](const char* stg, int e0, int live) {
+      constexpr int kT = kPrefixTilesPerStep;
+      f32x4_t acc[kT];
+#pragma unroll
+      for (int tx = 0; tx < kT; ++tx) acc[tx] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < kKK; ++kk) {
-        bf16x8_t kb;
-        if constexpr (kFp8) {
-          const u32x2_t wv2 = *reinterpret_cast<const u32x2_t*>(sk + 32 * kk);
-          const int w0 = static_cast<int>(wv2[0]), w1 = static_cast<int>(wv2[1]);
-          const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
-          const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
-          const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
-          const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
-          kb = bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-        } else {
-          kb = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(sk + 64 * kk));
+#pragma unroll
+        for (int tx = 0; tx < kT; ++tx) {
+          const char* sk = stg + tx * kTileLds + row * kPitch + 8 * quad * kE;
+          bf16x8_t kb;
+          if constexpr (kFp8) {
+            const u32x2_t wv2 = *reinterpret_cast<const u32x2_t*>(sk + 32 * kk);
+            const int w0 = static_cast<int>(wv2[0]), w1 = static_cast<int>(wv2[1]);
+            const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+            const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+            const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+            const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+            kb = bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+          } else {
+            kb = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(sk + 64 * kk));
+          }
+          acc[tx] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qa[kk], acc[tx], 0, 0, 0);
         }
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qa[kk], acc, 0, 0, 0);
       }
       // positions at or past a row's end are masked, where any lane has one
-      const int p0 = kTile * (c0 + e) + 4 * quad;                  // position of acc[0]
-      if (__builtin_amdgcn_ballot_w64(p0 + 3 >= hi) != 0) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] = p0 + r < hi ? acc[r] : -INFINITY;
+      for (int tx = 0; tx < kT; ++tx) {
+        const int hi = tx < live ? lim : 0;                       // positions below hi count
+        const int p0 = kTile * (c0 + e0 + tx) + 4 * quad;         // position of acc[tx][0]
+        if (__builtin_amdgcn_ballot_w64(p0 + 3 >= hi) != 0) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[tx][r] = p0 + r < hi ? acc[tx][r] : -INFINITY;
+        }
       }
       // the scale is positive: the largest logit is the scale times the
       // largest product, and each weight is exp2(fma(product, scale, -max))
-      const float xm = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])) * a.logit_scale;
+      float xm = -INFINITY;
+#pragma unroll
+      for (int tx = 0; tx < kT; ++tx)
+        xm = fmaxf(xm, fmaxf(fmaxf(acc[tx][0], acc[tx][1]), fmaxf(acc[tx][2], acc[tx][3])));
+      xm *= a.logit_scale;
       if (__builtin_amdgcn_ballot_w64(xm > m_ref + kRescaleSlack) != 0) {
         float mt = xm;
         mt = fmaxf(mt, __shfl_xor(mt, 16));
         mt = fmaxf(mt, __shfl_xor(mt, 32));
         const float mn = (mt > m_ref + kRescaleSlack) ? mt : m_ref;
         const float alpha = __builtin_amdgcn_exp2f(m_ref - mn);
-        l_part *= alpha;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) lacc[r] *= alpha;
 #pragma unroll
         for (int c = 0; c < kVC; ++c)
 #pragma unroll
           for (int r = 0; r < 4; ++r) oacc[c][r] *= alpha;
         m_ref = mn;
       }
-      bf16x4_t pb;
+      bf16x4_t pb[kT];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pb[r] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(acc[r], a.logit_scale, -m_ref)));
-        l_part += static_cast<float>(pb[r]);
-      }
-      const char* tv = tl + kTile * kPitch;                         // V rows
-      // bf16: one transposing LDS read per MFMA.  Within each 16 lanes it
-      // hands lane i, element k, element i mod 4 of the 8 bytes that lane
-      // 4k + i/4 addressed; lane (row, quad) addresses token 4 quad + row/4,
-      // dims 16c + 4 (row mod 4) .. +3, so it receives tokens 4 quad .. +3
-      // of dim 16c + row, the A operand of O^T += V^T P^T.
-      const char* vtr = tv + (4 * quad + (row >> 2)) * kVPitch + 8 * (row & 3);
-      const char* vsrc = tv + 4 * quad * kVPitch + row * kE;       // fp8: token 4*quad, dim `row`
+      for (int tx = 0; tx < kT; ++tx)
 #pragma unroll
-      for (int c = 0; c < kVC; ++c) {
-        u32x2_t vw;
-        if constexpr (kFp8) {
-          const char* p = vsrc + 16 * c;
-          const uint32_t b0 = static_cast<uint8_t>(p[0]), b1 = static_cast<uint8_t>(p[kVPitch]);
-          const uint32_t b2 = static_cast<uint8_t>(p[2 * kVPitch]), b3 = static_cast<uint8_t>(p[3 * kVPitch]);
-          const int w4 = static_cast<int>(b0 | (b1 << 8) | (b2 << 16) | (b3 << 24));
-          vw[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w4, 1.0f, false));
-          vw[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w4, 1.0f, true));
-        } else {
-          vw = lds_read_tr16(vtr + 32 * c);
+        for (int r = 0; r < 4; ++r)
+          pb[tx][r] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(acc[tx][r], a.logit_scale, -m_ref)));
+#pragma unroll
+      for (int pr = 0; pr < kT / 2; ++pr) {
+        const bf16x8_t pp = {pb[2 * pr][0], pb[2 * pr][1], pb[2 * pr][2], pb[2 * pr][3],
+                             pb[2 * pr + 1][0], pb[2 * pr + 1][1], pb[2 * pr + 1][2], pb[2 * pr + 1][3]};
+        lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, pp, lacc, 0, 0, 0);
+        // V rows of both tiles.  bf16: one transposing LDS read per tile and
+        // dim block; within each 16 lanes it hands lane i, element k,
+        // element i mod 4 of the 8 bytes that lane 4k + i/4 addressed; lane
+        // (row, quad) addresses position 4 quad + row/4, dims 16c +
+        // 4 (row mod 4) .. +3, so it receives positions 4 quad .. +3 of dim
+        // 16c + row.  fp8: the same positions gathered a byte at a time.
+        const char* tv0 = stg + (2 * pr) * kTileLds + kTile * kPitch;
+        const char* tv1 = tv0 + kTileLds;
+#pragma unroll
+        for (int c = 0; c < kVC; ++c) {
+          u32x2_t v0, v1;
+          if constexpr (kFp8) {
+            auto gather = [&](const char* tv) -> u32x2_t {
+              const char* p = tv + 4 * quad * kVPitch + row + 16 * c;
+              const uint32_t b0 = static_cast<uint8_t>(p[0]), b1 = static_cast<uint8_t>(p[kVPitch]);
+              const uint32_t b2 = static_cast<uint8_t>(p[2 * kVPitch]), b3 = static_cast<uint8_t>(p[3 * kVPitch]);
+              const int w4 = static_cast<int>(b0 | (b1 << 8) | (b2 << 16) | (b3 << 24));
+              return u32x2_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w4, 1.0f, false)),
+                             __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w4, 1.0f, true))};
+            };
+            v0 = gather(tv0);
+            v1 = gather(tv1);
+          } else {
+            const int tr = (4 * quad + (row >> 2)) * kVPitch + 8 * (row & 3) + 32 * c;
+            v0 = lds_read_tr16(tv0 + tr);
+            v1 = lds_read_tr16(tv1 + tr);
+          }
+          const u32x4_t vv = {v0[0], v0[1], v1[0], v1[1]};
+          oacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vv), pp, oacc[c], 0, 0, 0);
         }
-        oacc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, vw),
-                                                           __builtin_bit_cast(s16x4_t, pb),
-                                                           oacc[c], 0, 0, 0);
       }
     };
     // step i: registers (slot i mod kRing) -> LDS stage i mod 2 -> MFMA.
@@ -1730,16 +1803,12 @@ shared_prefix_kernel(PrefixArgs a) {
         issue(k, i + kRing);
         lds_barrier();
         const int e0 = kPrefixTilesPerStep * (i < nsteps ? step_at(i) : 0);
-#pragma unroll
-        for (int tx = 0; tx < kPrefixTilesPerStep; ++tx)
-          compute(stg + tx * kTileLds, e0 + tx, i < nsteps && e0 + tx < n);
+        compute_step(stg, e0, i < nsteps ? min(kPrefixTilesPerStep, n - e0) : 0);
       }
     }
   }
 
-  float l_tot = l_part;
-  l_tot += __shfl_xor(l_tot, 16);
-  l_tot += __shfl_xor(l_tot, 32);
+  const float l_tot = lacc[0];
   const int64_t row_off = (static_cast<int64_t>(s) * hq + g * G + h) * kRec;
   if (a.splits == 1) {
     if (row_ok) {
@@ -1986,15 +2055,24 @@ void launch_stream(bool fp8, bool pair, int nw, hipStream_t st, const StreamArgs
   }
 }
 
-// The same with shared-prefix groups decoded in the one launch.
+// The same with shared-prefix groups decoded in the one launch.  In the
+// head-major order the KV heads of one group run on neighbouring waves of
+// one XCD, so its prefix tiles are read with the default policy and stay
+// in that XCD's L2 for the next head; otherwise the loads are streamed.
 template <int kD>
 void launch_stream_groups(bool fp8, int nw, hipStream_t st, const StreamArgs& a,
                           const GroupTable& gt, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
   const dim3 grid(nw / kWavesPerGroup), block(64 * kWavesPerGroup);
-  if (fp8)
+  if (a.head_major) {
+    if (fp8)
+      launch_k(decode_stream_kernel<kD, true, 0, false, true>, grid, block, kPadLds, st, e0, e1, a, gt);
+    else
+      launch_k(decode_stream_kernel<kD, false, 0, false, true>, grid, block, kPadLds, st, e0, e1, a, gt);
+  } else if (fp8) {
     launch_k(decode_stream_kernel<kD, true, kAuxNonTemporal, false, true>, grid, block, kPadLds, st, e0, e1, a, gt);
-  else
+  } else {
     launch_k(decode_stream_kernel<kD, false, kAuxNonTemporal, false, true>, grid, block, kPadLds, st, e0, e1, a, gt);
+  }
 }
 
 }  // namespace
@@ -2208,6 +2286,7 @@ pa_status attend(const char* fn, const pa_cache_desc* c, const void* k_cache,
     a.causal = 1;
     a.rec_out = nullptr;
     a.rec_count = nullptr;
+    a.head_major = 0;
     // one pass per tpp chunk tokens; each pass leaves the counters zeroed
     for (int t0 = 0; t0 < T; t0 += tpp) {
       a.t_first = t0;
@@ -2558,22 +2637,36 @@ extern "C" pa_status pa_decode_shared_prefix(
   pa.grp_lens = nullptr;
   pa.grp_count = nullptr;
   const bool fp8 = c->cache_dtype == PA_FP8_E4M3;
-  if (max_count * G <= kMaxRows && num_seqs <= 256 &&
-      static_cast<uint32_t>(max_shared) <= kGrpMaxShared) {
-    // Small groups, at most 256 sequences: one launch of the decode kernel
-    // in which each (group, KV head) is one segment -- the prefix tiles,
-    // then every member's own tiles -- with all members' rows (kGrp).
+  // rows of a group of a KV head that fit one 16-row MFMA block
+  const int msub = std::max(1, kMaxRows / G);
+  const bool split_groups = max_count > msub;
+  if (num_seqs <= 256 && static_cast<uint32_t>(max_shared) <= kGrpMaxShared) {
+    // At most 256 sequences: one launch of the decode kernel in which each
+    // (group, KV head) is one segment -- the prefix tiles, then every
+    // member's own tiles -- with all members' rows (kGrp).  A group with
+    // more rows than 16 is split into row groups of msub members, each a
+    // segment over the shared prefix; the tile list is then ordered by KV
+    // head first so that the row groups of one head, which read the same
+    // prefix tiles, run on one XCD and find them in its L2.
     GroupTable gtab{};
     int64_t tiles = 0;
+    int rows_max = 0;
     for (int i = 0; i < num_groups; ++i) {
       const int f = groups[3 * i], n = groups[3 * i + 1];
       const uint32_t sh = static_cast<uint32_t>(groups[3 * i + 2]) << 11;
-      for (int m = 0; m < n; ++m)
-        gtab.info[f + m] = kGrpMember | sh | (m == 0 ? kGrpLeader | (static_cast<uint32_t>(n) << 2) : 0u);
+      for (int b0 = 0; b0 < n; b0 += msub) {
+        const int nn = std::min(msub, n - b0);
+        rows_max = std::max(rows_max, nn * G);
+        for (int m = 0; m < nn; ++m)
+          gtab.info[f + b0 + m] =
+              kGrpMember | sh | (m == 0 ? kGrpLeader | (static_cast<uint32_t>(nn) << 2) : 0u);
+      }
     }
     tiles = static_cast<int64_t>(hkv) * num_seqs * ((static_cast<int64_t>(max_context_len) + kTile - 1) / kTile);
     const int64_t waves_max = static_cast<int64_t>(device_cus()) * kWavesPerCU;
-    const int64_t nw = std::max<int64_t>(1, std::min(waves_max, (tiles + kMinTilesPerWave - 1) / kMinTilesPerWave));
+    int64_t nw = std::max<int64_t>(1, std::min(waves_max, (tiles + kMinTilesPerWave - 1) / kMinTilesPerWave));
+    const bool head_major = split_groups && nw >= 8;
+    if (head_major) nw = nw / 8 * 8;                       // XCD-major wave order needs whole rounds
     StreamArgs a;
     a.k_cache = pa.k_cache;
     a.v_cache = pa.v_cache;
@@ -2596,7 +2689,7 @@ extern "C" pa_status pa_decode_shared_prefix(
     a.prefix_len = nullptr;
     a.prefix_rec = nullptr;
     a.t_first = 0;
-    a.rows = G * max_count;
+    a.rows = rows_max;
     a.logit_scale = pa.logit_scale;
     a.v_scale = (c->cache_dtype == PA_FP8_E4M3) ? c->v_scale : 1.f;
     a.q_seq_rows = 1;
@@ -2604,6 +2697,7 @@ extern "C" pa_status pa_decode_shared_prefix(
     a.causal = 0;
     a.rec_out = nullptr;
     a.rec_count = nullptr;
+    a.head_major = head_major ? 1 : 0;
     if (D == 128) launch_stream_groups<128>(fp8, a.num_waves, hs, a, gtab);
     else launch_stream_groups<64>(fp8, a.num_waves, hs, a, gtab);
     return launch_status(fn);
@@ -2656,6 +2750,7 @@ extern "C" pa_status pa_decode_shared_prefix(
     a.causal = 0;
     a.rec_out = recs;
     a.rec_count = pa.grp_count;
+    a.head_major = 0;
     if (D == 128) launch_stream<128>(fp8, false, a.num_waves, hs, a);
     else launch_stream<64>(fp8, false, a.num_waves, hs, a);
     st = launch_status(fn);

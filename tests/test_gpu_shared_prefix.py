@@ -118,9 +118,11 @@ def _workloads(seed, Hq, Hkv, D, prefixes, counts, qmax=90):
                                              ("bf16", 64, 64, 32, 2), ("bf16", 16, 64, 4, 4),
                                              ("bf16", 32, 128, 8, 2), ("fp8", 64, 64, 4, 2)])
 def test_shared_prefix_decode_matches_oracle_and_decode(fmt, bs, D, Hq, Hkv):
-    """Groups of 3 and 4 members: with G <= 4 their rows of a KV head fit one
-    16-row block and the prefix takes the group pass through the decode
-    kernel; with G = 8 or 16 it takes the prefix kernel."""
+    """Groups of 3 and 4 members, 10 requests in one launch of the decode
+    kernel: with G <= 4 a group's rows of a KV head fit one 16-row block and
+    each (group, KV head) is one segment; with G = 8 or 16 the groups are cut
+    into row groups of 16 / G members over the same prefix, and the tile
+    stream runs KV head by KV head."""
     ws = _workloads(900 + bs + D, Hq, Hkv, D, (300, 100, 40), (5, 4, 1))
     # two runs that share a prompt, then requests left alone: one that
     # shares the first prompt but is not adjacent to its run, one with a
@@ -149,6 +151,36 @@ def test_shared_prefix_decode_matches_oracle_and_decode(fmt, bs, D, Hq, Hkv):
     none = b.shared(np.zeros((0, 3), np.int32))
     torch.cuda.synchronize()
     assert torch.equal(none.view(torch.int16), plain.view(torch.int16))
+
+
+@pytest.mark.parametrize("fmt,bs,D,Hq", [("bf16", 16, 128, 8), ("fp8", 32, 128, 16),
+                                          ("bf16", 64, 64, 32), ("fp8", 16, 64, 8)])
+def test_large_groups_beyond_256_requests(fmt, bs, D, Hq):
+    """Groups of 6 and 5 members whose rows of a KV head (members x G)
+    exceed 16, beside 260 requests that share nothing: more than 256
+    requests, so the prefix goes through the prefix kernel (each prefix tile
+    shared in LDS by up to 128 rows, position splits merged), then the
+    suffixes through the decode kernel with each row's prefix record folded
+    in.  Against the oracle and pa_decode; repeated calls are bit-identical."""
+    G = Hq // 2
+    ws = _workloads(990 + bs + D, Hq, 2, D, (300, 100), (6, 5), qmax=60)
+    ws.append(workloads.prefix_batch(995, 260, 8, 1, 20, Hq=Hq, Hkv=2, D=D))
+    order = [(0, r) for r in range(6)] + [(1, r) for r in range(5)] + [(2, r) for r in range(260)]
+    b = Batch(ws, order, fmt, bs, 17)
+    assert len(b.groups) == 2 and list(b.groups[:, 1]) == [6, 5] and 5 * G > 16
+    _say(f"large groups {fmt} bs={bs} D={D} G={G} B={b.B}: groups {b.groups.tolist()}")
+    out = b.shared(b.groups)
+    again = b.shared(b.groups)
+    plain = b.plain()
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), again.view(torch.int16))
+    got = out_to_f64(out)
+    ref = b.oracle()
+    par.check(got, ref, fmt, f"large groups beyond 256 requests {fmt} D={D} G={G}",
+              stats=par.value_stats(b.q, "bf16", b.kc_o, b.vc_o, fmt, b.bt, b.cl, ref, b.ks, b.vs))
+    diff = np.abs(got - out_to_f64(plain)).max()
+    _say(f"  max abs diff vs pa_decode {diff:.3e}")
+    assert diff <= TOL[fmt]
 
 
 def test_members_no_longer_than_the_shared_blocks():
