@@ -68,8 +68,9 @@ With ``--prefix`` the batch is 256 requests sharing a 2048-token system
 prompt, each with its own 64..512-token question, built with prefix
 caching (the prompt's blocks are stored once and shared); the step is the
 decode step above, with the block manager's shared-prefix groups and
-pa_decode_shared_prefix (the prompt attended once per KV head for all 256
-requests, then each request's own blocks) unless ``--prefix-path plain``
+pa_decode_shared_prefix (one launch: per KV head, row groups of 4 requests
+each attend the prompt from L2, then their own blocks) unless
+``--prefix-path plain``
 asks for pa_decode over every whole context.  The roofline takes the unique
 KV bytes a call reads (shared blocks once) over the whole call; the logical
 bytes (every sequence's whole context) are reported beside them, with the
@@ -641,8 +642,8 @@ def run_config(args):
         "copy_on_write_pairs": len(pairs),
         "shared_prefix_groups": len(groups),
         "other_path": other,
-        "roofline": {"kernel": ("decode_stream_kernel group pass + suffix pass "
-                                "(pa_decode_shared_prefix)" if cascade else "decode_stream_kernel (pa_decode)" if n != 4 else
+        "roofline": {"kernel": ("decode_stream_kernel in group mode "
+                                "(pa_decode_shared_prefix, one launch)" if cascade else "decode_stream_kernel (pa_decode)" if n != 4 else
                                 "decode_stream_kernel (pa_decode: long contexts split over waves)"),
                      "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None},
@@ -830,8 +831,8 @@ def run_prefix(args):
         "chat_sim": {"hit_rate": round(chat_rate, 4), "queried_blocks": chat_q,
                      "conversations": 64, "turns": 8,
                      "us_per_prompt_lookup": round(lookup_us, 2)},
-        "roofline": {"kernel": ("shared_prefix_prep_kernel + shared_prefix_kernel + "
-                               "decode_stream_kernel (pa_decode_shared_prefix, whole call)"
+        "roofline": {"kernel": ("decode_stream_kernel in group mode, KV head by KV head "
+                               "(pa_decode_shared_prefix, whole call)"
                                if cascade else
                                "decode_stream_kernel (pa_decode over shared prompt blocks)"),
                      "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
