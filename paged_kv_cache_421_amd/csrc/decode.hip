@@ -1065,11 +1065,13 @@ decode_stream_kernel(StreamArgs a,
     // ---- 5. the ring: kNT tiles in flight.  Every step issues the same
     // K and V loads (empty ranges move nothing), so the wait counts the
     // consumer needs never depend on the path taken.  The q rows are read
-    // the same way, except in group mode: its segments run over hundreds of
-    // tiles, so nearly every tile starts no piece and the q loads are
-    // issued only where one starts (3% on a batch of 256 requests sharing a
-    // 2048-token prompt; the plain decode, with short segments, keeps the
-    // unconditional form, 0.5% faster there).
+    // the same way, except in the KV-head-major group launches (the group
+    // launches with the default cache policy, kAux = 0): there the row
+    // groups' segments run over hundreds of tiles, nearly every tile starts
+    // no piece, and the q loads are issued only where one starts (3% on a
+    // batch of 256 requests sharing a 2048-token prompt).  Elsewhere the
+    // branch costs more than the loads it skips (1% on the parallel-sampling
+    // batch in group mode, 0.5% on the plain decode).
     auto issue = [&](int slot, int t) {
       int k_nrec = 0, v_nrec = 0, q_nrec = 0;
       int64_t tile_off = 0, q_off = 0;
@@ -1091,7 +1093,8 @@ decode_stream_kernel(StreamArgs a,
         }
       }
       const __amdgpu_buffer_rsrc_t rq = make_rsrc_uniform(reinterpret_cast<const char*>(a.q), q_off, q_nrec);
-      if (!kGrp || q_nrec > 0) {                           // (q_nrec is wave-uniform)
+      constexpr bool kQAtStartsOnly = kGrp && kAux == 0;
+      if (!kQAtStartsOnly || q_nrec > 0) {                 // (q_nrec is wave-uniform)
 #pragma unroll
         for (int kk = 0; kk < kKK; ++kk) qs[slot][kk] = __builtin_amdgcn_raw_buffer_load_b128(rq, q_lane_off + q_step_off(kk), 0, 0);
       } else {
