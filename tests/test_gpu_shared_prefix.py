@@ -183,6 +183,36 @@ def test_large_groups_beyond_256_requests(fmt, bs, D, Hq):
     assert diff <= TOL[fmt]
 
 
+@pytest.mark.parametrize("fmt,D,Hq,Hkv", [("bf16", 128, 8, 2), ("fp8", 64, 16, 1), ("bf16", 64, 32, 16)])
+def test_row_groups_mixed_with_whole_groups(fmt, D, Hq, Hkv):
+    """Groups of 9, 3 and 5 members beside requests that share nothing, in
+    one launch: a group whose rows of a KV head exceed 16 is cut into row
+    groups of 16 / G members (9 members at G = 4: 4 + 4 + 1), the others stay
+    whole, and the tile stream runs KV head by KV head; one KV head (G = 16,
+    every member its own row group) and 16 KV heads (G = 2).  Against the
+    oracle and pa_decode; repeated calls are bit-identical."""
+    G = Hq // Hkv
+    ws = _workloads(1010 + D + Hq, Hq, Hkv, D, (200, 120, 64), (9, 3, 5), qmax=50)
+    ws.append(workloads.prefix_batch(1015, 4, 8, 1, 20, Hq=Hq, Hkv=Hkv, D=D))
+    order = ([(0, r) for r in range(9)] + [(3, 0), (3, 1)] + [(1, r) for r in range(3)] +
+             [(3, 2)] + [(2, r) for r in range(5)] + [(3, 3)])
+    b = Batch(ws, order, fmt, 16, 21)
+    assert list(b.groups[:, 1]) == [9, 3, 5]
+    _say(f"row groups mixed {fmt} D={D} G={G} Hkv={Hkv}: groups {b.groups.tolist()}")
+    out = b.shared(b.groups)
+    again = b.shared(b.groups)
+    plain = b.plain()
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), again.view(torch.int16))
+    got = out_to_f64(out)
+    ref = b.oracle()
+    par.check(got, ref, fmt, f"row groups mixed with whole groups {fmt} D={D} G={G}",
+              stats=par.value_stats(b.q, "bf16", b.kc_o, b.vc_o, fmt, b.bt, b.cl, ref, b.ks, b.vs))
+    diff = np.abs(got - out_to_f64(plain)).max()
+    _say(f"  max abs diff vs pa_decode {diff:.3e}")
+    assert diff <= TOL[fmt]
+
+
 def test_members_no_longer_than_the_shared_blocks():
     """A group whose shared run covers a member's whole context (its suffix is
     empty) or more (the member sees only its own length of the prefix); a
