@@ -183,22 +183,25 @@ def test_large_groups_beyond_256_requests(fmt, bs, D, Hq):
     assert diff <= TOL[fmt]
 
 
-@pytest.mark.parametrize("fmt,D,Hq,Hkv", [("bf16", 128, 8, 2), ("fp8", 64, 16, 1), ("bf16", 64, 32, 16)])
-def test_row_groups_mixed_with_whole_groups(fmt, D, Hq, Hkv):
+@pytest.mark.parametrize("fmt,D,Hq,Hkv,bs", [("bf16", 128, 8, 2, 16), ("fp8", 64, 16, 1, 16),
+                                             ("bf16", 64, 32, 16, 16), ("bf16", 128, 8, 2, 32),
+                                             ("fp8", 128, 16, 2, 64)])
+def test_row_groups_mixed_with_whole_groups(fmt, D, Hq, Hkv, bs):
     """Groups of 9, 3 and 5 members beside requests that share nothing, in
     one launch: a group whose rows of a KV head exceed 16 is cut into row
     groups of 16 / G members (9 members at G = 4: 4 + 4 + 1), the others stay
     whole, and the tile stream runs KV head by KV head; one KV head (G = 16,
-    every member its own row group) and 16 KV heads (G = 2).  Against the
-    oracle and pa_decode; repeated calls are bit-identical."""
+    every member its own row group) and 16 KV heads (G = 2); blocks of 16,
+    32 and 64 tokens.  Against the oracle and pa_decode; repeated calls are
+    bit-identical."""
     G = Hq // Hkv
     ws = _workloads(1010 + D + Hq, Hq, Hkv, D, (200, 120, 64), (9, 3, 5), qmax=50)
     ws.append(workloads.prefix_batch(1015, 4, 8, 1, 20, Hq=Hq, Hkv=Hkv, D=D))
     order = ([(0, r) for r in range(9)] + [(3, 0), (3, 1)] + [(1, r) for r in range(3)] +
              [(3, 2)] + [(2, r) for r in range(5)] + [(3, 3)])
-    b = Batch(ws, order, fmt, 16, 21)
+    b = Batch(ws, order, fmt, bs, 21)
     assert list(b.groups[:, 1]) == [9, 3, 5]
-    _say(f"row groups mixed {fmt} D={D} G={G} Hkv={Hkv}: groups {b.groups.tolist()}")
+    _say(f"row groups mixed {fmt} D={D} G={G} Hkv={Hkv} bs={bs}: groups {b.groups.tolist()}")
     out = b.shared(b.groups)
     again = b.shared(b.groups)
     plain = b.plain()
